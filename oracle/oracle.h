@@ -1,0 +1,107 @@
+/*
+ * Paged-KV decode oracle -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, fp64 CPU statement of what single-query decode attention over
+ * a paged KV cache computes.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library; the product path never
+ * does.  It shares no code, header or constant with the GPU library.
+ *
+ * Sources (three web pages on PagedAttention):
+ *   [P1] "从正确到更快：PagedAttention 的优化路线"
+ *        (From correct to fast: the PagedAttention optimisation route)
+ *   [P2] "实现教学版 PagedAttention：从 block table 读取历史 KV cache"
+ *        (Implementing a teaching PagedAttention: reading the KV cache through
+ *        the block table)
+ *   [P3] "算子与编译器：推理 Attention 与 KV Kernel"
+ *        (Operators and compilers: inference attention and KV kernels)
+ *
+ * Element encodings (dtype argument): 0 = IEEE binary32, 1 = IEEE binary16,
+ * 2 = bfloat16 (upper half of a binary32).  16-bit elements are passed as their
+ * raw bit patterns.
+ *
+ * Return codes: 0 on success, a negative value when an argument or a table
+ * entry is out of range (the oracle checks device-side contents too, since it
+ * is a checker).
+ */
+#ifndef PKV_ORACLE_H
+#define PKV_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ORACLE_OK 0
+#define ORACLE_ERR_ARG (-1)
+#define ORACLE_ERR_RANGE (-2)
+#define ORACLE_ERR_NOMEM (-3)
+
+/* Decode one stored element to double (exact for all three encodings). */
+double oracle_decode_f16(uint16_t bits);
+double oracle_decode_bf16(uint16_t bits);
+
+/* [P2] section "从逻辑 token 到物理 block": logical token index -> logical
+ * block id -> physical block id, plus the offset inside the block.
+ * block_table has num_table_entries valid entries. */
+int oracle_block_address(const int32_t *block_table, int32_t num_table_entries,
+                         int64_t token_index, int32_t block_size,
+                         int64_t *logical_block_id, int64_t *block_offset,
+                         int64_t *physical_block_id);
+
+/* [P2] section "单个 Sequence 的 paged gather": copy the context_len history
+ * rows of one KV head, in logical token order, out of the paged pool
+ * [num_blocks, block_size, num_kv_heads, head_dim] into contiguous fp64
+ * arrays keys/values [context_len, head_dim]. */
+int oracle_paged_gather(double *keys, double *values,
+                        const void *key_cache, const void *value_cache,
+                        const int32_t *block_table, int32_t num_table_entries,
+                        int32_t context_len, int32_t block_size,
+                        int64_t num_blocks, int32_t num_kv_heads,
+                        int32_t kv_head, int32_t head_dim, int dtype);
+
+/* [P2] section "从 gather 后的 K/V 做 attention" with the score scale of
+ * [P1] section "attention kernel 真正在做什么": one query head against
+ * contiguous fp64 keys/values [context_len, head_dim]:
+ *   scores[t] = scale * dot(q, keys[t]); weights = softmax(scores);
+ *   out = sum_t weights[t] * values[t].
+ * context_len == 0 yields zeros. */
+int oracle_attention(double *out, const double *q, const double *keys,
+                     const double *values, int32_t context_len,
+                     int32_t head_dim, double scale);
+
+/* [P2] section "扩展到 batch：每个 Sequence 都有自己的 block table":
+ * for every sequence, gather its history through its block table and run
+ * standard attention for each query head.  Query head h reads KV head
+ * h / (num_heads / num_kv_heads).
+ *   query  [num_seqs, num_heads, head_dim]            (dtype)
+ *   out    [num_seqs, num_heads, head_dim]            (fp64)
+ *   block_tables [num_seqs, max_blocks_per_seq] int32, context_lens [num_seqs].
+ * num_threads <= 0 uses the OpenMP default. */
+int oracle_paged_decode(double *out, const void *query,
+                        const void *key_cache, const void *value_cache,
+                        const int32_t *block_tables,
+                        const int32_t *context_lens, int32_t num_seqs,
+                        int32_t num_heads, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t block_size,
+                        int32_t max_blocks_per_seq, int64_t num_blocks,
+                        double scale, int dtype, int num_threads);
+
+/* [P2] section "写入 slot 和读取 block table 必须一致": store token i's K/V
+ * rows [num_kv_heads, head_dim] at slot_mapping[i] = physical_block_id *
+ * block_size + block_offset, a byte copy.  Negative slots are skipped; tokens
+ * are applied in index order. */
+int oracle_paged_kv_write(const void *key, const void *value, void *key_cache,
+                          void *value_cache, const int64_t *slot_mapping,
+                          int64_t num_tokens, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t block_size,
+                          int64_t num_blocks, int elem_bytes);
+
+/* Number of OpenMP threads a parallel region of this library would use. */
+int oracle_max_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_ORACLE_H */

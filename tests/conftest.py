@@ -1,0 +1,22 @@
+import os
+import sys
+
+import pytest
+
+REPO = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if REPO not in sys.path:
+    sys.path.insert(0, REPO)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built libpagedkv")
+
+
+@pytest.fixture(scope="session")
+def cuda():
+    """The GPU device; GPU tests skip only where no GPU exists at all."""
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU in this environment")
+    return torch.device("cuda:0")

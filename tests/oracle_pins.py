@@ -1,0 +1,369 @@
+"""Pins of the fp64 oracle to facts that do not come from the oracle itself.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with:
+  - values printed on the pages (the worked block-table mapping, golden file);
+  - a library attention routine (torch scaled_dot_product_attention in fp64,
+    including its grouped-query mode) on a contiguous cache holding the same
+    rows -- the pages' own check ("和连续 KV cache 对齐验证");
+  - closed forms (one token, zero query, equal values, two tokens);
+  - exhaustive element decoding against numpy / torch;
+  - brute force with explicit loops on tiny inputs;
+  - invariances (page relabelling, batch independence).
+
+``python -m tests.oracle_pins --lib PATH`` runs every quick pin against another
+build of oracle.c and exits with the number of pins that failed; the planted
+mistake tests use it on deliberately broken copies.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+import sys
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+REPO = os.path.dirname(HERE)
+if REPO not in sys.path:
+    sys.path.insert(0, REPO)
+
+import oracle  # noqa: E402
+
+GOLDEN = os.path.join(HERE, "golden", "worked_mapping.json")
+
+
+def _golden():
+    with open(GOLDEN, encoding="utf-8") as f:
+        return json.load(f)
+
+
+def _sdpa(q, k, v, scale, enable_gqa=False):
+    """torch's attention in fp64 on the CPU: q [H, D], k/v [T, KVH, D]."""
+    import torch
+    import torch.nn.functional as F
+
+    qt = torch.from_numpy(np.ascontiguousarray(q, dtype=np.float64))[None, :, None, :]
+    kt = torch.from_numpy(np.ascontiguousarray(np.transpose(k, (1, 0, 2)), dtype=np.float64))[None]
+    vt = torch.from_numpy(np.ascontiguousarray(np.transpose(v, (1, 0, 2)), dtype=np.float64))[None]
+    out = F.scaled_dot_product_attention(qt, kt, vt, scale=float(scale), enable_gqa=enable_gqa)
+    return out[0, :, 0, :].numpy()
+
+
+def _scatter(contig, table, block_size, num_blocks, fill=np.nan):
+    """Lay a contiguous [T, KVH, D] history out in pages by a block table
+    (what the allocator plus the prefill writes produce)."""
+    t, kvh, d = contig.shape
+    pool = np.full((num_blocks, block_size, kvh, d), fill, dtype=contig.dtype)
+    for i in range(t):
+        pool[table[i // block_size], i % block_size] = contig[i]
+    return pool
+
+
+# ---------------------------------------------------------------------------
+# mapping
+
+
+def pin_printed_mapping():
+    g = _golden()
+    for row in g["printed_mapping"]:
+        lb, off, pb = oracle.block_address(g["block_table"], row["token"], g["block_size"])
+        assert (pb, off) == (row["physical_block"], row["offset"]), row
+    t5 = g["token5"]
+    assert oracle.block_address(g["block_table"], 5, g["block_size"]) == (
+        t5["logical_block_id"], t5["block_offset"], t5["physical_block_id"])
+
+
+def pin_batch_example_tables():
+    g = _golden()
+    bs = g["block_size"]
+    for seq in g["batch"]:
+        table, ctx = seq["block_table"], seq["context_len"]
+        assert len(table) == -(-ctx // bs), seq  # every table holds exactly ceil(ctx/bs) pages
+        lb, off, pb = oracle.block_address(table, ctx - 1, bs)
+        assert lb == len(table) - 1 and pb == table[-1]
+    # derived by the formulas (not printed): C's token 14 -> block 6 offset 2
+    assert oracle.block_address([8, 5, 3, 6], 14, 4)[1:] == (2, 6)
+
+
+def pin_tagged_gather():
+    """An address-tagged pool reveals which (block, offset, head) each
+    gathered row came from."""
+    g = _golden()
+    bs, nb, kvh, d = g["block_size"], 10, 2, 4
+    tag = np.zeros((nb, bs, kvh, d), np.float32)
+    for pb in range(nb):
+        for off in range(bs):
+            for h in range(kvh):
+                tag[pb, off, h] = [pb, off, h, 1000 * pb + 10 * off + h]
+    for h in range(kvh):
+        keys, values = oracle.paged_gather(tag, -tag, g["block_table"], 9, h, "f32")
+        for row in g["printed_mapping"]:
+            want = [row["physical_block"], row["offset"], h,
+                    1000 * row["physical_block"] + 10 * row["offset"] + h]
+            assert keys[row["token"]].tolist() == want, (h, row)
+            assert (-values[row["token"]]).tolist() == want
+    c = g["token5"]["cache_index"]
+    keys, _ = oracle.paged_gather(tag, tag, g["block_table"], 6, 1, "f32")
+    assert keys[5].tolist() == tag[c[0], c[1], 1].tolist()
+
+
+# ---------------------------------------------------------------------------
+# element decoding
+
+
+def pin_decode_f16_exhaustive():
+    bits = np.arange(65536, dtype=np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = oracle.to_float64(bits, "f16")
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def pin_decode_bf16_exhaustive():
+    import torch
+
+    bits = np.arange(65536, dtype=np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = oracle.to_float64(bits, "bf16")
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+# ---------------------------------------------------------------------------
+# attention
+
+
+def pin_attention_vs_library():
+    rng = np.random.default_rng(11)
+    for t, d in ((1, 4), (5, 4), (37, 64), (300, 64), (64, 128)):
+        q = rng.standard_normal(d)
+        k = rng.standard_normal((t, d))
+        v = rng.standard_normal((t, d))
+        scale = 1.0 / math.sqrt(d)
+        got = oracle.attention(q, k, v, scale)
+        ref = _sdpa(q[None], k[:, None], v[:, None], scale)[0]
+        assert np.max(np.abs(got - ref)) < 1e-12, (t, d)
+    # a different scale is honoured
+    q, k, v = rng.standard_normal(8), rng.standard_normal((9, 8)), rng.standard_normal((9, 8))
+    assert np.max(np.abs(oracle.attention(q, k, v, 0.7) - _sdpa(q[None], k[:, None], v[:, None], 0.7)[0])) < 1e-12
+
+
+def _paged_case(dtype, seed=5):
+    """Contiguous histories, paged by random tables, queries; G = 4."""
+    rng = np.random.default_rng(seed)
+    b, h, kvh, d, bs = 3, 8, 2, 16, 4
+    ctxs = [1, 7, 30]
+    nb = sum(-(-c // bs) for c in ctxs) + 2
+    perm = rng.permutation(nb)
+    tables = np.full((b, 8), nb - 1, np.int32)
+    contig_k, contig_v, pos = [], [], 0
+    kc = np.zeros((nb, bs, kvh, d), np.float64)
+    vc = np.zeros_like(kc)
+    for s, c in enumerate(ctxs):
+        n = -(-c // bs)
+        tables[s, :n] = perm[pos:pos + n]
+        pos += n
+        ck, cv = rng.standard_normal((c, kvh, d)), rng.standard_normal((c, kvh, d))
+        contig_k.append(ck)
+        contig_v.append(cv)
+        for i in range(c):
+            kc[tables[s, i // bs], i % bs] = ck[i]
+            vc[tables[s, i // bs], i % bs] = cv[i]
+    q = rng.standard_normal((b, h, d))
+    enc = {"f32": lambda a: a.astype(np.float32),
+           "f16": lambda a: a.astype(np.float16).view(np.uint16),
+           "bf16": lambda a: _bf16_bits(a)}[dtype]
+    kq, vq, qq = enc(kc), enc(vc), enc(q)
+    # the contiguous reference sees exactly the stored (rounded) values
+    dec = lambda a: oracle.to_float64(a, dtype)  # noqa: E731
+    contig_k = [dec(enc(x)) for x in contig_k]
+    contig_v = [dec(enc(x)) for x in contig_v]
+    return dict(q=qq, kc=kq, vc=vq, tables=tables, ctx=np.array(ctxs, np.int32), bs=bs,
+                contig_k=contig_k, contig_v=contig_v, qd=dec(qq))
+
+
+def _bf16_bits(a):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16).view(
+        torch.int16).numpy().view(np.uint16).copy()
+
+
+def pin_paged_equals_contiguous_gqa():
+    for dtype in ("f32", "f16", "bf16"):
+        c = _paged_case(dtype)
+        scale = float(np.float32(0.25))
+        out = oracle.paged_decode(c["q"], c["kc"], c["vc"], c["tables"], c["ctx"], c["bs"], scale, dtype)
+        for s in range(len(c["ctx"])):
+            ref = _sdpa(c["qd"][s], c["contig_k"][s], c["contig_v"][s], scale, enable_gqa=True)
+            assert np.max(np.abs(out[s] - ref)) < 1e-12, (dtype, s)
+
+
+def pin_closed_forms():
+    rng = np.random.default_rng(3)
+    d = 8
+    # one token: the output is that token's value row, exactly
+    q, k, v = rng.standard_normal(d), rng.standard_normal((1, d)), rng.standard_normal((1, d))
+    assert np.array_equal(oracle.attention(q, k, v, 0.5), v[0])
+    # zero query: uniform weights, the mean of the values
+    k, v = rng.standard_normal((6, d)), rng.standard_normal((6, d))
+    assert np.max(np.abs(oracle.attention(np.zeros(d), k, v, 0.5) - v.mean(axis=0))) < 1e-14
+    # all value rows equal: that row
+    row = rng.standard_normal(d)
+    assert np.max(np.abs(oracle.attention(q, k, np.tile(row, (6, 1)), 0.5) - row)) < 1e-14
+    # two tokens: sigmoid weights
+    k, v = rng.standard_normal((2, d)), rng.standard_normal((2, d))
+    s0, s1 = 0.3 * q @ k[0], 0.3 * q @ k[1]
+    w0 = 1.0 / (1.0 + math.exp(s1 - s0))
+    assert np.max(np.abs(oracle.attention(q, k, v, 0.3) - (w0 * v[0] + (1 - w0) * v[1]))) < 1e-14
+    # empty context: zeros
+    assert np.array_equal(oracle.attention(q, np.zeros((0, d)), np.zeros((0, d)), 0.5), np.zeros(d))
+    # one overwhelming score picks its row
+    k = np.zeros((5, d))
+    k[3] = 400.0 * q / np.linalg.norm(q)
+    v = rng.standard_normal((5, d))
+    assert np.max(np.abs(oracle.attention(q, k, v, 1.0) - v[3])) < 1e-12
+
+
+def pin_brute_force_tiny():
+    """Explicit loops over a tiny paged batch (B=2, H=2, KVH=1, D=4, bs=4)."""
+    rng = np.random.default_rng(17)
+    bs, kvh, d, h = 4, 1, 4, 2
+    for ctx in (1, 3, 4, 5, 9):
+        nb = 6
+        kc = rng.standard_normal((nb, bs, kvh, d)).astype(np.float32)
+        vc = rng.standard_normal((nb, bs, kvh, d)).astype(np.float32)
+        tables = np.array([[5, 0, 3], [1, 4, 2]], np.int32)
+        q = rng.standard_normal((2, h, d)).astype(np.float32)
+        lens = np.array([ctx, max(1, ctx - 2)], np.int32)
+        got = oracle.paged_decode(q, kc, vc, tables, lens, bs, 0.5, "f32")
+        for s in range(2):
+            for head in range(h):
+                sc = []
+                for t in range(int(lens[s])):
+                    blk, off = int(tables[s][t // bs]), t % bs
+                    sc.append(0.5 * sum(float(q[s, head, i]) * float(kc[blk, off, 0, i]) for i in range(d)))
+                mx = max(sc)
+                e = [math.exp(x - mx) for x in sc]
+                z = sum(e)
+                for i in range(d):
+                    ref = 0.0
+                    for t in range(int(lens[s])):
+                        blk, off = int(tables[s][t // bs]), t % bs
+                        ref += e[t] / z * float(vc[blk, off, 0, i])
+                    assert abs(got[s, head, i] - ref) < 1e-12, (ctx, s, head, i)
+
+
+def pin_invariances():
+    c = _paged_case("f32", seed=9)
+    base = oracle.paged_decode(c["q"], c["kc"], c["vc"], c["tables"], c["ctx"], c["bs"], 0.25, "f32")
+    # relabel physical pages (pool and tables together): bitwise identical
+    nb = c["kc"].shape[0]
+    perm = np.random.default_rng(1).permutation(nb)
+    inv = np.empty_like(perm)
+    inv[perm] = np.arange(nb)
+    kc2, vc2 = np.ascontiguousarray(c["kc"][inv]), np.ascontiguousarray(c["vc"][inv])
+    tables2 = perm[c["tables"]].astype(np.int32)
+    out2 = oracle.paged_decode(c["q"], kc2, vc2, tables2, c["ctx"], c["bs"], 0.25, "f32")
+    assert np.array_equal(base, out2)
+    # a sequence's output does not depend on the rest of the batch
+    one = oracle.paged_decode(np.ascontiguousarray(c["q"][2:3]), c["kc"], c["vc"],
+                              np.ascontiguousarray(c["tables"][2:3]), c["ctx"][2:3], c["bs"], 0.25, "f32")
+    assert np.array_equal(one[0], base[2])
+
+
+def pin_sensitivity():
+    """Pointing a table entry at another sequence's page, or changing a length,
+    changes the output (a wrong table or length must not go unnoticed).
+    Reordering a sequence's own full pages would not: attention does not
+    depend on the order of the history, which is why the tagged gather pins
+    the order separately."""
+    c = _paged_case("f32", seed=4)
+    base = oracle.paged_decode(c["q"], c["kc"], c["vc"], c["tables"], c["ctx"], c["bs"], 0.25, "f32")
+    t2 = c["tables"].copy()
+    t2[2, 1] = c["tables"][1, 0]
+    out = oracle.paged_decode(c["q"], c["kc"], c["vc"], t2, c["ctx"], c["bs"], 0.25, "f32")
+    assert np.max(np.abs(out[2] - base[2])) > 1e-3
+    ctx2 = c["ctx"].copy()
+    ctx2[1] -= 1
+    out = oracle.paged_decode(c["q"], c["kc"], c["vc"], c["tables"], ctx2, c["bs"], 0.25, "f32")
+    assert np.max(np.abs(out[1] - base[1])) > 1e-3
+
+
+# ---------------------------------------------------------------------------
+# slot write
+
+
+def pin_write():
+    g = _golden()
+    bs, nb, kvh, d = g["block_size"], 10, 2, 4
+    kc = np.zeros((nb, bs, kvh, d), np.float32)
+    vc = np.zeros_like(kc)
+    # the slot of token 5 of table [7, 2, 9] is (2, 1): flat 2 * 4 + 1
+    key = np.arange(kvh * d, dtype=np.float32).reshape(1, kvh, d) + 1
+    val = -key
+    c = g["token5"]["cache_index"]
+    oracle.paged_kv_write(key, val, kc, vc, np.array([c[0] * bs + c[1]], np.int64))
+    assert np.array_equal(kc[2, 1], key[0]) and np.array_equal(vc[2, 1], val[0])
+    assert np.count_nonzero(kc) == kvh * d  # nothing else touched
+    # written row reads back at the token's logical position
+    keys, values = oracle.paged_gather(kc, vc, g["block_table"], 6, 1, "f32")
+    assert np.array_equal(keys[5], key[0, 1]) and np.array_equal(values[5], val[0, 1])
+    # negative slots are skipped; 16-bit rows are copied bit for bit
+    bits = np.array([[[0x7E01, 0xFFFF, 0x0001, 0x8000]]], np.uint16)
+    kc16 = np.zeros((4, 4, 1, 4), np.uint16)
+    vc16 = np.zeros_like(kc16)
+    oracle.paged_kv_write(np.concatenate([bits, bits]), np.concatenate([bits, bits]), kc16, vc16,
+                          np.array([-1, 13], np.int64))
+    assert np.array_equal(kc16[3, 1], bits[0]) and np.count_nonzero(kc16) == 4
+
+
+QUICK_PINS = [
+    pin_printed_mapping,
+    pin_batch_example_tables,
+    pin_tagged_gather,
+    pin_decode_f16_exhaustive,
+    pin_decode_bf16_exhaustive,
+    pin_attention_vs_library,
+    pin_paged_equals_contiguous_gqa,
+    pin_closed_forms,
+    pin_brute_force_tiny,
+    pin_invariances,
+    pin_sensitivity,
+    pin_write,
+]
+
+
+def run_all(lib_path: str | None = None) -> list[str]:
+    """Names of the pins that fail (against ``lib_path`` if given)."""
+    failed = []
+
+    def go():
+        for pin in QUICK_PINS:
+            try:
+                pin()
+            except Exception as e:  # noqa: BLE001 -- any failure counts
+                failed.append(f"{pin.__name__}: {type(e).__name__}")
+
+    if lib_path is None:
+        go()
+    else:
+        with oracle.using_library(lib_path):
+            go()
+    return failed
+
+
+if __name__ == "__main__":
+    import argparse
+
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--lib", default=None)
+    args = ap.parse_args()
+    bad = run_all(args.lib)
+    for b in bad:
+        print("FAILED", b)
+    sys.exit(min(len(bad), 100))
