@@ -1,0 +1,305 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark for paged-KV decode attention on one MI355X.
+
+A step is one pass of the whole hot path over one decode batch: the slot
+write of each sequence's new K/V (paged_kv_write) followed by the fused paged
+decode attention (paged_decode_attention, plus its log-sum-exp merge when the
+context is split).  Inputs are seeded synthetic batches (see
+paged_kv_decode_13_amd/workloads.py) uploaded to HBM before the timed region.
+
+Prints ONE JSON line on stdout.  ``value`` is the effective KV-read bandwidth
+of the whole step: sum(ctx) * num_kv_heads * head_dim * 2 * bytes / step time.
+``roofline`` rates the decode call alone (HIP events on the launch stream)
+against the 8 TB/s HBM peak.  ``cpu_baseline`` is the fp64 oracle timed on a
+bounded sample of the same batch on the host cores.
+
+Usage: python bench.py [--steps K] [--warmup W] [--config gqa_bf16]
+       python bench.py --mode copy  (plain device copy, for counter scaling)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+REPO = os.path.dirname(os.path.abspath(__file__))
+if REPO not in sys.path:
+    sys.path.insert(0, REPO)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published
+METRIC = "effective KV-read HBM GB/s (% of MI355X peak) + decode tokens/s, paged attention"
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(REPO, "paged_kv_decode_13_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM bytes per decode launch measured by rocprofv3 counters, if they were
+    taken on the current kernel sources (else None)."""
+    path = os.path.join(REPO, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_digest") != source_digest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def upload(batch, dev):
+    import torch
+
+    from paged_kv_decode_13_amd import workloads as wl
+
+    t = {
+        "q": wl.torch_view(batch.query, batch.dtype).to(dev),
+        "kc": wl.torch_view(batch.key_cache, batch.dtype).to(dev),
+        "vc": wl.torch_view(batch.value_cache, batch.dtype).to(dev),
+        "bt": torch.from_numpy(batch.block_tables).to(dev),
+        "cl": torch.from_numpy(batch.context_lens).to(dev),
+    }
+    if batch.slot_mapping is not None:
+        t["nk"] = wl.torch_view(batch.new_key, batch.dtype).to(dev)
+        t["nv"] = wl.torch_view(batch.new_value, batch.dtype).to(dev)
+        t["slots"] = torch.from_numpy(batch.slot_mapping).to(dev)
+    return t
+
+
+def time_steps(batch, t, partition_size: int, steps: int, warmup: int):
+    import torch
+
+    import paged_kv_decode_13_amd as pkv
+
+    out = torch.empty((batch.num_seqs, batch.num_heads, batch.head_dim), dtype=t["q"].dtype,
+                      device=t["q"].device)
+    need = pkv.paged_decode_workspace_size(batch.num_seqs, batch.num_heads, batch.head_dim,
+                                           batch.max_context_len, partition_size)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=t["q"].device)
+    has_write = "slots" in t
+
+    def write():
+        if has_write:
+            pkv.paged_kv_write(t["nk"], t["nv"], t["kc"], t["vc"], t["slots"])
+
+    def decode():
+        pkv.paged_decode_attention(t["q"], t["kc"], t["vc"], t["bt"], t["cl"], batch.block_size,
+                                   batch.scale, max_context_len=batch.max_context_len,
+                                   partition_size=partition_size, out=out, workspace=ws)
+
+    for _ in range(warmup):
+        write()
+        decode()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for e in evs:
+        e[0].record()
+        write()
+        e[1].record()
+        decode()
+        e[2].record()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = [e[0].elapsed_time(e[2]) for e in evs]
+    write_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    decode_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    return {
+        "ms_per_step": start.elapsed_time(end) / steps,
+        "wall_ms_per_step": 1e3 * wall / steps,
+        "write_ms": statistics.mean(write_ms),
+        "decode_ms": statistics.mean(decode_ms),
+        "decode_ms_median": statistics.median(decode_ms),
+        "step_ms_p99": sorted(step_ms)[min(len(step_ms) - 1, int(0.99 * len(step_ms)))],
+        "out": out,
+    }
+
+
+def cpu_baseline(batch, target_s: float):
+    """The oracle, untouched, on an evenly spaced sample of the batch's
+    sequences sized to about ``target_s`` seconds of host work."""
+    import numpy as np
+
+    import oracle
+    from paged_kv_decode_13_amd import workloads as wl
+
+    order = np.arange(batch.num_seqs)
+    probe = wl.subset(batch, order[:: max(1, batch.num_seqs // 8)])
+    t0 = time.perf_counter()
+    oracle.paged_decode(probe.query, probe.key_cache, probe.value_cache, probe.block_tables,
+                        probe.context_lens, probe.block_size, probe.scale, probe.dtype)
+    probe_s = max(time.perf_counter() - t0, 1e-3)
+    frac = min(1.0, target_s / probe_s * probe.total_tokens / batch.total_tokens)
+    step = max(1, int(round(1.0 / frac))) if frac < 1.0 else 1
+    sample = wl.subset(batch, order[::step])
+    t0 = time.perf_counter()
+    oracle.paged_decode(sample.query, sample.key_cache, sample.value_cache, sample.block_tables,
+                        sample.context_lens, sample.block_size, sample.scale, sample.dtype)
+    secs = time.perf_counter() - t0
+    return {
+        "value": round(sample.kv_bytes_logical() / secs / 1e9, 4),
+        "unit": "GB/s",
+        "cores": oracle.max_threads(),
+        "kind": "oracle",
+        "sample": (f"every {step}th sequence of the same batch: {sample.num_seqs} sequences, "
+                   f"{sample.total_tokens} context tokens, fp64 gather + softmax attention, "
+                   f"{secs:.2f} s"),
+        "tokens_per_s": round(sample.num_seqs / secs, 3),
+    }
+
+
+def run_copy(size_mb: int, steps: int) -> None:
+    """A plain device-to-device copy of known size (counter calibration)."""
+    import torch
+
+    n = size_mb * (1 << 20)
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"mode": "copy", "bytes_read_per_copy": n, "bytes_written_per_copy": n,
+                      "copies": steps}), flush=True)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="gqa_bf16")
+    ap.add_argument("--block-size", type=int, default=None, help="prefix_fp16 only")
+    ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--sweep-partitions", default=None,
+                    help="comma list of partition sizes to time as well (stderr report)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--mode", default="decode", choices=["decode", "copy"])
+    ap.add_argument("--copy-mb", type=int, default=1024)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures the decode path on one GPU; --gpus {args.gpus} is not "
+              "supported (there is no multi-GPU path in this library).", file=sys.stderr)
+        return 2
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs as a single process on one GPU.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    if args.mode == "copy":
+        run_copy(args.copy_mb, args.steps)
+        return 0
+
+    import paged_kv_decode_13_amd as pkv
+    from paged_kv_decode_13_amd import workloads as wl
+
+    if not os.path.exists(pkv.library_path()):
+        from paged_kv_decode_13_amd import build
+
+        build.build()
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    batch = wl.make_config(args.config, block_size=args.block_size)
+    log(f"[bench] {args.config}: {batch.num_seqs} seqs, {batch.total_tokens} context tokens, "
+        f"generated in {time.time() - t0:.1f}s")
+    t = upload(batch, dev)
+    torch.cuda.synchronize()
+    ps = batch.partition_size if args.partition_size is None else args.partition_size
+
+    if args.sweep_partitions:
+        for p in [int(x) for x in args.sweep_partitions.split(",")]:
+            r = time_steps(batch, t, p, max(5, args.steps // 2), 3)
+            gbs = batch.kv_bytes_logical() / (r["decode_ms"] * 1e-3) / 1e9
+            log(f"[sweep] partition {p:6d}: decode {r['decode_ms']*1e3:8.1f} us "
+                f"({gbs:7.1f} GB/s, {100 * gbs / HBM_PEAK_GBS:5.1f}% of peak), "
+                f"write {r['write_ms']*1e3:6.1f} us")
+
+    r = time_steps(batch, t, ps, args.steps, args.warmup)
+    log(f"[bench] timed {args.steps} steps: {r['ms_per_step']:.4f} ms/step "
+        f"(decode {r['decode_ms']:.4f} ms, write {r['write_ms']:.4f} ms)")
+
+    kv_bytes = batch.kv_bytes_logical()
+    step_s = r["ms_per_step"] * 1e-3
+    value = kv_bytes / step_s / 1e9
+    achieved = kv_bytes / (r["decode_ms"] * 1e-3) / 1e9
+    traffic = load_traffic(args.config if args.block_size is None else f"{args.config}_bs{args.block_size}")
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": batch.dtype,
+        "data": "synthetic (seeded N(0,1) values, generated context lengths and page tables)",
+        "config": {
+            "workload": batch.name,
+            "num_seqs": batch.num_seqs,
+            "num_heads": batch.num_heads,
+            "num_kv_heads": batch.num_kv_heads,
+            "head_dim": batch.head_dim,
+            "block_size": batch.block_size,
+            "partition_size": ps,
+            "context_tokens": batch.total_tokens,
+            "max_context_len": batch.max_context_len,
+            "new_tokens_written": 0 if batch.slot_mapping is None else int((batch.slot_mapping >= 0).sum()),
+            "parallelism": "single GPU",
+        },
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "decode_tokens_per_s": round(batch.num_seqs / step_s, 1),
+        "kv_bytes_logical": kv_bytes,
+        "write_ms": round(r["write_ms"], 5),
+        "decode_ms": round(r["decode_ms"], 5),
+        "step_ms_p99": round(r["step_ms_p99"], 5),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "paged_decode_attention call (decode kernel" + (
+                " + log-sum-exp merge)" if ps and batch.max_context_len > ps else ")"),
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+        },
+    }
+    if args.block_size is not None:
+        line["config"]["unique_kv_bytes"] = batch.kv_bytes_unique()
+
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample ...")
+        line["cpu_baseline"] = cpu_baseline(batch, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

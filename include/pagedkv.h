@@ -1,0 +1,156 @@
+/*
+ * pagedkv -- single-query decode attention over a paged KV cache on gfx950.
+ *
+ * The operation (three web pages on PagedAttention):
+ *   [P1] "从正确到更快：PagedAttention 的优化路线"
+ *   [P2] "实现教学版 PagedAttention：从 block table 读取历史 KV cache"
+ *   [P3] "算子与编译器：推理 Attention 与 KV Kernel"
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor arguments are DEVICE pointers to contiguous row-major arrays
+ *    owned by the caller.  The library allocates nothing, frees nothing and
+ *    keeps no global state; calls are reentrant.
+ *  - KV pool layout ([P2] section "先定义一个简单的 KV cache 布局", with the
+ *    head axis holding the KV heads as grouped-query attention requires,
+ *    [P3] section "7. MQA / GQA 为什么会改变服务性能"):
+ *        key_cache, value_cache : [num_blocks, block_size, num_kv_heads, head_dim]
+ *  - Every call only enqueues kernels on `stream` (a hipStream_t; NULL is the
+ *    default stream) and returns.  Results are valid once the caller has
+ *    synchronised with that stream.  A write followed by a decode on the same
+ *    stream is ordered by the stream.
+ *  - Arguments are checked on the host before anything is launched; a
+ *    non-PKV_OK status means nothing was enqueued, except PKV_ERR_HIP, which
+ *    reports a launch failure.  No exception crosses this interface.
+ *  - Device-resident contents (table entries, slots, lengths) are range
+ *    checked inside the kernels so that no access leaves the buffers the
+ *    sizes describe: an out-of-range slot is skipped by the write, and a
+ *    sequence whose length or table entries are out of range gets NaN
+ *    outputs from the decode.
+ *  - Pointers to tensors must be 16-byte aligned.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types of queries, caches and outputs. */
+typedef enum pkv_dtype {
+    PKV_F32 = 0,  /* IEEE binary32 */
+    PKV_F16 = 1,  /* IEEE binary16 */
+    PKV_BF16 = 2  /* bfloat16 */
+} pkv_dtype;
+
+typedef enum pkv_status {
+    PKV_OK = 0,
+    PKV_ERR_NULL = 1,        /* a required pointer is NULL */
+    PKV_ERR_SHAPE = 2,       /* sizes negative or inconsistent */
+    PKV_ERR_DTYPE = 3,       /* unknown dtype or out_dtype combination */
+    PKV_ERR_UNSUPPORTED = 4, /* head_dim, block_size, group or partition not supported */
+    PKV_ERR_ALIGN = 5,       /* a tensor pointer is not 16-byte aligned */
+    PKV_ERR_WORKSPACE = 6,   /* workspace missing or too small */
+    PKV_ERR_HIP = 7          /* the HIP runtime reported an error at launch */
+} pkv_status;
+
+/*
+ * paged_kv_write -- store each new token's K and V rows in its slot.
+ *
+ * [P2] section "写入 slot 和读取 block table 必须一致": the slot handed out
+ * for the current token is a (physical_block_id, block_offset) pair, and the
+ * place a token is written to must be exactly the place the attention later
+ * reads it from; [P2] section "PagedAttention 如何接入 mini vLLM": the
+ * attention writes the current K/V through the slot mapping.
+ *
+ *   key, value    [num_tokens, num_kv_heads, head_dim]   dtype    (read)
+ *   key_cache,
+ *   value_cache   [num_blocks, block_size, num_kv_heads, head_dim] dtype (written)
+ *   slot_mapping  [num_tokens] int64: slot = physical_block_id * block_size
+ *                 + block_offset.  A negative slot skips the token; a slot
+ *                 >= num_blocks * block_size is skipped too.
+ *
+ * A bit copy: no conversion.  Tokens with equal slots race (the result is
+ * one of them).  num_tokens == 0 is a no-op.
+ * Supported: head_dim in {64, 128}; block_size in {4, 8, 16, 32, 64}.
+ */
+pkv_status paged_kv_write(const void *key, const void *value, void *key_cache,
+                          void *value_cache, const int64_t *slot_mapping,
+                          int64_t num_tokens, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t block_size,
+                          int64_t num_blocks, pkv_dtype dtype, void *stream);
+
+/*
+ * paged_decode_workspace_size -- bytes of scratch paged_decode_attention needs
+ * when the context is split into KV partitions (0 when it is not split).
+ * partition_size == 0 means one partition per sequence.  Layout (fp32):
+ * partial outputs [num_seqs, num_heads, P, head_dim] followed by the
+ * per-partition (running max, normaliser) pairs [num_seqs, num_heads, P, 2],
+ * P = ceil(max_context_len / partition_size).
+ */
+size_t paged_decode_workspace_size(int32_t num_seqs, int32_t num_heads,
+                                   int32_t head_dim, int32_t max_context_len,
+                                   int32_t partition_size);
+
+/*
+ * paged_decode_attention -- one query token per sequence attends to its
+ * cached history, read from the paged pool through its block table.
+ *
+ * Computes, for sequence s and query head h with KV head kvh = h / G
+ * (G = num_heads / num_kv_heads, contiguous head groups):
+ *   token t of the history lives at physical block block_tables[s][t /
+ *   block_size], offset t % block_size ([P2] section "从逻辑 token 到物理
+ *   block");
+ *   score_t = scale * dot(query[s][h], key_t)   ([P1] section "attention
+ *   kernel 真正在做什么" scales by 1/sqrt(head_dim); the caller passes it);
+ *   out[s][h] = sum_t softmax(score)_t * value_t   ([P2] section "从 gather
+ *   后的 K/V 做 attention"),
+ * over t < context_lens[s].  Decode needs no causal mask ([P2] section
+ * "attention mask 在哪里").  The result equals attention over a contiguous
+ * cache holding the same rows ([P2] section "和连续 KV cache 对齐验证").
+ * It is computed without gathering the history and without storing the
+ * scores ([P1] sections "高性能 PagedAttention 的核心思想" and "attention
+ * kernel 真正在做什么"): the kernel resolves every page itself and keeps a
+ * running softmax.  A sequence with context_lens[s] == 0 gets zeros.
+ *
+ *   out           [num_seqs, num_heads, head_dim]  out_dtype (written)
+ *   query         [num_seqs, num_heads, head_dim]  dtype
+ *   key_cache,
+ *   value_cache   [num_blocks, block_size, num_kv_heads, head_dim] dtype
+ *   block_tables  [num_seqs, max_blocks_per_seq] int32; entries at or past
+ *                 ceil(context_lens[s] / block_size) are never read
+ *   context_lens  [num_seqs] int32, each in [0, max_context_len] and
+ *                 <= max_blocks_per_seq * block_size
+ *   max_context_len  host-side upper bound of context_lens; sizes the grid
+ *   scale         score multiplier (normally 1/sqrt(head_dim))
+ *   partition_size   0: each (sequence, KV head) is one work unit; else the
+ *                 context is cut into partitions of this many tokens (a
+ *                 multiple of 16 and of block_size) whose partial results a
+ *                 second kernel merges by log-sum-exp
+ *   dtype         PKV_F32, PKV_F16 or PKV_BF16; out_dtype is dtype or PKV_F32
+ *   workspace     device scratch of at least paged_decode_workspace_size()
+ *                 bytes (may be NULL when that is 0), 16-byte aligned
+ *
+ * Accumulation is fp32 throughout.  Supported: head_dim in {64, 128};
+ * block_size in {4, 8, 16, 32, 64}; G in {1, 2, 4, 8}.
+ */
+pkv_status paged_decode_attention(
+    void *out, const void *query, const void *key_cache,
+    const void *value_cache, const int32_t *block_tables,
+    const int32_t *context_lens, int32_t num_seqs, int32_t num_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t max_blocks_per_seq, int64_t num_blocks, int32_t max_context_len,
+    float scale, int32_t partition_size, pkv_dtype dtype,
+    pkv_dtype out_dtype, void *workspace, size_t workspace_bytes,
+    void *stream);
+
+/* Static, NUL-terminated description of a status code (host memory). */
+const char *pkv_status_string(pkv_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -1,0 +1,189 @@
+"""Python binding of libpagedkv: paged-KV single-query decode attention on gfx950.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/pagedkv.h``.  PyTorch provides
+device memory and the stream.  There is no fallback: if the library is not
+built, or a tensor is not on a GPU, the call raises.
+
+Entry points (same names as the C ABI):
+  paged_kv_write(key, value, key_cache, value_cache, slot_mapping)
+  paged_decode_attention(query, key_cache, value_cache, block_tables,
+                         context_lens, block_size, scale, *, max_context_len,
+                         partition_size=0, out=None, out_dtype=None,
+                         workspace=None)
+  paged_decode_workspace_size(num_seqs, num_heads, head_dim, max_context_len,
+                              partition_size)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "paged_kv_write",
+    "paged_decode_attention",
+    "paged_decode_workspace_size",
+    "library_path",
+    "PagedKVError",
+]
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG_DIR, "libpagedkv.so")
+
+PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
+_STATUS = {0: "PKV_OK", 1: "PKV_ERR_NULL", 2: "PKV_ERR_SHAPE", 3: "PKV_ERR_DTYPE",
+           4: "PKV_ERR_UNSUPPORTED", 5: "PKV_ERR_ALIGN", 6: "PKV_ERR_WORKSPACE", 7: "PKV_ERR_HIP"}
+
+_lib = None
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        self.name = _STATUS.get(status, str(status))
+        msg = _load().pkv_status_string(status).decode()
+        super().__init__(f"{what}: {self.name} ({msg})")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"libpagedkv.so is not built ({_LIB_PATH}); run "
+            "`python -m paged_kv_decode_13_amd.build` (there is no fallback path)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    p, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.paged_kv_write.argtypes = [p, p, p, p, p, i64, i32, i32, i32, i64, ctypes.c_int, p]
+    lib.paged_kv_write.restype = ctypes.c_int
+    lib.paged_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    lib.paged_decode_workspace_size.restype = sz
+    lib.paged_decode_attention.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i64,
+                                           i32, ctypes.c_float, i32, ctypes.c_int, ctypes.c_int,
+                                           p, sz, p]
+    lib.paged_decode_attention.restype = ctypes.c_int
+    lib.pkv_status_string.argtypes = [ctypes.c_int]
+    lib.pkv_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dtype_code(dt) -> int:
+    torch = _torch()
+    if dt == torch.float32:
+        return PKV_F32
+    if dt == torch.float16:
+        return PKV_F16
+    if dt == torch.bfloat16:
+        return PKV_BF16
+    raise TypeError(f"unsupported dtype {dt}")
+
+
+def _gpu(t, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream_handle(device) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def paged_kv_write(key, value, key_cache, value_cache, slot_mapping) -> None:
+    """Store token i's K/V rows ``key[i]``/``value[i]`` ([num_kv_heads,
+    head_dim]) at ``slot_mapping[i]`` (int64, physical_block * block_size +
+    offset; negative = skip) of the paged pools, on the current stream."""
+    torch = _torch()
+    lib = _load()
+    for t, n in ((key, "key"), (value, "value"), (key_cache, "key_cache"),
+                 (value_cache, "value_cache"), (slot_mapping, "slot_mapping")):
+        _gpu(t, n)
+    if slot_mapping.dtype != torch.int64:
+        raise TypeError("slot_mapping must be int64")
+    nb, bs, kvh, d = key_cache.shape
+    tokens = key.shape[0]
+    if tuple(key.shape) != (tokens, kvh, d) or value.shape != key.shape:
+        raise ValueError("key/value must be [num_tokens, num_kv_heads, head_dim] of the pool")
+    if value_cache.shape != key_cache.shape or slot_mapping.shape != (tokens,):
+        raise ValueError("inconsistent shapes")
+    if not (key.dtype == value.dtype == key_cache.dtype == value_cache.dtype):
+        raise TypeError("key, value and the caches must share one dtype")
+    st = lib.paged_kv_write(key.data_ptr(), value.data_ptr(), key_cache.data_ptr(),
+                            value_cache.data_ptr(), slot_mapping.data_ptr(), tokens, kvh, d, bs,
+                            nb, _dtype_code(key.dtype), _stream_handle(key.device))
+    if st != 0:
+        raise PagedKVError(st, "paged_kv_write")
+
+
+def paged_decode_workspace_size(num_seqs: int, num_heads: int, head_dim: int,
+                                max_context_len: int, partition_size: int) -> int:
+    return int(_load().paged_decode_workspace_size(num_seqs, num_heads, head_dim,
+                                                   max_context_len, partition_size))
+
+
+def paged_decode_attention(query, key_cache, value_cache, block_tables, context_lens,
+                           block_size: int, scale: float, *, max_context_len: int,
+                           partition_size: int = 0, out=None, out_dtype=None, workspace=None):
+    """Decode attention of ``query`` [num_seqs, num_heads, head_dim] over the
+    paged pools [num_blocks, block_size, num_kv_heads, head_dim] through
+    ``block_tables`` (int32 [num_seqs, max_blocks]) and ``context_lens``
+    (int32 [num_seqs]).  Returns ``out`` [num_seqs, num_heads, head_dim] in
+    ``out_dtype`` (default: the cache dtype).  ``max_context_len`` is a host
+    upper bound of ``context_lens``; ``partition_size`` > 0 splits contexts
+    into KV partitions merged by log-sum-exp."""
+    torch = _torch()
+    lib = _load()
+    for t, n in ((query, "query"), (key_cache, "key_cache"), (value_cache, "value_cache"),
+                 (block_tables, "block_tables"), (context_lens, "context_lens")):
+        _gpu(t, n)
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    nb, bs, kvh, d = key_cache.shape
+    if bs != block_size:
+        raise ValueError("block_size does not match key_cache.shape[1]")
+    b, h, dq = query.shape
+    if dq != d or value_cache.shape != key_cache.shape:
+        raise ValueError("inconsistent shapes")
+    if block_tables.dim() != 2 or block_tables.shape[0] != b or tuple(context_lens.shape) != (b,):
+        raise ValueError("block_tables must be [num_seqs, max_blocks], context_lens [num_seqs]")
+    if not (query.dtype == key_cache.dtype == value_cache.dtype):
+        raise TypeError("query and caches must share one dtype")
+    dt = _dtype_code(query.dtype)
+    odt = query.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((b, h, d), dtype=odt, device=query.device)
+    else:
+        _gpu(out, "out")
+        if tuple(out.shape) != (b, h, d):
+            raise ValueError("out must be [num_seqs, num_heads, head_dim]")
+        odt = out.dtype
+    need = paged_decode_workspace_size(b, h, d, int(max_context_len), int(partition_size))
+    ws_ptr, ws_bytes = None, 0
+    if need:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
+        else:
+            _gpu(workspace, "workspace")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    st = lib.paged_decode_attention(
+        out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+        block_tables.data_ptr(), context_lens.data_ptr(), b, h, kvh, d, bs,
+        block_tables.shape[1], nb, int(max_context_len), float(scale), int(partition_size), dt,
+        _dtype_code(odt), ws_ptr, ws_bytes, _stream_handle(query.device))
+    if st != 0:
+        raise PagedKVError(st, "paged_decode_attention")
+    return out

@@ -1,0 +1,360 @@
+// Fused paged decode attention for gfx950, and the log-sum-exp merge of its
+// split-KV partials.
+//
+// What is computed (pages on PagedAttention):
+//  - "实现教学版 PagedAttention：从 block table 读取历史 KV cache", section
+//    "从逻辑 token 到物理 block": token t of a sequence lives at physical block
+//    block_table[t / block_size], offset t % block_size;
+//  - same page, section "从 gather 后的 K/V 做 attention": scores = q.K^T,
+//    softmax, weighted sum of V, per query head;
+//  - "从正确到更快：PagedAttention 的优化路线", section "高性能 PagedAttention
+//    的核心思想": the kernel resolves each page itself while computing the
+//    scores (no gathered copy), and section "attention kernel 真正在做什么":
+//    scores are scaled by 1/sqrt(head_dim) and folded chunk by chunk into a
+//    running max and normaliser instead of being stored;
+//  - same page, section "Triton 适合做什么": one program per head group and a
+//    segment of the history per program, with tail masking where the context
+//    is not a multiple of the block size.
+//
+// Work unit = (sequence, KV head, KV partition); one 256-thread workgroup
+// (4 waves) per unit.  The whole query-head group of the KV head is handled
+// by the unit, so each K/V row is loaded once for all G query heads.
+//
+// Data path inside a unit:
+//  1. the page ids of the partition are staged in LDS once (coalesced), so
+//     the per-token page lookup is an LDS read, never a dependent global load;
+//  2. every lane loads 16-byte vectors: a K/V row of D elements is read by
+//     LPR = D*bytes/16 adjacent lanes (one 128-bit load each), so a wave
+//     instruction reads RPW = 64/LPR whole rows;
+//  3. the partial dot products are summed over the LPR lanes of a row with
+//     DPP row exchanges;
+//  4. each row group keeps its own running (max, normaliser, accumulator) in
+//     registers; U rows per lane are folded in per step;
+//  5. row groups are merged with lane shuffles, waves through LDS.
+// Scores are kept in the exp2 domain (scale * log2 e folded into q).
+#include <math.h>
+
+#include "pkv_device.h"
+#include "pkv_launch.h"
+
+namespace pkv {
+
+constexpr int kNumWaves = 4;
+constexpr int kThreads = kNumWaves * kWave;
+constexpr int kSegPages = 256;  // page ids staged in LDS at a time
+
+struct UnitPos {
+    int s, kvh, p;
+};
+
+__device__ __forceinline__ UnitPos unit_pos(const DecodeArgs &a) {
+    // KV head fastest: the units that read the same pages run side by side.
+    int u = blockIdx.x;
+    UnitPos r;
+    r.kvh = u % a.num_kv_heads;
+    u /= a.num_kv_heads;
+    r.p = u % a.num_partitions;
+    r.s = u / a.num_partitions;
+    return r;
+}
+
+// A context length the grid or the table cannot cover makes the sequence's
+// output NaN instead of reading outside the table.
+__device__ __forceinline__ bool bad_context(const DecodeArgs &a, int ctx) {
+    return ctx < 0 || ctx > a.max_context_len ||
+           (int64_t)ctx > (int64_t)a.max_blocks_per_seq * a.block_size;
+}
+
+template <int DT>
+__device__ __forceinline__ void store_out(const DecodeArgs &a, int64_t idx, float v) {
+    if (a.out_f32) {
+        reinterpret_cast<float *>(a.out)[idx] = v;
+    } else if constexpr (DT == kF32) {
+        reinterpret_cast<float *>(a.out)[idx] = v;
+    } else {
+        reinterpret_cast<uint16_t *>(a.out)[idx] = f32_to_bits16<DT>(v);
+    }
+}
+
+template <int DT, int D, int G>
+__global__ __launch_bounds__(kThreads) void paged_decode_valu_kernel(DecodeArgs a) {
+    using TR = ElemTraits<DT>;
+    constexpr int EPL = TR::per16;  // elements per lane per row
+    constexpr int LPR = D / EPL;    // lanes per row
+    constexpr int RPW = kWave / LPR;  // rows per wave instruction
+    constexpr int U = 4;            // rows per lane per step
+    constexpr int CHUNK = RPW * U;  // tokens per wave per step
+    constexpr int ROW_BYTES = D * TR::bytes;
+    static_assert(LPR >= 4 && LPR <= 64 && (LPR & (LPR - 1)) == 0, "row layout");
+
+    __shared__ int s_pages[kSegPages];
+    __shared__ int s_bad;
+    __shared__ float s_m[kNumWaves][G];
+    __shared__ float s_l[kNumWaves][G];
+    __shared__ float s_acc[kNumWaves][G][D];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int rg = lane / LPR;  // row group inside the wave
+    const int li = lane % LPR;  // 16-byte column inside the row
+
+    const UnitPos up = unit_pos(a);
+    const int ctx = a.context_lens[up.s];
+    const bool bad_len = bad_context(a, ctx);
+    const int tok_begin = up.p * a.partition_size;
+    if (up.p > 0 && (bad_len || tok_begin >= ctx)) return;  // empty unit
+    const int tok_end = bad_len ? 0 : min(ctx, tok_begin + a.partition_size);
+    const int nparts = (bad_len || ctx == 0) ? 1 : (ctx + a.partition_size - 1) / a.partition_size;
+
+    if (tid == 0) s_bad = 0;
+
+    // query rows of the head group, pre-scaled into the exp2 domain
+    const int h0 = up.kvh * G;
+    float qf[G][EPL];
+    {
+        const char *qb = reinterpret_cast<const char *>(a.query);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int64_t off = (((int64_t)up.s * a.num_heads + h0 + g) * D) * TR::bytes + li * 16;
+            unpack16<DT>(load16(qb + off), qf[g]);
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) qf[g][e] *= a.scale_log2e;
+        }
+    }
+
+    float m[G], l[G], acc[G][EPL];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        m[g] = -INFINITY;
+        l[g] = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
+    }
+
+    const char *kbase = reinterpret_cast<const char *>(a.key_cache);
+    const char *vbase = reinterpret_cast<const char *>(a.value_cache);
+    const int bs = a.block_size;
+    const int lbs = a.log2_block_size;
+    const int32_t *table = a.block_tables + (int64_t)up.s * a.max_blocks_per_seq;
+
+    for (int seg = tok_begin; seg < tok_end; seg += kSegPages << lbs) {
+        const int seg_end = min(tok_end, seg + (kSegPages << lbs));
+        const int lb0 = seg >> lbs;
+        const int npages = (seg_end - seg + bs - 1) >> lbs;
+        __syncthreads();  // previous segment's readers are done with s_pages
+        for (int i = tid; i < npages; i += kThreads) {
+            int pb = table[lb0 + i];
+            if (pb < 0 || (int64_t)pb >= a.num_blocks) {
+                s_bad = 1;
+                pb = -1;
+            }
+            s_pages[i] = pb;
+        }
+        __syncthreads();
+
+        for (int c = seg + wave * CHUNK; c < seg_end; c += kNumWaves * CHUNK) {
+            u32x4 kr[U], vr[U];
+            bool ok[U];
+#pragma unroll
+            for (int i = 0; i < U; ++i) {
+                const int t = c + i * RPW + rg;
+                ok[i] = t < seg_end;
+                kr[i] = u32x4{0, 0, 0, 0};
+                vr[i] = u32x4{0, 0, 0, 0};
+                if (ok[i]) {
+                    // token -> logical block -> physical block, block offset
+                    const int pb = s_pages[(t - seg) >> lbs];
+                    ok[i] = pb >= 0;
+                    if (ok[i]) {
+                        const int64_t row = ((int64_t)pb * bs + (t & (bs - 1))) * a.num_kv_heads + up.kvh;
+                        const int64_t byte = row * ROW_BYTES + li * 16;
+                        kr[i] = load16_stream(kbase + byte);
+                        vr[i] = load16_stream(vbase + byte);
+                    }
+                }
+            }
+
+            float sc[G][U];
+#pragma unroll
+            for (int i = 0; i < U; ++i) {
+                float kf[EPL];
+                unpack16<DT>(kr[i], kf);
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    float d = 0.f;
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) d = fmaf(qf[g][e], kf[e], d);
+                    d = group_sum<LPR>(d);
+                    sc[g][i] = ok[i] ? d : -INFINITY;
+                }
+            }
+
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                float mc = sc[g][0];
+#pragma unroll
+                for (int i = 1; i < U; ++i) mc = fmaxf(mc, sc[g][i]);
+                const float mn = fmaxf(m[g], mc);
+                const bool none = mn == -INFINITY;  // nothing seen yet by this row group
+                const float alpha = none ? 1.f : fast_exp2(m[g] - mn);
+                m[g] = mn;
+                l[g] *= alpha;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) acc[g][e] *= alpha;
+#pragma unroll
+                for (int i = 0; i < U; ++i) sc[g][i] = none ? 0.f : fast_exp2(sc[g][i] - mn);
+            }
+
+#pragma unroll
+            for (int i = 0; i < U; ++i) {
+                float vf[EPL];
+                unpack16<DT>(vr[i], vf);
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    l[g] += sc[g][i];
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(sc[g][i], vf[e], acc[g][e]);
+                }
+            }
+        }
+    }
+
+    // merge the row groups of this wave (lanes li, li+LPR, ... hold one column)
+#pragma unroll
+    for (int msk = LPR; msk < kWave; msk <<= 1) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const float mo = __shfl_xor(m[g], msk);
+            const float lo = __shfl_xor(l[g], msk);
+            const float mn = fmaxf(m[g], mo);
+            const bool none = mn == -INFINITY;
+            const float a1 = none ? 0.f : fast_exp2(m[g] - mn);
+            const float a2 = none ? 0.f : fast_exp2(mo - mn);
+            l[g] = l[g] * a1 + lo * a2;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                const float ao = __shfl_xor(acc[g][e], msk);
+                acc[g][e] = acc[g][e] * a1 + ao * a2;
+            }
+            m[g] = mn;
+        }
+    }
+    if (lane < LPR) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) s_acc[wave][g][li * EPL + e] = acc[g][e];
+            if (li == 0) {
+                s_m[wave][g] = m[g];
+                s_l[wave][g] = l[g];
+            }
+        }
+    }
+    __syncthreads();
+
+    const bool bad = bad_len || s_bad != 0;
+    for (int i = tid; i < G * D; i += kThreads) {
+        const int g = i / D;
+        const int d = i % D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kNumWaves; ++w) M = fmaxf(M, s_m[w][g]);
+        float L = 0.f, O = 0.f;
+#pragma unroll
+        for (int w = 0; w < kNumWaves; ++w) {
+            const float f = (M == -INFINITY) ? 0.f : fast_exp2(s_m[w][g] - M);
+            L += s_l[w][g] * f;
+            O += s_acc[w][g][d] * f;
+        }
+        float res = L > 0.f ? O / L : 0.f;  // empty context -> zeros
+        if (bad) res = __builtin_nanf("");
+        const int h = h0 + g;
+        if (nparts == 1) {
+            store_out<DT>(a, ((int64_t)up.s * a.num_heads + h) * D + d, res);
+        } else {
+            const int64_t slot = ((int64_t)up.s * a.num_heads + h) * a.num_partitions + up.p;
+            a.part_out[slot * D + d] = res;
+            if (d == 0) {
+                a.part_ml[slot * 2] = bad ? __builtin_nanf("") : M;
+                a.part_ml[slot * 2 + 1] = L;
+            }
+        }
+    }
+}
+
+// Log-sum-exp merge of the partitions of one (sequence, query head):
+// with partition p holding normalised output o_p, running max m_p and
+// normaliser l_p (exp2 domain), out = sum_p w_p o_p / sum_p w_p,
+// w_p = l_p * 2^(m_p - max_q m_q).
+template <int DT, int D>
+__global__ __launch_bounds__(kWave) void lse_merge_kernel(DecodeArgs a) {
+    constexpr int PER_LANE = D / kWave;
+    const int s = blockIdx.x / a.num_heads;
+    const int h = blockIdx.x % a.num_heads;
+    const int ctx = a.context_lens[s];
+    if (bad_context(a, ctx) || ctx == 0) return;  // written by partition 0
+    int nparts = (ctx + a.partition_size - 1) / a.partition_size;
+    if (nparts <= 1) return;                       // written directly
+    nparts = min(nparts, a.num_partitions);
+    const int64_t base = ((int64_t)s * a.num_heads + h) * a.num_partitions;
+    const int lane = threadIdx.x;
+
+    float M = -INFINITY;
+    for (int p = 0; p < nparts; ++p) M = fmaxf(M, a.part_ml[(base + p) * 2]);
+    float L = 0.f, O[PER_LANE];
+#pragma unroll
+    for (int j = 0; j < PER_LANE; ++j) O[j] = 0.f;
+    for (int p = 0; p < nparts; ++p) {
+        const float w = a.part_ml[(base + p) * 2 + 1] * fast_exp2(a.part_ml[(base + p) * 2] - M);
+        L += w;
+#pragma unroll
+        for (int j = 0; j < PER_LANE; ++j) O[j] = fmaf(w, a.part_out[(base + p) * D + lane + j * kWave], O[j]);
+    }
+    const float inv = 1.f / L;
+#pragma unroll
+    for (int j = 0; j < PER_LANE; ++j)
+        store_out<DT>(a, ((int64_t)s * a.num_heads + h) * D + lane + j * kWave, O[j] * inv);
+}
+
+template <int DT, int D, int G>
+static hipError_t launch_typed(const DecodeArgs &a, hipStream_t stream) {
+    const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * a.num_partitions;
+    hipLaunchKernelGGL((paged_decode_valu_kernel<DT, D, G>), dim3((unsigned)units), dim3(kThreads), 0,
+                       stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.num_partitions <= 1) return e;
+    const int64_t rows = (int64_t)a.num_seqs * a.num_heads;
+    hipLaunchKernelGGL((lse_merge_kernel<DT, D>), dim3((unsigned)rows), dim3(kWave), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int DT, int D>
+static hipError_t launch_group(const DecodeArgs &a, hipStream_t stream) {
+    switch (a.num_heads / a.num_kv_heads) {
+        case 1: return launch_typed<DT, D, 1>(a, stream);
+        case 2: return launch_typed<DT, D, 2>(a, stream);
+        case 4: return launch_typed<DT, D, 4>(a, stream);
+        case 8: return launch_typed<DT, D, 8>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int DT>
+static hipError_t launch_dim(const DecodeArgs &a, int head_dim, hipStream_t stream) {
+    if (head_dim == 64) return launch_group<DT, 64>(a, stream);
+    if (head_dim == 128) return launch_group<DT, 128>(a, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_paged_decode(const DecodeArgs &a, int dtype, int head_dim, hipStream_t stream) {
+    if ((int64_t)a.num_seqs * a.num_kv_heads * a.num_partitions == 0) return hipSuccess;
+    switch (dtype) {
+        case kF32: return launch_dim<kF32>(a, head_dim, stream);
+        case kF16: return launch_dim<kF16>(a, head_dim, stream);
+        case kBF16: return launch_dim<kBF16>(a, head_dim, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace pkv

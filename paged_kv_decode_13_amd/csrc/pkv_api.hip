@@ -1,0 +1,152 @@
+// C-ABI layer of libpagedkv: host-side argument checks, work decomposition
+// and kernel selection.  Declarations and the contract live in pagedkv.h.
+#include <hip/hip_runtime.h>
+#include <limits.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/pagedkv.h"
+#include "pkv_launch.h"
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_bytes(pkv_dtype d) { return d == PKV_F32 ? 4 : 2; }
+
+bool valid_dtype(int d) { return d == PKV_F32 || d == PKV_F16 || d == PKV_BF16; }
+
+bool pow2_block(int32_t bs) { return bs == 4 || bs == 8 || bs == 16 || bs == 32 || bs == 64; }
+
+int log2i(int32_t v) {
+    int r = 0;
+    while ((1 << r) < v) ++r;
+    return r;
+}
+
+// Tokens per decode work unit: every partition starts on a page boundary and
+// on a 16-token boundary.
+int32_t partition_granule(int32_t block_size) { return block_size > 16 ? block_size : 16; }
+
+int32_t num_partitions(int32_t max_context_len, int32_t partition_size) {
+    if (partition_size <= 0 || max_context_len <= 0) return 1;
+    return (int32_t)(((int64_t)max_context_len + partition_size - 1) / partition_size);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *pkv_status_string(pkv_status status) {
+    switch (status) {
+        case PKV_OK: return "ok";
+        case PKV_ERR_NULL: return "a required pointer is NULL";
+        case PKV_ERR_SHAPE: return "sizes are negative or inconsistent";
+        case PKV_ERR_DTYPE: return "unsupported dtype or out_dtype";
+        case PKV_ERR_UNSUPPORTED: return "unsupported head_dim, block_size, head group or partition size";
+        case PKV_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+        case PKV_ERR_WORKSPACE: return "workspace missing or too small";
+        case PKV_ERR_HIP: return "HIP runtime error at launch";
+    }
+    return "unknown status";
+}
+
+pkv_status paged_kv_write(const void *key, const void *value, void *key_cache, void *value_cache,
+                          const int64_t *slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t block_size, int64_t num_blocks, pkv_dtype dtype,
+                          void *stream) {
+    if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks < 0) return PKV_ERR_SHAPE;
+    if (!valid_dtype(dtype)) return PKV_ERR_DTYPE;
+    if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
+    if (!pow2_block(block_size)) return PKV_ERR_UNSUPPORTED;
+    if (num_tokens == 0) return PKV_OK;
+    if (!key || !value || !key_cache || !value_cache || !slot_mapping) return PKV_ERR_NULL;
+    if (!aligned16(key) || !aligned16(value) || !aligned16(key_cache) || !aligned16(value_cache))
+        return PKV_ERR_ALIGN;
+    pkv::WriteArgs a;
+    a.key = key;
+    a.value = value;
+    a.key_cache = key_cache;
+    a.value_cache = value_cache;
+    a.slot_mapping = slot_mapping;
+    a.num_tokens = num_tokens;
+    a.num_blocks = num_blocks;
+    a.block_size = block_size;
+    a.vecs_per_token = (int32_t)(((int64_t)num_kv_heads * head_dim * elem_bytes(dtype)) / 16);
+    hipError_t e = pkv::launch_kv_write(a, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+size_t paged_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                   int32_t max_context_len, int32_t partition_size) {
+    if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0) return 0;
+    const int32_t p = num_partitions(max_context_len, partition_size);
+    if (p <= 1) return 0;
+    return (size_t)num_seqs * num_heads * p * (size_t)(head_dim + 2) * sizeof(float);
+}
+
+pkv_status paged_decode_attention(void *out, const void *query, const void *key_cache,
+                                  const void *value_cache, const int32_t *block_tables,
+                                  const int32_t *context_lens, int32_t num_seqs, int32_t num_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                  int32_t max_blocks_per_seq, int64_t num_blocks,
+                                  int32_t max_context_len, float scale, int32_t partition_size,
+                                  pkv_dtype dtype, pkv_dtype out_dtype, void *workspace,
+                                  size_t workspace_bytes, void *stream) {
+    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq < 0 ||
+        num_blocks < 0 || max_context_len < 0 || partition_size < 0)
+        return PKV_ERR_SHAPE;
+    if (num_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
+    if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return PKV_ERR_DTYPE;
+    if (out_dtype != dtype && out_dtype != PKV_F32) return PKV_ERR_DTYPE;
+    if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
+    if (!pow2_block(block_size)) return PKV_ERR_UNSUPPORTED;
+    const int32_t group = num_heads / num_kv_heads;
+    if (group != 1 && group != 2 && group != 4 && group != 8) return PKV_ERR_UNSUPPORTED;
+    if (partition_size != 0 && partition_size % partition_granule(block_size) != 0)
+        return PKV_ERR_UNSUPPORTED;
+    if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size) return PKV_ERR_SHAPE;
+    if (!isfinite(scale)) return PKV_ERR_SHAPE;
+    if (num_seqs == 0) return PKV_OK;
+    if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens)
+        return PKV_ERR_NULL;
+    if (!aligned16(out) || !aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache))
+        return PKV_ERR_ALIGN;
+
+    const int32_t parts = num_partitions(max_context_len, partition_size);
+    const int64_t units = (int64_t)num_seqs * num_kv_heads * parts;
+    if (units > INT_MAX || (int64_t)num_seqs * num_heads > INT_MAX) return PKV_ERR_SHAPE;
+    pkv::DecodeArgs a = {};
+    if (parts > 1) {
+        const size_t need = paged_decode_workspace_size(num_seqs, num_heads, head_dim,
+                                                        max_context_len, partition_size);
+        if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return PKV_ERR_ALIGN;
+        a.part_out = reinterpret_cast<float *>(workspace);
+        a.part_ml = a.part_out + (size_t)num_seqs * num_heads * parts * head_dim;
+    }
+    a.out = out;
+    a.query = query;
+    a.key_cache = key_cache;
+    a.value_cache = value_cache;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.num_blocks = num_blocks;
+    a.num_seqs = num_seqs;
+    a.num_heads = num_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.block_size = block_size;
+    a.log2_block_size = log2i(block_size);
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.max_context_len = max_context_len;
+    // Unsplit: one unit covers any admissible context.
+    a.partition_size = parts > 1 ? partition_size : (max_context_len > 0 ? max_context_len : 1);
+    a.num_partitions = parts;
+    a.scale_log2e = scale * 1.4426950408889634f;
+    a.out_f32 = out_dtype == PKV_F32 ? 1 : 0;
+    hipError_t e = pkv::launch_paged_decode(a, (int)dtype, head_dim,
+                                            reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+}  // extern "C"

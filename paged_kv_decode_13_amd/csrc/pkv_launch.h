@@ -1,0 +1,51 @@
+// Internal launch interface between the C-ABI layer (pkv_api.hip) and the
+// kernel translation units.  Not part of the public boundary.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+struct WriteArgs {
+    const void *key;
+    const void *value;
+    void *key_cache;
+    void *value_cache;
+    const int64_t *slot_mapping;
+    int64_t num_tokens;
+    int64_t num_blocks;
+    int32_t block_size;
+    int32_t vecs_per_token;  // (num_kv_heads * head_dim * elem_bytes) / 16
+};
+
+struct DecodeArgs {
+    void *out;                  // [B, H, D] (out dtype)
+    float *part_out;            // [B, H, P, D] when split
+    float *part_ml;             // [B, H, P, 2] when split
+    const void *query;          // [B, H, D]
+    const void *key_cache;      // [NB, bs, KVH, D]
+    const void *value_cache;
+    const int32_t *block_tables;  // [B, MB]
+    const int32_t *context_lens;  // [B]
+    int64_t num_blocks;
+    int32_t num_seqs;
+    int32_t num_heads;
+    int32_t num_kv_heads;
+    int32_t block_size;
+    int32_t log2_block_size;
+    int32_t max_blocks_per_seq;
+    int32_t max_context_len;
+    int32_t partition_size;     // tokens per work unit (whole context when not split)
+    int32_t num_partitions;     // P: grid extent along the context
+    float scale_log2e;          // scale * log2(e): scores live in the exp2 domain
+    int32_t out_f32;            // 1: out is binary32; 0: out has the cache dtype
+};
+
+hipError_t launch_kv_write(const WriteArgs &a, hipStream_t stream);
+
+// dtype: 0 f32, 1 f16, 2 bf16.  Launches the decode kernel and, when
+// num_partitions > 1, the log-sum-exp merge.
+hipError_t launch_paged_decode(const DecodeArgs &a, int dtype, int head_dim, hipStream_t stream);
+
+}  // namespace pkv

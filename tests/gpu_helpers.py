@@ -1,0 +1,91 @@
+"""Shared plumbing for the GPU tests: upload a seeded batch, run the HIP path
+through the binding, run the oracle on the same host arrays."""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+from paged_kv_decode_13_amd import workloads as wl
+
+# Parity bars: max |gpu - oracle| on the output, cache dtype as output type.
+TOL = {"f32": 1e-5, "f16": 5e-3, "bf16": 5e-3}
+# With fp32 outputs the 16-bit inputs are exact in fp32 and every product is
+# exact, so only fp32 accumulation and exp2 rounding remain (~1e-6 observed
+# scale); 1e-4 leaves margin yet catches a dropped or duplicated token.
+TIGHT = {"f32": 1e-5, "f16": 1e-4, "bf16": 1e-4}
+
+TORCH_DT = {"f32": "float32", "f16": "float16", "bf16": "bfloat16"}
+
+
+def upload(batch: wl.DecodeBatch, dev):
+    import torch
+
+    t = {}
+    t["q"] = wl.torch_view(batch.query, batch.dtype).to(dev)
+    t["kc"] = wl.torch_view(batch.key_cache, batch.dtype).to(dev)
+    t["vc"] = wl.torch_view(batch.value_cache, batch.dtype).to(dev)
+    t["bt"] = torch.from_numpy(batch.block_tables).to(dev)
+    t["cl"] = torch.from_numpy(batch.context_lens).to(dev)
+    if batch.slot_mapping is not None:
+        t["nk"] = wl.torch_view(batch.new_key, batch.dtype).to(dev)
+        t["nv"] = wl.torch_view(batch.new_value, batch.dtype).to(dev)
+        t["slots"] = torch.from_numpy(batch.slot_mapping).to(dev)
+    return t
+
+
+def gpu_step(batch: wl.DecodeBatch, t, *, partition_size=None, out_dtype=None, write=True,
+             max_context_len=None):
+    """paged_kv_write (if the batch has new tokens) then paged_decode_attention."""
+    import torch
+
+    import paged_kv_decode_13_amd as pkv
+
+    if write and batch.slot_mapping is not None:
+        pkv.paged_kv_write(t["nk"], t["nv"], t["kc"], t["vc"], t["slots"])
+    ps = batch.partition_size if partition_size is None else partition_size
+    odt = None if out_dtype is None else getattr(torch, TORCH_DT[out_dtype])
+    out = pkv.paged_decode_attention(
+        t["q"], t["kc"], t["vc"], t["bt"], t["cl"], batch.block_size, batch.scale,
+        max_context_len=batch.max_context_len if max_context_len is None else max_context_len,
+        partition_size=ps, out_dtype=odt)
+    torch.cuda.synchronize()
+    return out
+
+
+def to_f64(out) -> np.ndarray:
+    import torch
+
+    return out.to(torch.float64).cpu().numpy()
+
+
+def oracle_step(batch: wl.DecodeBatch, write=True, context_lens=None):
+    kc, vc = batch.key_cache, batch.value_cache
+    if write and batch.slot_mapping is not None:
+        kc, vc = kc.copy(), vc.copy()
+        oracle.paged_kv_write(batch.new_key, batch.new_value, kc, vc, batch.slot_mapping)
+    cl = batch.context_lens if context_lens is None else context_lens
+    return oracle.paged_decode(batch.query, kc, vc, batch.block_tables, cl, batch.block_size,
+                               batch.scale, batch.dtype)
+
+
+MANT_BITS = {"f16": 10, "bf16": 7}
+
+
+def rounded_out_ok(gpu: np.ndarray, ref: np.ndarray, dtype: str) -> bool:
+    """16-bit outputs: within the fp32-path bound plus half an ulp of the
+    output type at the reference's magnitude (the rounding of the stored
+    result itself, which alone can exceed a flat 5e-3 once |out| >= 2)."""
+    if dtype == "f32":
+        return max_err(gpu, ref) <= TIGHT["f32"]
+    if np.isnan(gpu).any():
+        return False
+    mag = np.maximum(np.abs(ref), 2.0 ** -14)
+    half_ulp = 0.5 * 2.0 ** (np.floor(np.log2(mag)) - MANT_BITS[dtype])
+    return bool(np.all(np.abs(gpu - ref) <= TIGHT[dtype] + half_ulp))
+
+
+def max_err(gpu: np.ndarray, ref: np.ndarray) -> float:
+    assert gpu.shape == ref.shape
+    if np.isnan(gpu).any():
+        return float("inf")
+    return float(np.max(np.abs(gpu - ref))) if gpu.size else 0.0

@@ -1,0 +1,127 @@
+"""The C-ABI library on the CPU: it loads, exports what the header declares,
+and rejects bad arguments on the host before anything is launched."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+REPO = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(REPO, "include", "pagedkv.h")
+
+OK, NULL, SHAPE, DTYPE, UNSUP, ALIGN, WORKSPACE, HIP = range(8)
+F32, F16, BF16 = 0, 1, 2
+A = 0x10000  # a 16-byte aligned fake device address: never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import paged_kv_decode_13_amd as pkv
+    from paged_kv_decode_13_amd import build
+
+    if not os.path.exists(pkv.library_path()):
+        build.build()
+    return pkv._load()
+
+
+def _declared():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert set(names) == {"paged_kv_write", "paged_decode_workspace_size",
+                          "paged_decode_attention", "pkv_status_string"}
+    out = subprocess.run(["nm", "-D", "--defined-only", lib._name], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
+    for n in names:
+        assert n in exported, n
+        getattr(lib, n)
+
+
+def test_status_strings(lib):
+    for s in range(8):
+        assert lib.pkv_status_string(s)
+    assert lib.pkv_status_string(0) == b"ok"
+
+
+def _write(lib, **kw):
+    a = dict(key=A, value=A, kc=A, vc=A, slots=A, n=1, kvh=8, d=128, bs=16, nb=100, dt=BF16)
+    a.update(kw)
+    return lib.paged_kv_write(a["key"], a["value"], a["kc"], a["vc"], a["slots"], a["n"], a["kvh"],
+                              a["d"], a["bs"], a["nb"], a["dt"], None)
+
+
+def test_write_validation(lib):
+    assert _write(lib, n=-1) == SHAPE
+    assert _write(lib, kvh=0) == SHAPE
+    assert _write(lib, dt=7) == DTYPE
+    assert _write(lib, d=96) == UNSUP
+    assert _write(lib, bs=12) == UNSUP
+    assert _write(lib, key=None) == NULL
+    assert _write(lib, slots=None) == NULL
+    assert _write(lib, kc=A + 8) == ALIGN
+    assert _write(lib, n=0, key=None) == OK  # nothing to do, nothing launched
+
+
+def _decode(lib, **kw):
+    a = dict(out=A, q=A, kc=A, vc=A, bt=A, cl=A, b=4, h=32, kvh=8, d=128, bs=16, mb=64, nb=1000,
+             maxc=1024, scale=0.088, ps=0, dt=BF16, odt=BF16, ws=None, wsb=0)
+    a.update(kw)
+    return lib.paged_decode_attention(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["cl"], a["b"],
+                                      a["h"], a["kvh"], a["d"], a["bs"], a["mb"], a["nb"], a["maxc"],
+                                      a["scale"], a["ps"], a["dt"], a["odt"], a["ws"], a["wsb"], None)
+
+
+def test_decode_validation(lib):
+    assert _decode(lib, b=-1) == SHAPE
+    assert _decode(lib, h=30) == SHAPE  # 30 % 8 != 0
+    assert _decode(lib, maxc=64 * 16 + 1) == SHAPE  # table cannot hold max_context_len
+    assert _decode(lib, scale=float("nan")) == SHAPE
+    assert _decode(lib, dt=5) == DTYPE
+    assert _decode(lib, odt=F16) == DTYPE  # bf16 cache, fp16 out
+    assert _decode(lib, d=96) == UNSUP
+    assert _decode(lib, bs=12) == UNSUP
+    assert _decode(lib, h=128, kvh=8) == UNSUP  # group of 16
+    assert _decode(lib, ps=24) == UNSUP  # not a multiple of 16
+    assert _decode(lib, bs=32, mb=32, ps=16) == UNSUP  # not a multiple of the block
+    assert _decode(lib, q=None) == NULL
+    assert _decode(lib, cl=None) == NULL
+    assert _decode(lib, out=A + 4) == ALIGN
+    assert _decode(lib, ps=512, ws=None) == WORKSPACE
+    need = lib.paged_decode_workspace_size(4, 32, 128, 1024, 512)
+    assert _decode(lib, ps=512, ws=A, wsb=need - 1) == WORKSPACE
+    assert _decode(lib, ps=512, ws=A + 8, wsb=need) == ALIGN
+    assert _decode(lib, b=0, q=None) == OK  # empty batch: nothing launched
+
+
+def test_workspace_size(lib):
+    assert lib.paged_decode_workspace_size(4, 32, 128, 1024, 0) == 0
+    assert lib.paged_decode_workspace_size(4, 32, 128, 512, 512) == 0  # one partition
+    assert lib.paged_decode_workspace_size(4, 32, 128, 1025, 512) == 4 * 32 * 3 * 130 * 4
+    assert lib.paged_decode_workspace_size(256, 32, 128, 16000, 512) == 256 * 32 * 32 * 130 * 4
+
+
+def test_binding_rejects_cpu_tensors(lib):
+    import torch
+
+    import paged_kv_decode_13_amd as pkv
+
+    x = torch.zeros(1, 8, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        pkv.paged_kv_write(x, x, x, x, torch.zeros(1, dtype=torch.int64))
+
+
+def test_no_oracle_in_product_path():
+    """The product package never imports, loads or runs the oracle."""
+    pkg = os.path.join(REPO, "paged_kv_decode_13_amd")
+    for root, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(root, f), encoding="utf-8").read()
+                assert not re.search(r"^\s*(import|from)\s+oracle", text, flags=re.M), f
+                assert "liboracle" not in text, f

@@ -1,0 +1,155 @@
+"""Seeded input generator: layout invariants and determinism (CPU only)."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from paged_kv_decode_13_amd import workloads as wl
+
+
+def _used(batch):
+    bs = batch.block_size
+    return [batch.block_tables[s, : -(-int(c) // bs)] for s, c in enumerate(batch.context_lens)]
+
+
+def _check_layout(batch, shared_prefix_pages=0):
+    bs, nb = batch.block_size, batch.num_blocks
+    assert batch.block_tables.dtype == np.int32 and batch.context_lens.dtype == np.int32
+    assert (batch.block_tables >= 0).all() and (batch.block_tables < nb).all()
+    used = _used(batch)
+    for s, u in enumerate(used):
+        assert len(u) == -(-int(batch.context_lens[s]) // bs)
+        assert (batch.block_tables[s, len(u):] == batch.poison_block).all()
+    # unique (non-shared) pages are never shared between sequences
+    own = np.concatenate([u[shared_prefix_pages:] for u in used])
+    assert len(np.unique(own)) == len(own)
+    if shared_prefix_pages:
+        pre = used[0][:shared_prefix_pages]
+        for u in used:
+            assert np.array_equal(u[:shared_prefix_pages], pre)
+        assert not np.isin(own, pre).any()
+    assert batch.poison_block not in own
+
+
+def test_small_batch_layout_and_poison():
+    b = wl.make_batch([0, 1, 3, 4, 5, 17], num_heads=4, num_kv_heads=2, head_dim=64, block_size=4,
+                      dtype="bf16", seed=3, write_new_token=True)
+    _check_layout(b)
+    kc = b.key_cache.view(np.uint16).reshape(-1, 2, 64)
+    nan = (kc & 0x7F80) == 0x7F80
+    bs = b.block_size
+    for s, c in enumerate(b.context_lens):
+        c = int(c)
+        for t in range(c):
+            row = int(b.block_tables[s, t // bs]) * bs + t % bs
+            is_new = b.slot_mapping[s] == row
+            # history rows are finite; the new token's slot is poisoned until written
+            assert nan[row].all() if is_new else not nan[row].any()
+    spare = b.poison_block
+    assert nan[spare * bs:(spare + 1) * bs].all()
+    assert nan[int(b.block_tables[5, 4]) * bs + 1:(int(b.block_tables[5, 4]) + 1) * bs].all()
+
+
+def test_new_token_slots_follow_the_page_mapping():
+    """The generator's slot for each new token is the oracle's address of
+    logical position ctx - 1 (write first, then attend)."""
+    b = wl.make_batch([1, 4, 5, 33], num_heads=2, num_kv_heads=2, head_dim=64, block_size=4,
+                      dtype="f32", seed=1, write_new_token=True)
+    for s, c in enumerate(b.context_lens):
+        lb, off, pb = oracle.block_address(b.block_tables[s], int(c) - 1, b.block_size)
+        assert b.slot_mapping[s] == pb * b.block_size + off
+    assert len(np.unique(b.slot_mapping)) == len(b.slot_mapping)
+
+
+def test_determinism():
+    a = wl.make_batch([9, 30], num_heads=2, num_kv_heads=1, head_dim=128, block_size=8,
+                      dtype="f16", seed=42)
+    b = wl.make_batch([9, 30], num_heads=2, num_kv_heads=1, head_dim=128, block_size=8,
+                      dtype="f16", seed=42)
+    c = wl.make_batch([9, 30], num_heads=2, num_kv_heads=1, head_dim=128, block_size=8,
+                      dtype="f16", seed=43)
+    for f in ("query", "key_cache", "value_cache", "block_tables"):
+        assert np.array_equal(getattr(a, f), getattr(b, f))
+    assert not np.array_equal(a.key_cache, c.key_cache)
+
+
+def test_normal_fill_independent_of_threads():
+    ss = np.random.SeedSequence(5)
+    x = wl._normal_f32(ss, 3 * wl._CHUNK + 17, threads=1)
+    y = wl._normal_f32(np.random.SeedSequence(5), 3 * wl._CHUNK + 17, threads=4)
+    assert np.array_equal(x, y)
+    assert abs(float(x.mean())) < 5e-3 and abs(float(x.std()) - 1) < 5e-3
+
+
+def test_tiny_config():
+    b = wl.make_config("tiny_fp32")
+    assert b.context_lens.tolist() == [37] and b.block_size == 4 and b.num_blocks == 16
+    t = b.block_tables[0]
+    assert len(t) == 10 and len(np.unique(t)) == 10 and t.max() < 16
+    assert b.slot_mapping.tolist() == [int(t[9]) * 4 + 0]  # position 36: block 9, offset 0
+    assert b.scale == np.float32(0.125)
+
+
+def test_mha_config_layout():
+    b = wl.make_config("mha_fp16", values=False)
+    assert b.num_seqs == 32 and b.num_heads == b.num_kv_heads == 32 and b.block_size == 16
+    assert b.context_lens.min() >= 1 and b.context_lens.max() <= 4096
+    assert b.num_blocks == int(sum(-(-int(c) // 16) for c in b.context_lens)) + 1
+    _check_layout(b)
+
+
+def test_gqa_config_layout():
+    b = wl.make_config("gqa_bf16", values=False)
+    assert b.num_seqs == 256 and (b.num_heads, b.num_kv_heads, b.head_dim) == (32, 8, 128)
+    c = b.context_lens
+    assert c.min() >= 128 and c.max() <= 16000
+    # log-uniform: the log-lengths are spread evenly, the median sits near the geometric mean
+    med = float(np.median(c))
+    assert 0.5 * math.sqrt(128 * 16000) < med < 2 * math.sqrt(128 * 16000)
+    assert b.slot_mapping.shape == (256,)
+    _check_layout(b)
+    # pages of one sequence are not laid out consecutively
+    t = b.block_tables[int(np.argmax(c))]
+    n = -(-int(c.max()) // 16)
+    assert np.mean(np.diff(t[:n]) == 1) < 0.05
+
+
+def test_long_config_layout():
+    b = wl.make_config("long_bf16", values=False)
+    assert b.context_lens.tolist() == [32768] * 4 and b.block_size == 32
+    assert sorted(np.concatenate(_used(b)).tolist()) == list(range(4096))
+    assert b.partition_size == 512
+
+
+@pytest.mark.parametrize("bs", wl.PREFIX_BLOCK_SIZES)
+def test_prefix_config_layout(bs):
+    b = wl.make_config("prefix_fp16", block_size=bs)
+    assert b.num_seqs == 128
+    suffix = b.context_lens - 2048
+    assert suffix.min() >= 0 and suffix.max() <= 1024
+    _check_layout(b, shared_prefix_pages=2048 // bs)
+    assert b.unique_tokens == 2048 + int(suffix.sum())
+    assert b.kv_bytes_logical() > b.kv_bytes_unique()
+
+
+def test_prefix_logical_data_independent_of_block_size():
+    ref = None
+    for bs in wl.PREFIX_BLOCK_SIZES:
+        b = wl.make_config("prefix_fp16", block_size=bs)
+        rows = []
+        for s in (0, 64, 127):
+            keys, values = oracle.paged_gather(b.key_cache, b.value_cache, b.block_tables[s],
+                                               int(b.context_lens[s]), 3, "f16")
+            rows.append((keys, values))
+        if ref is None:
+            ref = rows
+        else:
+            for (k0, v0), (k1, v1) in zip(ref, rows):
+                assert np.array_equal(k0, k1) and np.array_equal(v0, v1)
+
+
+def test_byte_accounting():
+    b = wl.make_batch([10, 20], num_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
+                      dtype="bf16", seed=0, values=False)
+    assert b.kv_bytes_logical() == 30 * 2 * 128 * 2 * 2
