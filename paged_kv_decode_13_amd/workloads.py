@@ -80,7 +80,7 @@ class DecodeBatch:
 
     @property
     def num_blocks(self) -> int:
-        return int(self.key_cache.shape[0])
+        return int(self.meta.get("num_blocks", self.key_cache.shape[0]))
 
     @property
     def max_blocks_per_seq(self) -> int:
@@ -216,14 +216,15 @@ def _tail_rows(tables, context_lens, block_size) -> np.ndarray:
 def make_batch(context_lens, *, num_heads: int, num_kv_heads: int, head_dim: int,
                block_size: int, dtype: str, seed: int, write_new_token: bool = False,
                poison: bool = True, partition_size: int = 0, name: str = "custom",
-               table_slack: int = 0) -> DecodeBatch:
+               table_slack: int = 0, values: bool = True) -> DecodeBatch:
     """A decode batch over disjoint shuffled pages.
 
     With ``write_new_token`` each sequence with a non-empty context gets one new
     K/V row whose slot is its logical position ``ctx - 1`` (the token is
     written first, then attended to); its pool row starts out NaN when
     ``poison`` is set.  ``table_slack`` adds spare table columns (padded with
-    the spare block id)."""
+    the spare block id).  ``values=False`` builds the layout only (lengths,
+    tables, slots); the value arrays are then zero-size placeholders."""
     ctx = np.asarray(context_lens, dtype=np.int64).reshape(-1)
     if ctx.size and ctx.min() < 0:
         raise ValueError("context lengths must be >= 0")
@@ -237,9 +238,13 @@ def make_batch(context_lens, *, num_heads: int, num_kv_heads: int, head_dim: int
             [tables, np.full((tables.shape[0], table_slack), spare, np.int32)], axis=1)
     b = ctx.size
     shape = (nb, block_size, num_kv_heads, head_dim)
-    kc = _random_storage(s_k, shape, dtype)
-    vc = _random_storage(s_v, shape, dtype)
-    q = _random_storage(s_q, (b, num_heads, head_dim), dtype)
+    if values:
+        kc = _random_storage(s_k, shape, dtype)
+        vc = _random_storage(s_v, shape, dtype)
+        q = _random_storage(s_q, (b, num_heads, head_dim), dtype)
+    else:
+        kc = vc = np.zeros((0, block_size, num_kv_heads, head_dim), storage_dtype(dtype))
+        q = np.zeros((0, num_heads, head_dim), storage_dtype(dtype))
     batch = DecodeBatch(name=name, dtype=dtype, num_heads=num_heads, num_kv_heads=num_kv_heads,
                         head_dim=head_dim, block_size=block_size, query=q, key_cache=kc,
                         value_cache=vc, block_tables=tables,
@@ -249,10 +254,12 @@ def make_batch(context_lens, *, num_heads: int, num_kv_heads: int, head_dim: int
     if write_new_token:
         slots = np.array([_row_index(tables, s, int(c) - 1, block_size) if c > 0 else -1
                           for s, c in enumerate(ctx)], dtype=np.int64)
-        batch.new_key = _random_storage(s_nk, (b, num_kv_heads, head_dim), dtype)
-        batch.new_value = _random_storage(s_nv, (b, num_kv_heads, head_dim), dtype)
+        if values:
+            batch.new_key = _random_storage(s_nk, (b, num_kv_heads, head_dim), dtype)
+            batch.new_value = _random_storage(s_nv, (b, num_kv_heads, head_dim), dtype)
         batch.slot_mapping = slots
-    if poison:
+    batch.meta["num_blocks"] = nb
+    if poison and values:
         rows = [np.arange(spare * block_size, (spare + 1) * block_size, dtype=np.int64),
                 _tail_rows(tables, ctx, block_size)]
         if write_new_token:
@@ -363,8 +370,9 @@ def _prefix_fp16(seed: int, block_size: int, poison: bool) -> DecodeBatch:
 
 
 def make_config(name: str, *, block_size: int | None = None, seed: int | None = None,
-                poison: bool = True) -> DecodeBatch:
-    """One of the five named decode workloads (seeded; default seed per name)."""
+                poison: bool = True, values: bool = True) -> DecodeBatch:
+    """One of the five named decode workloads (seeded; default seed per name).
+    ``values=False`` (not for tiny_fp32 / prefix_fp16) builds the layout only."""
     seed = CONFIG_SEEDS[name] if seed is None else seed
     if name == "tiny_fp32":
         return _tiny_fp32(seed, poison)
@@ -375,17 +383,17 @@ def make_config(name: str, *, block_size: int | None = None, seed: int | None = 
         ctx = rng.integers(1, 4096, size=32, endpoint=True)
         return make_batch(ctx, num_heads=32, num_kv_heads=32, head_dim=128, block_size=16,
                           dtype="f16", seed=seed, poison=poison, partition_size=512,
-                          name=name)
+                          name=name, values=values)
     if name == "gqa_bf16":
         ctx = np.floor(np.exp(rng.uniform(math.log(128), math.log(16000), size=256)))
         ctx = np.clip(ctx, 128, 16000).astype(np.int64)
         return make_batch(ctx, num_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
                           dtype="bf16", seed=seed, write_new_token=True, poison=poison,
-                          partition_size=512, name=name)
+                          partition_size=512, name=name, values=values)
     if name == "long_bf16":
         return make_batch(np.full(4, 32768), num_heads=64, num_kv_heads=8, head_dim=128,
                           block_size=32, dtype="bf16", seed=seed, poison=poison,
-                          partition_size=512, name=name)
+                          partition_size=512, name=name, values=values)
     raise KeyError(name)
 
 
