@@ -88,7 +88,7 @@ def time_steps(batch, t, partition_size: int, steps: int, warmup: int):
                       device=t["q"].device)
     need = pkv.paged_decode_workspace_size(batch.num_seqs, batch.num_heads, batch.head_dim,
                                            batch.max_context_len, partition_size)
-    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=t["q"].device)
+    ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=t["q"].device)  # counter starts at zero
     has_write = "slots" in t
 
     def write():

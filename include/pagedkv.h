@@ -45,6 +45,10 @@ typedef enum pkv_dtype {
     PKV_BF16 = 2  /* bfloat16 */
 } pkv_dtype;
 
+/* Largest batch one paged_decode_attention call accepts (every workgroup keeps
+ * the batch's partition prefix sum in LDS). */
+#define PKV_MAX_SEQS 8192
+
 typedef enum pkv_status {
     PKV_OK = 0,
     PKV_ERR_NULL = 1,        /* a required pointer is NULL */
@@ -83,12 +87,12 @@ pkv_status paged_kv_write(const void *key, const void *value, void *key_cache,
                           int64_t num_blocks, pkv_dtype dtype, void *stream);
 
 /*
- * paged_decode_workspace_size -- bytes of scratch paged_decode_attention needs
- * when the context is split into KV partitions (0 when it is not split).
- * partition_size == 0 means one partition per sequence.  Layout (fp32):
- * partial outputs [num_seqs, num_heads, P, head_dim] followed by the
- * per-partition (running max, normaliser) pairs [num_seqs, num_heads, P, 2],
- * P = ceil(max_context_len / partition_size).
+ * paged_decode_workspace_size -- bytes of device scratch paged_decode_attention
+ * needs (0 only for an empty batch).  partition_size == 0 means one partition
+ * per sequence.  Layout: a 256-byte work-counter area, then, when the context
+ * is split (P = ceil(max_context_len / partition_size) > 1), fp32 partial
+ * outputs [num_seqs, num_heads, P, head_dim] and per-partition (running max,
+ * normaliser) pairs [num_seqs, num_heads, P, 2].
  */
 size_t paged_decode_workspace_size(int32_t num_seqs, int32_t num_heads,
                                    int32_t head_dim, int32_t max_context_len,
@@ -131,10 +135,16 @@ size_t paged_decode_workspace_size(int32_t num_seqs, int32_t num_heads,
  *                 second kernel merges by log-sum-exp
  *   dtype         PKV_F32, PKV_F16 or PKV_BF16; out_dtype is dtype or PKV_F32
  *   workspace     device scratch of at least paged_decode_workspace_size()
- *                 bytes (may be NULL when that is 0), 16-byte aligned
+ *                 bytes, 16-byte aligned, owned by the caller.  Its counter
+ *                 area must be zero before the first call that uses it (fill
+ *                 the buffer with zeros once when allocating it); every call
+ *                 leaves it zero again when its kernels finish.  Calls that
+ *                 can run at the same time (different streams) must use
+ *                 different workspaces.
  *
  * Accumulation is fp32 throughout.  Supported: head_dim in {64, 128};
- * block_size in {4, 8, 16, 32, 64}; G in {1, 2, 4, 8}.
+ * block_size in {4, 8, 16, 32, 64}; G in {1, 2, 4, 8}; num_seqs <=
+ * PKV_MAX_SEQS.
  */
 pkv_status paged_decode_attention(
     void *out, const void *query, const void *key_cache,

@@ -144,7 +144,10 @@ def paged_decode_attention(query, key_cache, value_cache, block_tables, context_
     (int32 [num_seqs]).  Returns ``out`` [num_seqs, num_heads, head_dim] in
     ``out_dtype`` (default: the cache dtype).  ``max_context_len`` is a host
     upper bound of ``context_lens``; ``partition_size`` > 0 splits contexts
-    into KV partitions merged by log-sum-exp."""
+    into KV partitions merged by log-sum-exp.  ``workspace`` (a uint8 GPU
+    buffer of ``paged_decode_workspace_size`` bytes) may be passed to avoid an
+    allocation per call: zero it once when allocating it; calls leave it
+    zeroed."""
     torch = _torch()
     lib = _load()
     for t, n in ((query, "query"), (key_cache, "key_cache"), (value_cache, "value_cache"),
@@ -175,7 +178,8 @@ def paged_decode_attention(query, key_cache, value_cache, block_tables, context_
     ws_ptr, ws_bytes = None, 0
     if need:
         if workspace is None:
-            workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
+            # the work counter at its start must be zero before first use
+            workspace = torch.zeros(need, dtype=torch.uint8, device=query.device)
         else:
             _gpu(workspace, "workspace")
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()

@@ -34,47 +34,9 @@
 // Scores are kept in the exp2 domain (scale * log2 e folded into q).
 #include <math.h>
 
-#include "pkv_device.h"
-#include "pkv_launch.h"
+#include "pkv_decode_common.h"
 
 namespace pkv {
-
-constexpr int kNumWaves = 4;
-constexpr int kThreads = kNumWaves * kWave;
-constexpr int kSegPages = 256;  // page ids staged in LDS at a time
-
-struct UnitPos {
-    int s, kvh, p;
-};
-
-__device__ __forceinline__ UnitPos unit_pos(const DecodeArgs &a) {
-    // KV head fastest: the units that read the same pages run side by side.
-    int u = blockIdx.x;
-    UnitPos r;
-    r.kvh = u % a.num_kv_heads;
-    u /= a.num_kv_heads;
-    r.p = u % a.num_partitions;
-    r.s = u / a.num_partitions;
-    return r;
-}
-
-// A context length the grid or the table cannot cover makes the sequence's
-// output NaN instead of reading outside the table.
-__device__ __forceinline__ bool bad_context(const DecodeArgs &a, int ctx) {
-    return ctx < 0 || ctx > a.max_context_len ||
-           (int64_t)ctx > (int64_t)a.max_blocks_per_seq * a.block_size;
-}
-
-template <int DT>
-__device__ __forceinline__ void store_out(const DecodeArgs &a, int64_t idx, float v) {
-    if (a.out_f32) {
-        reinterpret_cast<float *>(a.out)[idx] = v;
-    } else if constexpr (DT == kF32) {
-        reinterpret_cast<float *>(a.out)[idx] = v;
-    } else {
-        reinterpret_cast<uint16_t *>(a.out)[idx] = f32_to_bits16<DT>(v);
-    }
-}
 
 template <int DT, int D, int G>
 __global__ __launch_bounds__(kThreads) void paged_decode_valu_kernel(DecodeArgs a) {
@@ -99,14 +61,10 @@ __global__ __launch_bounds__(kThreads) void paged_decode_valu_kernel(DecodeArgs 
     const int rg = lane / LPR;  // row group inside the wave
     const int li = lane % LPR;  // 16-byte column inside the row
 
-    const UnitPos up = unit_pos(a);
-    const int ctx = a.context_lens[up.s];
-    const bool bad_len = bad_context(a, ctx);
-    const int tok_begin = up.p * a.partition_size;
-    if (up.p > 0 && (bad_len || tok_begin >= ctx)) return;  // empty unit
-    const int tok_end = bad_len ? 0 : min(ctx, tok_begin + a.partition_size);
-    const int nparts = (bad_len || ctx == 0) ? 1 : (ctx + a.partition_size - 1) / a.partition_size;
-
+    const Unit up = make_unit(a);
+    if (up.empty) return;
+    const int tok_begin = up.tok_begin;
+    const int tok_end = up.tok_end;
     if (tid == 0) s_bad = 0;
 
     // query rows of the head group, pre-scaled into the exp2 domain
@@ -136,21 +94,13 @@ __global__ __launch_bounds__(kThreads) void paged_decode_valu_kernel(DecodeArgs 
     const char *vbase = reinterpret_cast<const char *>(a.value_cache);
     const int bs = a.block_size;
     const int lbs = a.log2_block_size;
-    const int32_t *table = a.block_tables + (int64_t)up.s * a.max_blocks_per_seq;
 
     for (int seg = tok_begin; seg < tok_end; seg += kSegPages << lbs) {
         const int seg_end = min(tok_end, seg + (kSegPages << lbs));
         const int lb0 = seg >> lbs;
         const int npages = (seg_end - seg + bs - 1) >> lbs;
         __syncthreads();  // previous segment's readers are done with s_pages
-        for (int i = tid; i < npages; i += kThreads) {
-            int pb = table[lb0 + i];
-            if (pb < 0 || (int64_t)pb >= a.num_blocks) {
-                s_bad = 1;
-                pb = -1;
-            }
-            s_pages[i] = pb;
-        }
+        stage_pages(a, up, lb0, npages, s_pages, &s_bad);
         __syncthreads();
 
         for (int c = seg + wave * CHUNK; c < seg_end; c += kNumWaves * CHUNK) {
@@ -253,34 +203,7 @@ __global__ __launch_bounds__(kThreads) void paged_decode_valu_kernel(DecodeArgs 
     }
     __syncthreads();
 
-    const bool bad = bad_len || s_bad != 0;
-    for (int i = tid; i < G * D; i += kThreads) {
-        const int g = i / D;
-        const int d = i % D;
-        float M = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < kNumWaves; ++w) M = fmaxf(M, s_m[w][g]);
-        float L = 0.f, O = 0.f;
-#pragma unroll
-        for (int w = 0; w < kNumWaves; ++w) {
-            const float f = (M == -INFINITY) ? 0.f : fast_exp2(s_m[w][g] - M);
-            L += s_l[w][g] * f;
-            O += s_acc[w][g][d] * f;
-        }
-        float res = L > 0.f ? O / L : 0.f;  // empty context -> zeros
-        if (bad) res = __builtin_nanf("");
-        const int h = h0 + g;
-        if (nparts == 1) {
-            store_out<DT>(a, ((int64_t)up.s * a.num_heads + h) * D + d, res);
-        } else {
-            const int64_t slot = ((int64_t)up.s * a.num_heads + h) * a.num_partitions + up.p;
-            a.part_out[slot * D + d] = res;
-            if (d == 0) {
-                a.part_ml[slot * 2] = bad ? __builtin_nanf("") : M;
-                a.part_ml[slot * 2 + 1] = L;
-            }
-        }
-    }
+    unit_epilogue<DT, D, G>(a, up, up.bad_len || s_bad != 0, s_m, s_l, s_acc);
 }
 
 // Log-sum-exp merge of the partitions of one (sequence, query head):
@@ -318,41 +241,53 @@ __global__ __launch_bounds__(kWave) void lse_merge_kernel(DecodeArgs a) {
 }
 
 template <int DT, int D, int G>
-static hipError_t launch_typed(const DecodeArgs &a, hipStream_t stream) {
+static hipError_t launch_valu(const DecodeArgs &a, hipStream_t stream) {
     const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * a.num_partitions;
     hipLaunchKernelGGL((paged_decode_valu_kernel<DT, D, G>), dim3((unsigned)units), dim3(kThreads), 0,
                        stream, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || a.num_partitions <= 1) return e;
+    return hipGetLastError();
+}
+
+template <int DT, int D>
+static hipError_t launch_valu_group(const DecodeArgs &a, hipStream_t stream) {
+    switch (a.num_heads / a.num_kv_heads) {
+        case 1: return launch_valu<DT, D, 1>(a, stream);
+        case 2: return launch_valu<DT, D, 2>(a, stream);
+        case 4: return launch_valu<DT, D, 4>(a, stream);
+        case 8: return launch_valu<DT, D, 8>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int DT, int D>
+static hipError_t launch_merge(const DecodeArgs &a, hipStream_t stream) {
+    if (a.num_partitions <= 1) return hipSuccess;
     const int64_t rows = (int64_t)a.num_seqs * a.num_heads;
     hipLaunchKernelGGL((lse_merge_kernel<DT, D>), dim3((unsigned)rows), dim3(kWave), 0, stream, a);
     return hipGetLastError();
 }
 
-template <int DT, int D>
-static hipError_t launch_group(const DecodeArgs &a, hipStream_t stream) {
-    switch (a.num_heads / a.num_kv_heads) {
-        case 1: return launch_typed<DT, D, 1>(a, stream);
-        case 2: return launch_typed<DT, D, 2>(a, stream);
-        case 4: return launch_typed<DT, D, 4>(a, stream);
-        case 8: return launch_typed<DT, D, 8>(a, stream);
-        default: return hipErrorInvalidValue;
-    }
-}
-
 template <int DT>
-static hipError_t launch_dim(const DecodeArgs &a, int head_dim, hipStream_t stream) {
-    if (head_dim == 64) return launch_group<DT, 64>(a, stream);
-    if (head_dim == 128) return launch_group<DT, 128>(a, stream);
+static hipError_t launch_dtype(const DecodeArgs &a, int head_dim, hipStream_t stream) {
+    hipError_t e;
+    if (head_dim == 128) {
+        // 16-bit caches take the matrix-core kernel; binary32 the VALU kernel
+        e = (DT == kF32) ? launch_valu_group<DT, 128>(a, stream) : launch_paged_decode_mfma(a, DT, stream);
+        return e != hipSuccess ? e : launch_merge<DT, 128>(a, stream);
+    }
+    if (head_dim == 64) {
+        e = launch_valu_group<DT, 64>(a, stream);
+        return e != hipSuccess ? e : launch_merge<DT, 64>(a, stream);
+    }
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_paged_decode(const DecodeArgs &a, int dtype, int head_dim, hipStream_t stream) {
     if ((int64_t)a.num_seqs * a.num_kv_heads * a.num_partitions == 0) return hipSuccess;
     switch (dtype) {
-        case kF32: return launch_dim<kF32>(a, head_dim, stream);
-        case kF16: return launch_dim<kF16>(a, head_dim, stream);
-        case kBF16: return launch_dim<kBF16>(a, head_dim, stream);
+        case kF32: return launch_dtype<kF32>(a, head_dim, stream);
+        case kF16: return launch_dtype<kF16>(a, head_dim, stream);
+        case kBF16: return launch_dtype<kBF16>(a, head_dim, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -1,0 +1,397 @@
+// Fused paged decode attention with the score product on the matrix cores
+// (gfx950 v_mfma_f32_16x16x32_{bf16,f16}), for 16-bit caches and head_dim 128.
+//
+// Same computation as the VALU kernel (pages on PagedAttention:
+// "实现教学版 PagedAttention：从 block table 读取历史 KV cache", sections
+// "从逻辑 token 到物理 block" and "从 gather 后的 K/V 做 attention";
+// "从正确到更快：PagedAttention 的优化路线", sections "高性能 PagedAttention 的核心
+// 思想" and "attention kernel 真正在做什么").  With a query-head group the
+// score step of a 16-token tile is a small dense product
+//     S[16 tokens x 16] = K_tile[16 x 128] . Q^T[128 x 16]
+// whose 16 columns carry the group's heads (replicated when G < 4; two
+// products of 4 heads each when G = 8).  Four MFMAs (k = 32 each) per tile
+// replace the dot-product and lane-reduction work of the VALU kernel.
+//
+// Work distribution: a persistent grid (as many workgroups as fit on the
+// chip) draws work units (sequence, KV partition, KV head) one at a time from
+// a counter, KV head fastest so that the units reading the same pages run
+// side by side.  Each workgroup first builds, in LDS, the prefix sum of
+// partitions over the sequences of the batch, which maps a unit index to its
+// sequence and partition; no workgroup is spent on a partition past the end
+// of its sequence, and no workgroup idles while units remain.
+//
+// Lane roles inside a wave (lane = 16 q + c):
+//  - K operand: lane reads token c of the tile, 16-byte chunks 4j + q
+//    (j = 0..3): each load instruction covers 64 contiguous bytes of 16 rows.
+//    The query operand uses the same chunk order, so the contraction pairs
+//    equal head-dim indices.
+//  - Scores come back as rows 4q + r (r = 0..3) of the tile for head c % 4
+//    (+4 for the second product): lane (q, c) owns tokens 4q..4q+3.
+//  - V is read in plain row order: lane (q, c) loads 16-byte chunk c of the
+//    same tokens 4q + r, so every lane already holds its tokens' scores; the
+//    other heads' probabilities come from the lanes of its quad (DPP quad
+//    broadcast).  The running softmax is kept per lane and per row group q
+//    and merged at the end, so the tile loop needs no cross-lane max.
+//  - The loads of a wave's next tile are issued before the current tile is
+//    computed (two register sets), so HBM requests stay in flight while the
+//    wave computes.
+#include <math.h>
+
+#include "pkv_decode_common.h"
+
+#ifndef PKV_TILES_PER_STEP
+#define PKV_TILES_PER_STEP 2
+#endif
+
+namespace pkv {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <int DT>
+__device__ __forceinline__ f32x4_t mfma_16x16x32(const u32x4 a, const u32x4 b, f32x4_t c) {
+    if constexpr (DT == kBF16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                      __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+// Value of head slot `hl` (0 <= hl < HS) held by the lanes of this lane's quad:
+// lane c of a quad carries head slot c % HS.
+template <int HS>
+__device__ __forceinline__ float head_bcast(float x, int hl) {
+    if constexpr (HS == 1) {
+        return x;
+    } else if constexpr (HS == 2) {
+        return hl == 0 ? dpp<0xA0>(x) : dpp<0xF5>(x);  // quad_perm [0,0,2,2] / [1,1,3,3]
+    } else {
+        switch (hl) {
+            case 0: return dpp<0x00>(x);  // quad_perm [0,0,0,0]
+            case 1: return dpp<0x55>(x);  // [1,1,1,1]
+            case 2: return dpp<0xAA>(x);  // [2,2,2,2]
+            default: return dpp<0xFF>(x); // [3,3,3,3]
+        }
+    }
+}
+
+struct TileRegs {
+    u32x4 k[4];      // token c, chunks 4j + q
+    u32x4 v[4];      // tokens 4q + r, chunk c
+    uint32_t vmask;  // bit r: V row r holds a valid token
+};
+
+// Partitions of a sequence in the work list (an empty or out-of-range
+// context still gets one unit, which writes its zeros or NaNs).
+__device__ __forceinline__ int seq_parts(const DecodeArgs &a, int ctx) {
+    if (bad_context(a, ctx) || ctx == 0) return 1;
+    return (ctx + a.partition_size - 1) / a.partition_size;
+}
+
+// Exclusive prefix of seq_parts over the batch into s_prefix[0..B], using
+// s_scan (kThreads ints) as scratch; lengths cached in s_ctx.
+__device__ __forceinline__ void build_prefix(const DecodeArgs &a, int *s_prefix, int *s_ctx, int *s_scan) {
+    const int B = a.num_seqs;
+    const int tid = threadIdx.x;
+    const int chunk = (B + kThreads - 1) / kThreads;
+    const int lo = min(B, tid * chunk), hi = min(B, lo + chunk);
+    int sum = 0;
+    for (int s = lo; s < hi; ++s) {
+        const int ctx = a.context_lens[s];
+        s_ctx[s] = ctx;
+        sum += seq_parts(a, ctx);
+    }
+    s_scan[tid] = sum;
+    __syncthreads();
+    for (int off = 1; off < kThreads; off <<= 1) {
+        const int v = tid >= off ? s_scan[tid - off] : 0;
+        __syncthreads();
+        s_scan[tid] += v;
+        __syncthreads();
+    }
+    int run = s_scan[tid] - sum;
+    for (int s = lo; s < hi; ++s) {
+        s_prefix[s] = run;
+        run += seq_parts(a, s_ctx[s]);
+    }
+    if (tid == kThreads - 1) s_prefix[B] = s_scan[tid];
+    __syncthreads();
+}
+
+template <int DT, int G>
+__global__ __launch_bounds__(kThreads) void paged_decode_mfma_kernel(DecodeArgs a) {
+    constexpr int D = 128;
+    constexpr int ROW_BYTES = D * 2;
+    constexpr int TILE = 16;
+    constexpr int HS = G < 4 ? G : 4;  // heads per score product
+    constexpr int NSET = G / HS;       // score products per tile
+
+    extern __shared__ int s_dyn[];     // prefix [B + 1], then lengths [B]
+    __shared__ int s_pages[kSegPages];
+    __shared__ int s_bad;
+    __shared__ float s_m[kNumWaves][G];
+    __shared__ float s_l[kNumWaves][G];
+    __shared__ float s_acc[kNumWaves][G][D];
+
+    int *s_prefix = s_dyn;
+    int *s_ctx = s_dyn + a.num_seqs + 1;
+    build_prefix(a, s_prefix, s_ctx, s_pages);
+    const int total_units = s_prefix[a.num_seqs] * a.num_kv_heads;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    // wave-uniform (scalar) so that the tile loop is a scalar loop
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int q = lane >> 4;  // row group: tokens 4q..4q+3 of a tile
+    const int c = lane & 15;  // column: head slot c % HS; V chunk c
+
+    const char *kbase = reinterpret_cast<const char *>(a.key_cache);
+    const char *vbase = reinterpret_cast<const char *>(a.value_cache);
+    const int bs = a.block_size;
+    const int lbs = a.log2_block_size;
+    const int64_t tok_stride = (int64_t)a.num_kv_heads * ROW_BYTES;  // bytes between slots
+    const float sl2 = a.scale_log2e;
+
+    // Units are handed out one at a time from a counter in the workspace, so
+    // a workgroup that drew short units simply takes more: with a static
+    // assignment the chip idles while the unluckiest workgroups finish.
+    // Every workgroup ends with exactly one failed draw; the draw that sees
+    // the last ticket of the launch (total + grid - 1) resets the counter to
+    // zero for the next call on this workspace.
+    __shared__ int s_unit;
+    for (;;) {
+        __syncthreads();  // previous unit's epilogue is done with LDS
+        if (threadIdx.x == 0) {
+            const unsigned got = atomicAdd(a.work_counter, 1u);
+            if (got == (unsigned)total_units + gridDim.x - 1u) atomicExch(a.work_counter, 0u);
+            s_unit = (int)got;
+        }
+        __syncthreads();
+        const int unit = s_unit;
+        if (unit >= total_units) break;
+        // unit -> (sequence, partition, KV head)
+        Unit u;
+        u.kvh = unit % a.num_kv_heads;
+        const int sp = unit / a.num_kv_heads;
+        int lo = 0, hi = a.num_seqs;  // largest s with s_prefix[s] <= sp
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (s_prefix[mid] <= sp) lo = mid; else hi = mid;
+        }
+        u.s = lo;
+        u.p = sp - s_prefix[lo];
+        u.ctx = s_ctx[lo];
+        u.bad_len = bad_context(a, u.ctx);
+        u.tok_begin = u.p * a.partition_size;
+        u.tok_end = u.bad_len ? 0 : min(u.ctx, u.tok_begin + a.partition_size);
+        u.nparts = seq_parts(a, u.ctx);
+        u.empty = false;
+
+        if (tid == 0) s_bad = 0;
+
+        // query operand: head (set*HS + c%HS), chunks 4j + q
+        const int h0 = u.kvh * G;
+        u32x4 qop[NSET][4];
+        {
+            const char *qb = reinterpret_cast<const char *>(a.query);
+#pragma unroll
+            for (int set = 0; set < NSET; ++set) {
+                const int h = h0 + set * HS + (c % HS);
+                const char *row = qb + ((int64_t)u.s * a.num_heads + h) * ROW_BYTES;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) qop[set][j] = load16(row + (4 * j + q) * 16);
+            }
+        }
+
+        float m[NSET], l[NSET], acc[G][8];
+#pragma unroll
+        for (int set = 0; set < NSET; ++set) {
+            m[set] = -INFINITY;
+            l[set] = 0.f;
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
+
+        const int64_t kvh_off = (int64_t)u.kvh * ROW_BYTES;
+
+        for (int seg = u.tok_begin; seg < u.tok_end; seg += kSegPages << lbs) {
+            const int seg_end = min(u.tok_end, seg + (kSegPages << lbs));
+            const int npages = (seg_end - seg + bs - 1) >> lbs;
+            __syncthreads();  // previous segment's readers are done with s_pages
+            stage_pages(a, u, seg >> lbs, npages, s_pages, &s_bad);
+            __syncthreads();
+
+            // token -> byte offset of its row in the pool.  Loads are issued
+            // unconditionally so the compiler can count outstanding loads
+            // exactly and keep the next tile's loads in flight: a token past
+            // the segment or on a bad page id reads a row of page 0 (always
+            // in the pool) and is flagged invalid; invalid V rows are zeroed
+            // where they are consumed and invalid scores are masked.
+            auto row_of = [&](int t, bool &valid) -> int64_t {
+                const int pb = s_pages[min((t - seg) >> lbs, npages - 1)];
+                valid = (t < seg_end) & (pb >= 0);
+                const int64_t page = valid ? pb : 0;
+                return (page * bs + (t & (bs - 1))) * tok_stride + kvh_off;
+            };
+            auto load_tile = [&](TileRegs &r, int t0) {
+                bool kok;
+                const char *kp = kbase + row_of(t0 + c, kok);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) r.k[j] = load16_stream(kp + (4 * j + q) * 16);
+                r.vmask = 0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    bool vok;
+                    r.v[i] = load16_stream(vbase + row_of(t0 + 4 * q + i, vok) + c * 16);
+                    r.vmask |= vok ? (1u << i) : 0u;
+                }
+            };
+            auto compute_tile = [&](const TileRegs &r, int t0) {
+                float p[NSET][4], alpha[NSET];
+#pragma unroll
+                for (int set = 0; set < NSET; ++set) {
+                    f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) sacc = mfma_16x16x32<DT>(r.k[j], qop[set][j], sacc);
+                    float sv[4];
+                    float mt = -INFINITY;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        sv[i] = (t0 + 4 * q + i < seg_end) ? sacc[i] * sl2 : -INFINITY;
+                        mt = fmaxf(mt, sv[i]);
+                    }
+                    const float mn = fmaxf(m[set], mt);
+                    const bool none = mn == -INFINITY;
+                    alpha[set] = none ? 1.f : fast_exp2(m[set] - mn);
+                    float ps = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        p[set][i] = none ? 0.f : fast_exp2(sv[i] - mn);
+                        ps += p[set][i];
+                    }
+                    l[set] = l[set] * alpha[set] + ps;
+                    m[set] = mn;
+                }
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const float ag = head_bcast<HS>(alpha[g / HS], g % HS);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[g][e] *= ag;
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float vf[8];
+                    unpack16<DT>((r.vmask >> i) & 1u ? r.v[i] : u32x4{0, 0, 0, 0}, vf);
+#pragma unroll
+                    for (int g = 0; g < G; ++g) {
+                        const float pg = head_bcast<HS>(p[g / HS][i], g % HS);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(pg, vf[e], acc[g][e]);
+                    }
+                }
+            };
+
+            // Each wave step issues the loads of TPS consecutive tiles at
+            // once and then computes them in order, so up to TPS * 8 KiB of
+            // HBM requests per wave are in flight while earlier tiles are
+            // computed.  Straight-line code: the compiler waits for exactly
+            // the loads a tile needs.  A tile past the segment is all
+            // invalid and computes to no change.
+            constexpr int TPS = PKV_TILES_PER_STEP;
+            constexpr int STEP = kNumWaves * TILE * TPS;
+            for (int t = seg + wave * TILE * TPS; t < seg_end; t += STEP) {
+                TileRegs r[TPS];
+#pragma unroll
+                for (int i = 0; i < TPS; ++i) load_tile(r[i], t + i * TILE);
+                // keep every load of the step ahead of the compute: left
+                // alone, the scheduler sinks each load next to its use and
+                // the wave then waits on one load at a time
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < TPS; ++i) compute_tile(r[i], t + i * TILE);
+            }
+        }
+
+        // merge the four row groups q of this wave (lanes c, c+16, c+32, c+48)
+        float f[NSET];
+#pragma unroll
+        for (int set = 0; set < NSET; ++set) {
+            float M = fmaxf(m[set], __shfl_xor(m[set], 16));
+            M = fmaxf(M, __shfl_xor(M, 32));
+            f[set] = (M == -INFINITY) ? 0.f : fast_exp2(m[set] - M);
+            float L = l[set] * f[set];
+            L += __shfl_xor(L, 16);
+            L += __shfl_xor(L, 32);
+            m[set] = M;
+            l[set] = L;
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const float fg = head_bcast<HS>(f[g / HS], g % HS);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float x = acc[g][e] * fg;
+                x += __shfl_xor(x, 16);
+                x += __shfl_xor(x, 32);
+                acc[g][e] = x;
+            }
+        }
+        if (q == 0) {
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) s_acc[wave][g][c * 8 + e] = acc[g][e];
+            if (c < HS) {
+#pragma unroll
+                for (int set = 0; set < NSET; ++set) {
+                    s_m[wave][set * HS + c] = m[set];
+                    s_l[wave][set * HS + c] = l[set];
+                }
+            }
+        }
+        __syncthreads();
+        unit_epilogue<DT, D, G>(a, u, u.bad_len || s_bad != 0, s_m, s_l, s_acc);
+    }
+}
+
+// Persistent grid: as many workgroups as are resident at once (queried once
+// per kernel and LDS size), capped by the number of units.
+template <typename K>
+static hipError_t launch_persistent(K kernel, const DecodeArgs &a, hipStream_t stream) {
+    const size_t dyn = (size_t)(2 * a.num_seqs + 1) * sizeof(int);
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(kernel),
+                                                         kThreads, dyn);
+    if (e != hipSuccess) return e;
+    int64_t grid = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
+    const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * a.num_partitions;  // upper bound
+    if (grid > units) grid = units;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), dyn, stream, a);
+    return hipGetLastError();
+}
+
+template <int DT>
+static hipError_t launch_group(const DecodeArgs &a, hipStream_t stream) {
+    switch (a.num_heads / a.num_kv_heads) {
+        case 1: return launch_persistent(paged_decode_mfma_kernel<DT, 1>, a, stream);
+        case 2: return launch_persistent(paged_decode_mfma_kernel<DT, 2>, a, stream);
+        case 4: return launch_persistent(paged_decode_mfma_kernel<DT, 4>, a, stream);
+        case 8: return launch_persistent(paged_decode_mfma_kernel<DT, 8>, a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_paged_decode_mfma(const DecodeArgs &a, int dtype, hipStream_t stream) {
+    if (dtype == kBF16) return launch_group<kBF16>(a, stream);
+    if (dtype == kF16) return launch_group<kF16>(a, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace pkv

@@ -5,7 +5,7 @@
 #include <math.h>
 #include <stdint.h>
 
-#include "../../include/pagedkv.h"
+#include "pagedkv.h"
 #include "pkv_launch.h"
 
 namespace {
@@ -27,6 +27,10 @@ int log2i(int32_t v) {
 // Tokens per decode work unit: every partition starts on a page boundary and
 // on a 16-token boundary.
 int32_t partition_granule(int32_t block_size) { return block_size > 16 ? block_size : 16; }
+
+// Workspace layout: the unit counter in the first kCounterBytes, then the
+// split partials (fp32 outputs, then (max, normaliser) pairs).
+constexpr size_t kCounterBytes = 256;
 
 int32_t num_partitions(int32_t max_context_len, int32_t partition_size) {
     if (partition_size <= 0 || max_context_len <= 0) return 1;
@@ -81,8 +85,8 @@ size_t paged_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t 
                                    int32_t max_context_len, int32_t partition_size) {
     if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0) return 0;
     const int32_t p = num_partitions(max_context_len, partition_size);
-    if (p <= 1) return 0;
-    return (size_t)num_seqs * num_heads * p * (size_t)(head_dim + 2) * sizeof(float);
+    if (p <= 1) return kCounterBytes;
+    return kCounterBytes + (size_t)num_seqs * num_heads * p * (size_t)(head_dim + 2) * sizeof(float);
 }
 
 pkv_status paged_decode_attention(void *out, const void *query, const void *key_cache,
@@ -106,7 +110,9 @@ pkv_status paged_decode_attention(void *out, const void *query, const void *key_
     if (partition_size != 0 && partition_size % partition_granule(block_size) != 0)
         return PKV_ERR_UNSUPPORTED;
     if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size) return PKV_ERR_SHAPE;
+    if (num_blocks == 0 && max_context_len > 0) return PKV_ERR_SHAPE;  // no page to read
     if (!isfinite(scale)) return PKV_ERR_SHAPE;
+    if (num_seqs > PKV_MAX_SEQS) return PKV_ERR_UNSUPPORTED;
     if (num_seqs == 0) return PKV_OK;
     if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens)
         return PKV_ERR_NULL;
@@ -117,12 +123,13 @@ pkv_status paged_decode_attention(void *out, const void *query, const void *key_
     const int64_t units = (int64_t)num_seqs * num_kv_heads * parts;
     if (units > INT_MAX || (int64_t)num_seqs * num_heads > INT_MAX) return PKV_ERR_SHAPE;
     pkv::DecodeArgs a = {};
+    const size_t need = paged_decode_workspace_size(num_seqs, num_heads, head_dim, max_context_len,
+                                                    partition_size);
+    if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return PKV_ERR_ALIGN;
+    a.work_counter = reinterpret_cast<unsigned *>(workspace);
     if (parts > 1) {
-        const size_t need = paged_decode_workspace_size(num_seqs, num_heads, head_dim,
-                                                        max_context_len, partition_size);
-        if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
-        if (!aligned16(workspace)) return PKV_ERR_ALIGN;
-        a.part_out = reinterpret_cast<float *>(workspace);
+        a.part_out = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + kCounterBytes);
         a.part_ml = a.part_out + (size_t)num_seqs * num_heads * parts * head_dim;
     }
     a.out = out;

@@ -1,0 +1,118 @@
+// Pieces shared by the two fused decode kernels: work-unit bookkeeping,
+// staging of page ids in LDS, and the cross-wave epilogue (merge of the
+// waves' running softmax states, then the output or the partition partial).
+#pragma once
+
+#include <math.h>
+
+#include "pkv_device.h"
+#include "pkv_launch.h"
+
+namespace pkv {
+
+constexpr int kNumWaves = 4;
+constexpr int kThreads = kNumWaves * kWave;
+constexpr int kSegPages = 256;  // page ids staged in LDS at a time
+
+struct Unit {
+    int s, kvh, p;
+    int ctx;
+    int tok_begin, tok_end;  // token range of this unit
+    int nparts;              // partitions of this sequence (1: write out directly)
+    bool bad_len;            // length outside what the table / grid can cover
+    bool empty;              // unit past the end of its sequence: exit
+};
+
+// A context length the grid or the table cannot cover makes the sequence's
+// output NaN instead of reading outside the table.
+__device__ __forceinline__ bool bad_context(const DecodeArgs &a, int ctx) {
+    return ctx < 0 || ctx > a.max_context_len ||
+           (int64_t)ctx > (int64_t)a.max_blocks_per_seq * a.block_size;
+}
+
+__device__ __forceinline__ Unit make_unit(const DecodeArgs &a) {
+    // KV head fastest: the units that read the same pages run side by side.
+    int u = blockIdx.x;
+    Unit r;
+    r.kvh = u % a.num_kv_heads;
+    u /= a.num_kv_heads;
+    r.p = u % a.num_partitions;
+    r.s = u / a.num_partitions;
+    r.ctx = a.context_lens[r.s];
+    r.bad_len = bad_context(a, r.ctx);
+    r.tok_begin = r.p * a.partition_size;
+    r.empty = r.p > 0 && (r.bad_len || r.tok_begin >= r.ctx);
+    r.tok_end = r.bad_len ? 0 : min(r.ctx, r.tok_begin + a.partition_size);
+    r.nparts = (r.bad_len || r.ctx == 0) ? 1 : (r.ctx + a.partition_size - 1) / a.partition_size;
+    return r;
+}
+
+// Stage the physical block ids of logical blocks [lb0, lb0 + npages) of the
+// sequence in LDS (-1 and a flag for ids outside the pool).  Caller brackets
+// with __syncthreads().
+__device__ __forceinline__ void stage_pages(const DecodeArgs &a, const Unit &u, int lb0, int npages,
+                                            int *s_pages, int *s_bad) {
+    const int32_t *table = a.block_tables + (int64_t)u.s * a.max_blocks_per_seq;
+    for (int i = threadIdx.x; i < npages; i += kThreads) {
+        int pb = table[lb0 + i];
+        if (pb < 0 || (int64_t)pb >= a.num_blocks) {
+            *s_bad = 1;
+            pb = -1;
+        }
+        s_pages[i] = pb;
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ void store_out(const DecodeArgs &a, int64_t idx, float v) {
+    if (a.out_f32) {
+        reinterpret_cast<float *>(a.out)[idx] = v;
+    } else if constexpr (DT == kF32) {
+        reinterpret_cast<float *>(a.out)[idx] = v;
+    } else {
+        reinterpret_cast<uint16_t *>(a.out)[idx] = f32_to_bits16<DT>(v);
+    }
+}
+
+// Merge the per-wave states (running max m, normaliser l, unnormalised
+// accumulator) of one unit and store either the final output (one partition)
+// or the partition's normalised partial with its (m, l).
+template <int DT, int D, int G>
+__device__ __forceinline__ void unit_epilogue(const DecodeArgs &a, const Unit &u, bool bad,
+                                              const float (*s_m)[G], const float (*s_l)[G],
+                                              const float (*s_acc)[G][D]) {
+    const int h0 = u.kvh * G;
+    for (int i = threadIdx.x; i < G * D; i += kThreads) {
+        const int g = i / D;
+        const int d = i % D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kNumWaves; ++w) M = fmaxf(M, s_m[w][g]);
+        float L = 0.f, O = 0.f;
+#pragma unroll
+        for (int w = 0; w < kNumWaves; ++w) {
+            const float f = (M == -INFINITY) ? 0.f : fast_exp2(s_m[w][g] - M);
+            L += s_l[w][g] * f;
+            O += s_acc[w][g][d] * f;
+        }
+        float res = L > 0.f ? O / L : 0.f;  // empty context -> zeros
+        if (bad) res = __builtin_nanf("");
+        const int h = h0 + g;
+        if (u.nparts == 1) {
+            store_out<DT>(a, ((int64_t)u.s * a.num_heads + h) * D + d, res);
+        } else {
+            const int64_t slot = ((int64_t)u.s * a.num_heads + h) * a.num_partitions + u.p;
+            a.part_out[slot * D + d] = res;
+            if (d == 0) {
+                a.part_ml[slot * 2] = bad ? __builtin_nanf("") : M;
+                a.part_ml[slot * 2 + 1] = L;
+            }
+        }
+    }
+}
+
+// MFMA decode kernel launcher (16-bit caches, head_dim 128); the merge
+// kernel is launched by the caller.
+hipError_t launch_paged_decode_mfma(const DecodeArgs &a, int dtype, hipStream_t stream);
+
+}  // namespace pkv

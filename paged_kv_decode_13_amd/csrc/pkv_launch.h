@@ -21,6 +21,7 @@ struct WriteArgs {
 
 struct DecodeArgs {
     void *out;                  // [B, H, D] (out dtype)
+    unsigned *work_counter;     // unit dispenser of the persistent kernel (zero between calls)
     float *part_out;            // [B, H, P, D] when split
     float *part_ml;             // [B, H, P, 2] when split
     const void *query;          // [B, H, D]

@@ -82,6 +82,7 @@ def test_decode_validation(lib):
     assert _decode(lib, h=30) == SHAPE  # 30 % 8 != 0
     assert _decode(lib, maxc=64 * 16 + 1) == SHAPE  # table cannot hold max_context_len
     assert _decode(lib, scale=float("nan")) == SHAPE
+    assert _decode(lib, nb=0) == SHAPE  # contexts but no pages
     assert _decode(lib, dt=5) == DTYPE
     assert _decode(lib, odt=F16) == DTYPE  # bf16 cache, fp16 out
     assert _decode(lib, d=96) == UNSUP
@@ -89,6 +90,7 @@ def test_decode_validation(lib):
     assert _decode(lib, h=128, kvh=8) == UNSUP  # group of 16
     assert _decode(lib, ps=24) == UNSUP  # not a multiple of 16
     assert _decode(lib, bs=32, mb=32, ps=16) == UNSUP  # not a multiple of the block
+    assert _decode(lib, b=8193) == UNSUP  # beyond PKV_MAX_SEQS
     assert _decode(lib, q=None) == NULL
     assert _decode(lib, cl=None) == NULL
     assert _decode(lib, out=A + 4) == ALIGN
@@ -96,14 +98,17 @@ def test_decode_validation(lib):
     need = lib.paged_decode_workspace_size(4, 32, 128, 1024, 512)
     assert _decode(lib, ps=512, ws=A, wsb=need - 1) == WORKSPACE
     assert _decode(lib, ps=512, ws=A + 8, wsb=need) == ALIGN
+    assert _decode(lib, ps=0, ws=None) == WORKSPACE  # the unit counter lives there too
     assert _decode(lib, b=0, q=None) == OK  # empty batch: nothing launched
 
 
 def test_workspace_size(lib):
-    assert lib.paged_decode_workspace_size(4, 32, 128, 1024, 0) == 0
-    assert lib.paged_decode_workspace_size(4, 32, 128, 512, 512) == 0  # one partition
-    assert lib.paged_decode_workspace_size(4, 32, 128, 1025, 512) == 4 * 32 * 3 * 130 * 4
-    assert lib.paged_decode_workspace_size(256, 32, 128, 16000, 512) == 256 * 32 * 32 * 130 * 4
+    # 256-byte work-counter area, then the split partials
+    assert lib.paged_decode_workspace_size(0, 32, 128, 1024, 0) == 0
+    assert lib.paged_decode_workspace_size(4, 32, 128, 1024, 0) == 256
+    assert lib.paged_decode_workspace_size(4, 32, 128, 512, 512) == 256  # one partition
+    assert lib.paged_decode_workspace_size(4, 32, 128, 1025, 512) == 256 + 4 * 32 * 3 * 130 * 4
+    assert lib.paged_decode_workspace_size(256, 32, 128, 16000, 512) == 256 + 256 * 32 * 32 * 130 * 4
 
 
 def test_binding_rejects_cpu_tensors(lib):

@@ -165,3 +165,26 @@ def test_parity_is_sensitive_to_mutations(cuda):
     sl[0] += 1
     t["slots"] = torch.from_numpy(sl).to(cuda)
     assert max_err(to_f64(gpu_step(b, t, out_dtype="f32")), ref) > TIGHT["bf16"]
+
+
+def test_workspace_counter_is_left_zero(cuda):
+    """One zero-filled workspace serves consecutive calls of different shapes:
+    each call leaves its work counter at zero, and every result matches."""
+    import torch
+
+    import paged_kv_decode_13_amd as pkv
+
+    ws = torch.zeros(1 << 22, dtype=torch.uint8, device=cuda)
+    cases = [([300, 17, 4000], 8, 2, 512), ([5000], 32, 8, 1024), ([1, 2, 3, 64, 65], 16, 4, 0),
+             ([2049, 99], 8, 8, 2048)]
+    for lens, h, kvh, ps in cases * 2:
+        b = wl.make_batch(lens, num_heads=h, num_kv_heads=kvh, head_dim=128, block_size=16,
+                          dtype="f16", seed=len(lens) + h)
+        t = upload(b, cuda)
+        assert pkv.paged_decode_workspace_size(b.num_seqs, h, 128, b.max_context_len, ps) <= ws.numel()
+        out = pkv.paged_decode_attention(t["q"], t["kc"], t["vc"], t["bt"], t["cl"], 16, b.scale,
+                                         max_context_len=b.max_context_len, partition_size=ps,
+                                         out_dtype=torch.float32, workspace=ws)
+        torch.cuda.synchronize()
+        assert int(ws[:4].view(torch.int32).item()) == 0
+        assert max_err(to_f64(out), oracle_step(b)) <= TIGHT["f16"]
