@@ -134,7 +134,7 @@ def time_steps(batch, t, partition_size: int, steps: int, warmup: int):
 
 def cpu_baseline(batch, target_s: float):
     """The oracle, untouched, on an evenly spaced sample of the batch's
-    sequences sized to about ``target_s`` seconds of host work."""
+    sequences, repeated until about ``target_s`` seconds of host work."""
     import numpy as np
 
     import oracle
@@ -149,19 +149,24 @@ def cpu_baseline(batch, target_s: float):
     frac = min(1.0, target_s / probe_s * probe.total_tokens / batch.total_tokens)
     step = max(1, int(round(1.0 / frac))) if frac < 1.0 else 1
     sample = wl.subset(batch, order[::step])
-    t0 = time.perf_counter()
-    oracle.paged_decode(sample.query, sample.key_cache, sample.value_cache, sample.block_tables,
-                        sample.context_lens, sample.block_size, sample.scale, sample.dtype)
-    secs = time.perf_counter() - t0
+    passes, secs = 0, 0.0
+    while passes == 0 or (secs < target_s and passes < 100):
+        t0 = time.perf_counter()
+        oracle.paged_decode(sample.query, sample.key_cache, sample.value_cache,
+                            sample.block_tables, sample.context_lens, sample.block_size,
+                            sample.scale, sample.dtype)
+        secs += time.perf_counter() - t0
+        passes += 1
+    per_pass = secs / passes
     return {
-        "value": round(sample.kv_bytes_logical() / secs / 1e9, 4),
+        "value": round(sample.kv_bytes_logical() / per_pass / 1e9, 4),
         "unit": "GB/s",
         "cores": oracle.max_threads(),
         "kind": "oracle",
-        "sample": (f"every {step}th sequence of the same batch: {sample.num_seqs} sequences, "
-                   f"{sample.total_tokens} context tokens, fp64 gather + softmax attention, "
-                   f"{secs:.2f} s"),
-        "tokens_per_s": round(sample.num_seqs / secs, 3),
+        "sample": (f"every {step}th sequence of the same batch ({sample.num_seqs} sequences, "
+                   f"{sample.total_tokens} context tokens), fp64 gather + softmax attention, "
+                   f"{passes} passes in {secs:.1f} s"),
+        "tokens_per_s": round(sample.num_seqs / per_pass, 3),
     }
 
 
