@@ -47,7 +47,7 @@ typedef enum pkv_dtype {
 
 /* Largest batch one paged_decode_attention call accepts (every workgroup keeps
  * the batch's partition prefix sum in LDS). */
-#define PKV_MAX_SEQS 8192
+#define PKV_MAX_SEQS 4096
 
 typedef enum pkv_status {
     PKV_OK = 0,

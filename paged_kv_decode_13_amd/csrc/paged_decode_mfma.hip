@@ -15,20 +15,25 @@
 // Work distribution: a persistent grid (as many workgroups as fit on the
 // chip) draws work units (sequence, KV partition, KV head) one at a time from
 // a counter, KV head fastest so that the units reading the same pages run
-// side by side.  Each workgroup first builds, in LDS, the prefix sum of
-// partitions over the sequences of the batch, which maps a unit index to its
-// sequence and partition; no workgroup is spent on a partition past the end
-// of its sequence, and no workgroup idles while units remain.
+// side by side, all full partitions before the shorter last ones.  Each
+// workgroup first builds, in LDS, the prefix sums of partitions over the
+// sequences of the batch, which map a unit index to its sequence and
+// partition; no workgroup is spent on a partition past the end of its
+// sequence, and no workgroup idles while units remain.
 //
 // Lane roles inside a wave (lane = 16 q + c):
-//  - K operand: lane reads token c of the tile, 16-byte chunks 4j + q
-//    (j = 0..3): each load instruction covers 64 contiguous bytes of 16 rows.
-//    The query operand uses the same chunk order, so the contraction pairs
+//  - K and V rows are loaded whole: load instruction i gives lane (q, c)
+//    16-byte chunk c of token 4q + i, so each instruction reads four complete
+//    256-byte rows.  (Reading the MFMA operand layout straight from HBM --
+//    64 bytes of 16 different rows per instruction -- measured 24% slower.)
+//  - K operand: the tile's K rows are transposed through a wave-private LDS
+//    tile so that lane (q, c) holds token c, chunks 4j + q (j = 0..3).  The
+//    query operand uses the same chunk order, so the contraction pairs
 //    equal head-dim indices.
 //  - Scores come back as rows 4q + r (r = 0..3) of the tile for head c % 4
 //    (+4 for the second product): lane (q, c) owns tokens 4q..4q+3.
-//  - V is read in plain row order: lane (q, c) loads 16-byte chunk c of the
-//    same tokens 4q + r, so every lane already holds its tokens' scores; the
+//  - V stays in the loaded row order: lane (q, c) holds chunk c of tokens
+//    4q + r, the same tokens whose scores it holds; the
 //    other heads' probabilities come from the lanes of its quad (DPP quad
 //    broadcast).  The running softmax is kept per lane and per row group q
 //    and merged at the end, so the tile loop needs no cross-lane max.
@@ -78,9 +83,9 @@ __device__ __forceinline__ float head_bcast(float x, int hl) {
 }
 
 struct TileRegs {
-    u32x4 k[4];      // token c, chunks 4j + q
-    u32x4 v[4];      // tokens 4q + r, chunk c
-    uint32_t vmask;  // bit r: V row r holds a valid token
+    u32x4 k[4];      // tokens 4q + i, chunk c (whole rows per load instruction)
+    u32x4 v[4];      // tokens 4q + i, chunk c
+    uint32_t vmask;  // bit i: row i holds a valid token
 };
 
 // Partitions of a sequence in the work list (an empty or out-of-range
@@ -90,34 +95,74 @@ __device__ __forceinline__ int seq_parts(const DecodeArgs &a, int ctx) {
     return (ctx + a.partition_size - 1) / a.partition_size;
 }
 
-// Exclusive prefix of seq_parts over the batch into s_prefix[0..B], using
-// s_scan (kThreads ints) as scratch; lengths cached in s_ctx.
-__device__ __forceinline__ void build_prefix(const DecodeArgs &a, int *s_prefix, int *s_ctx, int *s_scan) {
+// Full partitions of a sequence (its last partition is partial when the
+// length is not a multiple of the partition size; an empty or out-of-range
+// context has one partial unit).
+__device__ __forceinline__ int seq_full(const DecodeArgs &a, int ctx) {
+    if (bad_context(a, ctx) || ctx == 0) return 0;
+    return ctx / a.partition_size;
+}
+
+// Inclusive prefix sum over the workgroup's threads (s_scan: kThreads ints).
+__device__ __forceinline__ int block_scan(int v, int *s_scan) {
+    const int tid = threadIdx.x;
+    s_scan[tid] = v;
+    __syncthreads();
+    for (int off = 1; off < kThreads; off <<= 1) {
+        const int x = tid >= off ? s_scan[tid - off] : 0;
+        __syncthreads();
+        s_scan[tid] += x;
+        __syncthreads();
+    }
+    const int r = s_scan[tid];
+    __syncthreads();
+    return r;
+}
+
+// Unit order: all full partitions of the batch first, then the partial last
+// partitions.  Units of one size drain the grid evenly and the variable-size
+// units come at the end, where they fill the gaps.  Builds the exclusive
+// prefix sums s_pf[0..B] (full partitions) and s_pp[0..B] (partial ones)
+// and caches the lengths in s_ctx.
+__device__ __forceinline__ void build_unit_order(const DecodeArgs &a, int *s_pf, int *s_pp,
+                                                 int *s_ctx, int *s_scan) {
     const int B = a.num_seqs;
     const int tid = threadIdx.x;
     const int chunk = (B + kThreads - 1) / kThreads;
     const int lo = min(B, tid * chunk), hi = min(B, lo + chunk);
-    int sum = 0;
+    int nf = 0, np = 0;
     for (int s = lo; s < hi; ++s) {
         const int ctx = a.context_lens[s];
         s_ctx[s] = ctx;
-        sum += seq_parts(a, ctx);
+        const int f = seq_full(a, ctx);
+        nf += f;
+        np += seq_parts(a, ctx) - f;
     }
-    s_scan[tid] = sum;
-    __syncthreads();
-    for (int off = 1; off < kThreads; off <<= 1) {
-        const int v = tid >= off ? s_scan[tid - off] : 0;
-        __syncthreads();
-        s_scan[tid] += v;
-        __syncthreads();
-    }
-    int run = s_scan[tid] - sum;
+    const int incf = block_scan(nf, s_scan);
+    const int incp = block_scan(np, s_scan);
+    int rf = incf - nf, rp = incp - np;
     for (int s = lo; s < hi; ++s) {
-        s_prefix[s] = run;
-        run += seq_parts(a, s_ctx[s]);
+        s_pf[s] = rf;
+        s_pp[s] = rp;
+        const int f = seq_full(a, s_ctx[s]);
+        rf += f;
+        rp += seq_parts(a, s_ctx[s]) - f;
     }
-    if (tid == kThreads - 1) s_prefix[B] = s_scan[tid];
+    if (tid == kThreads - 1) {
+        s_pf[B] = incf;
+        s_pp[B] = incp;
+    }
     __syncthreads();
+}
+
+// Largest s in [0, n) with pre[s] <= x (pre non-decreasing, pre[0] = 0 <= x).
+__device__ __forceinline__ int search_le(const int *pre, int n, int x) {
+    int lo = 0, hi = n;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (pre[mid] <= x) lo = mid; else hi = mid;
+    }
+    return lo;
 }
 
 template <int DT, int G>
@@ -128,17 +173,20 @@ __global__ __launch_bounds__(kThreads) void paged_decode_mfma_kernel(DecodeArgs 
     constexpr int HS = G < 4 ? G : 4;  // heads per score product
     constexpr int NSET = G / HS;       // score products per tile
 
-    extern __shared__ int s_dyn[];     // prefix [B + 1], then lengths [B]
+    extern __shared__ int s_dyn[];     // full-unit prefix [B + 1], partial-unit prefix [B + 1], lengths [B]
     __shared__ int s_pages[kSegPages];
     __shared__ int s_bad;
     __shared__ float s_m[kNumWaves][G];
     __shared__ float s_l[kNumWaves][G];
     __shared__ float s_acc[kNumWaves][G][D];
+    __shared__ __attribute__((aligned(16))) char s_ktile[kNumWaves][TILE * ROW_BYTES];
 
-    int *s_prefix = s_dyn;
-    int *s_ctx = s_dyn + a.num_seqs + 1;
-    build_prefix(a, s_prefix, s_ctx, s_pages);
-    const int total_units = s_prefix[a.num_seqs] * a.num_kv_heads;
+    int *s_pf = s_dyn;
+    int *s_pp = s_dyn + a.num_seqs + 1;
+    int *s_ctx = s_dyn + 2 * (a.num_seqs + 1);
+    build_unit_order(a, s_pf, s_pp, s_ctx, s_pages);
+    const int total_full = s_pf[a.num_seqs];
+    const int total_units = (total_full + s_pp[a.num_seqs]) * a.num_kv_heads;
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -153,6 +201,7 @@ __global__ __launch_bounds__(kThreads) void paged_decode_mfma_kernel(DecodeArgs 
     const int lbs = a.log2_block_size;
     const int64_t tok_stride = (int64_t)a.num_kv_heads * ROW_BYTES;  // bytes between slots
     const float sl2 = a.scale_log2e;
+    char *ktile = s_ktile[wave];
 
     // Units are handed out one at a time from a counter in the workspace, so
     // a workgroup that drew short units simply takes more: with a static
@@ -175,14 +224,14 @@ __global__ __launch_bounds__(kThreads) void paged_decode_mfma_kernel(DecodeArgs 
         Unit u;
         u.kvh = unit % a.num_kv_heads;
         const int sp = unit / a.num_kv_heads;
-        int lo = 0, hi = a.num_seqs;  // largest s with s_prefix[s] <= sp
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (s_prefix[mid] <= sp) lo = mid; else hi = mid;
+        if (sp < total_full) {
+            u.s = search_le(s_pf, a.num_seqs, sp);
+            u.p = sp - s_pf[u.s];
+        } else {
+            u.s = search_le(s_pp, a.num_seqs, sp - total_full);
+            u.p = seq_full(a, s_ctx[u.s]);
         }
-        u.s = lo;
-        u.p = sp - s_prefix[lo];
-        u.ctx = s_ctx[lo];
+        u.ctx = s_ctx[u.s];
         u.bad_len = bad_context(a, u.ctx);
         u.tok_begin = u.p * a.partition_size;
         u.tok_end = u.bad_len ? 0 : min(u.ctx, u.tok_begin + a.partition_size);
@@ -238,25 +287,38 @@ __global__ __launch_bounds__(kThreads) void paged_decode_mfma_kernel(DecodeArgs 
                 return (page * bs + (t & (bs - 1))) * tok_stride + kvh_off;
             };
             auto load_tile = [&](TileRegs &r, int t0) {
-                bool kok;
-                const char *kp = kbase + row_of(t0 + c, kok);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) r.k[j] = load16_stream(kp + (4 * j + q) * 16);
                 r.vmask = 0;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    bool vok;
-                    r.v[i] = load16_stream(vbase + row_of(t0 + 4 * q + i, vok) + c * 16);
-                    r.vmask |= vok ? (1u << i) : 0u;
+                    bool ok;
+                    const int64_t row = row_of(t0 + 4 * q + i, ok) + c * 16;
+                    r.k[i] = load16_stream(kbase + row);
+                    r.v[i] = load16_stream(vbase + row);
+                    r.vmask |= ok ? (1u << i) : 0u;
                 }
             };
             auto compute_tile = [&](const TileRegs &r, int t0) {
+                // K rows arrive whole (16 lanes per 256-byte row); the score
+                // MFMA wants lane (q, c) to hold token c, chunks 4j + q.
+                // Transpose through this wave's LDS tile, 16-byte chunks
+                // XOR-swizzled by token so that writes and reads are free of
+                // bank conflicts.  Rows are private to the wave and LDS
+                // operations of one wave complete in order: no barrier.
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int tt = 4 * q + i;
+                    *reinterpret_cast<u32x4 *>(ktile + tt * ROW_BYTES + ((c ^ tt) & 15) * 16) = r.k[i];
+                }
+                u32x4 kop[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    kop[j] = *reinterpret_cast<const u32x4 *>(ktile + c * ROW_BYTES + (((4 * j + q) ^ c) & 15) * 16);
                 float p[NSET][4], alpha[NSET];
 #pragma unroll
                 for (int set = 0; set < NSET; ++set) {
                     f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) sacc = mfma_16x16x32<DT>(r.k[j], qop[set][j], sacc);
+                    for (int j = 0; j < 4; ++j) sacc = mfma_16x16x32<DT>(kop[j], qop[set][j], sacc);
                     float sv[4];
                     float mt = -INFINITY;
 #pragma unroll
@@ -362,7 +424,7 @@ __global__ __launch_bounds__(kThreads) void paged_decode_mfma_kernel(DecodeArgs 
 // per kernel and LDS size), capped by the number of units.
 template <typename K>
 static hipError_t launch_persistent(K kernel, const DecodeArgs &a, hipStream_t stream) {
-    const size_t dyn = (size_t)(2 * a.num_seqs + 1) * sizeof(int);
+    const size_t dyn = (size_t)(3 * a.num_seqs + 2) * sizeof(int);
     int dev = 0, cus = 0, per_cu = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);

@@ -90,7 +90,7 @@ def test_decode_validation(lib):
     assert _decode(lib, h=128, kvh=8) == UNSUP  # group of 16
     assert _decode(lib, ps=24) == UNSUP  # not a multiple of 16
     assert _decode(lib, bs=32, mb=32, ps=16) == UNSUP  # not a multiple of the block
-    assert _decode(lib, b=8193) == UNSUP  # beyond PKV_MAX_SEQS
+    assert _decode(lib, b=4097) == UNSUP  # beyond PKV_MAX_SEQS
     assert _decode(lib, q=None) == NULL
     assert _decode(lib, cl=None) == NULL
     assert _decode(lib, out=A + 4) == ALIGN

@@ -188,3 +188,25 @@ def test_workspace_counter_is_left_zero(cuda):
         torch.cuda.synchronize()
         assert int(ws[:4].view(torch.int32).item()) == 0
         assert max_err(to_f64(out), oracle_step(b)) <= TIGHT["f16"]
+
+
+def test_unit_order_edges(cuda):
+    """Full-partition-first unit order: lengths that are exact multiples of
+    the partition (no partial unit), all-partial batches, empty contexts,
+    and the largest batch one call accepts."""
+    import torch
+
+    cases = [([512, 1024, 2048], 512), ([3, 5, 200, 0, 511], 512), ([0, 0, 700, 1536], 256),
+             ([1 + (i * 37) % 300 for i in range(4096)], 128)]
+    for lens, ps in cases:
+        b = wl.make_batch(lens, num_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
+                          dtype="bf16", seed=len(lens))
+        ref = oracle_step(b)
+        out = to_f64(gpu_step(b, upload(b, cuda), partition_size=ps, out_dtype="f32"))
+        assert max_err(out, ref) <= TIGHT["bf16"], (len(lens), ps)
+    import paged_kv_decode_13_amd as pkv
+
+    with pytest.raises(pkv.PagedKVError):
+        b = wl.make_batch([4] * 4097, num_heads=2, num_kv_heads=2, head_dim=128, block_size=16,
+                          dtype="bf16", seed=1)
+        gpu_step(b, upload(b, cuda), partition_size=0)
