@@ -165,13 +165,17 @@ __device__ __forceinline__ int search_le(const int *pre, int n, int x) {
     return lo;
 }
 
+// Three waves per SIMD (<= 168 VGPRs) keep enough loads in flight; the
+// allocator is held to that budget.
 template <int DT, int G>
-__global__ __launch_bounds__(kThreads) void paged_decode_mfma_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8)))
+void paged_decode_mfma_kernel(DecodeArgs a) {
     constexpr int D = 128;
     constexpr int ROW_BYTES = D * 2;
     constexpr int TILE = 16;
     constexpr int HS = G < 4 ? G : 4;  // heads per score product
     constexpr int NSET = G / HS;       // score products per tile
+    constexpr bool kQopInLds = NSET > 1;
 
     extern __shared__ int s_dyn[];     // full-unit prefix [B + 1], partial-unit prefix [B + 1], lengths [B]
     __shared__ int s_pages[kSegPages];
@@ -180,6 +184,7 @@ __global__ __launch_bounds__(kThreads) void paged_decode_mfma_kernel(DecodeArgs 
     __shared__ float s_l[kNumWaves][G];
     __shared__ float s_acc[kNumWaves][G][D];
     __shared__ __attribute__((aligned(16))) char s_ktile[kNumWaves][TILE * ROW_BYTES];
+    __shared__ u32x4 s_qop[kQopInLds ? NSET : 1][4][kWave];
 
     int *s_pf = s_dyn;
     int *s_pp = s_dyn + a.num_seqs + 1;
@@ -240,17 +245,23 @@ __global__ __launch_bounds__(kThreads) void paged_decode_mfma_kernel(DecodeArgs 
 
         if (tid == 0) s_bad = 0;
 
-        // query operand: head (set*HS + c%HS), chunks 4j + q
+        // query operand: head (set*HS + c%HS), chunks 4j + q.  It is the
+        // same for every wave; with two score products (G = 8) it is parked
+        // in LDS (wave 0 writes it before the first barrier below) to keep
+        // the register count at three waves per SIMD.
         const int h0 = u.kvh * G;
         u32x4 qop[NSET][4];
-        {
+        if (!kQopInLds || wave == 0) {
             const char *qb = reinterpret_cast<const char *>(a.query);
 #pragma unroll
             for (int set = 0; set < NSET; ++set) {
                 const int h = h0 + set * HS + (c % HS);
                 const char *row = qb + ((int64_t)u.s * a.num_heads + h) * ROW_BYTES;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) qop[set][j] = load16(row + (4 * j + q) * 16);
+                for (int j = 0; j < 4; ++j) {
+                    qop[set][j] = load16(row + (4 * j + q) * 16);
+                    if constexpr (kQopInLds) s_qop[set][j][lane] = qop[set][j];
+                }
             }
         }
 
@@ -318,7 +329,8 @@ __global__ __launch_bounds__(kThreads) void paged_decode_mfma_kernel(DecodeArgs 
                 for (int set = 0; set < NSET; ++set) {
                     f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) sacc = mfma_16x16x32<DT>(kop[j], qop[set][j], sacc);
+                    for (int j = 0; j < 4; ++j)
+                        sacc = mfma_16x16x32<DT>(kop[j], kQopInLds ? s_qop[set][j][lane] : qop[set][j], sacc);
                     float sv[4];
                     float mt = -INFINITY;
 #pragma unroll
@@ -363,7 +375,7 @@ __global__ __launch_bounds__(kThreads) void paged_decode_mfma_kernel(DecodeArgs 
             // computed.  Straight-line code: the compiler waits for exactly
             // the loads a tile needs.  A tile past the segment is all
             // invalid and computes to no change.
-            constexpr int TPS = PKV_TILES_PER_STEP;
+            constexpr int TPS = G == 8 ? 1 : PKV_TILES_PER_STEP;  // register budget
             constexpr int STEP = kNumWaves * TILE * TPS;
             for (int t = seg + wave * TILE * TPS; t < seg_end; t += STEP) {
                 TileRegs r[TPS];
