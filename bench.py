@@ -170,6 +170,51 @@ def cpu_baseline(batch, target_s: float):
     }
 
 
+def run_write(batch, t, steps: int, warmup: int) -> dict:
+    """The slot write alone (a bulk prompt write for the prefill workload),
+    timed with HIP events; bytes moved = new rows read + rows written."""
+    import torch
+
+    import paged_kv_decode_13_amd as pkv
+
+    def write():
+        pkv.paged_kv_write(t["nk"], t["nv"], t["kc"], t["vc"], t["slots"])
+
+    for _ in range(warmup):
+        write()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        write()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    moved = 2 * 2 * batch.new_key.nbytes  # K and V, read and written
+    gbs = moved / (ms * 1e-3) / 1e9
+    return {
+        "metric": "paged KV slot write GB/s (bytes read + written)",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": batch.dtype,
+        "data": "synthetic (seeded N(0,1) rows, generated page tables)",
+        "config": {"workload": batch.name, "tokens": int(batch.new_key.shape[0]),
+                   "num_kv_heads": batch.num_kv_heads, "head_dim": batch.head_dim,
+                   "block_size": batch.block_size, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "kv_write_kernel", "achieved": round(gbs, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None},
+        "cpu_baseline": None,
+    }
+
+
 def run_copy(size_mb: int, steps: int) -> None:
     """A plain device-to-device copy of known size (counter calibration)."""
     import torch
@@ -196,7 +241,7 @@ def main() -> int:
                     help="comma list of partition sizes to time as well (stderr report)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--mode", default="decode", choices=["decode", "copy"])
+    ap.add_argument("--mode", default="decode", choices=["decode", "write", "copy"])
     ap.add_argument("--copy-mb", type=int, default=1024)
     args = ap.parse_args()
 
@@ -226,12 +271,21 @@ def main() -> int:
         build.build()
     dev = torch.device("cuda:0")
     t0 = time.time()
-    batch = wl.make_config(args.config, block_size=args.block_size)
+    if args.config in wl.PREFILL_NAMES:
+        batch = wl.make_prefill_config(args.config)
+    else:
+        batch = wl.make_config(args.config, block_size=args.block_size)
     log(f"[bench] {args.config}: {batch.num_seqs} seqs, {batch.total_tokens} context tokens, "
         f"generated in {time.time() - t0:.1f}s")
     t = upload(batch, dev)
     torch.cuda.synchronize()
     ps = batch.partition_size if args.partition_size is None else args.partition_size
+    if args.mode == "write":
+        if batch.slot_mapping is None:
+            print(f"{args.config} writes no tokens", file=sys.stderr)
+            return 2
+        print(json.dumps(run_write(batch, t, args.steps, args.warmup)), flush=True)
+        return 0
 
     if args.sweep_partitions:
         for p in [int(x) for x in args.sweep_partitions.split(",")]:

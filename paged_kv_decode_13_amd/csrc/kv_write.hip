@@ -1,48 +1,73 @@
-// paged_kv_write kernel: each step's new K/V rows are stored at the slot the
+// paged_kv_write kernel: each new token's K/V rows are stored at the slot the
 // block allocator handed out for them.
 //
 // Page "实现教学版 PagedAttention：从 block table 读取历史 KV cache", section
 // "写入 slot 和读取 block table 必须一致": the slot is (physical_block_id,
-// block_offset); the write position must be exactly the read position.
+// block_offset); the write position must be exactly the read position.  The
+// same page, section "attention mask 在哪里": prefill stores the prompt's K/V
+// in the blocks, decode stores one token per sequence per step.
 //
-// The copy is HBM-bound and tiny for decode (one token per sequence), large
-// for a prompt's bulk write.  Work is flattened over 16-byte vectors of all
-// tokens' K and V rows so that one grid shape serves both: consecutive lanes
-// copy consecutive 16-byte vectors of one token row.
+// A pure copy, bound by HBM: every byte is read once and written once.  One
+// slot lookup serves a whole token: a workgroup of 256 threads copies
+// 256 / TPT tokens at a time, TPT (a power of two) threads per token
+// striding over the token's 16-byte vectors of K then V, so consecutive
+// lanes touch consecutive 16 bytes of a row.  Large writes (a prompt's
+// thousands of tokens) loop grid-stride over token groups.
 #include "pkv_device.h"
 #include "pkv_launch.h"
 
 namespace pkv {
 
+template <int TPT>
 __global__ __launch_bounds__(256) void kv_write_kernel(WriteArgs a) {
-    const int64_t per_token = 2 * (int64_t)a.vecs_per_token;  // K then V
-    const int64_t total = a.num_tokens * per_token;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < total; v += stride) {
-        const int64_t token = v / per_token;
-        int64_t j = v - token * per_token;
+    constexpr int TOKENS_PER_GROUP = 256 / TPT;
+    const int sub = threadIdx.x % TPT;      // lane inside the token's team
+    const int team = threadIdx.x / TPT;     // token inside the group
+    const int vpt = a.vecs_per_token;       // 16-byte vectors per K (or V) row set
+    const u32x4 *key = reinterpret_cast<const u32x4 *>(a.key);
+    const u32x4 *value = reinterpret_cast<const u32x4 *>(a.value);
+    u32x4 *kc = reinterpret_cast<u32x4 *>(a.key_cache);
+    u32x4 *vc = reinterpret_cast<u32x4 *>(a.value_cache);
+    for (int64_t token = (int64_t)blockIdx.x * TOKENS_PER_GROUP + team; token < a.num_tokens;
+         token += (int64_t)gridDim.x * TOKENS_PER_GROUP) {
         const int64_t slot = a.slot_mapping[token];
         if (slot < 0) continue;
         // slot -> (physical block, offset inside the block)
         const int64_t pb = slot / a.block_size;
         const int64_t off = slot - pb * a.block_size;
         if (pb >= a.num_blocks) continue;
-        const bool is_v = j >= a.vecs_per_token;
-        if (is_v) j -= a.vecs_per_token;
-        const int64_t dst = (pb * a.block_size + off) * a.vecs_per_token + j;
-        const int64_t src = token * a.vecs_per_token + j;
-        const u32x4 *s = reinterpret_cast<const u32x4 *>(is_v ? a.value : a.key);
-        u32x4 *d = reinterpret_cast<u32x4 *>(is_v ? a.value_cache : a.key_cache);
-        d[dst] = s[src];
+        const int64_t dst = (pb * a.block_size + off) * vpt;
+        const int64_t src = token * vpt;
+        for (int j = sub; j < vpt; j += TPT) {
+            const u32x4 kv = key[src + j];
+            const u32x4 vv = value[src + j];
+            kc[dst + j] = kv;
+            vc[dst + j] = vv;
+        }
     }
 }
 
 hipError_t launch_kv_write(const WriteArgs &a, hipStream_t stream) {
     if (a.num_tokens == 0) return hipSuccess;
-    const int64_t total = a.num_tokens * 2 * (int64_t)a.vecs_per_token;
-    int64_t blocks = (total + 255) / 256;
-    if (blocks > 8192) blocks = 8192;  // grid-stride beyond ~32 waves per CU
-    hipLaunchKernelGGL(kv_write_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    // threads per token: the token's vector count rounded down to a power of
+    // two, at most 256 (head_dim 64..128, 1+ KV heads: 8..4096 vectors)
+    int tpt = 1;
+    while (tpt * 2 <= a.vecs_per_token && tpt < 256) tpt *= 2;
+    const int64_t per_group = 256 / tpt;
+    int64_t groups = (a.num_tokens + per_group - 1) / per_group;
+    if (groups > 16384) groups = 16384;  // grid-stride beyond
+    const dim3 grid((unsigned)groups), block(256);
+    switch (tpt) {
+        case 1: hipLaunchKernelGGL(kv_write_kernel<1>, grid, block, 0, stream, a); break;
+        case 2: hipLaunchKernelGGL(kv_write_kernel<2>, grid, block, 0, stream, a); break;
+        case 4: hipLaunchKernelGGL(kv_write_kernel<4>, grid, block, 0, stream, a); break;
+        case 8: hipLaunchKernelGGL(kv_write_kernel<8>, grid, block, 0, stream, a); break;
+        case 16: hipLaunchKernelGGL(kv_write_kernel<16>, grid, block, 0, stream, a); break;
+        case 32: hipLaunchKernelGGL(kv_write_kernel<32>, grid, block, 0, stream, a); break;
+        case 64: hipLaunchKernelGGL(kv_write_kernel<64>, grid, block, 0, stream, a); break;
+        case 128: hipLaunchKernelGGL(kv_write_kernel<128>, grid, block, 0, stream, a); break;
+        default: hipLaunchKernelGGL(kv_write_kernel<256>, grid, block, 0, stream, a); break;
+    }
     return hipGetLastError();
 }
 

@@ -48,6 +48,7 @@ DTYPE_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
 NAN_BITS = {"f32": 0x7FC00000, "f16": 0x7E00, "bf16": 0x7FC0}
 
 CONFIG_NAMES = ("tiny_fp32", "mha_fp16", "gqa_bf16", "long_bf16", "prefix_fp16")
+PREFILL_NAMES = ("prefill_bf16",)
 CONFIG_SEEDS = {name: i + 1 for i, name in enumerate(CONFIG_NAMES)}
 PREFIX_BLOCK_SIZES = (8, 16, 32, 64)
 
@@ -399,6 +400,54 @@ def make_config(name: str, *, block_size: int | None = None, seed: int | None = 
                           block_size=32, dtype="bf16", seed=seed, poison=poison,
                           partition_size=512, name=name, values=values)
     raise KeyError(name)
+
+
+def make_prefill(prompt_lens, *, num_heads: int, num_kv_heads: int, head_dim: int,
+                 block_size: int, dtype: str, seed: int, name: str = "prefill",
+                 partition_size: int = 0) -> DecodeBatch:
+    """A prompt-sized write: every token of every prompt gets its K/V row and
+    the slot of its logical position in the sequence's (shuffled) pages.  The
+    pool starts all NaN -- nothing is cached yet -- so after the write a
+    decode over the prompt reads exactly the written rows."""
+    ctx = np.asarray(prompt_lens, dtype=np.int64).reshape(-1)
+    ss = np.random.SeedSequence(seed)
+    s_perm, s_q, s_k, s_v = ss.spawn(4)
+    rng = np.random.Generator(np.random.PCG64(s_perm))
+    bps = (ctx + block_size - 1) // block_size
+    tables, nb, spare = _disjoint_tables(rng, bps)
+    tokens = int(ctx.sum())
+    slots = np.empty(tokens, dtype=np.int64)
+    pos = 0
+    for s, c in enumerate(ctx):
+        t = np.arange(int(c))
+        slots[pos:pos + c] = tables[s, t // block_size].astype(np.int64) * block_size + t % block_size
+        pos += int(c)
+    sdt = storage_dtype(dtype)
+    kc = np.empty((nb, block_size, num_kv_heads, head_dim), sdt)
+    kc[...] = nan_value(dtype)
+    vc = kc.copy()
+    return DecodeBatch(name=name, dtype=dtype, num_heads=num_heads, num_kv_heads=num_kv_heads,
+                       head_dim=head_dim, block_size=block_size,
+                       query=_random_storage(s_q, (ctx.size, num_heads, head_dim), dtype),
+                       key_cache=kc, value_cache=vc, block_tables=tables,
+                       context_lens=ctx.astype(np.int32),
+                       scale=float(np.float32(1.0 / math.sqrt(head_dim))),
+                       new_key=_random_storage(s_k, (tokens, num_kv_heads, head_dim), dtype),
+                       new_value=_random_storage(s_v, (tokens, num_kv_heads, head_dim), dtype),
+                       slot_mapping=slots, partition_size=partition_size, poison_block=spare)
+
+
+def make_prefill_config(name: str, *, seed: int | None = None) -> DecodeBatch:
+    """prefill_bf16: 32 prompts with lengths uniform in [1024, 8192] written
+    into GQA-shaped pages (8 KV heads, head_dim 128, block 16, bf16) --
+    the step just before decode, measured as a copy."""
+    if name != "prefill_bf16":
+        raise KeyError(name)
+    seed = 11 if seed is None else seed
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 7])))
+    lens = rng.integers(1024, 8192, size=32, endpoint=True)
+    return make_prefill(lens, num_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                        dtype="bf16", seed=seed, name=name, partition_size=2048)
 
 
 def subset(batch: DecodeBatch, seqs) -> DecodeBatch:

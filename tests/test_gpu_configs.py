@@ -35,3 +35,25 @@ def test_full_config(cuda, name, bs):
     assert err <= TIGHT[b.dtype]
     out = to_f64(gpu_step(b, upload(b, cuda), partition_size=0, out_dtype="f32"))
     assert max_err(out, ref) <= TIGHT[b.dtype]
+
+
+def test_full_prefill_write(cuda):
+    """The bulk prompt write at full size (144k tokens, 591 MB of K/V): the
+    pools are byte-equal to the oracle's write, and the decode over the
+    written prompts matches the oracle."""
+    import torch
+
+    import oracle
+    import paged_kv_decode_13_amd as pkv
+
+    b = wl.make_prefill_config("prefill_bf16")
+    t = upload(b, cuda)
+    pkv.paged_kv_write(t["nk"], t["nv"], t["kc"], t["vc"], t["slots"])
+    torch.cuda.synchronize()
+    kc, vc = b.key_cache.copy(), b.value_cache.copy()
+    oracle.paged_kv_write(b.new_key, b.new_value, kc, vc, b.slot_mapping)
+    assert np.array_equal(t["kc"].cpu().view(torch.uint8).numpy().ravel(), kc.view(np.uint8).ravel())
+    assert np.array_equal(t["vc"].cpu().view(torch.uint8).numpy().ravel(), vc.view(np.uint8).ravel())
+    out = to_f64(gpu_step(b, t, write=False))
+    ref = oracle_step(b)
+    assert max_err(out, ref) <= TOL["bf16"]

@@ -210,3 +210,25 @@ def test_unit_order_edges(cuda):
         b = wl.make_batch([4] * 4097, num_heads=2, num_kv_heads=2, head_dim=128, block_size=16,
                           dtype="bf16", seed=1)
         gpu_step(b, upload(b, cuda), partition_size=0)
+
+
+def test_bulk_prefill_write_then_decode(cuda):
+    """A prompt-sized write (every token of every prompt) is bit-exact, and a
+    decode over the prompts then reads exactly the written rows."""
+    import torch
+
+    import paged_kv_decode_13_amd as pkv
+
+    for dtype, d, bs, kvh in (("bf16", 128, 16, 8), ("f16", 64, 4, 2), ("f32", 128, 32, 1)):
+        b = wl.make_prefill([700, 1, 16, 2049], num_heads=4 * kvh, num_kv_heads=kvh, head_dim=d,
+                            block_size=bs, dtype=dtype, seed=3)
+        t = upload(b, cuda)
+        pkv.paged_kv_write(t["nk"], t["nv"], t["kc"], t["vc"], t["slots"])
+        torch.cuda.synchronize()
+        kc, vc = b.key_cache.copy(), b.value_cache.copy()
+        oracle.paged_kv_write(b.new_key, b.new_value, kc, vc, b.slot_mapping)
+        assert np.array_equal(t["kc"].cpu().view(torch.uint8).numpy().ravel(), kc.view(np.uint8).ravel())
+        assert np.array_equal(t["vc"].cpu().view(torch.uint8).numpy().ravel(), vc.view(np.uint8).ravel())
+        out = to_f64(gpu_step(b, t, write=False, partition_size=512 if bs <= 32 else 0,
+                              out_dtype="f32"))
+        assert max_err(out, oracle_step(b)) <= TIGHT[dtype], dtype

@@ -153,3 +153,20 @@ def test_byte_accounting():
     b = wl.make_batch([10, 20], num_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
                       dtype="bf16", seed=0, values=False)
     assert b.kv_bytes_logical() == 30 * 2 * 128 * 2 * 2
+
+
+def test_prefill_layout():
+    """Every prompt token gets the slot of its logical position; the pool
+    starts all NaN."""
+    b = wl.make_prefill([5, 1, 33], num_heads=4, num_kv_heads=2, head_dim=64, block_size=8,
+                        dtype="f16", seed=4)
+    assert b.new_key.shape == (39, 2, 64) and b.slot_mapping.shape == (39,)
+    assert len(np.unique(b.slot_mapping)) == 39
+    pos = 0
+    for s, c in enumerate(b.context_lens):
+        for t in range(int(c)):
+            lb, off, pb = oracle.block_address(b.block_tables[s], t, 8)
+            assert b.slot_mapping[pos] == pb * 8 + off
+            pos += 1
+    assert ((b.key_cache.view(np.uint16) & 0x7C00) == 0x7C00).all()
+    _check_layout(b)
