@@ -10,6 +10,7 @@ code with the GPU library and never imports it.
 Pages cited in this package:
   [P1] "从正确到更快：PagedAttention 的优化路线"
   [P2] "实现教学版 PagedAttention：从 block table 读取历史 KV cache"
+  [P3] "算子与编译器：推理 Attention 与 KV Kernel"
 
 Parity pins: every function here is pinned by ``tests/test_oracle_pins.py``
 (worked mapping printed on [P2], library attention, closed forms, brute force,
@@ -60,6 +61,8 @@ def _bind(lib):
     lib.oracle_attention.argtypes = [p, p, p, p, i32, i32, dbl]
     lib.oracle_paged_decode.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i64,
                                         dbl, ctypes.c_int, ctypes.c_int]
+    lib.oracle_paged_prefix_decode.argtypes = [p, p, p, p, p, i32, p, p, i32, i32, i32, i32, i32,
+                                               i32, i64, dbl, ctypes.c_int, ctypes.c_int]
     lib.oracle_paged_kv_write.argtypes = [p, p, p, p, p, i64, i32, i32, i32, i64, ctypes.c_int]
     lib.oracle_max_threads.argtypes = []
     return lib
@@ -193,6 +196,36 @@ def paged_decode(query, key_cache, value_cache, block_tables, context_lens, bloc
                                      _ptr(bt), _ptr(cl), b, h, kvh, d, bs, bt.shape[1], nb,
                                      float(np.float32(scale)), DTYPE_CODE[dtype], int(num_threads))
     _check(rc, "paged_decode")
+    return out
+
+
+def paged_prefix_decode(query, key_cache, value_cache, prefix_table, prefix_len: int,
+                        block_tables, context_lens, block_size: int, scale: float, dtype: str,
+                        num_threads: int = 0):
+    """[P3] "4.1 为什么页面化会改变 kernel 设计" / "6. Prefix Cache 与 Attention
+    Kernel 的关系": decode where tokens t < ``prefix_len`` of every sequence
+    live in the shared pages ``prefix_table`` and later tokens in the
+    sequence's own ``block_tables`` row (whose first prefix_len / block_size
+    entries are ignored).  fp64 output [num_seqs, num_heads, head_dim]."""
+    for a in (query, key_cache, value_cache):
+        _elem_check(a, dtype)
+    nb, bs, kvh, d = key_cache.shape
+    if bs != block_size:
+        raise ValueError("block_size does not match the pool shape")
+    b, h, dq = query.shape
+    assert dq == d and value_cache.shape == key_cache.shape
+    pt = np.ascontiguousarray(prefix_table, dtype=np.int32).reshape(-1)
+    if pt.size == 0:
+        pt = np.zeros(1, dtype=np.int32)
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+    assert bt.ndim == 2 and bt.shape[0] == b and cl.shape == (b,)
+    out = np.zeros((b, h, d), dtype=np.float64)
+    rc = _load().oracle_paged_prefix_decode(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(pt), int(prefix_len),
+        _ptr(bt), _ptr(cl), b, h, kvh, d, bs, bt.shape[1], nb, float(np.float32(scale)),
+        DTYPE_CODE[dtype], int(num_threads))
+    _check(rc, "paged_prefix_decode")
     return out
 
 

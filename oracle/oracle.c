@@ -9,6 +9,7 @@
  * Pages cited:
  *   [P1] "从正确到更快：PagedAttention 的优化路线"
  *   [P2] "实现教学版 PagedAttention：从 block table 读取历史 KV cache"
+ *   [P3] "算子与编译器：推理 Attention 与 KV Kernel"
  */
 #include "oracle.h"
 
@@ -210,6 +211,43 @@ int oracle_paged_decode(double *out, const void *query,
         free(qd);
     }
     return status;
+}
+
+/* [P3] "4.1 为什么页面化会改变 kernel 设计" and "6. Prefix Cache 与 Attention
+ * Kernel 的关系": the shared prefix occupies read-only pages common to every
+ * sequence, followed by each sequence's own pages.  Compose each sequence's
+ * block table from the two and run the plain paged decode on it. */
+int oracle_paged_prefix_decode(double *out, const void *query,
+                               const void *key_cache, const void *value_cache,
+                               const int32_t *prefix_table, int32_t prefix_len,
+                               const int32_t *block_tables,
+                               const int32_t *context_lens, int32_t num_seqs,
+                               int32_t num_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block_size,
+                               int32_t max_blocks_per_seq, int64_t num_blocks,
+                               double scale, int dtype, int num_threads) {
+    if (num_seqs < 0 || block_size <= 0 || max_blocks_per_seq < 0 ||
+        prefix_len < 0 || prefix_len % block_size != 0 ||
+        prefix_len / block_size > max_blocks_per_seq ||
+        (prefix_len > 0 && !prefix_table))
+        return ORACLE_ERR_ARG;
+    const int32_t prefix_blocks = prefix_len / block_size;
+    const size_t entries = (size_t)num_seqs * (size_t)max_blocks_per_seq;
+    int32_t *tables = (int32_t *)malloc(sizeof(int32_t) * (entries ? entries : 1));
+    if (!tables) return ORACLE_ERR_NOMEM;
+    for (int32_t s = 0; s < num_seqs; ++s) {
+        const int32_t *own = block_tables + (int64_t)s * max_blocks_per_seq;
+        int32_t *row = tables + (int64_t)s * max_blocks_per_seq;
+        for (int32_t lb = 0; lb < max_blocks_per_seq; ++lb)
+            row[lb] = lb < prefix_blocks ? prefix_table[lb] : own[lb];
+    }
+    int rc = oracle_paged_decode(out, query, key_cache, value_cache, tables,
+                                 context_lens, num_seqs, num_heads,
+                                 num_kv_heads, head_dim, block_size,
+                                 max_blocks_per_seq, num_blocks, scale, dtype,
+                                 num_threads);
+    free(tables);
+    return rc;
 }
 
 /* [P2] "写入 slot 和读取 block table 必须一致": the current token's K/V goes

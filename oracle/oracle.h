@@ -87,6 +87,26 @@ int oracle_paged_decode(double *out, const void *query,
                         int32_t max_blocks_per_seq, int64_t num_blocks,
                         double scale, int dtype, int num_threads);
 
+/* [P3] sections "4.1 为什么页面化会改变 kernel 设计" and "6. Prefix Cache 与
+ * Attention Kernel 的关系": sequences that share a prompt prefix read the same
+ * read-only pages for it and append pages of their own.  Token t of sequence
+ * s lives at prefix_table[t / block_size] when t < prefix_len and at
+ * block_tables[s][t / block_size] otherwise; the attention is the ordinary
+ * paged decode above over that composed table.  prefix_len is a multiple of
+ * block_size and at most max_blocks_per_seq * block_size; the first
+ * prefix_len / block_size entries of each block_tables row are ignored.  A
+ * sequence shorter than the prefix sees the first context_lens[s] tokens of
+ * it. */
+int oracle_paged_prefix_decode(double *out, const void *query,
+                               const void *key_cache, const void *value_cache,
+                               const int32_t *prefix_table, int32_t prefix_len,
+                               const int32_t *block_tables,
+                               const int32_t *context_lens, int32_t num_seqs,
+                               int32_t num_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block_size,
+                               int32_t max_blocks_per_seq, int64_t num_blocks,
+                               double scale, int dtype, int num_threads);
+
 /* [P2] section "写入 slot 和读取 block table 必须一致": store token i's K/V
  * rows [num_kv_heads, head_dim] at slot_mapping[i] = physical_block_id *
  * block_size + block_offset, a byte copy.  Negative slots are skipped; tokens

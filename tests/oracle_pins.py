@@ -295,6 +295,89 @@ def pin_sensitivity():
 
 
 # ---------------------------------------------------------------------------
+# shared prefix
+
+
+def _prefix_case(dtype, seed=21):
+    """A prompt prefix of 3 pages shared by four sequences (lengths 0, 5,
+    12 = the prefix, 19), each with its own suffix pages.  The sequences' own
+    table rows point their prefix entries, and every entry past the history,
+    at a NaN page, so using them anywhere shows in the output."""
+    rng = np.random.default_rng(seed)
+    b, h, kvh, d, bs, plen = 4, 8, 2, 16, 4, 12
+    ctxs = [0, 5, 12, 19]
+    suffix = [max(c - plen, 0) for c in ctxs]
+    n_own = [-(-x // bs) for x in suffix]
+    nb = plen // bs + sum(n_own) + 1
+    perm = rng.permutation(nb)
+    poison = int(perm[-1])
+    prefix_table = perm[: plen // bs].astype(np.int32)
+    tables = np.full((b, 8), poison, np.int32)
+    pk, pv = rng.standard_normal((plen, kvh, d)), rng.standard_normal((plen, kvh, d))
+    kc = np.full((nb, bs, kvh, d), np.nan)
+    vc = np.full_like(kc, np.nan)
+    for i in range(plen):
+        kc[prefix_table[i // bs], i % bs] = pk[i]
+        vc[prefix_table[i // bs], i % bs] = pv[i]
+    pos = plen // bs
+    sk, sv = [], []
+    for s in range(b):
+        tables[s, plen // bs: plen // bs + n_own[s]] = perm[pos:pos + n_own[s]]
+        pos += n_own[s]
+        k1, v1 = rng.standard_normal((suffix[s], kvh, d)), rng.standard_normal((suffix[s], kvh, d))
+        sk.append(k1)
+        sv.append(v1)
+        for i in range(suffix[s]):
+            t = plen + i
+            kc[tables[s, t // bs], t % bs] = k1[i]
+            vc[tables[s, t // bs], t % bs] = v1[i]
+    q = rng.standard_normal((b, h, d))
+    enc = {"f32": lambda a: a.astype(np.float32),
+           "f16": lambda a: a.astype(np.float16).view(np.uint16),
+           "bf16": lambda a: _bf16_bits(a)}[dtype]
+    dec = lambda a: oracle.to_float64(enc(a), dtype)  # noqa: E731
+    contig = []
+    for s in range(b):
+        c = ctxs[s]
+        kk = np.concatenate([pk[: min(c, plen)], sk[s]])
+        vv = np.concatenate([pv[: min(c, plen)], sv[s]])
+        contig.append((dec(kk), dec(vv)))
+    return dict(q=enc(q), qd=dec(q), kc=enc(kc), vc=enc(vc), prefix_table=prefix_table,
+                plen=plen, tables=tables, ctx=np.array(ctxs, np.int32), bs=bs, contig=contig)
+
+
+def pin_prefix_equals_contiguous():
+    """Shared-prefix decode equals attention over the contiguous history
+    prefix[:min(ctx, prefix_len)] + own suffix (torch fp64, grouped-query
+    mode); empty context gives zeros; the ignored table entries are NaN."""
+    for dtype in ("f32", "bf16"):
+        c = _prefix_case(dtype)
+        scale = float(np.float32(0.25))
+        out = oracle.paged_prefix_decode(c["q"], c["kc"], c["vc"], c["prefix_table"], c["plen"],
+                                         c["tables"], c["ctx"], c["bs"], scale, dtype)
+        assert np.array_equal(out[0], np.zeros_like(out[0]))
+        for s in range(1, len(c["ctx"])):
+            kk, vv = c["contig"][s]
+            ref = _sdpa(c["qd"][s], kk, vv, scale, enable_gqa=True)
+            assert np.max(np.abs(out[s] - ref)) < 1e-12, (dtype, s)
+
+
+def pin_prefix_reduces_to_paged_decode():
+    """With the prefix entries written into every row, or with an empty
+    prefix, the shared-prefix decode is the plain paged decode bit for bit."""
+    c = _prefix_case("f32", seed=22)
+    full = c["tables"].copy()
+    full[:, : c["plen"] // c["bs"]] = c["prefix_table"]
+    ref = oracle.paged_decode(c["q"], c["kc"], c["vc"], full, c["ctx"], c["bs"], 0.25, "f32")
+    out = oracle.paged_prefix_decode(c["q"], c["kc"], c["vc"], c["prefix_table"], c["plen"],
+                                     c["tables"], c["ctx"], c["bs"], 0.25, "f32")
+    assert np.array_equal(out, ref)
+    out0 = oracle.paged_prefix_decode(c["q"], c["kc"], c["vc"], np.zeros(0, np.int32), 0, full,
+                                      c["ctx"], c["bs"], 0.25, "f32")
+    assert np.array_equal(out0, ref)
+
+
+# ---------------------------------------------------------------------------
 # slot write
 
 
@@ -334,6 +417,8 @@ QUICK_PINS = [
     pin_brute_force_tiny,
     pin_invariances,
     pin_sensitivity,
+    pin_prefix_equals_contiguous,
+    pin_prefix_reduces_to_paged_decode,
     pin_write,
 ]
 

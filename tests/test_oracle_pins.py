@@ -37,6 +37,14 @@ PLANTED = {
                             "mag = ldexp(1.0 + (double)frac / 1024.0, expo - 16);"),
     "write_offset_dropped": ("int64_t off = slot % block_size;", "int64_t off = 0;"),
     "max_not_subtracted_sign": ("scores[t] = exp(scores[t] - smax);", "scores[t] = exp(smax - scores[t]);"),
+    "prefix_table_ignored": ("row[lb] = lb < prefix_blocks ? prefix_table[lb] : own[lb];",
+                             "row[lb] = own[lb];"),
+    "prefix_last_page_from_own_row": ("row[lb] = lb < prefix_blocks ? prefix_table[lb] : own[lb];",
+                                      "row[lb] = lb < prefix_blocks - 1 ? prefix_table[lb] : own[lb];"),
+    "prefix_pages_reversed": ("row[lb] = lb < prefix_blocks ? prefix_table[lb] : own[lb];",
+                              "row[lb] = lb < prefix_blocks ? prefix_table[prefix_blocks - 1 - lb] : own[lb];"),
+    "suffix_table_relative": ("row[lb] = lb < prefix_blocks ? prefix_table[lb] : own[lb];",
+                              "row[lb] = lb < prefix_blocks ? prefix_table[lb] : own[lb - prefix_blocks];"),
 }
 
 
