@@ -32,6 +32,7 @@ if REPO not in sys.path:
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published
 METRIC = "effective KV-read HBM GB/s (% of MI355X peak) + decode tokens/s, paged attention"
+SHARED_PREFIX_PARTITION = 512
 
 
 def log(msg: str) -> None:
@@ -79,15 +80,22 @@ def upload(batch, dev):
     return t
 
 
-def time_steps(batch, t, partition_size: int, steps: int, warmup: int):
+def time_steps(batch, t, partition_size: int, steps: int, warmup: int, shared_prefix: bool = False):
     import torch
 
     import paged_kv_decode_13_amd as pkv
 
     out = torch.empty((batch.num_seqs, batch.num_heads, batch.head_dim), dtype=t["q"].dtype,
                       device=t["q"].device)
-    need = pkv.paged_decode_workspace_size(batch.num_seqs, batch.num_heads, batch.head_dim,
-                                           batch.max_context_len, partition_size)
+    if shared_prefix:
+        plen = batch.meta["shared_prefix_tokens"]
+        ptab = torch.from_numpy(batch.meta["prefix_table"]).to(t["q"].device)
+        need = pkv.paged_prefix_decode_workspace_size(
+            batch.num_seqs, batch.num_heads, batch.num_kv_heads, batch.head_dim,
+            batch.max_context_len, plen, partition_size)
+    else:
+        need = pkv.paged_decode_workspace_size(batch.num_seqs, batch.num_heads, batch.head_dim,
+                                               batch.max_context_len, partition_size)
     ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=t["q"].device)  # counter starts at zero
     has_write = "slots" in t
 
@@ -96,9 +104,15 @@ def time_steps(batch, t, partition_size: int, steps: int, warmup: int):
             pkv.paged_kv_write(t["nk"], t["nv"], t["kc"], t["vc"], t["slots"])
 
     def decode():
-        pkv.paged_decode_attention(t["q"], t["kc"], t["vc"], t["bt"], t["cl"], batch.block_size,
-                                   batch.scale, max_context_len=batch.max_context_len,
-                                   partition_size=partition_size, out=out, workspace=ws)
+        if shared_prefix:
+            pkv.paged_prefix_decode_attention(
+                t["q"], t["kc"], t["vc"], ptab, plen, t["bt"], t["cl"], batch.block_size,
+                batch.scale, max_context_len=batch.max_context_len,
+                partition_size=partition_size, out=out, workspace=ws)
+        else:
+            pkv.paged_decode_attention(t["q"], t["kc"], t["vc"], t["bt"], t["cl"], batch.block_size,
+                                       batch.scale, max_context_len=batch.max_context_len,
+                                       partition_size=partition_size, out=out, workspace=ws)
 
     for _ in range(warmup):
         write()
@@ -241,6 +255,9 @@ def main() -> int:
                     help="comma list of partition sizes to time as well (stderr report)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--shared-prefix", action="store_true",
+                    help="prefix_fp16: decode through paged_prefix_decode_attention (the shared "
+                         "prefix read once per KV head for the batch)")
     ap.add_argument("--mode", default="decode", choices=["decode", "write", "copy"])
     ap.add_argument("--copy-mb", type=int, default=1024)
     args = ap.parse_args()
@@ -279,7 +296,15 @@ def main() -> int:
         f"generated in {time.time() - t0:.1f}s")
     t = upload(batch, dev)
     torch.cuda.synchronize()
+    shared = bool(args.shared_prefix)
     ps = batch.partition_size if args.partition_size is None else args.partition_size
+    if shared and args.partition_size is None:
+        # the suffixes (0..1024 tokens) are cut finer than the whole histories:
+        # measured best on the shared-prefix path
+        ps = SHARED_PREFIX_PARTITION
+    if shared and "prefix_table" not in batch.meta:
+        print(f"{args.config} has no shared prefix", file=sys.stderr)
+        return 2
     if args.mode == "write":
         if batch.slot_mapping is None:
             print(f"{args.config} writes no tokens", file=sys.stderr)
@@ -289,21 +314,31 @@ def main() -> int:
 
     if args.sweep_partitions:
         for p in [int(x) for x in args.sweep_partitions.split(",")]:
-            r = time_steps(batch, t, p, max(5, args.steps // 2), 3)
+            r = time_steps(batch, t, p, max(5, args.steps // 2), 3, shared)
             gbs = batch.kv_bytes_logical() / (r["decode_ms"] * 1e-3) / 1e9
             log(f"[sweep] partition {p:6d}: decode {r['decode_ms']*1e3:8.1f} us "
                 f"({gbs:7.1f} GB/s, {100 * gbs / HBM_PEAK_GBS:5.1f}% of peak), "
                 f"write {r['write_ms']*1e3:6.1f} us")
 
-    r = time_steps(batch, t, ps, args.steps, args.warmup)
+    r = time_steps(batch, t, ps, args.steps, args.warmup, shared)
     log(f"[bench] timed {args.steps} steps: {r['ms_per_step']:.4f} ms/step "
         f"(decode {r['decode_ms']:.4f} ms, write {r['write_ms']:.4f} ms)")
 
     kv_bytes = batch.kv_bytes_logical()
     step_s = r["ms_per_step"] * 1e-3
     value = kv_bytes / step_s / 1e9
-    achieved = kv_bytes / (r["decode_ms"] * 1e-3) / 1e9
-    traffic = load_traffic(args.config if args.block_size is None else f"{args.config}_bs{args.block_size}")
+    # the roofline rates algorithmic HBM bytes: with the shared prefix read
+    # once, that is the distinct cached rows, not the logical history
+    alg_bytes = batch.kv_bytes_unique() if shared else kv_bytes
+    achieved = alg_bytes / (r["decode_ms"] * 1e-3) / 1e9
+    workload = args.config if args.block_size is None else f"{args.config}_bs{args.block_size}"
+    traffic = load_traffic(workload + ("_shared" if shared else ""))
+    if shared:
+        kernel = ("paged_prefix_decode_attention call (prefix MFMA kernel + suffix decode kernel "
+                  "+ log-sum-exp merge)")
+    else:
+        kernel = "paged_decode_attention call (decode kernel" + (
+            " + log-sum-exp merge)" if ps and batch.max_context_len > ps else ")")
 
     line = {
         "metric": METRIC,
@@ -339,8 +374,8 @@ def main() -> int:
         "step_ms_p99": round(r["step_ms_p99"], 5),
         "roofline": {
             "bound": "hbm",
-            "kernel": "paged_decode_attention call (decode kernel" + (
-                " + log-sum-exp merge)" if ps and batch.max_context_len > ps else ")"),
+            "kernel": kernel,
+            "algorithmic_bytes": alg_bytes,
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -348,8 +383,11 @@ def main() -> int:
             "traffic": traffic,
         },
     }
-    if args.block_size is not None:
+    if args.block_size is not None or shared:
         line["config"]["unique_kv_bytes"] = batch.kv_bytes_unique()
+    if shared:
+        line["config"]["shared_prefix_tokens"] = batch.meta["shared_prefix_tokens"]
+        line["config"]["entry_point"] = "paged_prefix_decode_attention"
 
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample ...")

@@ -156,6 +156,67 @@ pkv_status paged_decode_attention(
     pkv_dtype out_dtype, void *workspace, size_t workspace_bytes,
     void *stream);
 
+/*
+ * paged_prefix_decode_workspace_size -- bytes of device scratch
+ * paged_prefix_decode_attention needs (0 for an empty batch or invalid
+ * sizes).  Layout: the 256-byte work-counter area, then fp32 partial outputs
+ * [num_seqs, num_heads, S, head_dim] and (running max, normaliser) pairs
+ * [num_seqs, num_heads, S, 2], where S counts the prefix splits the library
+ * plans for these sizes plus the suffix partitions
+ * (ceil((max_context_len - prefix_len) / partition_size), at least 1; 1 when
+ * partition_size == 0).
+ */
+size_t paged_prefix_decode_workspace_size(int32_t num_seqs, int32_t num_heads,
+                                          int32_t num_kv_heads, int32_t head_dim,
+                                          int32_t max_context_len,
+                                          int32_t prefix_len,
+                                          int32_t partition_size);
+
+/*
+ * paged_prefix_decode_attention -- decode attention for a batch whose
+ * sequences share a prompt prefix held in shared, read-only pages.
+ *
+ * [P3] section "4.1 为什么页面化会改变 kernel 设计": the pages decode reads
+ * include prefix pages that several requests share; [P3] section "6. Prefix
+ * Cache 与 Attention Kernel 的关系": shared prefix pages are read-only and the
+ * access pattern becomes reuse of old pages plus appended new ones.
+ *
+ * Computes exactly what paged_decode_attention computes when token t of
+ * sequence s lives at prefix_table[t / block_size] for t < prefix_len and at
+ * block_tables[s][t / block_size] otherwise.  A sequence with
+ * context_lens[s] < prefix_len attends to the first context_lens[s] tokens of
+ * the prefix.  The prefix is read once per KV head for the whole batch: its
+ * score and value products for all num_seqs * G query rows are dense
+ * matrix products; the rest of each history goes through the paged decode,
+ * and a log-sum-exp merge joins the partial results.
+ *
+ *   prefix_table  [prefix_len / block_size] int32 physical block ids
+ *                 (device); may be NULL when prefix_len == 0
+ *   prefix_len    tokens of the shared prefix, a multiple of block_size and
+ *                 at most max_blocks_per_seq * block_size
+ *   block_tables  [num_seqs, max_blocks_per_seq] int32; entries below
+ *                 prefix_len / block_size and at or past
+ *                 ceil(context_lens[s] / block_size) are never read
+ *   workspace     at least paged_prefix_decode_workspace_size() bytes, same
+ *                 rules as for paged_decode_attention (counter area zero
+ *                 before first use; left zero by every call; one workspace
+ *                 per concurrently running call)
+ * Every other argument, the output and the error behaviour are those of
+ * paged_decode_attention; an out-of-range prefix table entry makes the
+ * outputs of the sequences that reach that page NaN.
+ * Supported: dtype PKV_F16 or PKV_BF16, head_dim 128, block_size in
+ * {4, 8, 16, 32, 64}, G in {1, 2, 4, 8}, num_seqs <= PKV_MAX_SEQS.
+ */
+pkv_status paged_prefix_decode_attention(
+    void *out, const void *query, const void *key_cache,
+    const void *value_cache, const int32_t *prefix_table, int32_t prefix_len,
+    const int32_t *block_tables, const int32_t *context_lens,
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+    int64_t num_blocks, int32_t max_context_len, float scale,
+    int32_t partition_size, pkv_dtype dtype, pkv_dtype out_dtype,
+    void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static, NUL-terminated description of a status code (host memory). */
 const char *pkv_status_string(pkv_status status);
 

@@ -13,6 +13,14 @@ Entry points (same names as the C ABI):
                          workspace=None)
   paged_decode_workspace_size(num_seqs, num_heads, head_dim, max_context_len,
                               partition_size)
+  paged_prefix_decode_attention(query, key_cache, value_cache, prefix_table,
+                                prefix_len, block_tables, context_lens,
+                                block_size, scale, *, max_context_len,
+                                partition_size=0, out=None, out_dtype=None,
+                                workspace=None)
+  paged_prefix_decode_workspace_size(num_seqs, num_heads, num_kv_heads,
+                                     head_dim, max_context_len, prefix_len,
+                                     partition_size)
 """
 from __future__ import annotations
 
@@ -23,6 +31,8 @@ __all__ = [
     "paged_kv_write",
     "paged_decode_attention",
     "paged_decode_workspace_size",
+    "paged_prefix_decode_attention",
+    "paged_prefix_decode_workspace_size",
     "library_path",
     "PagedKVError",
 ]
@@ -67,6 +77,12 @@ def _load():
                                            i32, ctypes.c_float, i32, ctypes.c_int, ctypes.c_int,
                                            p, sz, p]
     lib.paged_decode_attention.restype = ctypes.c_int
+    lib.paged_prefix_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    lib.paged_prefix_decode_workspace_size.restype = sz
+    lib.paged_prefix_decode_attention.argtypes = [p, p, p, p, p, i32, p, p, i32, i32, i32, i32, i32,
+                                                  i32, i64, i32, ctypes.c_float, i32, ctypes.c_int,
+                                                  ctypes.c_int, p, sz, p]
+    lib.paged_prefix_decode_attention.restype = ctypes.c_int
     lib.pkv_status_string.argtypes = [ctypes.c_int]
     lib.pkv_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -190,4 +206,72 @@ def paged_decode_attention(query, key_cache, value_cache, block_tables, context_
         _dtype_code(odt), ws_ptr, ws_bytes, _stream_handle(query.device))
     if st != 0:
         raise PagedKVError(st, "paged_decode_attention")
+    return out
+
+
+def paged_prefix_decode_workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int,
+                                       head_dim: int, max_context_len: int, prefix_len: int,
+                                       partition_size: int) -> int:
+    return int(_load().paged_prefix_decode_workspace_size(num_seqs, num_heads, num_kv_heads,
+                                                          head_dim, max_context_len, prefix_len,
+                                                          partition_size))
+
+
+def paged_prefix_decode_attention(query, key_cache, value_cache, prefix_table, prefix_len: int,
+                                  block_tables, context_lens, block_size: int, scale: float, *,
+                                  max_context_len: int, partition_size: int = 0, out=None,
+                                  out_dtype=None, workspace=None):
+    """Decode attention for a batch whose sequences share a prompt prefix:
+    tokens t < ``prefix_len`` (a multiple of ``block_size``) of every sequence
+    live in the pages ``prefix_table`` (int32 [prefix_len / block_size]),
+    later tokens in the sequence's own ``block_tables`` row (whose first
+    prefix_len / block_size entries are not read).  The prefix is read once
+    per KV head for the whole batch.  Other arguments as
+    ``paged_decode_attention``; 16-bit caches, head_dim 128."""
+    torch = _torch()
+    lib = _load()
+    for t, n in ((query, "query"), (key_cache, "key_cache"), (value_cache, "value_cache"),
+                 (prefix_table, "prefix_table"), (block_tables, "block_tables"),
+                 (context_lens, "context_lens")):
+        _gpu(t, n)
+    if prefix_table.dtype != torch.int32 or block_tables.dtype != torch.int32 \
+            or context_lens.dtype != torch.int32:
+        raise TypeError("prefix_table, block_tables and context_lens must be int32")
+    nb, bs, kvh, d = key_cache.shape
+    if bs != block_size:
+        raise ValueError("block_size does not match key_cache.shape[1]")
+    b, h, dq = query.shape
+    if dq != d or value_cache.shape != key_cache.shape:
+        raise ValueError("inconsistent shapes")
+    if block_tables.dim() != 2 or block_tables.shape[0] != b or tuple(context_lens.shape) != (b,):
+        raise ValueError("block_tables must be [num_seqs, max_blocks], context_lens [num_seqs]")
+    if prefix_table.numel() * block_size < prefix_len:
+        raise ValueError("prefix_table holds fewer pages than prefix_len needs")
+    if not (query.dtype == key_cache.dtype == value_cache.dtype):
+        raise TypeError("query and caches must share one dtype")
+    dt = _dtype_code(query.dtype)
+    odt = query.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((b, h, d), dtype=odt, device=query.device)
+    else:
+        _gpu(out, "out")
+        if tuple(out.shape) != (b, h, d):
+            raise ValueError("out must be [num_seqs, num_heads, head_dim]")
+        odt = out.dtype
+    need = paged_prefix_decode_workspace_size(b, h, kvh, d, int(max_context_len), int(prefix_len),
+                                              int(partition_size))
+    ws_ptr, ws_bytes = None, 0
+    if need:
+        if workspace is None:
+            workspace = torch.zeros(need, dtype=torch.uint8, device=query.device)
+        else:
+            _gpu(workspace, "workspace")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    st = lib.paged_prefix_decode_attention(
+        out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+        prefix_table.data_ptr(), int(prefix_len), block_tables.data_ptr(), context_lens.data_ptr(),
+        b, h, kvh, d, bs, block_tables.shape[1], nb, int(max_context_len), float(scale),
+        int(partition_size), dt, _dtype_code(odt), ws_ptr, ws_bytes, _stream_handle(query.device))
+    if st != 0:
+        raise PagedKVError(st, "paged_prefix_decode_attention")
     return out

@@ -20,7 +20,8 @@ OBJ_DIR = os.path.join(PKG_DIR, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libpagedkv.so")
 ARCH = "gfx950"
 
-SOURCES = ["pkv_api.hip", "kv_write.hip", "paged_decode.hip", "paged_decode_mfma.hip"]
+SOURCES = ["pkv_api.hip", "kv_write.hip", "paged_decode.hip", "paged_decode_mfma.hip",
+           "paged_prefix_mfma.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",

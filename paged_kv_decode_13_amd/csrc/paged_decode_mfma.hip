@@ -43,26 +43,13 @@
 #include <math.h>
 
 #include "pkv_decode_common.h"
+#include "pkv_mfma.h"
 
 #ifndef PKV_TILES_PER_STEP
 #define PKV_TILES_PER_STEP 2
 #endif
 
 namespace pkv {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-template <int DT>
-__device__ __forceinline__ f32x4_t mfma_16x16x32(const u32x4 a, const u32x4 b, f32x4_t c) {
-    if constexpr (DT == kBF16)
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-    else
-        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
-                                                      __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
-}
 
 // Value of head slot `hl` (0 <= hl < HS) held by the lanes of this lane's quad:
 // lane c of a quad carries head slot c % HS.
@@ -88,21 +75,6 @@ struct TileRegs {
     uint32_t vmask;  // bit i: row i holds a valid token
 };
 
-// Partitions of a sequence in the work list (an empty or out-of-range
-// context still gets one unit, which writes its zeros or NaNs).
-__device__ __forceinline__ int seq_parts(const DecodeArgs &a, int ctx) {
-    if (bad_context(a, ctx) || ctx == 0) return 1;
-    return (ctx + a.partition_size - 1) / a.partition_size;
-}
-
-// Full partitions of a sequence (its last partition is partial when the
-// length is not a multiple of the partition size; an empty or out-of-range
-// context has one partial unit).
-__device__ __forceinline__ int seq_full(const DecodeArgs &a, int ctx) {
-    if (bad_context(a, ctx) || ctx == 0) return 0;
-    return ctx / a.partition_size;
-}
-
 // Inclusive prefix sum over the workgroup's threads (s_scan: kThreads ints).
 __device__ __forceinline__ int block_scan(int v, int *s_scan) {
     const int tid = threadIdx.x;
@@ -124,6 +96,7 @@ __device__ __forceinline__ int block_scan(int v, int *s_scan) {
 // units come at the end, where they fill the gaps.  Builds the exclusive
 // prefix sums s_pf[0..B] (full partitions) and s_pp[0..B] (partial ones)
 // and caches the lengths in s_ctx.
+template <bool PFX>
 __device__ __forceinline__ void build_unit_order(const DecodeArgs &a, int *s_pf, int *s_pp,
                                                  int *s_ctx, int *s_scan) {
     const int B = a.num_seqs;
@@ -134,9 +107,9 @@ __device__ __forceinline__ void build_unit_order(const DecodeArgs &a, int *s_pf,
     for (int s = lo; s < hi; ++s) {
         const int ctx = a.context_lens[s];
         s_ctx[s] = ctx;
-        const int f = seq_full(a, ctx);
+        const int f = seq_full<PFX>(a, ctx);
         nf += f;
-        np += seq_parts(a, ctx) - f;
+        np += seq_parts<PFX>(a, ctx) - f;
     }
     const int incf = block_scan(nf, s_scan);
     const int incp = block_scan(np, s_scan);
@@ -144,9 +117,9 @@ __device__ __forceinline__ void build_unit_order(const DecodeArgs &a, int *s_pf,
     for (int s = lo; s < hi; ++s) {
         s_pf[s] = rf;
         s_pp[s] = rp;
-        const int f = seq_full(a, s_ctx[s]);
+        const int f = seq_full<PFX>(a, s_ctx[s]);
         rf += f;
-        rp += seq_parts(a, s_ctx[s]) - f;
+        rp += seq_parts<PFX>(a, s_ctx[s]) - f;
     }
     if (tid == kThreads - 1) {
         s_pf[B] = incf;
@@ -167,7 +140,11 @@ __device__ __forceinline__ int search_le(const int *pre, int n, int x) {
 
 // Three waves per SIMD (<= 168 VGPRs) keep enough loads in flight; the
 // allocator is held to that budget.
-template <int DT, int G>
+//
+// PFX: the launch covers tokens [token_begin, ctx) of each sequence and
+// always writes partials (slots part_base.. of part_stride), for the
+// shared-prefix path; the plain instantiation never reads those fields.
+template <int DT, int G, bool PFX>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8)))
 void paged_decode_mfma_kernel(DecodeArgs a) {
     constexpr int D = 128;
@@ -189,7 +166,7 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
     int *s_pf = s_dyn;
     int *s_pp = s_dyn + a.num_seqs + 1;
     int *s_ctx = s_dyn + 2 * (a.num_seqs + 1);
-    build_unit_order(a, s_pf, s_pp, s_ctx, s_pages);
+    build_unit_order<PFX>(a, s_pf, s_pp, s_ctx, s_pages);
     const int total_full = s_pf[a.num_seqs];
     const int total_units = (total_full + s_pp[a.num_seqs]) * a.num_kv_heads;
 
@@ -234,13 +211,13 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
             u.p = sp - s_pf[u.s];
         } else {
             u.s = search_le(s_pp, a.num_seqs, sp - total_full);
-            u.p = seq_full(a, s_ctx[u.s]);
+            u.p = seq_full<PFX>(a, s_ctx[u.s]);
         }
         u.ctx = s_ctx[u.s];
         u.bad_len = bad_context(a, u.ctx);
-        u.tok_begin = u.p * a.partition_size;
+        u.tok_begin = first_token<PFX>(a) + u.p * a.partition_size;
         u.tok_end = u.bad_len ? 0 : min(u.ctx, u.tok_begin + a.partition_size);
-        u.nparts = seq_parts(a, u.ctx);
+        u.nparts = seq_parts<PFX>(a, u.ctx);
         u.empty = false;
 
         if (tid == 0) s_bad = 0;
@@ -428,7 +405,7 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
             }
         }
         __syncthreads();
-        unit_epilogue<DT, D, G>(a, u, u.bad_len || s_bad != 0, s_m, s_l, s_acc);
+        unit_epilogue<DT, D, G, PFX>(a, u, u.bad_len || s_bad != 0, s_m, s_l, s_acc);
     }
 }
 
@@ -451,20 +428,26 @@ static hipError_t launch_persistent(K kernel, const DecodeArgs &a, hipStream_t s
     return hipGetLastError();
 }
 
-template <int DT>
+template <int DT, bool PFX>
 static hipError_t launch_group(const DecodeArgs &a, hipStream_t stream) {
     switch (a.num_heads / a.num_kv_heads) {
-        case 1: return launch_persistent(paged_decode_mfma_kernel<DT, 1>, a, stream);
-        case 2: return launch_persistent(paged_decode_mfma_kernel<DT, 2>, a, stream);
-        case 4: return launch_persistent(paged_decode_mfma_kernel<DT, 4>, a, stream);
-        case 8: return launch_persistent(paged_decode_mfma_kernel<DT, 8>, a, stream);
+        case 1: return launch_persistent(paged_decode_mfma_kernel<DT, 1, PFX>, a, stream);
+        case 2: return launch_persistent(paged_decode_mfma_kernel<DT, 2, PFX>, a, stream);
+        case 4: return launch_persistent(paged_decode_mfma_kernel<DT, 4, PFX>, a, stream);
+        case 8: return launch_persistent(paged_decode_mfma_kernel<DT, 8, PFX>, a, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_paged_decode_mfma(const DecodeArgs &a, int dtype, hipStream_t stream) {
-    if (dtype == kBF16) return launch_group<kBF16>(a, stream);
-    if (dtype == kF16) return launch_group<kF16>(a, stream);
+    if (dtype == kBF16) return launch_group<kBF16, false>(a, stream);
+    if (dtype == kF16) return launch_group<kF16, false>(a, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_paged_decode_mfma_suffix(const DecodeArgs &a, int dtype, hipStream_t stream) {
+    if (dtype == kBF16) return launch_group<kBF16, true>(a, stream);
+    if (dtype == kF16) return launch_group<kF16, true>(a, stream);
     return hipErrorInvalidValue;
 }
 

@@ -37,6 +37,51 @@ int32_t num_partitions(int32_t max_context_len, int32_t partition_size) {
     return (int32_t)(((int64_t)max_context_len + partition_size - 1) / partition_size);
 }
 
+// Shared-prefix plan: 64-query-row blocks per KV head, and the prefix cut
+// into splits of whole 64-token chunks (at most 2048 tokens each) so that
+// about kPrefixTargetUnits workgroups share the prefix work.
+constexpr int32_t kPrefixChunk = 64;
+constexpr int32_t kPrefixMaxSplitChunks = 32;
+#ifndef PKV_PFX_TARGET_UNITS
+#define PKV_PFX_TARGET_UNITS 256
+#endif
+constexpr int64_t kPrefixTargetUnits = PKV_PFX_TARGET_UNITS;
+
+struct PrefixPlan {
+    int32_t row_blocks, num_splits, split_tokens;
+    int32_t suffix_parts, suffix_partition;
+};
+
+PrefixPlan prefix_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                       int32_t max_context_len, int32_t prefix_len, int32_t partition_size) {
+    PrefixPlan p;
+    const int64_t rows = (int64_t)num_seqs * (num_heads / num_kv_heads);
+    p.row_blocks = (int32_t)((rows + 63) / 64);
+    p.num_splits = 0;
+    p.split_tokens = kPrefixChunk;
+    if (prefix_len > 0) {
+        const int64_t chunks = (prefix_len + kPrefixChunk - 1) / kPrefixChunk;
+        const int64_t base = (int64_t)num_kv_heads * p.row_blocks;
+        int64_t want = (kPrefixTargetUnits + base - 1) / base;
+        const int64_t most = (chunks + 3) / 4;  // keep >= 4 chunks per split
+        if (want > most) want = most;
+        const int64_t least = (chunks + kPrefixMaxSplitChunks - 1) / kPrefixMaxSplitChunks;
+        if (want < least) want = least;
+        const int64_t per = (chunks + want - 1) / want;
+        p.split_tokens = (int32_t)(per * kPrefixChunk);
+        p.num_splits = (int32_t)((chunks + per - 1) / per);
+    }
+    const int32_t span = max_context_len - prefix_len;
+    if (partition_size > 0) {
+        p.suffix_parts = span > 0 ? (int32_t)(((int64_t)span + partition_size - 1) / partition_size) : 1;
+        p.suffix_partition = partition_size;
+    } else {
+        p.suffix_parts = 1;
+        p.suffix_partition = span > 0 ? span : 1;
+    }
+    return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -151,8 +196,127 @@ pkv_status paged_decode_attention(void *out, const void *query, const void *key_
     a.num_partitions = parts;
     a.scale_log2e = scale * 1.4426950408889634f;
     a.out_f32 = out_dtype == PKV_F32 ? 1 : 0;
+    a.token_begin = 0;
+    a.part_stride = parts;
+    a.part_base = 0;
+    a.fold_prefix = 0;
     hipError_t e = pkv::launch_paged_decode(a, (int)dtype, head_dim,
                                             reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+}  // extern "C"
+
+extern "C" {
+
+size_t paged_prefix_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                          int32_t head_dim, int32_t max_context_len,
+                                          int32_t prefix_len, int32_t partition_size) {
+    if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        num_heads % num_kv_heads != 0 || prefix_len < 0 || max_context_len < 0 || partition_size < 0)
+        return 0;
+    const PrefixPlan p = prefix_plan(num_seqs, num_heads, num_kv_heads, max_context_len, prefix_len,
+                                     partition_size);
+    const int64_t slots = (int64_t)p.num_splits + p.suffix_parts;
+    return kCounterBytes + (size_t)num_seqs * num_heads * (size_t)slots * (size_t)(head_dim + 2) * sizeof(float);
+}
+
+pkv_status paged_prefix_decode_attention(
+    void *out, const void *query, const void *key_cache, const void *value_cache,
+    const int32_t *prefix_table, int32_t prefix_len, const int32_t *block_tables,
+    const int32_t *context_lens, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+    int32_t max_context_len, float scale, int32_t partition_size, pkv_dtype dtype,
+    pkv_dtype out_dtype, void *workspace, size_t workspace_bytes, void *stream) {
+    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq < 0 ||
+        num_blocks < 0 || max_context_len < 0 || partition_size < 0 || prefix_len < 0)
+        return PKV_ERR_SHAPE;
+    if (num_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
+    if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return PKV_ERR_DTYPE;
+    if (out_dtype != dtype && out_dtype != PKV_F32) return PKV_ERR_DTYPE;
+    if (dtype == PKV_F32 || head_dim != 128) return PKV_ERR_UNSUPPORTED;
+    if (!pow2_block(block_size)) return PKV_ERR_UNSUPPORTED;
+    const int32_t group = num_heads / num_kv_heads;
+    if (group != 1 && group != 2 && group != 4 && group != 8) return PKV_ERR_UNSUPPORTED;
+    if (partition_size != 0 && partition_size % partition_granule(block_size) != 0)
+        return PKV_ERR_UNSUPPORTED;
+    if (prefix_len % block_size != 0) return PKV_ERR_SHAPE;  // whole pages are shared
+    if ((int64_t)prefix_len > (int64_t)max_blocks_per_seq * block_size) return PKV_ERR_SHAPE;
+    if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size) return PKV_ERR_SHAPE;
+    if (num_blocks == 0 && (max_context_len > 0 || prefix_len > 0)) return PKV_ERR_SHAPE;
+    if (!isfinite(scale)) return PKV_ERR_SHAPE;
+    if (num_seqs > PKV_MAX_SEQS) return PKV_ERR_UNSUPPORTED;
+    if (num_seqs == 0) return PKV_OK;
+    if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens)
+        return PKV_ERR_NULL;
+    if (prefix_len > 0 && !prefix_table) return PKV_ERR_NULL;
+    if (!aligned16(out) || !aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache))
+        return PKV_ERR_ALIGN;
+
+    const PrefixPlan plan = prefix_plan(num_seqs, num_heads, num_kv_heads, max_context_len,
+                                        prefix_len, partition_size);
+    const int64_t slots = (int64_t)plan.num_splits + plan.suffix_parts;
+    if ((int64_t)num_seqs * num_kv_heads * plan.suffix_parts > INT_MAX ||
+        (int64_t)num_seqs * num_heads > INT_MAX ||
+        (int64_t)plan.row_blocks * plan.num_splits * num_kv_heads > INT_MAX || slots > INT_MAX)
+        return PKV_ERR_SHAPE;
+    const size_t need = paged_prefix_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim,
+                                                           max_context_len, prefix_len, partition_size);
+    if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return PKV_ERR_ALIGN;
+    float *part_out = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + kCounterBytes);
+    float *part_ml = part_out + (size_t)num_seqs * num_heads * (size_t)slots * head_dim;
+    const float sl2 = scale * 1.4426950408889634f;
+
+    pkv::PrefixArgs p = {};
+    p.part_out = part_out;
+    p.part_ml = part_ml;
+    p.query = query;
+    p.key_cache = key_cache;
+    p.value_cache = value_cache;
+    p.prefix_table = prefix_table;
+    p.context_lens = context_lens;
+    p.num_blocks = num_blocks;
+    p.num_seqs = num_seqs;
+    p.num_heads = num_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.log2_group = log2i(group);
+    p.block_size = block_size;
+    p.log2_block_size = log2i(block_size);
+    p.prefix_len = prefix_len;
+    p.split_tokens = plan.split_tokens;
+    p.num_splits = plan.num_splits;
+    p.row_blocks = plan.row_blocks;
+    p.part_stride = (int32_t)slots;
+    p.scale_log2e = sl2;
+
+    pkv::DecodeArgs a = {};
+    a.out = out;
+    a.work_counter = reinterpret_cast<unsigned *>(workspace);
+    a.part_out = part_out;
+    a.part_ml = part_ml;
+    a.query = query;
+    a.key_cache = key_cache;
+    a.value_cache = value_cache;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.num_blocks = num_blocks;
+    a.num_seqs = num_seqs;
+    a.num_heads = num_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.block_size = block_size;
+    a.log2_block_size = log2i(block_size);
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.max_context_len = max_context_len;
+    a.partition_size = plan.suffix_partition;
+    a.num_partitions = plan.suffix_parts;
+    a.scale_log2e = sl2;
+    a.out_f32 = out_dtype == PKV_F32 ? 1 : 0;
+    a.token_begin = prefix_len;
+    a.part_stride = (int32_t)slots;
+    a.part_base = plan.num_splits;
+    a.fold_prefix = plan.suffix_parts == 1 ? 1 : 0;
+    hipError_t e = pkv::launch_paged_prefix_decode(p, a, (int)dtype, reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 

@@ -30,6 +30,35 @@ __device__ __forceinline__ bool bad_context(const DecodeArgs &a, int ctx) {
            (int64_t)ctx > (int64_t)a.max_blocks_per_seq * a.block_size;
 }
 
+// First token a launch reads: 0, or the end of a shared prefix when the
+// launch covers only the rest of each history (PFX instantiations; the
+// plain ones never read the extra fields, which keeps their registers).
+template <bool PFX>
+__device__ __forceinline__ int first_token(const DecodeArgs &a) {
+    if constexpr (PFX) return a.token_begin; else return 0;
+}
+
+// Partitions of a sequence in the work list: its tokens [first_token, ctx)
+// cut into partition_size pieces.  A sequence with nothing to read, or an
+// out-of-range length, still gets one unit, which writes its zeros, empty
+// partial or NaNs.
+template <bool PFX = false>
+__device__ __forceinline__ int seq_parts(const DecodeArgs &a, int ctx) {
+    const int span = ctx - first_token<PFX>(a);
+    if (bad_context(a, ctx) || span <= 0) return 1;
+    return (span + a.partition_size - 1) / a.partition_size;
+}
+
+// Full partitions of a sequence (its last partition is partial when the
+// span is not a multiple of the partition size; an empty or out-of-range
+// context has one partial unit).
+template <bool PFX = false>
+__device__ __forceinline__ int seq_full(const DecodeArgs &a, int ctx) {
+    const int span = ctx - first_token<PFX>(a);
+    if (bad_context(a, ctx) || span <= 0) return 0;
+    return span / a.partition_size;
+}
+
 __device__ __forceinline__ Unit make_unit(const DecodeArgs &a) {
     // KV head fastest: the units that read the same pages run side by side.
     int u = blockIdx.x;
@@ -77,7 +106,7 @@ __device__ __forceinline__ void store_out(const DecodeArgs &a, int64_t idx, floa
 // Merge the per-wave states (running max m, normaliser l, unnormalised
 // accumulator) of one unit and store either the final output (one partition)
 // or the partition's normalised partial with its (m, l).
-template <int DT, int D, int G>
+template <int DT, int D, int G, bool PFX = false>
 __device__ __forceinline__ void unit_epilogue(const DecodeArgs &a, const Unit &u, bool bad,
                                               const float (*s_m)[G], const float (*s_l)[G],
                                               const float (*s_acc)[G][D]) {
@@ -95,13 +124,45 @@ __device__ __forceinline__ void unit_epilogue(const DecodeArgs &a, const Unit &u
             L += s_l[w][g] * f;
             O += s_acc[w][g][d] * f;
         }
+        const int h = h0 + g;
+        if constexpr (PFX) {
+            if (a.fold_prefix) {
+                // One partition per suffix: join the shared prefix's partials
+                // (written by the prefix kernel earlier on this stream) here
+                // and store the output; no merge kernel follows.
+                const int64_t base = ((int64_t)u.s * a.num_heads + h) * a.part_stride;
+                float Mx = M;
+                bool poisoned = bad;  // a bad prefix page marks its partial's max NaN
+                for (int p = 0; p < a.part_base; ++p) {
+                    const float mp = a.part_ml[(base + p) * 2];
+                    poisoned |= mp != mp;
+                    Mx = fmaxf(Mx, mp);
+                }
+                float res = 0.f;  // nothing seen (empty context) -> zeros
+                if (poisoned) {
+                    res = __builtin_nanf("");
+                } else if (Mx != -INFINITY) {
+                    const float f = (M == -INFINITY) ? 0.f : fast_exp2(M - Mx);
+                    float Lt = L * f, Ot = O * f;
+                    for (int p = 0; p < a.part_base; ++p) {
+                        const float w = a.part_ml[(base + p) * 2 + 1] * fast_exp2(a.part_ml[(base + p) * 2] - Mx);
+                        Lt += w;
+                        Ot = fmaf(w, a.part_out[(base + p) * D + d], Ot);
+                    }
+                    res = Ot / Lt;
+                }
+                store_out<DT>(a, ((int64_t)u.s * a.num_heads + h) * D + d, res);
+                continue;
+            }
+        }
         float res = L > 0.f ? O / L : 0.f;  // empty context -> zeros
         if (bad) res = __builtin_nanf("");
-        const int h = h0 + g;
-        if (u.nparts == 1) {
+        if (!PFX && u.nparts == 1) {
             store_out<DT>(a, ((int64_t)u.s * a.num_heads + h) * D + d, res);
         } else {
-            const int64_t slot = ((int64_t)u.s * a.num_heads + h) * a.num_partitions + u.p;
+            // a prefix launch always writes partials, after the prefix's slots
+            const int64_t slot = PFX ? ((int64_t)u.s * a.num_heads + h) * a.part_stride + a.part_base + u.p
+                                     : ((int64_t)u.s * a.num_heads + h) * a.num_partitions + u.p;
             a.part_out[slot * D + d] = res;
             if (d == 0) {
                 a.part_ml[slot * 2] = bad ? __builtin_nanf("") : M;
@@ -114,5 +175,7 @@ __device__ __forceinline__ void unit_epilogue(const DecodeArgs &a, const Unit &u
 // MFMA decode kernel launcher (16-bit caches, head_dim 128); the merge
 // kernel is launched by the caller.
 hipError_t launch_paged_decode_mfma(const DecodeArgs &a, int dtype, hipStream_t stream);
+// The same over tokens [token_begin, ctx), partials only (shared-prefix path).
+hipError_t launch_paged_decode_mfma_suffix(const DecodeArgs &a, int dtype, hipStream_t stream);
 
 }  // namespace pkv

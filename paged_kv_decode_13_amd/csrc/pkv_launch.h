@@ -41,6 +41,36 @@ struct DecodeArgs {
     int32_t num_partitions;     // P: grid extent along the context
     float scale_log2e;          // scale * log2(e): scores live in the exp2 domain
     int32_t out_f32;            // 1: out is binary32; 0: out has the cache dtype
+    int32_t token_begin;        // first token read (a page boundary; 0 = whole history)
+    int32_t part_stride;        // partial slots per (sequence, head) in the workspace
+    int32_t part_base;          // slot of this launch's partition 0
+    int32_t fold_prefix;        // 1: one partition per suffix; the epilogue joins
+                                // slots 0..part_base-1 and stores out (no merge)
+};
+
+// Shared-prefix score/value kernel: every query row of every sequence
+// against the prefix pages of one KV head, split along the prefix.
+struct PrefixArgs {
+    float *part_out;            // [B, H, part_stride, D]: slots 0..num_splits-1
+    float *part_ml;             // [B, H, part_stride, 2]
+    const void *query;          // [B, H, D]
+    const void *key_cache;      // [NB, bs, KVH, D]
+    const void *value_cache;
+    const int32_t *prefix_table;  // [prefix_len / bs]
+    const int32_t *context_lens;  // [B]
+    int64_t num_blocks;
+    int32_t num_seqs;
+    int32_t num_heads;
+    int32_t num_kv_heads;
+    int32_t log2_group;         // log2(H / KVH)
+    int32_t block_size;
+    int32_t log2_block_size;
+    int32_t prefix_len;         // tokens, a multiple of block_size
+    int32_t split_tokens;       // prefix tokens per unit (a multiple of 64)
+    int32_t num_splits;
+    int32_t row_blocks;         // ceil(B * G / 64)
+    int32_t part_stride;
+    float scale_log2e;
 };
 
 hipError_t launch_kv_write(const WriteArgs &a, hipStream_t stream);
@@ -48,5 +78,12 @@ hipError_t launch_kv_write(const WriteArgs &a, hipStream_t stream);
 // dtype: 0 f32, 1 f16, 2 bf16.  Launches the decode kernel and, when
 // num_partitions > 1, the log-sum-exp merge.
 hipError_t launch_paged_decode(const DecodeArgs &a, int dtype, int head_dim, hipStream_t stream);
+
+// Shared-prefix decode (16-bit caches, head_dim 128): the prefix kernel
+// (when num_splits > 0), then the suffix decode over tokens [token_begin,
+// ctx): with fold_prefix its epilogue joins the prefix slots and stores out;
+// otherwise it writes partial slots num_splits.. and a merge kernel follows.
+hipError_t launch_paged_prefix_decode(const PrefixArgs &p, const DecodeArgs &a, int dtype,
+                                      hipStream_t stream);
 
 }  // namespace pkv

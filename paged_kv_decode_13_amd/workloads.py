@@ -371,7 +371,67 @@ def _prefix_fp16(seed: int, block_size: int, poison: bool) -> DecodeBatch:
                        scale=float(np.float32(1.0 / math.sqrt(d))),
                        partition_size=1024, poison_block=spare,
                        unique_tokens=prefix + n_suffix,
-                       meta={"shared_prefix_tokens": prefix})
+                       meta={"shared_prefix_tokens": prefix,
+                             "prefix_table": np.ascontiguousarray(tables[0, :n_pre])})
+
+
+def make_prefix_batch(context_lens, prefix_len: int, *, num_heads: int, num_kv_heads: int,
+                      head_dim: int, block_size: int, dtype: str, seed: int,
+                      partition_size: int = 0, own_prefix_entries: str = "invalid",
+                      name: str = "prefix") -> DecodeBatch:
+    """Sequences sharing a ``prefix_len``-token prompt prefix held in shared
+    pages (``meta["prefix_table"]``), each followed by its own shuffled pages
+    up to its context length; a sequence shorter than the prefix sees the
+    first ``ctx`` prefix tokens.  ``own_prefix_entries`` fills the first
+    prefix_len / block_size entries of every table row: "copy" (the shared
+    ids, as a plain paged table would hold them), "poison" (the NaN spare
+    page) or "invalid" (an id outside the pool) -- the shared-prefix decode
+    must not read them.  Rows past each context in its last own page and the
+    spare page are NaN."""
+    if prefix_len % block_size:
+        raise ValueError("the shared prefix is whole pages")
+    ctx = np.asarray(context_lens, dtype=np.int64).reshape(-1)
+    ss = np.random.SeedSequence(seed)
+    s_perm, s_q, s_k, s_v = ss.spawn(4)
+    rng = np.random.Generator(np.random.PCG64(s_perm))
+    n_pre = prefix_len // block_size
+    suf_pages = (np.maximum(ctx - prefix_len, 0) + block_size - 1) // block_size
+    total = n_pre + int(suf_pages.sum())
+    ids = rng.permutation(total).astype(np.int32)
+    spare = total
+    nb = total + 1
+    mb = max(1, n_pre + int(suf_pages.max(initial=0)))
+    tables = np.full((ctx.size, mb), spare, dtype=np.int32)
+    fill = {"copy": None, "poison": spare, "invalid": nb + 7}[own_prefix_entries]
+    tables[:, :n_pre] = ids[:n_pre] if fill is None else fill
+    pos = n_pre
+    for s in range(ctx.size):
+        n = int(suf_pages[s])
+        tables[s, n_pre:n_pre + n] = ids[pos:pos + n]
+        pos += n
+    shape = (nb, block_size, num_kv_heads, head_dim)
+    kc = _random_storage(s_k, shape, dtype)
+    vc = _random_storage(s_v, shape, dtype)
+    q = _random_storage(s_q, (ctx.size, num_heads, head_dim), dtype)
+    rows = [np.arange(spare * block_size, (spare + 1) * block_size, dtype=np.int64)]
+    for s, c in enumerate(ctx):
+        c = int(c)
+        if c > prefix_len and c % block_size:
+            last = int(tables[s, (c - 1) // block_size])
+            rows.append(np.arange(last * block_size + c % block_size, (last + 1) * block_size))
+    rows = np.concatenate(rows).astype(np.int64)
+    _poison_rows(kc, rows, dtype)
+    _poison_rows(vc, rows, dtype)
+    batch = DecodeBatch(name=name, dtype=dtype, num_heads=num_heads, num_kv_heads=num_kv_heads,
+                        head_dim=head_dim, block_size=block_size, query=q, key_cache=kc,
+                        value_cache=vc, block_tables=tables, context_lens=ctx.astype(np.int32),
+                        scale=float(np.float32(1.0 / math.sqrt(head_dim))),
+                        partition_size=partition_size, poison_block=spare,
+                        unique_tokens=min(prefix_len, int(ctx.max(initial=0)))
+                        + int(np.maximum(ctx - prefix_len, 0).sum()))
+    batch.meta.update(num_blocks=nb, shared_prefix_tokens=prefix_len,
+                      prefix_table=np.ascontiguousarray(ids[:n_pre]))
+    return batch
 
 
 def make_config(name: str, *, block_size: int | None = None, seed: int | None = None,

@@ -52,6 +52,34 @@ def gpu_step(batch: wl.DecodeBatch, t, *, partition_size=None, out_dtype=None, w
     return out
 
 
+def gpu_prefix_step(batch: wl.DecodeBatch, t, *, partition_size=None, out_dtype=None,
+                    max_context_len=None, prefix_table=None):
+    """paged_prefix_decode_attention with the batch's shared prefix table."""
+    import torch
+
+    import paged_kv_decode_13_amd as pkv
+
+    pt = batch.meta["prefix_table"] if prefix_table is None else prefix_table
+    pt = torch.from_numpy(np.ascontiguousarray(pt, dtype=np.int32)).to(t["q"].device)
+    ps = batch.partition_size if partition_size is None else partition_size
+    odt = None if out_dtype is None else getattr(torch, TORCH_DT[out_dtype])
+    out = pkv.paged_prefix_decode_attention(
+        t["q"], t["kc"], t["vc"], pt, batch.meta["shared_prefix_tokens"], t["bt"], t["cl"],
+        batch.block_size, batch.scale,
+        max_context_len=batch.max_context_len if max_context_len is None else max_context_len,
+        partition_size=ps, out_dtype=odt)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_prefix_step(batch: wl.DecodeBatch, prefix_table=None):
+    pt = batch.meta["prefix_table"] if prefix_table is None else prefix_table
+    return oracle.paged_prefix_decode(batch.query, batch.key_cache, batch.value_cache, pt,
+                                      batch.meta["shared_prefix_tokens"], batch.block_tables,
+                                      batch.context_lens, batch.block_size, batch.scale,
+                                      batch.dtype)
+
+
 def to_f64(out) -> np.ndarray:
     import torch
 

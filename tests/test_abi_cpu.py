@@ -34,7 +34,8 @@ def _declared():
 def test_exports_every_declared_symbol(lib):
     names = _declared()
     assert set(names) == {"paged_kv_write", "paged_decode_workspace_size",
-                          "paged_decode_attention", "pkv_status_string"}
+                          "paged_decode_attention", "paged_prefix_decode_workspace_size",
+                          "paged_prefix_decode_attention", "pkv_status_string"}
     out = subprocess.run(["nm", "-D", "--defined-only", lib._name], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
@@ -109,6 +110,55 @@ def test_workspace_size(lib):
     assert lib.paged_decode_workspace_size(4, 32, 128, 512, 512) == 256  # one partition
     assert lib.paged_decode_workspace_size(4, 32, 128, 1025, 512) == 256 + 4 * 32 * 3 * 130 * 4
     assert lib.paged_decode_workspace_size(256, 32, 128, 16000, 512) == 256 + 256 * 32 * 32 * 130 * 4
+
+
+def _prefix(lib, **kw):
+    a = dict(out=A, q=A, kc=A, vc=A, pt=A, plen=2048, bt=A, cl=A, b=128, h=32, kvh=8, d=128, bs=16,
+             mb=192, nb=5000, maxc=3072, scale=0.088, ps=0, dt=F16, odt=F16, ws=A, wsb=1 << 30)
+    a.update(kw)
+    return lib.paged_prefix_decode_attention(
+        a["out"], a["q"], a["kc"], a["vc"], a["pt"], a["plen"], a["bt"], a["cl"], a["b"], a["h"],
+        a["kvh"], a["d"], a["bs"], a["mb"], a["nb"], a["maxc"], a["scale"], a["ps"], a["dt"],
+        a["odt"], a["ws"], a["wsb"], None)
+
+
+def test_prefix_decode_validation(lib):
+    assert _prefix(lib, plen=-16) == SHAPE
+    assert _prefix(lib, plen=2040) == SHAPE  # not whole pages
+    assert _prefix(lib, plen=192 * 16 + 16) == SHAPE  # longer than a table
+    assert _prefix(lib, maxc=192 * 16 + 1) == SHAPE
+    assert _prefix(lib, nb=0) == SHAPE
+    assert _prefix(lib, h=30) == SHAPE
+    assert _prefix(lib, dt=F32, odt=F32) == UNSUP  # 16-bit caches only
+    assert _prefix(lib, d=64) == UNSUP
+    assert _prefix(lib, bs=12) == UNSUP
+    assert _prefix(lib, h=128) == UNSUP
+    assert _prefix(lib, ps=24) == UNSUP
+    assert _prefix(lib, b=4097) == UNSUP
+    assert _prefix(lib, odt=BF16) == DTYPE
+    assert _prefix(lib, pt=None) == NULL
+    assert _prefix(lib, bt=None) == NULL
+    assert _prefix(lib, q=A + 2) == ALIGN
+    assert _prefix(lib, ws=None) == WORKSPACE
+    need = lib.paged_prefix_decode_workspace_size(128, 32, 8, 128, 3072, 2048, 0)
+    assert _prefix(lib, wsb=need - 1) == WORKSPACE
+    assert _prefix(lib, ws=A + 8, wsb=need) == ALIGN
+    assert _prefix(lib, b=0, q=None) == OK
+
+
+def test_prefix_workspace_size(lib):
+    # 128 sequences x G = 4: 512 query rows = 8 row blocks per KV head; 64
+    # blocks in all, so the 2048-token prefix is cut into 4 splits of 512
+    # tokens; one suffix slot unsplit, two at partition 512 for 1024 tokens
+    per = 128 * 32 * 130 * 4
+    assert lib.paged_prefix_decode_workspace_size(128, 32, 8, 128, 3072, 2048, 0) == 256 + 5 * per
+    assert lib.paged_prefix_decode_workspace_size(128, 32, 8, 128, 3072, 2048, 512) == 256 + 6 * per
+    # no prefix: the suffix partitions only
+    assert lib.paged_prefix_decode_workspace_size(128, 32, 8, 128, 3072, 0, 1024) == 256 + 3 * per
+    # a long prefix is cut into splits of at most 2048 tokens
+    big = lib.paged_prefix_decode_workspace_size(2048, 32, 8, 128, 40000, 32768, 0)
+    assert big == 256 + 2048 * 32 * (16 + 1) * 130 * 4
+    assert lib.paged_prefix_decode_workspace_size(0, 32, 8, 128, 3072, 2048, 0) == 0
 
 
 def test_binding_rejects_cpu_tensors(lib):

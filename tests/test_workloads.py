@@ -170,3 +170,23 @@ def test_prefill_layout():
             pos += 1
     assert ((b.key_cache.view(np.uint16) & 0x7C00) == 0x7C00).all()
     _check_layout(b)
+
+
+def test_prefix_batch_layout():
+    """Shared prefix pages are the first pages of the pool order; own rows'
+    prefix entries point outside the pool; suffix pages are disjoint."""
+    plen, bs = 24, 8
+    b = wl.make_prefix_batch([0, 5, 24, 25, 60], plen, num_heads=4, num_kv_heads=2, head_dim=64,
+                             block_size=bs, dtype="bf16", seed=2)
+    pt = b.meta["prefix_table"]
+    assert pt.shape == (3,) and b.meta["shared_prefix_tokens"] == plen
+    assert (b.block_tables[:, :3] >= b.num_blocks).all()  # never to be read
+    own = [b.block_tables[s, 3:3 + -(-max(int(c) - plen, 0) // bs)] for s, c in enumerate(b.context_lens)]
+    flat = np.concatenate(own)
+    assert len(np.unique(flat)) == len(flat) and not np.isin(flat, pt).any()
+    assert (np.concatenate([pt, flat]) < b.num_blocks).all()
+    assert b.unique_tokens == plen + (1 + 36)
+    # the composed history of sequence 4 is the prefix then its own pages
+    keys, _ = oracle.paged_gather(b.key_cache, b.value_cache,
+                                  np.concatenate([pt, b.block_tables[4, 3:]]), 60, 1, "bf16")
+    assert not np.isnan(keys).any()
