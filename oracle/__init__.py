@@ -18,7 +18,7 @@ invariances, exhaustive element decoding).  No function is parity unpinned.
 
 Array conventions: float32 arrays hold binary32 data; 16-bit data (binary16 or
 bfloat16) is held as ``uint16`` bit patterns and needs an explicit ``dtype``
-tag ('f16' or 'bf16').
+tag ('f16' or 'bf16'); quantised caches hold OCP E4M3 codes as ``uint8``.
 """
 from __future__ import annotations
 
@@ -64,6 +64,13 @@ def _bind(lib):
     lib.oracle_paged_prefix_decode.argtypes = [p, p, p, p, p, i32, p, p, i32, i32, i32, i32, i32,
                                                i32, i64, dbl, ctypes.c_int, ctypes.c_int]
     lib.oracle_paged_kv_write.argtypes = [p, p, p, p, p, i64, i32, i32, i32, i64, ctypes.c_int]
+    lib.oracle_decode_e4m3.argtypes = [ctypes.c_uint8]
+    lib.oracle_decode_e4m3.restype = dbl
+    lib.oracle_encode_e4m3.argtypes = [ctypes.c_float]
+    lib.oracle_encode_e4m3.restype = ctypes.c_uint8
+    lib.oracle_paged_kv_write_e4m3.argtypes = [p, p, p, p, p, p, p, i64, i32, i32, i32, i64, ctypes.c_int]
+    lib.oracle_paged_decode_e4m3.argtypes = [p, p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i64,
+                                             dbl, ctypes.c_int, ctypes.c_int]
     lib.oracle_max_threads.argtypes = []
     return lib
 
@@ -241,3 +248,73 @@ def paged_kv_write(key, value, key_cache, value_cache, slot_mapping) -> None:
     rc = _load().oracle_paged_kv_write(_ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache),
                                        _ptr(sm), t, kvh, d, bs, nb, key.dtype.itemsize)
     _check(rc, "paged_kv_write")
+
+
+def decode_e4m3(bits: int) -> float:
+    """One OCP E4M3 code as a float (NaN for 0x7F / 0xFF)."""
+    return float(_load().oracle_decode_e4m3(int(bits)))
+
+
+def encode_e4m3(values) -> np.ndarray:
+    """binary32 values -> E4M3 codes (saturating at 448, ties to even)."""
+    v = np.ascontiguousarray(values, dtype=np.float32).reshape(-1)
+    enc = _load().oracle_encode_e4m3
+    return np.array([enc(float(x)) for x in v], dtype=np.uint8).reshape(np.shape(values))
+
+
+@functools.lru_cache(maxsize=1)
+def _e4m3_table() -> np.ndarray:
+    return np.array([decode_e4m3(b) for b in range(256)], dtype=np.float64)
+
+
+def e4m3_to_float64(codes: np.ndarray) -> np.ndarray:
+    """Decode E4M3 codes with the oracle's own decoder."""
+    if codes.dtype != np.uint8:
+        raise TypeError("E4M3 codes are held as uint8")
+    return _e4m3_table()[codes]
+
+
+def paged_kv_write_e4m3(key, value, key_cache, value_cache, slot_mapping, k_scale, v_scale,
+                        src_dtype: str) -> None:
+    """Quantised slot write: codes = encode(x * (1 / scale[kv head]))."""
+    _elem_check(key, src_dtype)
+    _elem_check(value, src_dtype)
+    nb, bs, kvh, d = key_cache.shape
+    assert key_cache.dtype == np.uint8 and value_cache.dtype == np.uint8
+    t = key.shape[0]
+    assert key.shape == (t, kvh, d) and value.shape == key.shape
+    sm = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+    ks = np.ascontiguousarray(k_scale, dtype=np.float32)
+    vs = np.ascontiguousarray(v_scale, dtype=np.float32)
+    assert sm.shape == (t,) and ks.shape == (kvh,) and vs.shape == (kvh,)
+    rc = _load().oracle_paged_kv_write_e4m3(_ptr(key), _ptr(value), _ptr(key_cache),
+                                            _ptr(value_cache), _ptr(sm), _ptr(ks), _ptr(vs), t, kvh,
+                                            d, bs, nb, DTYPE_CODE[src_dtype])
+    _check(rc, "paged_kv_write_e4m3")
+
+
+def paged_decode_e4m3(query, key_cache, value_cache, k_scale, v_scale, block_tables,
+                      context_lens, block_size: int, scale: float, dtype: str,
+                      num_threads: int = 0):
+    """Decode over E4M3 caches with per-KV-head scales; ``dtype`` is the
+    query's element type.  fp64 output [num_seqs, num_heads, head_dim]."""
+    _elem_check(query, dtype)
+    nb, bs, kvh, d = key_cache.shape
+    assert key_cache.dtype == np.uint8 and value_cache.shape == key_cache.shape
+    if bs != block_size:
+        raise ValueError("block_size does not match the pool shape")
+    b, h, dq = query.shape
+    assert dq == d
+    ks = np.ascontiguousarray(k_scale, dtype=np.float32)
+    vs = np.ascontiguousarray(v_scale, dtype=np.float32)
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+    assert ks.shape == (kvh,) and vs.shape == (kvh,)
+    assert bt.ndim == 2 and bt.shape[0] == b and cl.shape == (b,)
+    out = np.zeros((b, h, d), dtype=np.float64)
+    rc = _load().oracle_paged_decode_e4m3(_ptr(out), _ptr(query), _ptr(key_cache),
+                                          _ptr(value_cache), _ptr(ks), _ptr(vs), _ptr(bt), _ptr(cl),
+                                          b, h, kvh, d, bs, bt.shape[1], nb, float(np.float32(scale)),
+                                          DTYPE_CODE[dtype], int(num_threads))
+    _check(rc, "paged_decode_e4m3")
+    return out

@@ -277,6 +277,163 @@ int oracle_paged_kv_write(const void *key, const void *value, void *key_cache,
     return ORACLE_OK;
 }
 
+/* OCP E4M3: sign, 4-bit exponent with bias 7, 3-bit fraction. */
+double oracle_decode_e4m3(uint8_t bits) {
+    int sign = (bits >> 7) & 1;
+    int expo = (bits >> 3) & 0xf;
+    int frac = bits & 0x7;
+    double mag;
+    if (expo == 0xf && frac == 0x7) {
+        mag = NAN;
+    } else if (expo == 0) {
+        mag = ldexp((double)frac, -9); /* subnormal: frac/8 * 2^(1-7) */
+    } else {
+        mag = ldexp(1.0 + (double)frac / 8.0, expo - 7);
+    }
+    return sign ? -mag : mag;
+}
+
+/* Round |v| to the E4M3 grid: in the binade [2^e, 2^(e+1)) the step is
+ * 2^(e-3); below 2^-6 (subnormals) the step is 2^-9.  rint() rounds to
+ * nearest with ties to even in the default rounding mode. */
+uint8_t oracle_encode_e4m3(float v) {
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    if (isnan(v)) return (uint8_t)(sign | 0x7f);
+    double a = fabs((double)v);
+    if (a > 448.0) a = 448.0;
+    if (a < ldexp(1.0, -6)) {
+        /* subnormal grid m * 2^-9, m = 0..8 (8 is the smallest normal) */
+        double m = rint(ldexp(a, 9));
+        return (uint8_t)(sign | (uint8_t)m);
+    }
+    int e;
+    frexp(a, &e);        /* a = f * 2^e, f in [0.5, 1) */
+    e -= 1;              /* a in [2^e, 2^(e+1)) */
+    double m = rint(ldexp(a, -e) * 8.0) - 8.0; /* fraction steps, 0..8 */
+    if (m >= 8.0) {      /* rounded up into the next binade */
+        m = 0.0;
+        e += 1;
+    }
+    return (uint8_t)(sign | (uint8_t)(((e + 7) << 3) | (int)m));
+}
+
+static float load_f32(const void *base, int64_t index, int dtype) {
+    return (float)load_elem(base, index, dtype); /* every source type is exact in binary32 */
+}
+
+int oracle_paged_kv_write_e4m3(const void *key, const void *value,
+                               uint8_t *key_cache, uint8_t *value_cache,
+                               const int64_t *slot_mapping,
+                               const float *k_scale, const float *v_scale,
+                               int64_t num_tokens, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block_size,
+                               int64_t num_blocks, int src_dtype) {
+    if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        block_size <= 0 || src_dtype < 0 || src_dtype > 2)
+        return ORACLE_ERR_ARG;
+    const int64_t token_elems = (int64_t)num_kv_heads * head_dim;
+    for (int64_t i = 0; i < num_tokens; ++i) {
+        int64_t slot = slot_mapping[i];
+        if (slot < 0) continue;
+        int64_t block = slot / block_size;
+        int64_t offset = slot % block_size;
+        if (block >= num_blocks) return ORACLE_ERR_RANGE;
+        int64_t dst = (block * block_size + offset) * token_elems;
+        for (int32_t h = 0; h < num_kv_heads; ++h) {
+            const float kinv = 1.0f / k_scale[h];
+            const float vinv = 1.0f / v_scale[h];
+            for (int32_t d = 0; d < head_dim; ++d) {
+                int64_t e = (int64_t)h * head_dim + d;
+                float kx = load_f32(key, i * token_elems + e, src_dtype) * kinv;
+                float vx = load_f32(value, i * token_elems + e, src_dtype) * vinv;
+                key_cache[dst + e] = oracle_encode_e4m3(kx);
+                value_cache[dst + e] = oracle_encode_e4m3(vx);
+            }
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* The same batch loop as oracle_paged_decode, gathering E4M3 codes and
+ * scaling them by the KV head's scale. */
+int oracle_paged_decode_e4m3(double *out, const void *query,
+                             const uint8_t *key_cache,
+                             const uint8_t *value_cache,
+                             const float *k_scale, const float *v_scale,
+                             const int32_t *block_tables,
+                             const int32_t *context_lens, int32_t num_seqs,
+                             int32_t num_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t block_size,
+                             int32_t max_blocks_per_seq, int64_t num_blocks,
+                             double scale, int dtype, int num_threads) {
+    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 ||
+        num_heads % num_kv_heads != 0 || head_dim <= 0 || block_size <= 0 ||
+        max_blocks_per_seq < 0 || dtype < 0 || dtype > 2)
+        return ORACLE_ERR_ARG;
+    const int32_t group = num_heads / num_kv_heads;
+    const int64_t units = (int64_t)num_seqs * num_kv_heads;
+    int status = ORACLE_OK;
+#ifdef _OPENMP
+    if (num_threads <= 0) num_threads = omp_get_max_threads();
+#pragma omp parallel num_threads(num_threads)
+#endif
+    {
+        double *keys = NULL, *values = NULL, *qd = NULL;
+        int64_t cap = 0;
+        qd = (double *)malloc(sizeof(double) * (size_t)head_dim);
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+        for (int64_t u = 0; u < units; ++u) {
+            int32_t s = (int32_t)(u / num_kv_heads);
+            int32_t kvh = (int32_t)(u % num_kv_heads);
+            int32_t ctx = context_lens[s];
+            int rc = ORACLE_OK;
+            if (ctx < 0 || !qd) rc = ORACLE_ERR_ARG;
+            if (!rc && ctx > cap) {
+                free(keys);
+                free(values);
+                cap = ctx;
+                keys = (double *)malloc(sizeof(double) * (size_t)cap * head_dim);
+                values = (double *)malloc(sizeof(double) * (size_t)cap * head_dim);
+                if (!keys || !values) {
+                    rc = ORACLE_ERR_NOMEM;
+                    cap = 0;
+                }
+            }
+            const int32_t *table = block_tables + (int64_t)s * max_blocks_per_seq;
+            for (int64_t t = 0; t < ctx && !rc; ++t) {
+                int64_t lb, off, pb;
+                rc = oracle_block_address(table, max_blocks_per_seq, t, block_size, &lb, &off, &pb);
+                if (!rc && (pb < 0 || pb >= num_blocks)) rc = ORACLE_ERR_RANGE;
+                if (rc) break;
+                int64_t row = ((pb * block_size + off) * num_kv_heads + kvh) * (int64_t)head_dim;
+                for (int32_t d = 0; d < head_dim; ++d) {
+                    keys[t * head_dim + d] = oracle_decode_e4m3(key_cache[row + d]) * (double)k_scale[kvh];
+                    values[t * head_dim + d] = oracle_decode_e4m3(value_cache[row + d]) * (double)v_scale[kvh];
+                }
+            }
+            for (int32_t g = 0; g < group && !rc; ++g) {
+                int32_t qh = kvh * group + g; /* query head of the group */
+                int64_t qrow = ((int64_t)s * num_heads + qh) * head_dim;
+                for (int32_t d = 0; d < head_dim; ++d)
+                    qd[d] = load_elem(query, qrow + d, dtype);
+                rc = oracle_attention(out + qrow, qd, keys, values, ctx, head_dim, scale);
+            }
+            if (rc) {
+#ifdef _OPENMP
+#pragma omp critical
+#endif
+                status = rc;
+            }
+        }
+        free(keys);
+        free(values);
+        free(qd);
+    }
+    return status;
+}
+
 int oracle_max_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

@@ -17,7 +17,7 @@
  *
  * Element encodings (dtype argument): 0 = IEEE binary32, 1 = IEEE binary16,
  * 2 = bfloat16 (upper half of a binary32).  16-bit elements are passed as their
- * raw bit patterns.
+ * raw bit patterns; 8-bit E4M3 codes (quantised caches) as bytes.
  *
  * Return codes: 0 on success, a negative value when an argument or a table
  * entry is out of range (the oracle checks device-side contents too, since it
@@ -116,6 +116,45 @@ int oracle_paged_kv_write(const void *key, const void *value, void *key_cache,
                           int64_t num_tokens, int32_t num_kv_heads,
                           int32_t head_dim, int32_t block_size,
                           int64_t num_blocks, int elem_bytes);
+
+/* 8-bit floating point for a quantised KV cache ([P1] section "Triton 适合做
+ *什么": the first kernel leaves quantisation out, a later one adds it).  The
+ * format is OCP E4M3 ("e4m3fn"): 1 sign bit, 4 exponent bits (bias 7), 3
+ * fraction bits; exponent field 0 is subnormal (fraction * 2^-9); no
+ * infinities; 0x7F and 0xFF are NaN; the largest finite magnitude is 448. */
+double oracle_decode_e4m3(uint8_t bits);
+
+/* binary32 value -> E4M3 code: magnitudes above 448 saturate to 448, NaN
+ * stays NaN (0x7F with the input's sign), everything else rounds to the
+ * nearest representable value, ties to even fraction. */
+uint8_t oracle_encode_e4m3(float v);
+
+/* Quantised slot write: like oracle_paged_kv_write, but element e of KV head
+ * h is stored as oracle_encode_e4m3(x * (1 / scale[h])), the reciprocal and
+ * the product in binary32.  key/value hold src_dtype elements (0 f32, 1 f16,
+ * 2 bf16); the caches hold E4M3 codes [num_blocks, block_size, num_kv_heads,
+ * head_dim]; k_scale/v_scale have num_kv_heads entries. */
+int oracle_paged_kv_write_e4m3(const void *key, const void *value,
+                               uint8_t *key_cache, uint8_t *value_cache,
+                               const int64_t *slot_mapping,
+                               const float *k_scale, const float *v_scale,
+                               int64_t num_tokens, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block_size,
+                               int64_t num_blocks, int src_dtype);
+
+/* oracle_paged_decode over E4M3 caches: the cached element of KV head h is
+ * oracle_decode_e4m3(code) * k_scale[h] (keys) or * v_scale[h] (values),
+ * formed in fp64; query is dtype (0 f32, 1 f16, 2 bf16). */
+int oracle_paged_decode_e4m3(double *out, const void *query,
+                             const uint8_t *key_cache,
+                             const uint8_t *value_cache,
+                             const float *k_scale, const float *v_scale,
+                             const int32_t *block_tables,
+                             const int32_t *context_lens, int32_t num_seqs,
+                             int32_t num_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t block_size,
+                             int32_t max_blocks_per_seq, int64_t num_blocks,
+                             double scale, int dtype, int num_threads);
 
 /* Number of OpenMP threads a parallel region of this library would use. */
 int oracle_max_threads(void);

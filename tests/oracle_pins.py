@@ -378,6 +378,125 @@ def pin_prefix_reduces_to_paged_decode():
 
 
 # ---------------------------------------------------------------------------
+# 8-bit (E4M3) KV cache
+
+
+def _torch_e4m3(v32):
+    """torch's binary32 -> float8_e4m3fn codes (round to nearest even)."""
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(v32, dtype=np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def pin_e4m3_decode_exhaustive():
+    import torch
+
+    codes = np.arange(256, dtype=np.uint8)
+    mine = oracle.e4m3_to_float64(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+    assert np.array_equal(mine[~np.isnan(mine)], ref[~np.isnan(ref)])
+    # closed forms of the format: 1.0, smallest subnormal and normal, largest
+    assert (mine[0x38], mine[0x01], mine[0x08], mine[0x7E]) == (1.0, 2.0 ** -9, 2.0 ** -6, 448.0)
+    assert np.isnan(mine[0x7F]) and np.isnan(mine[0xFF]) and mine[0x80] == 0 and np.signbit(mine[0x80])
+
+
+def pin_e4m3_encode():
+    table = oracle.e4m3_to_float64(np.arange(256, dtype=np.uint8))
+    finite = [c for c in range(256) if not np.isnan(table[c])]
+    # every representable value encodes to its own code (both zeros included)
+    vals = np.array([table[c] for c in finite], np.float32)
+    assert np.array_equal(oracle.encode_e4m3(vals), np.array(finite, np.uint8))
+    # midpoints between neighbours go to the even fraction; just off them, to the nearer
+    pos = sorted(set(table[c] for c in range(0, 0x7F)))
+    mids = np.array([(a + b) / 2 for a, b in zip(pos, pos[1:])], np.float32)
+    got = oracle.encode_e4m3(mids)
+    assert np.array_equal(got, _torch_e4m3(mids))
+    assert all(int(g) % 2 == 0 for g in got)
+    up = np.nextafter(mids, np.float32(np.inf))
+    dn = np.nextafter(mids, np.float32(0))
+    assert np.array_equal(oracle.encode_e4m3(up), _torch_e4m3(up))
+    assert np.array_equal(oracle.encode_e4m3(dn), _torch_e4m3(dn))
+    # saturation beyond 448 (torch would give NaN from 480 on), NaN kept
+    big = np.array([448, 455.9, 464, 479.9, 480, 1e6, 3e38], np.float32)
+    assert (oracle.encode_e4m3(big) == 0x7E).all() and (oracle.encode_e4m3(-big) == 0xFE).all()
+    assert np.isnan(oracle.decode_e4m3(int(oracle.encode_e4m3(np.array([np.nan], np.float32))[0])))
+    # a library routine on random magnitudes across the whole range
+    x = (np.random.default_rng(8).standard_normal(50000) * 60).astype(np.float32)
+    assert np.array_equal(oracle.encode_e4m3(x), _torch_e4m3(np.clip(x, -448, 448)))
+
+
+def pin_e4m3_write():
+    """The quantised write stores encode(x * fl(1/scale)) at the slot, per
+    KV head scale, for every source type; nothing else changes.  The product
+    and the division differ: x = 3.5624998 (just below 3 * 1.1875) times
+    fl(1/3) lands on the 1.1875 tie and goes to the even 1.25 (0x3A), while
+    x / 3 stays below the tie and gives 1.125 (0x39)."""
+    bs, nb, kvh, d = 4, 6, 2, 8
+    rng = np.random.default_rng(12)
+    ks = np.array([3.0, 0.05], np.float32)
+    vs = np.array([0.02, 7.0], np.float32)
+    for dtype in ("f32", "f16", "bf16"):
+        x = rng.standard_normal((2, kvh, d)) * 4
+        x[0, 0, 0] = np.float32(3.562499761581421)
+        enc = {"f32": lambda a: a.astype(np.float32),
+               "f16": lambda a: a.astype(np.float16).view(np.uint16),
+               "bf16": lambda a: _bf16_bits(a)}[dtype]
+        key, val = enc(x), enc(-x)
+        kc = np.full((nb, bs, kvh, d), 0x55, np.uint8)
+        vc = kc.copy()
+        slots = np.array([2 * bs + 1, -1], np.int64)
+        oracle.paged_kv_write_e4m3(key, val, kc, vc, slots, ks, vs, dtype)
+        xf = oracle.to_float64(key, dtype).astype(np.float32)
+        vf = oracle.to_float64(val, dtype).astype(np.float32)
+        want_k = _torch_e4m3(np.clip(xf[0] * (np.float32(1) / ks)[:, None], -448, 448))
+        want_v = _torch_e4m3(np.clip(vf[0] * (np.float32(1) / vs)[:, None], -448, 448))
+        assert np.array_equal(kc[2, 1], want_k) and np.array_equal(vc[2, 1], want_v), dtype
+        if dtype == "f32":
+            assert kc[2, 1, 0, 0] == 0x3A
+        kc[2, 1] = 0x55
+        vc[2, 1] = 0x55
+        assert (kc == 0x55).all() and (vc == 0x55).all()
+
+
+def pin_e4m3_decode_attention():
+    """Decode over E4M3 pools equals torch fp64 attention over the
+    dequantised contiguous history (torch's own float8 decoding times the
+    KV head's scale), grouped-query mode, per-head K and V scales."""
+    import torch
+
+    rng = np.random.default_rng(30)
+    b, h, kvh, d, bs = 3, 8, 2, 16, 4
+    ctxs = [1, 9, 22]
+    nb = sum(-(-c // bs) for c in ctxs) + 1
+    perm = rng.permutation(nb)
+    tables = np.full((b, 6), perm[-1], np.int32)
+    kc = rng.integers(0, 256, (nb, bs, kvh, d)).astype(np.uint8)
+    kc[(kc & 0x7F) == 0x7F] = 0x3C
+    vc = rng.integers(0, 256, (nb, bs, kvh, d)).astype(np.uint8)
+    vc[(vc & 0x7F) == 0x7F] = 0x41
+    ks = np.array([0.011, 0.0031], np.float32)
+    vs = np.array([0.0075, 0.02], np.float32)
+    pos = 0
+    for s_, c in enumerate(ctxs):
+        n = -(-c // bs)
+        tables[s_, :n] = perm[pos:pos + n]
+        pos += n
+    q = rng.standard_normal((b, h, d)).astype(np.float32)
+    scale = float(np.float32(0.25))
+    out = oracle.paged_decode_e4m3(q, kc, vc, ks, vs, tables, np.array(ctxs, np.int32), bs, scale,
+                                   "f32")
+    f8 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).view(torch.float8_e4m3fn).double().numpy()  # noqa: E731
+    for s_, c in enumerate(ctxs):
+        rows = [(tables[s_, t // bs], t % bs) for t in range(c)]
+        kk = np.stack([f8(kc[p, o]) for p, o in rows]) * ks[None, :, None].astype(np.float64)
+        vv = np.stack([f8(vc[p, o]) for p, o in rows]) * vs[None, :, None].astype(np.float64)
+        ref = _sdpa(q[s_].astype(np.float64), kk, vv, scale, enable_gqa=True)
+        assert np.max(np.abs(out[s_] - ref)) < 1e-12, s_
+
+
+# ---------------------------------------------------------------------------
 # slot write
 
 
@@ -419,6 +538,10 @@ QUICK_PINS = [
     pin_sensitivity,
     pin_prefix_equals_contiguous,
     pin_prefix_reduces_to_paged_decode,
+    pin_e4m3_decode_exhaustive,
+    pin_e4m3_encode,
+    pin_e4m3_write,
+    pin_e4m3_decode_attention,
     pin_write,
 ]
 

@@ -45,6 +45,19 @@ PLANTED = {
                               "row[lb] = lb < prefix_blocks ? prefix_table[prefix_blocks - 1 - lb] : own[lb];"),
     "suffix_table_relative": ("row[lb] = lb < prefix_blocks ? prefix_table[lb] : own[lb];",
                               "row[lb] = lb < prefix_blocks ? prefix_table[lb] : own[lb - prefix_blocks];"),
+    "e4m3_bias_off_by_one": ("mag = ldexp(1.0 + (double)frac / 8.0, expo - 7);",
+                             "mag = ldexp(1.0 + (double)frac / 8.0, expo - 8);"),
+    "e4m3_subnormal_as_normal": ("mag = ldexp((double)frac, -9); /* subnormal",
+                                 "mag = ldexp(1.0 + (double)frac / 8.0, -7); /* subnormal"),
+    "e4m3_no_saturation": ("if (a > 448.0) a = 448.0;", "if (a > 1e30) a = 448.0;"),
+    "e4m3_ties_away": ("double m = rint(ldexp(a, -e) * 8.0) - 8.0;",
+                       "double m = floor(ldexp(a, -e) * 8.0 + 0.5) - 8.0;"),
+    "e4m3_write_divides": ("float kx = load_f32(key, i * token_elems + e, src_dtype) * kinv;",
+                           "float kx = load_f32(key, i * token_elems + e, src_dtype) / k_scale[h];"),
+    "e4m3_gqa_heads_interleaved": ("int32_t qh = kvh * group + g;", "int32_t qh = g * num_kv_heads + kvh;"),
+    "e4m3_write_offset_dropped": ("int64_t offset = slot % block_size;", "int64_t offset = 0;"),
+    "e4m3_value_scale_on_keys": ("keys[t * head_dim + d] = oracle_decode_e4m3(key_cache[row + d]) * (double)k_scale[kvh];",
+                                 "keys[t * head_dim + d] = oracle_decode_e4m3(key_cache[row + d]) * (double)v_scale[kvh];"),
 }
 
 
