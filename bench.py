@@ -68,11 +68,14 @@ def upload(batch, dev):
 
     t = {
         "q": wl.torch_view(batch.query, batch.dtype).to(dev),
-        "kc": wl.torch_view(batch.key_cache, batch.dtype).to(dev),
-        "vc": wl.torch_view(batch.value_cache, batch.dtype).to(dev),
+        "kc": wl.torch_view(batch.key_cache, batch.cache_dtype).to(dev),
+        "vc": wl.torch_view(batch.value_cache, batch.cache_dtype).to(dev),
         "bt": torch.from_numpy(batch.block_tables).to(dev),
         "cl": torch.from_numpy(batch.context_lens).to(dev),
     }
+    if batch.k_scale is not None:
+        t["ks"] = torch.from_numpy(batch.k_scale).to(dev)
+        t["vs"] = torch.from_numpy(batch.v_scale).to(dev)
     if batch.slot_mapping is not None:
         t["nk"] = wl.torch_view(batch.new_key, batch.dtype).to(dev)
         t["nv"] = wl.torch_view(batch.new_value, batch.dtype).to(dev)
@@ -98,13 +101,21 @@ def time_steps(batch, t, partition_size: int, steps: int, warmup: int, shared_pr
                                                batch.max_context_len, partition_size)
     ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=t["q"].device)  # counter starts at zero
     has_write = "slots" in t
+    quant = batch.cache_dtype == "e4m3"
 
     def write():
-        if has_write:
+        if has_write and quant:
+            pkv.paged_kv_write_fp8(t["nk"], t["nv"], t["kc"], t["vc"], t["slots"], t["ks"], t["vs"])
+        elif has_write:
             pkv.paged_kv_write(t["nk"], t["nv"], t["kc"], t["vc"], t["slots"])
 
     def decode():
-        if shared_prefix:
+        if quant:
+            pkv.paged_decode_attention_fp8(
+                t["q"], t["kc"], t["vc"], t["ks"], t["vs"], t["bt"], t["cl"], batch.block_size,
+                batch.scale, max_context_len=batch.max_context_len,
+                partition_size=partition_size, out=out, workspace=ws)
+        elif shared_prefix:
             pkv.paged_prefix_decode_attention(
                 t["q"], t["kc"], t["vc"], ptab, plen, t["bt"], t["cl"], batch.block_size,
                 batch.scale, max_context_len=batch.max_context_len,
@@ -156,9 +167,16 @@ def cpu_baseline(batch, target_s: float):
 
     order = np.arange(batch.num_seqs)
     probe = wl.subset(batch, order[:: max(1, batch.num_seqs // 8)])
+    def run(b):
+        if b.cache_dtype == "e4m3":
+            oracle.paged_decode_e4m3(b.query, b.key_cache, b.value_cache, b.k_scale, b.v_scale,
+                                     b.block_tables, b.context_lens, b.block_size, b.scale, b.dtype)
+        else:
+            oracle.paged_decode(b.query, b.key_cache, b.value_cache, b.block_tables,
+                                b.context_lens, b.block_size, b.scale, b.dtype)
+
     t0 = time.perf_counter()
-    oracle.paged_decode(probe.query, probe.key_cache, probe.value_cache, probe.block_tables,
-                        probe.context_lens, probe.block_size, probe.scale, probe.dtype)
+    run(probe)
     probe_s = max(time.perf_counter() - t0, 1e-3)
     frac = min(1.0, target_s / probe_s * probe.total_tokens / batch.total_tokens)
     step = max(1, int(round(1.0 / frac))) if frac < 1.0 else 1
@@ -166,9 +184,7 @@ def cpu_baseline(batch, target_s: float):
     passes, secs = 0, 0.0
     while passes == 0 or (secs < target_s and passes < 100):
         t0 = time.perf_counter()
-        oracle.paged_decode(sample.query, sample.key_cache, sample.value_cache,
-                            sample.block_tables, sample.context_lens, sample.block_size,
-                            sample.scale, sample.dtype)
+        run(sample)
         secs += time.perf_counter() - t0
         passes += 1
     per_pass = secs / passes
@@ -364,6 +380,7 @@ def main() -> int:
             "context_tokens": batch.total_tokens,
             "max_context_len": batch.max_context_len,
             "new_tokens_written": 0 if batch.slot_mapping is None else int((batch.slot_mapping >= 0).sum()),
+            "kv_cache_dtype": batch.cache_dtype,
             "parallelism": "single GPU",
         },
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),

@@ -217,6 +217,63 @@ pkv_status paged_prefix_decode_attention(
     int32_t partition_size, pkv_dtype dtype, pkv_dtype out_dtype,
     void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * 8-bit quantised KV cache.  [P1] section "Triton 适合做什么": the first
+ * kernel leaves quantisation out; this is the later version that adds it.
+ * Element format: OCP E4M3 ("e4m3fn": 1 sign, 4 exponent bits with bias 7, 3
+ * fraction bits, no infinities, 0x7F/0xFF NaN, largest finite 448).  One
+ * binary32 scale per KV head for K and one for V: the cached element of KV
+ * head h stands for code * k_scale[h] (keys) or code * v_scale[h] (values).
+ */
+
+/*
+ * paged_kv_write_fp8 -- paged_kv_write into E4M3 caches: element e of KV head
+ * h of each token is stored as E4M3(x * (1 / scale[h])), the reciprocal and
+ * the product in binary32 (correctly rounded), saturated to +-448 (NaN stays
+ * NaN), rounded to nearest with ties to even.
+ *
+ *   key, value    [num_tokens, num_kv_heads, head_dim]  src_dtype (F32/F16/BF16)
+ *   key_cache,
+ *   value_cache   [num_blocks, block_size, num_kv_heads, head_dim] E4M3 bytes
+ *   k_scale,
+ *   v_scale       [num_kv_heads] binary32 (device), nonzero
+ * Slots, errors and supported sizes as paged_kv_write.
+ */
+pkv_status paged_kv_write_fp8(const void *key, const void *value, void *key_cache,
+                              void *value_cache, const int64_t *slot_mapping,
+                              const float *k_scale, const float *v_scale,
+                              int64_t num_tokens, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size,
+                              int64_t num_blocks, pkv_dtype src_dtype, void *stream);
+
+/*
+ * paged_decode_attention_fp8 -- paged_decode_attention over E4M3 caches with
+ * per-KV-head scales: the same result as over caches holding code * scale.
+ * The codes are widened exactly to the query's type (keys, for the score
+ * product on the matrix cores) and to binary32 (values); k_scale joins the
+ * score scale, v_scale multiplies the output.  Half the bytes of a 16-bit
+ * cache are read.
+ *
+ *   query, out    as paged_decode_attention; dtype is PKV_F16 or PKV_BF16
+ *                 (the query's type), out_dtype is dtype or PKV_F32
+ *   key_cache,
+ *   value_cache   [num_blocks, block_size, num_kv_heads, head_dim] E4M3 bytes
+ *   k_scale,
+ *   v_scale       [num_kv_heads] binary32 (device)
+ *   workspace     paged_decode_workspace_size() bytes, same rules
+ * Supported: head_dim 128, block_size in {4, 8, 16, 32, 64}, G in {1, 2, 4,
+ * 8}, num_seqs <= PKV_MAX_SEQS.
+ */
+pkv_status paged_decode_attention_fp8(
+    void *out, const void *query, const void *key_cache,
+    const void *value_cache, const float *k_scale, const float *v_scale,
+    const int32_t *block_tables, const int32_t *context_lens,
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+    int64_t num_blocks, int32_t max_context_len, float scale,
+    int32_t partition_size, pkv_dtype dtype, pkv_dtype out_dtype,
+    void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static, NUL-terminated description of a status code (host memory). */
 const char *pkv_status_string(pkv_status status);
 

@@ -21,6 +21,13 @@ Entry points (same names as the C ABI):
   paged_prefix_decode_workspace_size(num_seqs, num_heads, num_kv_heads,
                                      head_dim, max_context_len, prefix_len,
                                      partition_size)
+  paged_kv_write_fp8(key, value, key_cache, value_cache, slot_mapping,
+                     k_scale, v_scale)
+  paged_decode_attention_fp8(query, key_cache, value_cache, k_scale, v_scale,
+                             block_tables, context_lens, block_size, scale,
+                             *, max_context_len, partition_size=0, out=None,
+                             out_dtype=None, workspace=None)
+E4M3 caches are uint8 or torch.float8_e4m3fn tensors.
 """
 from __future__ import annotations
 
@@ -33,6 +40,8 @@ __all__ = [
     "paged_decode_workspace_size",
     "paged_prefix_decode_attention",
     "paged_prefix_decode_workspace_size",
+    "paged_kv_write_fp8",
+    "paged_decode_attention_fp8",
     "library_path",
     "PagedKVError",
 ]
@@ -83,6 +92,12 @@ def _load():
                                                   i32, i64, i32, ctypes.c_float, i32, ctypes.c_int,
                                                   ctypes.c_int, p, sz, p]
     lib.paged_prefix_decode_attention.restype = ctypes.c_int
+    lib.paged_kv_write_fp8.argtypes = [p, p, p, p, p, p, p, i64, i32, i32, i32, i64, ctypes.c_int, p]
+    lib.paged_kv_write_fp8.restype = ctypes.c_int
+    lib.paged_decode_attention_fp8.argtypes = [p, p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32,
+                                               i64, i32, ctypes.c_float, i32, ctypes.c_int,
+                                               ctypes.c_int, p, sz, p]
+    lib.paged_decode_attention_fp8.restype = ctypes.c_int
     lib.pkv_status_string.argtypes = [ctypes.c_int]
     lib.pkv_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -274,4 +289,98 @@ def paged_prefix_decode_attention(query, key_cache, value_cache, prefix_table, p
         int(partition_size), dt, _dtype_code(odt), ws_ptr, ws_bytes, _stream_handle(query.device))
     if st != 0:
         raise PagedKVError(st, "paged_prefix_decode_attention")
+    return out
+
+
+def _e4m3_cache(t, name: str):
+    torch = _torch()
+    _gpu(t, name)
+    if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+        raise TypeError(f"{name} must hold E4M3 codes (uint8 or float8_e4m3fn)")
+    return t
+
+
+def _scales(k_scale, v_scale, kvh: int):
+    torch = _torch()
+    for t, n in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+        _gpu(t, n)
+        if t.dtype != torch.float32 or tuple(t.shape) != (kvh,):
+            raise ValueError(f"{n} must be float32 [num_kv_heads]")
+
+
+def paged_kv_write_fp8(key, value, key_cache, value_cache, slot_mapping, k_scale, v_scale) -> None:
+    """Quantise token i's K/V rows ``key[i]``/``value[i]`` (f32/f16/bf16,
+    [num_kv_heads, head_dim]) with the per-KV-head scales into the E4M3 pools
+    at ``slot_mapping[i]``."""
+    torch = _torch()
+    lib = _load()
+    for t, n in ((key, "key"), (value, "value"), (slot_mapping, "slot_mapping")):
+        _gpu(t, n)
+    _e4m3_cache(key_cache, "key_cache")
+    _e4m3_cache(value_cache, "value_cache")
+    if slot_mapping.dtype != torch.int64:
+        raise TypeError("slot_mapping must be int64")
+    nb, bs, kvh, d = key_cache.shape
+    tokens = key.shape[0]
+    if tuple(key.shape) != (tokens, kvh, d) or value.shape != key.shape or key.dtype != value.dtype:
+        raise ValueError("key/value must be [num_tokens, num_kv_heads, head_dim] of the pool, one dtype")
+    if value_cache.shape != key_cache.shape or slot_mapping.shape != (tokens,):
+        raise ValueError("inconsistent shapes")
+    _scales(k_scale, v_scale, kvh)
+    st = lib.paged_kv_write_fp8(key.data_ptr(), value.data_ptr(), key_cache.data_ptr(),
+                                value_cache.data_ptr(), slot_mapping.data_ptr(), k_scale.data_ptr(),
+                                v_scale.data_ptr(), tokens, kvh, d, bs, nb, _dtype_code(key.dtype),
+                                _stream_handle(key.device))
+    if st != 0:
+        raise PagedKVError(st, "paged_kv_write_fp8")
+
+
+def paged_decode_attention_fp8(query, key_cache, value_cache, k_scale, v_scale, block_tables,
+                               context_lens, block_size: int, scale: float, *,
+                               max_context_len: int, partition_size: int = 0, out=None,
+                               out_dtype=None, workspace=None):
+    """``paged_decode_attention`` over E4M3 pools with per-KV-head scales;
+    ``query`` is f16 or bf16 and sets the output type (or ``out_dtype``
+    float32)."""
+    torch = _torch()
+    lib = _load()
+    for t, n in ((query, "query"), (block_tables, "block_tables"), (context_lens, "context_lens")):
+        _gpu(t, n)
+    _e4m3_cache(key_cache, "key_cache")
+    _e4m3_cache(value_cache, "value_cache")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    nb, bs, kvh, d = key_cache.shape
+    if bs != block_size:
+        raise ValueError("block_size does not match key_cache.shape[1]")
+    b, h, dq = query.shape
+    if dq != d or value_cache.shape != key_cache.shape:
+        raise ValueError("inconsistent shapes")
+    if block_tables.dim() != 2 or block_tables.shape[0] != b or tuple(context_lens.shape) != (b,):
+        raise ValueError("block_tables must be [num_seqs, max_blocks], context_lens [num_seqs]")
+    _scales(k_scale, v_scale, kvh)
+    dt = _dtype_code(query.dtype)
+    odt = query.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((b, h, d), dtype=odt, device=query.device)
+    else:
+        _gpu(out, "out")
+        if tuple(out.shape) != (b, h, d):
+            raise ValueError("out must be [num_seqs, num_heads, head_dim]")
+        odt = out.dtype
+    need = paged_decode_workspace_size(b, h, d, int(max_context_len), int(partition_size))
+    ws_ptr, ws_bytes = None, 0
+    if need:
+        if workspace is None:
+            workspace = torch.zeros(need, dtype=torch.uint8, device=query.device)
+        else:
+            _gpu(workspace, "workspace")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    st = lib.paged_decode_attention_fp8(
+        out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+        k_scale.data_ptr(), v_scale.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(),
+        b, h, kvh, d, bs, block_tables.shape[1], nb, int(max_context_len), float(scale),
+        int(partition_size), dt, _dtype_code(odt), ws_ptr, ws_bytes, _stream_handle(query.device))
+    if st != 0:
+        raise PagedKVError(st, "paged_decode_attention_fp8")
     return out

@@ -48,6 +48,11 @@
 #ifndef PKV_TILES_PER_STEP
 #define PKV_TILES_PER_STEP 2
 #endif
+// E4M3 caches: a tile is half the bytes, so twice the tiles per step keep
+// the same bytes in flight
+#ifndef PKV_TILES_PER_STEP_E4M3
+#define PKV_TILES_PER_STEP_E4M3 4
+#endif
 
 namespace pkv {
 
@@ -69,11 +74,40 @@ __device__ __forceinline__ float head_bcast(float x, int hl) {
     }
 }
 
-struct TileRegs {
+// Loaded rows of one 16-token tile: 16-byte chunks of 16-bit rows, or
+// 8-byte chunks (eight E4M3 codes, the same head dims) of quantised rows.
+template <bool KV8>
+struct TileRegsT {
     u32x4 k[4];      // tokens 4q + i, chunk c (whole rows per load instruction)
     u32x4 v[4];      // tokens 4q + i, chunk c
     uint32_t vmask;  // bit i: row i holds a valid token
 };
+template <>
+struct TileRegsT<true> {
+    u32x2 k[4];
+    u32x2 v[4];
+    uint32_t vmask;
+};
+
+// Eight E4M3 codes -> the same eight values in the 16-bit compute type
+// (exact: E4M3 values are representable in binary16 and bfloat16).
+template <int DT>
+__device__ __forceinline__ u32x4 widen_e4m3(const u32x2 w) {
+    // one instruction per pair (scale 1: the plain value)
+    u32x4 r;
+    if constexpr (DT == kBF16) {
+        r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.f, false));
+        r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.f, true));
+        r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.f, false));
+        r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.f, true));
+    } else {
+        r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.x, 1.f, false));
+        r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.x, 1.f, true));
+        r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.y, 1.f, false));
+        r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.y, 1.f, true));
+    }
+    return r;
+}
 
 // Inclusive prefix sum over the workgroup's threads (s_scan: kThreads ints).
 __device__ __forceinline__ int block_scan(int v, int *s_scan) {
@@ -144,7 +178,11 @@ __device__ __forceinline__ int search_le(const int *pre, int n, int x) {
 // PFX: the launch covers tokens [token_begin, ctx) of each sequence and
 // always writes partials (slots part_base.. of part_stride), for the
 // shared-prefix path; the plain instantiation never reads those fields.
-template <int DT, int G, bool PFX>
+// KV8: the caches hold E4M3 codes (128-byte rows) with per-KV-head scales;
+// DT is then the type of the query and the output.  K is widened to DT
+// before the score MFMA, V to fp32 before the value product; k_scale joins
+// the score scale and v_scale multiplies the result.
+template <int DT, int G, bool PFX, bool KV8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8)))
 void paged_decode_mfma_kernel(DecodeArgs a) {
     constexpr int D = 128;
@@ -153,6 +191,9 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
     constexpr int HS = G < 4 ? G : 4;  // heads per score product
     constexpr int NSET = G / HS;       // score products per tile
     constexpr bool kQopInLds = NSET > 1;
+    constexpr int KV_ROW = KV8 ? D : D * 2;     // bytes of one cached row
+    constexpr int KV_CHUNK = KV8 ? 8 : 16;      // bytes of one lane's chunk
+    using TileRegs = TileRegsT<KV8>;
 
     extern __shared__ int s_dyn[];     // full-unit prefix [B + 1], partial-unit prefix [B + 1], lengths [B]
     __shared__ int s_pages[kSegPages];
@@ -181,8 +222,8 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
     const char *vbase = reinterpret_cast<const char *>(a.value_cache);
     const int bs = a.block_size;
     const int lbs = a.log2_block_size;
-    const int64_t tok_stride = (int64_t)a.num_kv_heads * ROW_BYTES;  // bytes between slots
-    const float sl2 = a.scale_log2e;
+    const int64_t tok_stride = (int64_t)a.num_kv_heads * KV_ROW;  // bytes between slots
+    const float sl2_q = a.scale_log2e;
     char *ktile = s_ktile[wave];
 
     // Units are handed out one at a time from a counter in the workspace, so
@@ -253,7 +294,9 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
 
-        const int64_t kvh_off = (int64_t)u.kvh * ROW_BYTES;
+        const int64_t kvh_off = (int64_t)u.kvh * KV_ROW;
+        float sl2 = sl2_q;
+        if constexpr (KV8) sl2 *= a.k_scale[u.kvh];
 
         for (int seg = u.tok_begin; seg < u.tok_end; seg += kSegPages << lbs) {
             const int seg_end = min(u.tok_end, seg + (kSegPages << lbs));
@@ -279,9 +322,14 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     bool ok;
-                    const int64_t row = row_of(t0 + 4 * q + i, ok) + c * 16;
-                    r.k[i] = load16_stream(kbase + row);
-                    r.v[i] = load16_stream(vbase + row);
+                    const int64_t row = row_of(t0 + 4 * q + i, ok) + c * KV_CHUNK;
+                    if constexpr (KV8) {
+                        r.k[i] = load8_stream(kbase + row);
+                        r.v[i] = load8_stream(vbase + row);
+                    } else {
+                        r.k[i] = load16_stream(kbase + row);
+                        r.v[i] = load16_stream(vbase + row);
+                    }
                     r.vmask |= ok ? (1u << i) : 0u;
                 }
             };
@@ -295,13 +343,21 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int tt = 4 * q + i;
-                    *reinterpret_cast<u32x4 *>(ktile + tt * ROW_BYTES + ((c ^ tt) & 15) * 16) = r.k[i];
+                    u32x4 krow;
+                    if constexpr (KV8) krow = widen_e4m3<DT>(r.k[i]); else krow = r.k[i];
+                    *reinterpret_cast<u32x4 *>(ktile + tt * ROW_BYTES + ((c ^ tt) & 15) * 16) = krow;
                 }
                 u32x4 kop[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     kop[j] = *reinterpret_cast<const u32x4 *>(ktile + c * ROW_BYTES + (((4 * j + q) ^ c) & 15) * 16);
+                // The reference max of a lane's row group moves only when a
+                // score passes it by more than kMaxSlack, so the accumulator
+                // rescale (a multiply per accumulator) is skipped in nearly
+                // every tile; the merges weight each state by its own
+                // (max, normaliser), so any reference gives the same result.
                 float p[NSET][4], alpha[NSET];
+                bool bump_any = false;
 #pragma unroll
                 for (int set = 0; set < NSET; ++set) {
                     f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
@@ -315,28 +371,39 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
                         sv[i] = (t0 + 4 * q + i < seg_end) ? sacc[i] * sl2 : -INFINITY;
                         mt = fmaxf(mt, sv[i]);
                     }
-                    const float mn = fmaxf(m[set], mt);
-                    const bool none = mn == -INFINITY;
-                    alpha[set] = none ? 1.f : fast_exp2(m[set] - mn);
+                    const bool bump = mt > m[set] + kMaxSlack;  // m = -inf: any valid score
+                    alpha[set] = !bump ? 1.f : (m[set] == -INFINITY ? 0.f : fast_exp2(m[set] - mt));
+                    m[set] = bump ? mt : m[set];
+                    bump_any |= bump;
+                    // m = -inf only while the row group has seen no valid
+                    // score: then every score here is masked and 2^(-inf) = 0
+                    const float mref = m[set] == -INFINITY ? 0.f : m[set];
                     float ps = 0.f;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        p[set][i] = none ? 0.f : fast_exp2(sv[i] - mn);
+                        p[set][i] = fast_exp2(sv[i] - mref);
                         ps += p[set][i];
                     }
                     l[set] = l[set] * alpha[set] + ps;
-                    m[set] = mn;
                 }
+                if (__builtin_amdgcn_ballot_w64(bump_any)) {
 #pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    const float ag = head_bcast<HS>(alpha[g / HS], g % HS);
+                    for (int g = 0; g < G; ++g) {
+                        const float ag = head_bcast<HS>(alpha[g / HS], g % HS);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) acc[g][e] *= ag;
+                        for (int e = 0; e < 8; ++e) acc[g][e] *= ag;
+                    }
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     float vf[8];
-                    unpack16<DT>((r.vmask >> i) & 1u ? r.v[i] : u32x4{0, 0, 0, 0}, vf);
+                    if constexpr (KV8) {
+                        const u32x2 vw = (r.vmask >> i) & 1u ? r.v[i] : u32x2{0, 0};
+                        e4m3x4_to_f32(vw.x, vf);
+                        e4m3x4_to_f32(vw.y, vf + 4);
+                    } else {
+                        unpack16<DT>((r.vmask >> i) & 1u ? r.v[i] : u32x4{0, 0, 0, 0}, vf);
+                    }
 #pragma unroll
                     for (int g = 0; g < G; ++g) {
                         const float pg = head_bcast<HS>(p[g / HS][i], g % HS);
@@ -352,7 +419,8 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
             // computed.  Straight-line code: the compiler waits for exactly
             // the loads a tile needs.  A tile past the segment is all
             // invalid and computes to no change.
-            constexpr int TPS = G == 8 ? 1 : PKV_TILES_PER_STEP;  // register budget
+            constexpr int TPS = KV8 ? (G == 8 ? 2 : PKV_TILES_PER_STEP_E4M3)
+                                    : (G == 8 ? 1 : PKV_TILES_PER_STEP);  // register budget
             constexpr int STEP = kNumWaves * TILE * TPS;
             for (int t = seg + wave * TILE * TPS; t < seg_end; t += STEP) {
                 TileRegs r[TPS];
@@ -405,7 +473,8 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
             }
         }
         __syncthreads();
-        unit_epilogue<DT, D, G, PFX>(a, u, u.bad_len || s_bad != 0, s_m, s_l, s_acc);
+        unit_epilogue<DT, D, G, PFX>(a, u, u.bad_len || s_bad != 0, s_m, s_l, s_acc,
+                                     KV8 ? a.v_scale[u.kvh] : 1.f);
     }
 }
 
@@ -428,13 +497,13 @@ static hipError_t launch_persistent(K kernel, const DecodeArgs &a, hipStream_t s
     return hipGetLastError();
 }
 
-template <int DT, bool PFX>
+template <int DT, bool PFX, bool KV8 = false>
 static hipError_t launch_group(const DecodeArgs &a, hipStream_t stream) {
     switch (a.num_heads / a.num_kv_heads) {
-        case 1: return launch_persistent(paged_decode_mfma_kernel<DT, 1, PFX>, a, stream);
-        case 2: return launch_persistent(paged_decode_mfma_kernel<DT, 2, PFX>, a, stream);
-        case 4: return launch_persistent(paged_decode_mfma_kernel<DT, 4, PFX>, a, stream);
-        case 8: return launch_persistent(paged_decode_mfma_kernel<DT, 8, PFX>, a, stream);
+        case 1: return launch_persistent(paged_decode_mfma_kernel<DT, 1, PFX, KV8>, a, stream);
+        case 2: return launch_persistent(paged_decode_mfma_kernel<DT, 2, PFX, KV8>, a, stream);
+        case 4: return launch_persistent(paged_decode_mfma_kernel<DT, 4, PFX, KV8>, a, stream);
+        case 8: return launch_persistent(paged_decode_mfma_kernel<DT, 8, PFX, KV8>, a, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -442,6 +511,12 @@ static hipError_t launch_group(const DecodeArgs &a, hipStream_t stream) {
 hipError_t launch_paged_decode_mfma(const DecodeArgs &a, int dtype, hipStream_t stream) {
     if (dtype == kBF16) return launch_group<kBF16, false>(a, stream);
     if (dtype == kF16) return launch_group<kF16, false>(a, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_paged_decode_mfma_e4m3(const DecodeArgs &a, int dtype, hipStream_t stream) {
+    if (dtype == kBF16) return launch_group<kBF16, false, true>(a, stream);
+    if (dtype == kF16) return launch_group<kF16, false, true>(a, stream);
     return hipErrorInvalidValue;
 }
 

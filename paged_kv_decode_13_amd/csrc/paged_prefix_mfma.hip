@@ -57,7 +57,6 @@ constexpr int kPfxChunk = 64;                       // prefix tokens per LDS chu
 constexpr int kPfxMaxSplitTokens = 2048;            // matches the host-side plan
 constexpr int kPfxMaxSplitPages = kPfxMaxSplitTokens / 4;
 constexpr int kXcds = 8;
-constexpr float kMaxSlack = 8.f;  // exp2 domain: probabilities stay <= 256
 
 // 16-byte column of transposed-V row d that holds column `col`: XOR swizzle
 // so that the transposing writes (rows 8c + e) and the operand reads (rows

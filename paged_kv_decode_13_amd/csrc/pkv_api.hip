@@ -321,3 +321,107 @@ pkv_status paged_prefix_decode_attention(
 }
 
 }  // extern "C"
+
+extern "C" {
+
+pkv_status paged_kv_write_fp8(const void *key, const void *value, void *key_cache, void *value_cache,
+                              const int64_t *slot_mapping, const float *k_scale, const float *v_scale,
+                              int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t block_size, int64_t num_blocks, pkv_dtype src_dtype,
+                              void *stream) {
+    if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks < 0) return PKV_ERR_SHAPE;
+    if (!valid_dtype(src_dtype)) return PKV_ERR_DTYPE;
+    if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
+    if (!pow2_block(block_size)) return PKV_ERR_UNSUPPORTED;
+    if (num_tokens == 0) return PKV_OK;
+    if (!key || !value || !key_cache || !value_cache || !slot_mapping || !k_scale || !v_scale)
+        return PKV_ERR_NULL;
+    if (!aligned16(key) || !aligned16(value) || !aligned16(key_cache) || !aligned16(value_cache))
+        return PKV_ERR_ALIGN;
+    pkv::WriteE4M3Args a;
+    a.key = key;
+    a.value = value;
+    a.key_cache = key_cache;
+    a.value_cache = value_cache;
+    a.slot_mapping = slot_mapping;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.num_tokens = num_tokens;
+    a.num_blocks = num_blocks;
+    a.block_size = block_size;
+    a.groups_per_token = (int32_t)(((int64_t)num_kv_heads * head_dim) / 8);
+    a.groups_per_head = head_dim / 8;
+    hipError_t e = pkv::launch_kv_write_e4m3(a, (int)src_dtype, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+pkv_status paged_decode_attention_fp8(void *out, const void *query, const void *key_cache,
+                                      const void *value_cache, const float *k_scale,
+                                      const float *v_scale, const int32_t *block_tables,
+                                      const int32_t *context_lens, int32_t num_seqs,
+                                      int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t block_size, int32_t max_blocks_per_seq,
+                                      int64_t num_blocks, int32_t max_context_len, float scale,
+                                      int32_t partition_size, pkv_dtype dtype, pkv_dtype out_dtype,
+                                      void *workspace, size_t workspace_bytes, void *stream) {
+    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq < 0 ||
+        num_blocks < 0 || max_context_len < 0 || partition_size < 0)
+        return PKV_ERR_SHAPE;
+    if (num_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
+    if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return PKV_ERR_DTYPE;
+    if (out_dtype != dtype && out_dtype != PKV_F32) return PKV_ERR_DTYPE;
+    if (dtype == PKV_F32 || head_dim != 128) return PKV_ERR_UNSUPPORTED;
+    if (!pow2_block(block_size)) return PKV_ERR_UNSUPPORTED;
+    const int32_t group = num_heads / num_kv_heads;
+    if (group != 1 && group != 2 && group != 4 && group != 8) return PKV_ERR_UNSUPPORTED;
+    if (partition_size != 0 && partition_size % partition_granule(block_size) != 0)
+        return PKV_ERR_UNSUPPORTED;
+    if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size) return PKV_ERR_SHAPE;
+    if (num_blocks == 0 && max_context_len > 0) return PKV_ERR_SHAPE;
+    if (!isfinite(scale)) return PKV_ERR_SHAPE;
+    if (num_seqs > PKV_MAX_SEQS) return PKV_ERR_UNSUPPORTED;
+    if (num_seqs == 0) return PKV_OK;
+    if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens ||
+        !k_scale || !v_scale)
+        return PKV_ERR_NULL;
+    if (!aligned16(out) || !aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache))
+        return PKV_ERR_ALIGN;
+    const int32_t parts = num_partitions(max_context_len, partition_size);
+    if ((int64_t)num_seqs * num_kv_heads * parts > INT_MAX || (int64_t)num_seqs * num_heads > INT_MAX)
+        return PKV_ERR_SHAPE;
+    const size_t need = paged_decode_workspace_size(num_seqs, num_heads, head_dim, max_context_len,
+                                                    partition_size);
+    if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return PKV_ERR_ALIGN;
+    pkv::DecodeArgs a = {};
+    a.work_counter = reinterpret_cast<unsigned *>(workspace);
+    if (parts > 1) {
+        a.part_out = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + kCounterBytes);
+        a.part_ml = a.part_out + (size_t)num_seqs * num_heads * parts * head_dim;
+    }
+    a.out = out;
+    a.query = query;
+    a.key_cache = key_cache;
+    a.value_cache = value_cache;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.num_blocks = num_blocks;
+    a.num_seqs = num_seqs;
+    a.num_heads = num_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.block_size = block_size;
+    a.log2_block_size = log2i(block_size);
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.max_context_len = max_context_len;
+    a.partition_size = parts > 1 ? partition_size : (max_context_len > 0 ? max_context_len : 1);
+    a.num_partitions = parts;
+    a.scale_log2e = scale * 1.4426950408889634f;
+    a.out_f32 = out_dtype == PKV_F32 ? 1 : 0;
+    a.part_stride = parts;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    hipError_t e = pkv::launch_paged_decode_e4m3(a, (int)dtype, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+}  // extern "C"

@@ -13,6 +13,9 @@ namespace pkv {
 constexpr int kNumWaves = 4;
 constexpr int kThreads = kNumWaves * kWave;
 constexpr int kSegPages = 256;  // page ids staged in LDS at a time
+// Lazy running max: a reference max moves only when passed by more than this
+// (exp2 domain), so probabilities stay <= 256 and rescales are rare.
+constexpr float kMaxSlack = 8.f;
 
 struct Unit {
     int s, kvh, p;
@@ -109,7 +112,7 @@ __device__ __forceinline__ void store_out(const DecodeArgs &a, int64_t idx, floa
 template <int DT, int D, int G, bool PFX = false>
 __device__ __forceinline__ void unit_epilogue(const DecodeArgs &a, const Unit &u, bool bad,
                                               const float (*s_m)[G], const float (*s_l)[G],
-                                              const float (*s_acc)[G][D]) {
+                                              const float (*s_acc)[G][D], float vscale = 1.f) {
     const int h0 = u.kvh * G;
     for (int i = threadIdx.x; i < G * D; i += kThreads) {
         const int g = i / D;
@@ -155,7 +158,7 @@ __device__ __forceinline__ void unit_epilogue(const DecodeArgs &a, const Unit &u
                 continue;
             }
         }
-        float res = L > 0.f ? O / L : 0.f;  // empty context -> zeros
+        float res = L > 0.f ? O / L * vscale : 0.f;  // empty context -> zeros
         if (bad) res = __builtin_nanf("");
         if (!PFX && u.nparts == 1) {
             store_out<DT>(a, ((int64_t)u.s * a.num_heads + h) * D + d, res);
@@ -175,6 +178,8 @@ __device__ __forceinline__ void unit_epilogue(const DecodeArgs &a, const Unit &u
 // MFMA decode kernel launcher (16-bit caches, head_dim 128); the merge
 // kernel is launched by the caller.
 hipError_t launch_paged_decode_mfma(const DecodeArgs &a, int dtype, hipStream_t stream);
+// The same over E4M3 caches with per-KV-head scales (DT: query and output).
+hipError_t launch_paged_decode_mfma_e4m3(const DecodeArgs &a, int dtype, hipStream_t stream);
 // The same over tokens [token_begin, ctx), partials only (shared-prefix path).
 hipError_t launch_paged_decode_mfma_suffix(const DecodeArgs &a, int dtype, hipStream_t stream);
 

@@ -95,6 +95,37 @@ __device__ __forceinline__ u32x4 load16_stream(const void *p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
 }
 
+// 8 bytes: eight E4M3 elements of a quantised cache row.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x2 load8_stream(const void *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+}
+
+// OCP E4M3 ("e4m3fn") <-> binary32 with the gfx950 conversion instructions.
+// Four E4M3 bytes of a word -> four floats (exact).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float *f) {
+    const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+    const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+    f[0] = lo[0];
+    f[1] = lo[1];
+    f[2] = hi[0];
+    f[3] = hi[1];
+}
+
+// Largest finite E4M3 magnitude; quantised values saturate there.
+constexpr float kE4M3Max = 448.f;
+
+// Four floats -> four E4M3 bytes (round to nearest even after saturation to
+// +-448; comparisons are false for NaN, which stays NaN).
+__device__ __forceinline__ float sat_e4m3(float x) {
+    return x > kE4M3Max ? kE4M3Max : (x < -kE4M3Max ? -kE4M3Max : x);
+}
+__device__ __forceinline__ uint32_t f32x4_to_e4m3(float a, float b, float c, float d) {
+    uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(a), sat_e4m3(b), 0u, false);
+    return __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(c), sat_e4m3(d), w, true);
+}
+
 // ---------------------------------------------------------------------------
 // DPP lane exchanges inside rows of 16 lanes.
 template <int CTRL>

@@ -19,6 +19,23 @@ struct WriteArgs {
     int32_t vecs_per_token;  // (num_kv_heads * head_dim * elem_bytes) / 16
 };
 
+// Quantising slot write: 16-bit or binary32 K/V rows -> E4M3 cache rows,
+// element e of KV head h stored as encode(x * (1 / scale[h])).
+struct WriteE4M3Args {
+    const void *key;
+    const void *value;
+    void *key_cache;               // E4M3 bytes [NB, bs, KVH, D]
+    void *value_cache;
+    const int64_t *slot_mapping;
+    const float *k_scale;          // [KVH]
+    const float *v_scale;
+    int64_t num_tokens;
+    int64_t num_blocks;
+    int32_t block_size;
+    int32_t groups_per_token;      // KVH * D / 8 (eight elements per group)
+    int32_t groups_per_head;       // D / 8
+};
+
 struct DecodeArgs {
     void *out;                  // [B, H, D] (out dtype)
     unsigned *work_counter;     // unit dispenser of the persistent kernel (zero between calls)
@@ -46,6 +63,8 @@ struct DecodeArgs {
     int32_t part_base;          // slot of this launch's partition 0
     int32_t fold_prefix;        // 1: one partition per suffix; the epilogue joins
                                 // slots 0..part_base-1 and stores out (no merge)
+    const float *k_scale;       // [KVH] E4M3 caches only: cached K = code * k_scale
+    const float *v_scale;       // [KVH]
 };
 
 // Shared-prefix score/value kernel: every query row of every sequence
@@ -74,10 +93,16 @@ struct PrefixArgs {
 };
 
 hipError_t launch_kv_write(const WriteArgs &a, hipStream_t stream);
+// src_dtype: 0 f32, 1 f16, 2 bf16.
+hipError_t launch_kv_write_e4m3(const WriteE4M3Args &a, int src_dtype, hipStream_t stream);
 
 // dtype: 0 f32, 1 f16, 2 bf16.  Launches the decode kernel and, when
 // num_partitions > 1, the log-sum-exp merge.
 hipError_t launch_paged_decode(const DecodeArgs &a, int dtype, int head_dim, hipStream_t stream);
+
+// Decode over E4M3 caches (head_dim 128; dtype of query and output: f16 or
+// bf16), then the merge when the context is split.
+hipError_t launch_paged_decode_e4m3(const DecodeArgs &a, int dtype, hipStream_t stream);
 
 // Shared-prefix decode (16-bit caches, head_dim 128): the prefix kernel
 // (when num_splits > 0), then the suffix decode over tokens [token_begin,

@@ -44,12 +44,16 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-DTYPE_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
-NAN_BITS = {"f32": 0x7FC00000, "f16": 0x7E00, "bf16": 0x7FC0}
+DTYPE_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "e4m3": 1}
+NAN_BITS = {"f32": 0x7FC00000, "f16": 0x7E00, "bf16": 0x7FC0, "e4m3": 0x7F}
 
 CONFIG_NAMES = ("tiny_fp32", "mha_fp16", "gqa_bf16", "long_bf16", "prefix_fp16")
 PREFILL_NAMES = ("prefill_bf16",)
+# the GQA batch-256 workload over an 8-bit (E4M3) cache: same lengths and
+# page tables as gqa_bf16 (same seed), bf16 queries, per-KV-head scales
+QUANT_NAMES = ("gqa_fp8",)
 CONFIG_SEEDS = {name: i + 1 for i, name in enumerate(CONFIG_NAMES)}
+CONFIG_SEEDS["gqa_fp8"] = CONFIG_SEEDS["gqa_bf16"]
 PREFIX_BLOCK_SIZES = (8, 16, 32, 64)
 
 _CHUNK = 1 << 22  # elements per independently seeded chunk of a large fill
@@ -78,6 +82,9 @@ class DecodeBatch:
     poison_block: int | None = None
     unique_tokens: int | None = None  # distinct cached tokens (shared prefix counted once)
     meta: dict = field(default_factory=dict)
+    kv_dtype: str | None = None  # cache element type when it differs from dtype ("e4m3")
+    k_scale: np.ndarray | None = None  # float32 [KVH]: E4M3 caches only
+    v_scale: np.ndarray | None = None
 
     @property
     def num_seqs(self) -> int:
@@ -96,8 +103,13 @@ class DecodeBatch:
         return int(self.context_lens.max()) if self.num_seqs else 0
 
     @property
+    def cache_dtype(self) -> str:
+        return self.kv_dtype or self.dtype
+
+    @property
     def elem_bytes(self) -> int:
-        return DTYPE_BYTES[self.dtype]
+        """Bytes of one cached K or V element."""
+        return DTYPE_BYTES[self.cache_dtype]
 
     @property
     def total_tokens(self) -> int:
@@ -162,14 +174,36 @@ def _random_storage(seed_seq, shape, dtype: str) -> np.ndarray:
     return out.reshape(shape)
 
 
+def _random_e4m3(seed_seq, shape, scales: np.ndarray) -> np.ndarray:
+    """E4M3 codes of N(0,1) values divided by their KV head's scale (the
+    head is axis -2 of ``shape``), saturated to +-448 and rounded by torch's
+    float8_e4m3fn conversion."""
+    import torch
+
+    n = int(np.prod(shape))
+    d, kvh = shape[-1], shape[-2]
+    out = np.empty(n, dtype=np.uint8)
+    flat = _normal_f32(seed_seq, n)
+    inv = (np.float32(1) / scales.astype(np.float32)).astype(np.float32)
+    step = (1 << 26) // (kvh * d) * (kvh * d)
+    for lo in range(0, n, step):
+        x = flat[lo:lo + step].reshape(-1, kvh, d) * inv[None, :, None]
+        x = np.clip(x, -448.0, 448.0).astype(np.float32)
+        out[lo:lo + step] = torch.from_numpy(x.reshape(-1)).to(torch.float8_e4m3fn).view(
+            torch.uint8).numpy()
+    return out.reshape(shape)
+
+
 def nan_value(dtype: str):
     if dtype == "f32":
         return np.array([NAN_BITS["f32"]], dtype=np.uint32).view(np.float32)[0]
+    if dtype == "e4m3":
+        return np.uint8(NAN_BITS["e4m3"])
     return np.uint16(NAN_BITS[dtype])
 
 
 def storage_dtype(dtype: str):
-    return np.float32 if dtype == "f32" else np.uint16
+    return {"f32": np.float32, "e4m3": np.uint8}.get(dtype, np.uint16)
 
 
 # ----------------------------------------------------------------------------
@@ -221,7 +255,7 @@ def _tail_rows(tables, context_lens, block_size) -> np.ndarray:
 def make_batch(context_lens, *, num_heads: int, num_kv_heads: int, head_dim: int,
                block_size: int, dtype: str, seed: int, write_new_token: bool = False,
                poison: bool = True, partition_size: int = 0, name: str = "custom",
-               table_slack: int = 0, values: bool = True) -> DecodeBatch:
+               table_slack: int = 0, values: bool = True, kv_dtype: str | None = None) -> DecodeBatch:
     """A decode batch over disjoint shuffled pages.
 
     With ``write_new_token`` each sequence with a non-empty context gets one new
@@ -243,19 +277,34 @@ def make_batch(context_lens, *, num_heads: int, num_kv_heads: int, head_dim: int
             [tables, np.full((tables.shape[0], table_slack), spare, np.int32)], axis=1)
     b = ctx.size
     shape = (nb, block_size, num_kv_heads, head_dim)
+    cdt = kv_dtype or dtype
+    k_scale = v_scale = None
+    if cdt == "e4m3":
+        # per-KV-head scales in [1/64, 1/32]: N(0,1) values stay well inside +-448
+        s_ks, s_vs = ss.spawn(2)
+        k_scale = np.random.Generator(np.random.PCG64(s_ks)).uniform(
+            1 / 64, 1 / 32, num_kv_heads).astype(np.float32)
+        v_scale = np.random.Generator(np.random.PCG64(s_vs)).uniform(
+            1 / 64, 1 / 32, num_kv_heads).astype(np.float32)
     if values:
-        kc = _random_storage(s_k, shape, dtype)
-        vc = _random_storage(s_v, shape, dtype)
+        if cdt == "e4m3":
+            kc = _random_e4m3(s_k, shape, k_scale)
+            vc = _random_e4m3(s_v, shape, v_scale)
+        else:
+            kc = _random_storage(s_k, shape, dtype)
+            vc = _random_storage(s_v, shape, dtype)
         q = _random_storage(s_q, (b, num_heads, head_dim), dtype)
     else:
-        kc = vc = np.zeros((0, block_size, num_kv_heads, head_dim), storage_dtype(dtype))
+        kc = vc = np.zeros((0, block_size, num_kv_heads, head_dim), storage_dtype(cdt))
         q = np.zeros((0, num_heads, head_dim), storage_dtype(dtype))
     batch = DecodeBatch(name=name, dtype=dtype, num_heads=num_heads, num_kv_heads=num_kv_heads,
                         head_dim=head_dim, block_size=block_size, query=q, key_cache=kc,
                         value_cache=vc, block_tables=tables,
                         context_lens=ctx.astype(np.int32),
                         scale=float(np.float32(1.0 / math.sqrt(head_dim))),
-                        partition_size=partition_size, poison_block=spare)
+                        partition_size=partition_size, poison_block=spare,
+                        kv_dtype=kv_dtype if cdt != dtype else None, k_scale=k_scale,
+                        v_scale=v_scale)
     if write_new_token:
         slots = np.array([_row_index(tables, s, int(c) - 1, block_size) if c > 0 else -1
                           for s, c in enumerate(ctx)], dtype=np.int64)
@@ -270,8 +319,8 @@ def make_batch(context_lens, *, num_heads: int, num_kv_heads: int, head_dim: int
         if write_new_token:
             rows.append(batch.slot_mapping[batch.slot_mapping >= 0])
         rows = np.concatenate(rows)
-        _poison_rows(kc, rows, dtype)
-        _poison_rows(vc, rows, dtype)
+        _poison_rows(kc, rows, cdt)
+        _poison_rows(vc, rows, cdt)
     return batch
 
 
@@ -449,12 +498,13 @@ def make_config(name: str, *, block_size: int | None = None, seed: int | None = 
         return make_batch(ctx, num_heads=32, num_kv_heads=32, head_dim=128, block_size=16,
                           dtype="f16", seed=seed, poison=poison, partition_size=512,
                           name=name, values=values)
-    if name == "gqa_bf16":
+    if name in ("gqa_bf16", "gqa_fp8"):
         ctx = np.floor(np.exp(rng.uniform(math.log(128), math.log(16000), size=256)))
         ctx = np.clip(ctx, 128, 16000).astype(np.int64)
         return make_batch(ctx, num_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
                           dtype="bf16", seed=seed, write_new_token=True, poison=poison,
-                          partition_size=2048, name=name, values=values)
+                          partition_size=4096 if name == "gqa_fp8" else 2048, name=name,
+                          values=values, kv_dtype="e4m3" if name == "gqa_fp8" else None)
     if name == "long_bf16":
         return make_batch(np.full(4, 32768), num_heads=64, num_kv_heads=8, head_dim=128,
                           block_size=32, dtype="bf16", seed=seed, poison=poison,
@@ -531,6 +581,8 @@ def torch_view(a: np.ndarray, dtype: str):
     """A CPU torch tensor sharing ``a``'s memory, typed as ``dtype``."""
     import torch
 
+    if dtype == "e4m3":
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8))
     if dtype == "f32":
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
     t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16))

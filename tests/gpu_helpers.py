@@ -22,8 +22,11 @@ def upload(batch: wl.DecodeBatch, dev):
 
     t = {}
     t["q"] = wl.torch_view(batch.query, batch.dtype).to(dev)
-    t["kc"] = wl.torch_view(batch.key_cache, batch.dtype).to(dev)
-    t["vc"] = wl.torch_view(batch.value_cache, batch.dtype).to(dev)
+    t["kc"] = wl.torch_view(batch.key_cache, batch.cache_dtype).to(dev)
+    t["vc"] = wl.torch_view(batch.value_cache, batch.cache_dtype).to(dev)
+    if batch.k_scale is not None:
+        t["ks"] = torch.from_numpy(batch.k_scale).to(dev)
+        t["vs"] = torch.from_numpy(batch.v_scale).to(dev)
     t["bt"] = torch.from_numpy(batch.block_tables).to(dev)
     t["cl"] = torch.from_numpy(batch.context_lens).to(dev)
     if batch.slot_mapping is not None:
@@ -40,14 +43,23 @@ def gpu_step(batch: wl.DecodeBatch, t, *, partition_size=None, out_dtype=None, w
 
     import paged_kv_decode_13_amd as pkv
 
+    quant = batch.cache_dtype == "e4m3"
     if write and batch.slot_mapping is not None:
-        pkv.paged_kv_write(t["nk"], t["nv"], t["kc"], t["vc"], t["slots"])
+        if quant:
+            pkv.paged_kv_write_fp8(t["nk"], t["nv"], t["kc"], t["vc"], t["slots"], t["ks"], t["vs"])
+        else:
+            pkv.paged_kv_write(t["nk"], t["nv"], t["kc"], t["vc"], t["slots"])
     ps = batch.partition_size if partition_size is None else partition_size
     odt = None if out_dtype is None else getattr(torch, TORCH_DT[out_dtype])
-    out = pkv.paged_decode_attention(
-        t["q"], t["kc"], t["vc"], t["bt"], t["cl"], batch.block_size, batch.scale,
-        max_context_len=batch.max_context_len if max_context_len is None else max_context_len,
-        partition_size=ps, out_dtype=odt)
+    mcl = batch.max_context_len if max_context_len is None else max_context_len
+    if quant:
+        out = pkv.paged_decode_attention_fp8(
+            t["q"], t["kc"], t["vc"], t["ks"], t["vs"], t["bt"], t["cl"], batch.block_size,
+            batch.scale, max_context_len=mcl, partition_size=ps, out_dtype=odt)
+    else:
+        out = pkv.paged_decode_attention(
+            t["q"], t["kc"], t["vc"], t["bt"], t["cl"], batch.block_size, batch.scale,
+            max_context_len=mcl, partition_size=ps, out_dtype=odt)
     torch.cuda.synchronize()
     return out
 
@@ -88,10 +100,19 @@ def to_f64(out) -> np.ndarray:
 
 def oracle_step(batch: wl.DecodeBatch, write=True, context_lens=None):
     kc, vc = batch.key_cache, batch.value_cache
+    quant = batch.cache_dtype == "e4m3"
     if write and batch.slot_mapping is not None:
         kc, vc = kc.copy(), vc.copy()
-        oracle.paged_kv_write(batch.new_key, batch.new_value, kc, vc, batch.slot_mapping)
+        if quant:
+            oracle.paged_kv_write_e4m3(batch.new_key, batch.new_value, kc, vc, batch.slot_mapping,
+                                       batch.k_scale, batch.v_scale, batch.dtype)
+        else:
+            oracle.paged_kv_write(batch.new_key, batch.new_value, kc, vc, batch.slot_mapping)
     cl = batch.context_lens if context_lens is None else context_lens
+    if quant:
+        return oracle.paged_decode_e4m3(batch.query, kc, vc, batch.k_scale, batch.v_scale,
+                                        batch.block_tables, cl, batch.block_size, batch.scale,
+                                        batch.dtype)
     return oracle.paged_decode(batch.query, kc, vc, batch.block_tables, cl, batch.block_size,
                                batch.scale, batch.dtype)
 

@@ -35,7 +35,8 @@ def test_exports_every_declared_symbol(lib):
     names = _declared()
     assert set(names) == {"paged_kv_write", "paged_decode_workspace_size",
                           "paged_decode_attention", "paged_prefix_decode_workspace_size",
-                          "paged_prefix_decode_attention", "pkv_status_string"}
+                          "paged_prefix_decode_attention", "paged_kv_write_fp8",
+                          "paged_decode_attention_fp8", "pkv_status_string"}
     out = subprocess.run(["nm", "-D", "--defined-only", lib._name], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
@@ -159,6 +160,50 @@ def test_prefix_workspace_size(lib):
     big = lib.paged_prefix_decode_workspace_size(2048, 32, 8, 128, 40000, 32768, 0)
     assert big == 256 + 2048 * 32 * (16 + 1) * 130 * 4
     assert lib.paged_prefix_decode_workspace_size(0, 32, 8, 128, 3072, 2048, 0) == 0
+
+
+def _write8(lib, **kw):
+    a = dict(key=A, value=A, kc=A, vc=A, slots=A, ks=A, vs=A, n=1, kvh=8, d=128, bs=16, nb=100,
+             dt=BF16)
+    a.update(kw)
+    return lib.paged_kv_write_fp8(a["key"], a["value"], a["kc"], a["vc"], a["slots"], a["ks"],
+                                  a["vs"], a["n"], a["kvh"], a["d"], a["bs"], a["nb"], a["dt"], None)
+
+
+def test_fp8_write_validation(lib):
+    assert _write8(lib, n=-1) == SHAPE
+    assert _write8(lib, dt=9) == DTYPE
+    assert _write8(lib, d=96) == UNSUP
+    assert _write8(lib, bs=3) == UNSUP
+    assert _write8(lib, ks=None) == NULL
+    assert _write8(lib, vs=None) == NULL
+    assert _write8(lib, kc=A + 4) == ALIGN
+    assert _write8(lib, n=0, key=None) == OK
+
+
+def _decode8(lib, **kw):
+    a = dict(out=A, q=A, kc=A, vc=A, ks=A, vs=A, bt=A, cl=A, b=4, h=32, kvh=8, d=128, bs=16, mb=64,
+             nb=1000, maxc=1024, scale=0.088, ps=0, dt=BF16, odt=BF16, ws=A, wsb=1 << 20)
+    a.update(kw)
+    return lib.paged_decode_attention_fp8(
+        a["out"], a["q"], a["kc"], a["vc"], a["ks"], a["vs"], a["bt"], a["cl"], a["b"], a["h"],
+        a["kvh"], a["d"], a["bs"], a["mb"], a["nb"], a["maxc"], a["scale"], a["ps"], a["dt"],
+        a["odt"], a["ws"], a["wsb"], None)
+
+
+def test_fp8_decode_validation(lib):
+    assert _decode8(lib, h=30) == SHAPE
+    assert _decode8(lib, maxc=64 * 16 + 1) == SHAPE
+    assert _decode8(lib, dt=F32, odt=F32) == UNSUP  # 16-bit queries only
+    assert _decode8(lib, d=64) == UNSUP
+    assert _decode8(lib, h=128) == UNSUP
+    assert _decode8(lib, ps=24) == UNSUP
+    assert _decode8(lib, odt=F16) == DTYPE
+    assert _decode8(lib, ks=None) == NULL
+    assert _decode8(lib, vs=None) == NULL
+    assert _decode8(lib, vc=A + 8) == ALIGN
+    assert _decode8(lib, ws=None) == WORKSPACE
+    assert _decode8(lib, b=0, q=None) == OK
 
 
 def test_binding_rejects_cpu_tensors(lib):
