@@ -64,6 +64,8 @@ def _bind(lib):
     lib.oracle_paged_prefix_decode.argtypes = [p, p, p, p, p, i32, p, p, i32, i32, i32, i32, i32,
                                                i32, i64, dbl, ctypes.c_int, ctypes.c_int]
     lib.oracle_paged_kv_write.argtypes = [p, p, p, p, p, i64, i32, i32, i32, i64, ctypes.c_int]
+    lib.oracle_paged_prefill.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i64,
+                                         dbl, ctypes.c_int, ctypes.c_int]
     lib.oracle_decode_e4m3.argtypes = [ctypes.c_uint8]
     lib.oracle_decode_e4m3.restype = dbl
     lib.oracle_encode_e4m3.argtypes = [ctypes.c_float]
@@ -233,6 +235,33 @@ def paged_prefix_decode(query, key_cache, value_cache, prefix_table, prefix_len:
         _ptr(bt), _ptr(cl), b, h, kvh, d, bs, bt.shape[1], nb, float(np.float32(scale)),
         DTYPE_CODE[dtype], int(num_threads))
     _check(rc, "paged_prefix_decode")
+    return out
+
+
+def paged_prefill(query, key_cache, value_cache, block_tables, context_lens, query_start_loc,
+                  block_size: int, scale: float, dtype: str, num_threads: int = 0):
+    """[P2] "attention mask 在哪里": multi-token paged attention with a causal
+    mask.  ``query`` [total_queries, H, D] packs each sequence's q_len =
+    query_start_loc[s+1] - query_start_loc[s] queries, the last q_len
+    positions of its context; fp64 output of the same shape."""
+    for a in (query, key_cache, value_cache):
+        _elem_check(a, dtype)
+    nb, bs, kvh, d = key_cache.shape
+    if bs != block_size:
+        raise ValueError("block_size does not match the pool shape")
+    tq, h, dq = query.shape
+    assert dq == d and value_cache.shape == key_cache.shape
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+    qsl = np.ascontiguousarray(query_start_loc, dtype=np.int32)
+    b = cl.shape[0]
+    assert bt.ndim == 2 and bt.shape[0] == b and qsl.shape == (b + 1,) and qsl[-1] == tq
+    out = np.zeros((tq, h, d), dtype=np.float64)
+    rc = _load().oracle_paged_prefill(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
+                                      _ptr(bt), _ptr(cl), _ptr(qsl), b, h, kvh, d, bs, bt.shape[1],
+                                      nb, float(np.float32(scale)), DTYPE_CODE[dtype],
+                                      int(num_threads))
+    _check(rc, "paged_prefill")
     return out
 
 

@@ -277,6 +277,90 @@ int oracle_paged_kv_write(const void *key, const void *value, void *key_cache,
     return ORACLE_OK;
 }
 
+/* [P2] "attention mask 在哪里": each prompt token attends to itself and the
+ * tokens before it.  The history of (sequence, KV head) is gathered once;
+ * query i of the sequence attends to its first p + 1 rows (p = its
+ * position), which is the causal mask applied to the gathered history. */
+int oracle_paged_prefill(double *out, const void *query,
+                         const void *key_cache, const void *value_cache,
+                         const int32_t *block_tables, const int32_t *context_lens,
+                         const int32_t *query_start_loc, int32_t num_seqs,
+                         int32_t num_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size,
+                         int32_t max_blocks_per_seq, int64_t num_blocks,
+                         double scale, int dtype, int num_threads) {
+    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 ||
+        num_heads % num_kv_heads != 0 || head_dim <= 0 || block_size <= 0 ||
+        max_blocks_per_seq < 0 || dtype < 0 || dtype > 2 ||
+        (num_seqs > 0 && query_start_loc[0] != 0))
+        return ORACLE_ERR_ARG;
+    for (int32_t s = 0; s < num_seqs; ++s) {
+        int32_t q_len = query_start_loc[s + 1] - query_start_loc[s];
+        if (q_len < 0 || q_len > context_lens[s]) return ORACLE_ERR_ARG;
+    }
+    const int32_t group = num_heads / num_kv_heads;
+    const int64_t units = (int64_t)num_seqs * num_kv_heads;
+    int status = ORACLE_OK;
+#ifdef _OPENMP
+    if (num_threads <= 0) num_threads = omp_get_max_threads();
+#pragma omp parallel num_threads(num_threads)
+#endif
+    {
+        double *keys = NULL, *values = NULL, *qd = NULL;
+        int64_t cap = 0;
+        qd = (double *)malloc(sizeof(double) * (size_t)head_dim);
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+        for (int64_t u = 0; u < units; ++u) {
+            int32_t s = (int32_t)(u / num_kv_heads);
+            int32_t kvh = (int32_t)(u % num_kv_heads);
+            int32_t ctx = context_lens[s];
+            int32_t q0 = query_start_loc[s];
+            int32_t q_len = query_start_loc[s + 1] - q0;
+            int rc = qd ? ORACLE_OK : ORACLE_ERR_NOMEM;
+            if (!rc && ctx > cap) {
+                free(keys);
+                free(values);
+                cap = ctx;
+                keys = (double *)malloc(sizeof(double) * (size_t)cap * head_dim);
+                values = (double *)malloc(sizeof(double) * (size_t)cap * head_dim);
+                if (!keys || !values) {
+                    rc = ORACLE_ERR_NOMEM;
+                    cap = 0;
+                }
+            }
+            if (!rc && q_len > 0)
+                rc = oracle_paged_gather(
+                    keys, values, key_cache, value_cache,
+                    block_tables + (int64_t)s * max_blocks_per_seq,
+                    max_blocks_per_seq, ctx, block_size, num_blocks,
+                    num_kv_heads, kvh, head_dim, dtype);
+            for (int32_t i = 0; i < q_len && !rc; ++i) {
+                int32_t pos = ctx - q_len + i; /* this query's position */
+                for (int32_t g = 0; g < group && !rc; ++g) {
+                    int32_t head = kvh * group + g;
+                    int64_t qrow = ((int64_t)(q0 + i) * num_heads + head) * head_dim;
+                    for (int32_t d = 0; d < head_dim; ++d)
+                        qd[d] = load_elem(query, qrow + d, dtype);
+                    rc = oracle_attention(out + qrow, qd, keys, values, pos + 1,
+                                          head_dim, scale);
+                }
+            }
+            if (rc) {
+#ifdef _OPENMP
+#pragma omp critical
+#endif
+                status = rc;
+            }
+        }
+        free(keys);
+        free(values);
+        free(qd);
+    }
+    return status;
+}
+
 /* OCP E4M3: sign, 4-bit exponent with bias 7, 3-bit fraction. */
 double oracle_decode_e4m3(uint8_t bits) {
     int sign = (bits >> 7) & 1;

@@ -117,6 +117,26 @@ int oracle_paged_kv_write(const void *key, const void *value, void *key_cache,
                           int32_t head_dim, int32_t block_size,
                           int64_t num_blocks, int elem_bytes);
 
+/* [P2] section "attention mask 在哪里" and [P1] section "decode attention 和
+ * prefill attention 不一样": a prefill processes a whole prompt at once, and
+ * each prompt token may only see itself and the tokens before it (causal
+ * mask).  Multi-token paged attention: sequence s has
+ * q_len = query_start_loc[s+1] - query_start_loc[s] new query tokens, the
+ * last q_len positions of its context_lens[s]-token history (already in the
+ * pool); query i sits at position p = context_lens[s] - q_len + i and
+ * attends to tokens 0..p through the sequence's block table.  q_len ==
+ * context_lens[s] is a whole-prompt prefill; q_len == 1 is a decode step.
+ *   query, out  [total_queries, num_heads, head_dim], rows packed in sequence
+ *               order (query_start_loc[0] == 0, non-decreasing, q_len <= ctx). */
+int oracle_paged_prefill(double *out, const void *query,
+                         const void *key_cache, const void *value_cache,
+                         const int32_t *block_tables, const int32_t *context_lens,
+                         const int32_t *query_start_loc, int32_t num_seqs,
+                         int32_t num_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size,
+                         int32_t max_blocks_per_seq, int64_t num_blocks,
+                         double scale, int dtype, int num_threads);
+
 /* 8-bit floating point for a quantised KV cache ([P1] section "Triton 适合做
  *什么": the first kernel leaves quantisation out, a later one adds it).  The
  * format is OCP E4M3 ("e4m3fn"): 1 sign bit, 4 exponent bits (bias 7), 3

@@ -378,6 +378,104 @@ def pin_prefix_reduces_to_paged_decode():
 
 
 # ---------------------------------------------------------------------------
+# prefill: multi-token paged attention with a causal mask
+
+
+def _sdpa_masked(q, k, v, scale, mask):
+    """torch fp64 attention with an explicit boolean mask: q [Tq, H, D],
+    k/v [Tk, KVH, D], mask [Tq, Tk] (True = may attend)."""
+    import torch
+    import torch.nn.functional as F
+
+    qt = torch.from_numpy(np.ascontiguousarray(np.transpose(q, (1, 0, 2)), dtype=np.float64))[None]
+    kt = torch.from_numpy(np.ascontiguousarray(np.transpose(k, (1, 0, 2)), dtype=np.float64))[None]
+    vt = torch.from_numpy(np.ascontiguousarray(np.transpose(v, (1, 0, 2)), dtype=np.float64))[None]
+    out = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=torch.from_numpy(mask),
+                                         scale=float(scale), enable_gqa=True)
+    return np.transpose(out[0].numpy(), (1, 0, 2))
+
+
+def _prefill_case(seed=40):
+    """Contiguous histories paged by random tables; sequence 0 is a whole
+    prompt (q_len = ctx), the others continue a cached history (q_len < ctx)."""
+    rng = np.random.default_rng(seed)
+    h, kvh, d, bs = 8, 2, 16, 4
+    ctxs, qlens = [13, 30, 9, 1], [13, 7, 1, 1]
+    nb = sum(-(-c // bs) for c in ctxs) + 1
+    perm = rng.permutation(nb)
+    tables = np.full((4, 8), perm[-1], np.int32)
+    kc = np.full((nb, bs, kvh, d), np.nan, np.float32)
+    vc = np.full_like(kc, np.nan)
+    hist, pos = [], 0
+    for s_, c in enumerate(ctxs):
+        n = -(-c // bs)
+        tables[s_, :n] = perm[pos:pos + n]
+        pos += n
+        k1 = rng.standard_normal((c, kvh, d)).astype(np.float32)
+        v1 = rng.standard_normal((c, kvh, d)).astype(np.float32)
+        for t in range(c):
+            kc[tables[s_, t // bs], t % bs] = k1[t]
+            vc[tables[s_, t // bs], t % bs] = v1[t]
+        hist.append((k1, v1))
+    qsl = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    q = rng.standard_normal((int(qsl[-1]), h, d)).astype(np.float32)
+    return dict(q=q, kc=kc, vc=vc, tables=tables, ctx=np.array(ctxs, np.int32), qsl=qsl, bs=bs,
+                hist=hist, qlens=qlens)
+
+
+def pin_prefill_vs_library():
+    """Each sequence's queries against torch fp64 attention over its
+    contiguous history with the bottom-right causal mask: query i of q_len
+    sees tokens 0 .. ctx - q_len + i; the unused rows of the pool are NaN."""
+    c = _prefill_case()
+    scale = float(np.float32(0.25))
+    out = oracle.paged_prefill(c["q"], c["kc"], c["vc"], c["tables"], c["ctx"], c["qsl"], c["bs"],
+                               scale, "f32")
+    for s_, (k1, v1) in enumerate(c["hist"]):
+        ctx, ql = int(c["ctx"][s_]), c["qlens"][s_]
+        mask = np.arange(ctx)[None, :] <= (ctx - ql + np.arange(ql))[:, None]
+        qs = c["q"][c["qsl"][s_]:c["qsl"][s_ + 1]].astype(np.float64)
+        ref = _sdpa_masked(qs, k1.astype(np.float64), v1.astype(np.float64), scale, mask)
+        assert np.max(np.abs(out[c["qsl"][s_]:c["qsl"][s_ + 1]] - ref)) < 1e-12, s_
+
+
+def pin_prefill_reduces_to_decode():
+    """One query per sequence (the last position) is the decode, bit for bit;
+    and a whole prompt's first token sees only itself: its output is its own
+    value row."""
+    c = _prefill_case(41)
+    ones = np.arange(5, dtype=np.int32)
+    qlast = np.ascontiguousarray(c["q"][c["qsl"][1:] - 1])
+    got = oracle.paged_prefill(qlast, c["kc"], c["vc"], c["tables"], c["ctx"], ones, c["bs"], 0.3,
+                               "f32")
+    ref = oracle.paged_decode(qlast, c["kc"], c["vc"], c["tables"], c["ctx"], c["bs"], 0.3, "f32")
+    assert np.array_equal(got, ref)
+    out = oracle.paged_prefill(c["q"], c["kc"], c["vc"], c["tables"], c["ctx"], c["qsl"], c["bs"],
+                               0.3, "f32")
+    k1, v1 = c["hist"][0]
+    for head in range(8):
+        assert np.array_equal(out[0, head], v1[0, head // 4].astype(np.float64))
+
+
+def pin_prefill_causality():
+    """Changing the last token's K/V row changes only the queries that see it
+    (the last query of each sequence)."""
+    c = _prefill_case(42)
+    base = oracle.paged_prefill(c["q"], c["kc"], c["vc"], c["tables"], c["ctx"], c["qsl"], c["bs"],
+                                0.25, "f32")
+    kc, vc = c["kc"].copy(), c["vc"].copy()
+    s_, ctx = 1, int(c["ctx"][1])
+    row = (c["tables"][s_, (ctx - 1) // c["bs"]], (ctx - 1) % c["bs"])
+    kc[row] += 1.5
+    vc[row] -= 2.0
+    out = oracle.paged_prefill(c["q"], kc, vc, c["tables"], c["ctx"], c["qsl"], c["bs"], 0.25, "f32")
+    changed = np.abs(out - base).max(axis=(1, 2)) > 0
+    want = np.zeros(len(changed), bool)
+    want[c["qsl"][2] - 1] = True  # the last query of sequence 1
+    assert np.array_equal(changed, want)
+
+
+# ---------------------------------------------------------------------------
 # 8-bit (E4M3) KV cache
 
 
@@ -538,6 +636,9 @@ QUICK_PINS = [
     pin_sensitivity,
     pin_prefix_equals_contiguous,
     pin_prefix_reduces_to_paged_decode,
+    pin_prefill_vs_library,
+    pin_prefill_reduces_to_decode,
+    pin_prefill_causality,
     pin_e4m3_decode_exhaustive,
     pin_e4m3_encode,
     pin_e4m3_write,

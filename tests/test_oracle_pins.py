@@ -45,6 +45,15 @@ PLANTED = {
                               "row[lb] = lb < prefix_blocks ? prefix_table[prefix_blocks - 1 - lb] : own[lb];"),
     "suffix_table_relative": ("row[lb] = lb < prefix_blocks ? prefix_table[lb] : own[lb];",
                               "row[lb] = lb < prefix_blocks ? prefix_table[lb] : own[lb - prefix_blocks];"),
+    "prefill_query_cannot_see_itself": ("rc = oracle_attention(out + qrow, qd, keys, values, pos + 1,",
+                                        "rc = oracle_attention(out + qrow, qd, keys, values, pos,"),
+    "prefill_top_left_causal": ("int32_t pos = ctx - q_len + i; /* this query's position */",
+                                "int32_t pos = i; /* this query's position */"),
+    "prefill_sees_the_future": ("rc = oracle_attention(out + qrow, qd, keys, values, pos + 1,",
+                                "rc = oracle_attention(out + qrow, qd, keys, values, ctx,"),
+    "prefill_query_offset_dropped": ("int64_t qrow = ((int64_t)(q0 + i) * num_heads + head) * head_dim;",
+                                     "int64_t qrow = ((int64_t)i * num_heads + head) * head_dim;"),
+    "prefill_gqa_heads_interleaved": ("int32_t head = kvh * group + g;", "int32_t head = g * num_kv_heads + kvh;"),
     "e4m3_bias_off_by_one": ("mag = ldexp(1.0 + (double)frac / 8.0, expo - 7);",
                              "mag = ldexp(1.0 + (double)frac / 8.0, expo - 8);"),
     "e4m3_subnormal_as_normal": ("mag = ldexp((double)frac, -9); /* subnormal",
