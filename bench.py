@@ -245,6 +245,88 @@ def run_write(batch, t, steps: int, warmup: int) -> dict:
     }
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 matrix peak, AMD published
+
+
+def prefill_flops(batch) -> int:
+    """Algorithmic flops of causal attention over the prompts: query i of a
+    prompt sees i + 1 tokens; scores and values each take 2 * D flops per
+    (query head, visible token)."""
+    import numpy as np
+
+    n = batch.context_lens.astype(np.int64)
+    visible = int((n * (n + 1) // 2).sum())
+    return 4 * batch.head_dim * batch.num_heads * visible
+
+
+def run_prefill(batch, t, steps: int, warmup: int) -> dict:
+    """One prefill step: the bulk write of every prompt token's K/V through
+    slot_mapping, then causal attention of every prompt token over its
+    prompt (paged_prefill_attention); HIP events on the launch stream."""
+    import torch
+
+    import paged_kv_decode_13_amd as pkv
+
+    dev = t["q"].device
+    from paged_kv_decode_13_amd import workloads as wl
+
+    pq = wl.torch_view(batch.meta["prompt_query"], batch.dtype).to(dev)
+    qsl = torch.from_numpy(batch.meta["query_start_loc"]).to(dev)
+    out = torch.empty_like(pq)
+
+    def write():
+        pkv.paged_kv_write(t["nk"], t["nv"], t["kc"], t["vc"], t["slots"])
+
+    def attend():
+        pkv.paged_prefill_attention(pq, t["kc"], t["vc"], t["bt"], t["cl"], qsl, batch.block_size,
+                                    batch.scale, max_context_len=batch.max_context_len, out=out)
+
+    for _ in range(warmup):
+        write()
+        attend()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for e in evs:
+        e[0].record()
+        write()
+        e[1].record()
+        attend()
+        e[2].record()
+    torch.cuda.synchronize()
+    step_ms = statistics.mean(e[0].elapsed_time(e[2]) for e in evs)
+    attn_ms = statistics.mean(e[1].elapsed_time(e[2]) for e in evs)
+    write_ms = statistics.mean(e[0].elapsed_time(e[1]) for e in evs)
+    flops = prefill_flops(batch)
+    tflops = flops / (attn_ms * 1e-3) / 1e12
+    tokens = int(batch.context_lens.astype("int64").sum())
+    return {
+        "metric": "causal paged prefill attention TFLOP/s (+ prompt tokens/s)",
+        "value": round(flops / (step_ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": batch.dtype,
+        "data": "synthetic (seeded N(0,1) prompts and queries, generated page tables)",
+        "config": {"workload": batch.name, "prompts": batch.num_seqs, "prompt_tokens": tokens,
+                   "num_heads": batch.num_heads, "num_kv_heads": batch.num_kv_heads,
+                   "head_dim": batch.head_dim, "block_size": batch.block_size,
+                   "parallelism": "single GPU"},
+        "prompt_tokens_per_s": round(tokens / (step_ms * 1e-3), 1),
+        "write_ms": round(write_ms, 4),
+        "attention_ms": round(attn_ms, 4),
+        "algorithmic_flops": flops,
+        "roofline": {"bound": "mfma", "kernel": "paged_prefill_mfma_kernel",
+                     "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
+        "cpu_baseline": None,
+    }
+
+
 def run_copy(size_mb: int, steps: int) -> None:
     """A plain device-to-device copy of known size (counter calibration)."""
     import torch
@@ -274,7 +356,7 @@ def main() -> int:
     ap.add_argument("--shared-prefix", action="store_true",
                     help="prefix_fp16: decode through paged_prefix_decode_attention (the shared "
                          "prefix read once per KV head for the batch)")
-    ap.add_argument("--mode", default="decode", choices=["decode", "write", "copy"])
+    ap.add_argument("--mode", default="decode", choices=["decode", "write", "copy", "prefill"])
     ap.add_argument("--copy-mb", type=int, default=1024)
     args = ap.parse_args()
 
@@ -321,6 +403,14 @@ def main() -> int:
     if shared and "prefix_table" not in batch.meta:
         print(f"{args.config} has no shared prefix", file=sys.stderr)
         return 2
+    if args.mode == "prefill":
+        if args.config not in wl.PREFILL_NAMES:
+            print("--mode prefill runs on a prompt workload (prefill_bf16)", file=sys.stderr)
+            return 2
+        wl.add_prompt_queries(batch, seed=11)
+        t = upload(batch, dev)
+        print(json.dumps(run_prefill(batch, t, args.steps, args.warmup)), flush=True)
+        return 0
     if args.mode == "write":
         if batch.slot_mapping is None:
             print(f"{args.config} writes no tokens", file=sys.stderr)

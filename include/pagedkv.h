@@ -218,6 +218,44 @@ pkv_status paged_prefix_decode_attention(
     void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * paged_prefill_attention -- multi-token paged attention with a causal mask
+ * (prefill and chunked prefill) over the same pool.
+ *
+ * [P2] section "attention mask 在哪里": a prefill processes the whole prompt
+ * at once and each prompt token may only see itself and the tokens before
+ * it; [P1] section "decode attention 和 prefill attention 不一样": prefill is
+ * causal attention over the prompt.  Sequence s has q_len =
+ * query_start_loc[s+1] - query_start_loc[s] new query tokens, the last q_len
+ * positions of its context_lens[s]-token history, whose K/V are already in
+ * the pool (paged_kv_write first).  Query i sits at position p =
+ * context_lens[s] - q_len + i and attends to tokens 0..p through
+ * block_tables[s].  q_len == context_lens[s] is a whole-prompt prefill;
+ * q_len == 1 is one decode step.
+ *
+ *   out             [total_queries, num_heads, head_dim]  out_dtype (written)
+ *   query           [total_queries, num_heads, head_dim]  dtype, rows packed
+ *                   in sequence order
+ *   query_start_loc [num_seqs + 1] int32 (device): 0 = query_start_loc[0] <=
+ *                   ... <= query_start_loc[num_seqs] = total_queries.  A
+ *                   sequence whose range leaves [0, total_queries] is skipped
+ *                   (its rows are not written); one with q_len >
+ *                   context_lens[s] or an out-of-range length or page id gets
+ *                   NaN rows (only the rows that reach a bad page).
+ *   other arguments as paged_decode_attention; no workspace is needed.
+ * Supported: dtype PKV_F16 or PKV_BF16 (out_dtype dtype or PKV_F32),
+ * head_dim 128, block_size in {4, 8, 16, 32, 64}, G in {1, 2, 4, 8},
+ * num_seqs <= PKV_MAX_SEQS.
+ */
+pkv_status paged_prefill_attention(
+    void *out, const void *query, const void *key_cache,
+    const void *value_cache, const int32_t *block_tables,
+    const int32_t *context_lens, const int32_t *query_start_loc,
+    int32_t num_seqs, int32_t total_queries, int32_t num_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t max_blocks_per_seq, int64_t num_blocks, int32_t max_context_len,
+    float scale, pkv_dtype dtype, pkv_dtype out_dtype, void *stream);
+
+/*
  * 8-bit quantised KV cache.  [P1] section "Triton 适合做什么": the first
  * kernel leaves quantisation out; this is the later version that adds it.
  * Element format: OCP E4M3 ("e4m3fn": 1 sign, 4 exponent bits with bias 7, 3

@@ -27,6 +27,9 @@ Entry points (same names as the C ABI):
                              block_tables, context_lens, block_size, scale,
                              *, max_context_len, partition_size=0, out=None,
                              out_dtype=None, workspace=None)
+  paged_prefill_attention(query, key_cache, value_cache, block_tables,
+                          context_lens, query_start_loc, block_size, scale,
+                          *, max_context_len, out=None, out_dtype=None)
 E4M3 caches are uint8 or torch.float8_e4m3fn tensors.
 """
 from __future__ import annotations
@@ -42,6 +45,7 @@ __all__ = [
     "paged_prefix_decode_workspace_size",
     "paged_kv_write_fp8",
     "paged_decode_attention_fp8",
+    "paged_prefill_attention",
     "library_path",
     "PagedKVError",
 ]
@@ -98,6 +102,9 @@ def _load():
                                                i64, i32, ctypes.c_float, i32, ctypes.c_int,
                                                ctypes.c_int, p, sz, p]
     lib.paged_decode_attention_fp8.restype = ctypes.c_int
+    lib.paged_prefill_attention.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i32,
+                                            i64, i32, ctypes.c_float, ctypes.c_int, ctypes.c_int, p]
+    lib.paged_prefill_attention.restype = ctypes.c_int
     lib.pkv_status_string.argtypes = [ctypes.c_int]
     lib.pkv_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -383,4 +390,50 @@ def paged_decode_attention_fp8(query, key_cache, value_cache, k_scale, v_scale, 
         int(partition_size), dt, _dtype_code(odt), ws_ptr, ws_bytes, _stream_handle(query.device))
     if st != 0:
         raise PagedKVError(st, "paged_decode_attention_fp8")
+    return out
+
+
+def paged_prefill_attention(query, key_cache, value_cache, block_tables, context_lens,
+                            query_start_loc, block_size: int, scale: float, *,
+                            max_context_len: int, out=None, out_dtype=None):
+    """Causal multi-token attention over the paged pools: ``query``
+    [total_queries, num_heads, head_dim] packs each sequence's new queries
+    (``query_start_loc`` int32 [num_seqs + 1]), the last positions of its
+    ``context_lens`` history, whose K/V are already in the pools."""
+    torch = _torch()
+    lib = _load()
+    for t, n in ((query, "query"), (key_cache, "key_cache"), (value_cache, "value_cache"),
+                 (block_tables, "block_tables"), (context_lens, "context_lens"),
+                 (query_start_loc, "query_start_loc")):
+        _gpu(t, n)
+    if (block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32
+            or query_start_loc.dtype != torch.int32):
+        raise TypeError("block_tables, context_lens and query_start_loc must be int32")
+    nb, bs, kvh, d = key_cache.shape
+    if bs != block_size:
+        raise ValueError("block_size does not match key_cache.shape[1]")
+    tq, h, dq = query.shape
+    b = context_lens.shape[0]
+    if dq != d or value_cache.shape != key_cache.shape:
+        raise ValueError("inconsistent shapes")
+    if block_tables.dim() != 2 or block_tables.shape[0] != b or tuple(query_start_loc.shape) != (b + 1,):
+        raise ValueError("block_tables must be [num_seqs, max_blocks], query_start_loc [num_seqs + 1]")
+    if not (query.dtype == key_cache.dtype == value_cache.dtype):
+        raise TypeError("query and caches must share one dtype")
+    dt = _dtype_code(query.dtype)
+    odt = query.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((tq, h, d), dtype=odt, device=query.device)
+    else:
+        _gpu(out, "out")
+        if tuple(out.shape) != (tq, h, d):
+            raise ValueError("out must be [total_queries, num_heads, head_dim]")
+        odt = out.dtype
+    st = lib.paged_prefill_attention(
+        out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+        block_tables.data_ptr(), context_lens.data_ptr(), query_start_loc.data_ptr(), b, tq, h, kvh,
+        d, bs, block_tables.shape[1], nb, int(max_context_len), float(scale), dt, _dtype_code(odt),
+        _stream_handle(query.device))
+    if st != 0:
+        raise PagedKVError(st, "paged_prefill_attention")
     return out

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libpagedkv.so")
 ARCH = "gfx950"
 
 SOURCES = ["pkv_api.hip", "kv_write.hip", "paged_decode.hip", "paged_decode_mfma.hip",
-           "paged_prefix_mfma.hip"]
+           "paged_prefix_mfma.hip", "paged_prefill_mfma.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",

@@ -109,22 +109,6 @@ __device__ __forceinline__ u32x4 widen_e4m3(const u32x2 w) {
     return r;
 }
 
-// Inclusive prefix sum over the workgroup's threads (s_scan: kThreads ints).
-__device__ __forceinline__ int block_scan(int v, int *s_scan) {
-    const int tid = threadIdx.x;
-    s_scan[tid] = v;
-    __syncthreads();
-    for (int off = 1; off < kThreads; off <<= 1) {
-        const int x = tid >= off ? s_scan[tid - off] : 0;
-        __syncthreads();
-        s_scan[tid] += x;
-        __syncthreads();
-    }
-    const int r = s_scan[tid];
-    __syncthreads();
-    return r;
-}
-
 // Unit order: all full partitions of the batch first, then the partial last
 // partitions.  Units of one size drain the grid evenly and the variable-size
 // units come at the end, where they fill the gaps.  Builds the exclusive
@@ -160,16 +144,6 @@ __device__ __forceinline__ void build_unit_order(const DecodeArgs &a, int *s_pf,
         s_pp[B] = incp;
     }
     __syncthreads();
-}
-
-// Largest s in [0, n) with pre[s] <= x (pre non-decreasing, pre[0] = 0 <= x).
-__device__ __forceinline__ int search_le(const int *pre, int n, int x) {
-    int lo = 0, hi = n;
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (pre[mid] <= x) lo = mid; else hi = mid;
-    }
-    return lo;
 }
 
 // Three waves per SIMD (<= 168 VGPRs) keep enough loads in flight; the

@@ -425,3 +425,62 @@ pkv_status paged_decode_attention_fp8(void *out, const void *query, const void *
 }
 
 }  // extern "C"
+
+extern "C" {
+
+pkv_status paged_prefill_attention(void *out, const void *query, const void *key_cache,
+                                   const void *value_cache, const int32_t *block_tables,
+                                   const int32_t *context_lens, const int32_t *query_start_loc,
+                                   int32_t num_seqs, int32_t total_queries, int32_t num_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                   int32_t max_blocks_per_seq, int64_t num_blocks,
+                                   int32_t max_context_len, float scale, pkv_dtype dtype,
+                                   pkv_dtype out_dtype, void *stream) {
+    if (num_seqs < 0 || total_queries < 0 || num_heads <= 0 || num_kv_heads <= 0 ||
+        max_blocks_per_seq < 0 || num_blocks < 0 || max_context_len < 0)
+        return PKV_ERR_SHAPE;
+    if (num_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
+    if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return PKV_ERR_DTYPE;
+    if (out_dtype != dtype && out_dtype != PKV_F32) return PKV_ERR_DTYPE;
+    if (dtype == PKV_F32 || head_dim != 128) return PKV_ERR_UNSUPPORTED;
+    if (!pow2_block(block_size)) return PKV_ERR_UNSUPPORTED;
+    const int32_t group = num_heads / num_kv_heads;
+    if (group != 1 && group != 2 && group != 4 && group != 8) return PKV_ERR_UNSUPPORTED;
+    if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size) return PKV_ERR_SHAPE;
+    if (num_blocks == 0 && max_context_len > 0) return PKV_ERR_SHAPE;
+    if (!isfinite(scale)) return PKV_ERR_SHAPE;
+    if (num_seqs > PKV_MAX_SEQS) return PKV_ERR_UNSUPPORTED;
+    if (num_seqs == 0 || total_queries == 0) return PKV_OK;
+    if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens ||
+        !query_start_loc)
+        return PKV_ERR_NULL;
+    if (!aligned16(out) || !aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache))
+        return PKV_ERR_ALIGN;
+    const int64_t rows = (int64_t)total_queries * group;
+    if (((rows + 63) / 64 + num_seqs) * num_kv_heads > INT_MAX || rows * num_kv_heads > INT_MAX)
+        return PKV_ERR_SHAPE;
+    pkv::PrefillArgs a = {};
+    a.out = out;
+    a.query = query;
+    a.key_cache = key_cache;
+    a.value_cache = value_cache;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.query_start_loc = query_start_loc;
+    a.num_blocks = num_blocks;
+    a.num_seqs = num_seqs;
+    a.total_queries = total_queries;
+    a.num_heads = num_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.log2_group = log2i(group);
+    a.block_size = block_size;
+    a.log2_block_size = log2i(block_size);
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.max_context_len = max_context_len;
+    a.scale_log2e = scale * 1.4426950408889634f;
+    a.out_f32 = out_dtype == PKV_F32 ? 1 : 0;
+    hipError_t e = pkv::launch_paged_prefill(a, (int)dtype, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+}  // extern "C"

@@ -79,6 +79,32 @@ __device__ __forceinline__ Unit make_unit(const DecodeArgs &a) {
     return r;
 }
 
+// Inclusive prefix sum over the workgroup's threads (s_scan: kThreads ints).
+__device__ __forceinline__ int block_scan(int v, int *s_scan) {
+    const int tid = threadIdx.x;
+    s_scan[tid] = v;
+    __syncthreads();
+    for (int off = 1; off < kThreads; off <<= 1) {
+        const int x = tid >= off ? s_scan[tid - off] : 0;
+        __syncthreads();
+        s_scan[tid] += x;
+        __syncthreads();
+    }
+    const int r = s_scan[tid];
+    __syncthreads();
+    return r;
+}
+
+// Largest s in [0, n) with pre[s] <= x (pre non-decreasing, pre[0] = 0 <= x).
+__device__ __forceinline__ int search_le(const int *pre, int n, int x) {
+    int lo = 0, hi = n;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (pre[mid] <= x) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
 // Stage the physical block ids of logical blocks [lb0, lb0 + npages) of the
 // sequence in LDS (-1 and a flag for ids outside the pool).  Caller brackets
 // with __syncthreads().

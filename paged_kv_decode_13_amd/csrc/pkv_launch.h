@@ -92,7 +92,33 @@ struct PrefixArgs {
     float scale_log2e;
 };
 
+// Multi-token paged attention with a causal mask (prefill, chunked prefill).
+struct PrefillArgs {
+    void *out;                      // [total_queries, H, D] (out dtype)
+    const void *query;              // [total_queries, H, D]
+    const void *key_cache;          // [NB, bs, KVH, D]
+    const void *value_cache;
+    const int32_t *block_tables;    // [B, MB]
+    const int32_t *context_lens;    // [B]
+    const int32_t *query_start_loc; // [B + 1]
+    int64_t num_blocks;
+    int32_t num_seqs;
+    int32_t total_queries;
+    int32_t num_heads;
+    int32_t num_kv_heads;
+    int32_t log2_group;
+    int32_t block_size;
+    int32_t log2_block_size;
+    int32_t max_blocks_per_seq;
+    int32_t max_context_len;
+    float scale_log2e;
+    int32_t out_f32;
+};
+
 hipError_t launch_kv_write(const WriteArgs &a, hipStream_t stream);
+
+// dtype: f16 or bf16 (queries, caches and, unless out_f32, the output).
+hipError_t launch_paged_prefill(const PrefillArgs &a, int dtype, hipStream_t stream);
 // src_dtype: 0 f32, 1 f16, 2 bf16.
 hipError_t launch_kv_write_e4m3(const WriteE4M3Args &a, int src_dtype, hipStream_t stream);
 

@@ -1,0 +1,214 @@
+// Chunk machinery shared by the multi-query MFMA kernels (the shared-prefix
+// kernel and the prefill kernel): a workgroup of four waves holds 64 query
+// rows (16 per wave, one MFMA column block) and streams the K/V rows of one
+// KV head through LDS 64 tokens at a time, 16-bit caches, head_dim 128.
+//
+//  - K keeps its row layout in LDS (16-byte chunks XOR-swizzled by token);
+//    the score MFMA reads lane (i, q) = token i, head-dim chunk 4kk + q, and
+//    the query operand uses the same chunk order:
+//        S^T[16 tokens x 16 rows] = K[16 x 128] . Q^T[128 x 16].
+//  - V is transposed while it is staged (V^T[d][token], tokens of a 32-token
+//    block interleaved so that one 16-byte read gives a lane the eight tokens
+//    whose probabilities it already holds):
+//        O^T[16 d x 16 rows] += V^T[16 x 32 tokens] . P^T[32 x 16].
+//    The probabilities enter the 16-bit MFMA as a two-term split p = hi + lo,
+//    so the product keeps about 16 (bf16) or 21 (fp16) bits of p and the
+//    accumulation is fp32.
+//  - One reference max per row, shared by the row's four lane groups (two
+//    lane shuffles per chunk), so every probability of a chunk is relative to
+//    the same max and the value product can sum across lane groups.  It
+//    moves only when passed by more than 2^kMaxSlack, so the accumulators
+//    are rarely rescaled.
+#pragma once
+
+#include <math.h>
+
+#include "pkv_decode_common.h"
+#include "pkv_mfma.h"
+
+namespace pkv {
+
+constexpr int kMqaWaveRows = 16;                    // query rows per wave
+constexpr int kMqaRows = kNumWaves * kMqaWaveRows;  // query rows per workgroup
+constexpr int kMqaChunk = 64;                       // tokens per LDS chunk
+constexpr int kMqaRowBytes = 256;                   // one 16-bit K or V row (D = 128)
+constexpr int kMqaVtRow = kMqaChunk * 2;            // bytes of one transposed-V row
+
+// Double-buffered LDS chunk: K rows and transposed V.
+struct MqaLds {
+    char k[2][kMqaChunk * kMqaRowBytes];
+    char vt[2][128 * kMqaVtRow];
+};
+
+// 16-byte column of transposed-V row d that holds column `col`: XOR swizzle
+// so that the transposing writes (rows 8c + e) and the operand reads (rows
+// 16 dt + i) both spread over the LDS banks.
+__device__ __forceinline__ int vt_swz(int d, int col) { return col ^ ((d ^ (d >> 3)) & 7); }
+
+// Two probabilities -> packed 16-bit pairs (hi, lo) with hi + lo = p to
+// about 16 (bf16: hardware round-to-nearest-even both times) or 21 (fp16:
+// hardware pack with round toward zero; the remainder carries the rest)
+// significant bits.
+template <int DT>
+__device__ __forceinline__ void split_pack(float p0, float p1, uint32_t &hi, uint32_t &lo) {
+    if constexpr (DT == kBF16) {
+        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+        const bf16x2_t h = {(__bf16)p0, (__bf16)p1};
+        hi = __builtin_bit_cast(uint32_t, h);
+        const float r0 = p0 - __uint_as_float(hi << 16);
+        const float r1 = p1 - __uint_as_float(hi & 0xffff0000u);
+        const bf16x2_t l = {(__bf16)r0, (__bf16)r1};
+        lo = __builtin_bit_cast(uint32_t, l);
+    } else {
+        const auto h = __builtin_amdgcn_cvt_pkrtz(p0, p1);
+        hi = __builtin_bit_cast(uint32_t, h);
+        const float r0 = p0 - (float)h[0];
+        const float r1 = p1 - (float)h[1];
+        lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(r0, r1));
+    }
+}
+
+// Stage the four tokens 4 lg .. 4 lg + 3 of a chunk that this thread loaded
+// (16-byte chunk lc of each row): K rows into kt, V transposed into vt.  V
+// of tokens that are not valid (bit k of `okmask` clear: past the range or
+// on a bad page) is staged as zeros -- a zero probability times a NaN row
+// would still be NaN -- and their scores are masked by the caller.
+__device__ __forceinline__ void mqa_store_chunk(char *kt, char *vt, int lc, int lg,
+                                                const u32x4 (&kr)[4], const u32x4 (&vin)[4],
+                                                uint32_t okmask) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int tt = 4 * lg + i;
+        *reinterpret_cast<u32x4 *>(kt + tt * kMqaRowBytes + ((lc ^ tt) & 15) * 16) = kr[i];
+    }
+    u32x4 vr[4] = {vin[0], vin[1], vin[2], vin[3]};
+    if (__builtin_amdgcn_ballot_w64(okmask != 0xFu)) {  // only at the end of a range
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vr[i] = (okmask >> i) & 1u ? vr[i] : u32x4{0, 0, 0, 0};
+    }
+    // tokens 4 lg .. +3 sit in block lg / 8 (32 tokens), tile (lg / 4) & 1
+    // of the block, row group lg & 3 of the tile
+    const int col = ((lg >> 3) << 2) | (lg & 3);
+    const int half = (lg >> 2) & 1;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        // word w of a row holds head dims 8 lc + 2w (low half) and + 1 (high
+        // half); gather each across the four tokens: v_perm picks 16-bit
+        // halves of two registers
+        uint2 ev, od;
+        ev.x = __builtin_amdgcn_perm(vr[1][w], vr[0][w], 0x05040100u);
+        ev.y = __builtin_amdgcn_perm(vr[3][w], vr[2][w], 0x05040100u);
+        od.x = __builtin_amdgcn_perm(vr[1][w], vr[0][w], 0x07060302u);
+        od.y = __builtin_amdgcn_perm(vr[3][w], vr[2][w], 0x07060302u);
+        const int d0 = 8 * lc + 2 * w;
+        *reinterpret_cast<uint2 *>(vt + d0 * kMqaVtRow + vt_swz(d0, col) * 16 + half * 8) = ev;
+        *reinterpret_cast<uint2 *>(vt + (d0 + 1) * kMqaVtRow + vt_swz(d0 + 1, col) * 16 + half * 8) = od;
+    }
+}
+
+// Running state of one query row (lane j of each lane group q).
+struct MqaRowState {
+    float m;          // reference max (equal in the row's four lane groups)
+    float lsum;       // this lane's share of the normaliser
+    f32x4_t acc[8];   // O^T: head dims 16 dt + 4q + r of row j
+};
+
+__device__ __forceinline__ void mqa_init(MqaRowState &st) {
+    st.m = -INFINITY;
+    st.lsum = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) st.acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+}
+
+// One 64-token chunk (tokens t0 .. t0 + 63 staged in kt / vt) for this
+// wave's 16 rows.  Row j sees tokens t < lim; `masked` (wave-uniform) says
+// some token of the chunk lies past some row's limit.
+template <int DT>
+__device__ __forceinline__ void mqa_chunk(const char *kt, const char *vt, const u32x4 (&qop)[4],
+                                          int j, int q, int t0, int lim, bool masked, float sl2,
+                                          MqaRowState &st) {
+    float sc[4][4];  // [16-token tile][r]: token tile*16 + 4q + r, row j
+    float mx = -INFINITY;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+        f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const u32x4 kop = *reinterpret_cast<const u32x4 *>(
+                kt + (tt * 16 + j) * kMqaRowBytes + (((4 * kk + q) ^ j) & 15) * 16);
+            sacc = mfma_16x16x32<DT>(kop, qop[kk], sacc);
+        }
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) sc[tt][rr] = sacc[rr] * sl2;
+    }
+    if (masked) {
+        // the empty asm keeps this a branch: full chunks skip the masking
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+                sc[tt][rr] = (t0 + tt * 16 + 4 * q + rr < lim) ? sc[tt][rr] : -INFINITY;
+    }
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) mx = fmaxf(mx, sc[tt][rr]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    // m = -inf until the row has seen a valid token
+    const bool bump = mx > st.m + kMaxSlack;
+    if (__builtin_amdgcn_ballot_w64(bump)) {
+        const float alpha = !bump ? 1.f : (st.m == -INFINITY ? 0.f : fast_exp2(st.m - mx));
+        st.m = bump ? mx : st.m;
+        st.lsum *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) st.acc[dt] *= alpha;
+    }
+    // a row with m = -inf has only masked scores here: 2^(-inf - 0) = 0
+    const float mref = st.m == -INFINITY ? 0.f : st.m;
+    float ps = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            sc[tt][rr] = fast_exp2(sc[tt][rr] - mref);
+            ps += sc[tt][rr];
+        }
+    st.lsum += ps;
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+        // B operand: tokens (tile 2bb, 4q + e) for e < 4, (tile 2bb+1, 4q + e - 4) after
+        uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
+        split_pack<DT>(sc[2 * bb][0], sc[2 * bb][1], h0, l0);
+        split_pack<DT>(sc[2 * bb][2], sc[2 * bb][3], h1, l1);
+        split_pack<DT>(sc[2 * bb + 1][0], sc[2 * bb + 1][1], h2, l2);
+        split_pack<DT>(sc[2 * bb + 1][2], sc[2 * bb + 1][3], h3, l3);
+        const u32x4 ph = {h0, h1, h2, h3};
+        const u32x4 pl = {l0, l1, l2, l3};
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            const int d = 16 * dt + j;
+            const u32x4 vop = *reinterpret_cast<const u32x4 *>(vt + d * kMqaVtRow + vt_swz(d, bb * 4 + q) * 16);
+            st.acc[dt] = mfma_16x16x32<DT>(vop, ph, st.acc[dt]);
+            st.acc[dt] = mfma_16x16x32<DT>(vop, pl, st.acc[dt]);
+        }
+    }
+}
+
+// The row's normaliser: the sum of the four lane groups' shares.
+__device__ __forceinline__ float mqa_row_sum(const MqaRowState &st) {
+    float L = st.lsum + __shfl_xor(st.lsum, 16);
+    return L + __shfl_xor(L, 32);
+}
+
+// Workgroup id -> unit so that consecutive units share an XCD (consecutive
+// workgroup ids are dealt to the 8 XCDs in turn); a bijection on [0, n).
+__device__ __forceinline__ int xcd_unit(int id, int n) {
+    constexpr int kXcds = 8;
+    const int xcd = id % kXcds, slot = id / kXcds;
+    const int per = n / kXcds, rem = n % kXcds;
+    return (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + slot;
+}
+
+}  // namespace pkv

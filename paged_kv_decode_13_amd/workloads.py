@@ -560,6 +560,37 @@ def make_prefill_config(name: str, *, seed: int | None = None) -> DecodeBatch:
                         dtype="bf16", seed=seed, name=name, partition_size=2048)
 
 
+def make_prefill_attention(context_lens, query_lens, *, num_heads: int, num_kv_heads: int,
+                           head_dim: int, block_size: int, dtype: str, seed: int,
+                           name: str = "prefill_attention") -> DecodeBatch:
+    """A causal multi-token attention batch: every sequence's whole
+    ``context_lens`` history is in a shuffled page pool (rows past each
+    context and the spare page NaN), and its ``query_lens`` new queries are
+    its last positions.  ``meta["prompt_query"]`` [sum(q_len), H, D] and
+    ``meta["query_start_loc"]`` [B + 1] hold the packed queries."""
+    ctx = np.asarray(context_lens, dtype=np.int64).reshape(-1)
+    ql = np.asarray(query_lens, dtype=np.int64).reshape(-1)
+    if ql.shape != ctx.shape or (ql > ctx).any() or (ql < 0).any():
+        raise ValueError("each query count must lie in [0, context_len]")
+    batch = make_batch(ctx, num_heads=num_heads, num_kv_heads=num_kv_heads, head_dim=head_dim,
+                       block_size=block_size, dtype=dtype, seed=seed, name=name)
+    s_pq = np.random.SeedSequence([seed, 17])
+    batch.meta["prompt_query"] = _random_storage(s_pq, (int(ql.sum()), num_heads, head_dim), dtype)
+    batch.meta["query_start_loc"] = np.concatenate([[0], np.cumsum(ql)]).astype(np.int32)
+    return batch
+
+
+def add_prompt_queries(batch: DecodeBatch, seed: int) -> DecodeBatch:
+    """Queries for every token of every prompt of a prefill batch (q_len =
+    context_len), for the causal prefill attention after the prompt write."""
+    ctx = batch.context_lens.astype(np.int64)
+    s_pq = np.random.SeedSequence([seed, 17])
+    batch.meta["prompt_query"] = _random_storage(
+        s_pq, (int(ctx.sum()), batch.num_heads, batch.head_dim), batch.dtype)
+    batch.meta["query_start_loc"] = np.concatenate([[0], np.cumsum(ctx)]).astype(np.int32)
+    return batch
+
+
 def subset(batch: DecodeBatch, seqs) -> DecodeBatch:
     """The same pool restricted to some sequences (tables, lengths, queries
     and new tokens sliced; the pool is shared, not copied)."""

@@ -36,7 +36,8 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == {"paged_kv_write", "paged_decode_workspace_size",
                           "paged_decode_attention", "paged_prefix_decode_workspace_size",
                           "paged_prefix_decode_attention", "paged_kv_write_fp8",
-                          "paged_decode_attention_fp8", "pkv_status_string"}
+                          "paged_decode_attention_fp8", "paged_prefill_attention",
+                          "pkv_status_string"}
     out = subprocess.run(["nm", "-D", "--defined-only", lib._name], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
@@ -204,6 +205,32 @@ def test_fp8_decode_validation(lib):
     assert _decode8(lib, vc=A + 8) == ALIGN
     assert _decode8(lib, ws=None) == WORKSPACE
     assert _decode8(lib, b=0, q=None) == OK
+
+
+def _prefill(lib, **kw):
+    a = dict(out=A, q=A, kc=A, vc=A, bt=A, cl=A, qsl=A, b=4, tq=100, h=32, kvh=8, d=128, bs=16,
+             mb=64, nb=1000, maxc=1024, scale=0.088, dt=BF16, odt=BF16)
+    a.update(kw)
+    return lib.paged_prefill_attention(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["cl"],
+                                       a["qsl"], a["b"], a["tq"], a["h"], a["kvh"], a["d"], a["bs"],
+                                       a["mb"], a["nb"], a["maxc"], a["scale"], a["dt"], a["odt"],
+                                       None)
+
+
+def test_prefill_validation(lib):
+    assert _prefill(lib, tq=-1) == SHAPE
+    assert _prefill(lib, h=30) == SHAPE
+    assert _prefill(lib, maxc=64 * 16 + 1) == SHAPE
+    assert _prefill(lib, nb=0) == SHAPE
+    assert _prefill(lib, dt=F32, odt=F32) == UNSUP
+    assert _prefill(lib, d=64) == UNSUP
+    assert _prefill(lib, bs=2) == UNSUP
+    assert _prefill(lib, h=128) == UNSUP
+    assert _prefill(lib, b=4097) == UNSUP
+    assert _prefill(lib, odt=F16) == DTYPE
+    assert _prefill(lib, qsl=None) == NULL
+    assert _prefill(lib, out=A + 2) == ALIGN
+    assert _prefill(lib, tq=0, q=None) == OK
 
 
 def test_binding_rejects_cpu_tensors(lib):

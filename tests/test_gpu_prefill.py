@@ -1,0 +1,151 @@
+"""Causal multi-token paged attention (paged_prefill_attention) against the
+oracle's prefill on identical seeded inputs (MI355X)."""
+import itertools
+
+import numpy as np
+import pytest
+
+import oracle
+from paged_kv_decode_13_amd import workloads as wl
+from tests.gpu_helpers import TIGHT, TOL, max_err, rounded_out_ok, to_f64, upload
+
+pytestmark = pytest.mark.gpu
+
+TORCH_DT = {"f16": "float16", "bf16": "bfloat16", "f32": "float32"}
+
+
+def _gpu_prefill(b, t, out_dtype=None, max_context_len=None):
+    import torch
+
+    import paged_kv_decode_13_amd as pkv
+
+    dev = t["q"].device
+    pq = wl.torch_view(b.meta["prompt_query"], b.dtype).to(dev)
+    qsl = torch.from_numpy(b.meta["query_start_loc"]).to(dev)
+    odt = None if out_dtype is None else getattr(torch, TORCH_DT[out_dtype])
+    out = pkv.paged_prefill_attention(pq, t["kc"], t["vc"], t["bt"], t["cl"], qsl, b.block_size,
+                                      b.scale, max_context_len=max_context_len or b.max_context_len,
+                                      out_dtype=odt)
+    torch.cuda.synchronize()
+    return out
+
+
+def _oracle_prefill(b, kc=None, vc=None):
+    return oracle.paged_prefill(b.meta["prompt_query"], b.key_cache if kc is None else kc,
+                                b.value_cache if vc is None else vc, b.block_tables,
+                                b.context_lens, b.meta["query_start_loc"], b.block_size, b.scale,
+                                b.dtype)
+
+
+EDGE = [(dt, bs, g) for dt, bs, g in itertools.product(("f16", "bf16"), (4, 8, 16, 32, 64),
+                                                       (1, 2, 4, 8))]
+
+
+@pytest.mark.parametrize("dtype,bs,group", EDGE, ids=[f"{a}-bs{b}-g{c}" for a, b, c in EDGE])
+def test_prefill_edges(cuda, dtype, bs, group):
+    """Whole prompts of ragged lengths (one past 2048 tokens, so several
+    staged page segments at block 4), chunked prefills continuing a cached
+    history, single-query rows, an empty sequence and q_len = ctx = 1."""
+    ctx = [1, 37, 64, 65, 200, 300, 2100, 70, 0, 5]
+    ql = [1, 37, 64, 13, 200, 1, 40, 70, 0, 5]
+    b = wl.make_prefill_attention(ctx, ql, num_heads=2 * group, num_kv_heads=2, head_dim=128,
+                                  block_size=bs, dtype=dtype, seed=3000 + bs + group)
+    print(f"\n[prefill-edge] {dtype} bs={bs} G={group}", flush=True)
+    ref = _oracle_prefill(b)
+    out = to_f64(_gpu_prefill(b, upload(b, cuda), out_dtype="f32"))
+    assert max_err(out, ref) <= TIGHT[dtype], max_err(out, ref)
+    out = to_f64(_gpu_prefill(b, upload(b, cuda)))
+    assert rounded_out_ok(out, ref, dtype), max_err(out, ref)
+
+
+def test_prefill_single_queries_match_decode(cuda):
+    """q_len = 1 for every sequence: the prefill entry point and the decode
+    entry point both match the oracle's decode."""
+    import torch
+
+    import paged_kv_decode_13_amd as pkv
+
+    ctx = [5, 700, 1500, 33]
+    b = wl.make_prefill_attention(ctx, [1, 1, 1, 1], num_heads=32, num_kv_heads=8, head_dim=128,
+                                  block_size=16, dtype="bf16", seed=5)
+    q = b.meta["prompt_query"]
+    ref = oracle.paged_decode(q, b.key_cache, b.value_cache, b.block_tables, b.context_lens, 16,
+                              b.scale, "bf16")
+    t = upload(b, cuda)
+    out = to_f64(_gpu_prefill(b, t, out_dtype="f32"))
+    assert max_err(out, ref) <= TIGHT["bf16"]
+    dec = pkv.paged_decode_attention(wl.torch_view(q, "bf16").to(cuda), t["kc"], t["vc"], t["bt"],
+                                     t["cl"], 16, b.scale, max_context_len=b.max_context_len,
+                                     out_dtype=torch.float32)
+    assert max_err(to_f64(dec), ref) <= TIGHT["bf16"]
+
+
+def test_prefill_out_of_range_contents(cuda):
+    """A bad page id makes NaN exactly the rows that reach it; q_len > ctx or
+    a context past max_context_len makes the sequence's rows NaN; a query
+    range outside the packed rows is skipped; the rest match the oracle."""
+    import torch
+
+    ctx = [100, 300, 50, 80]
+    ql = [100, 60, 50, 10]
+    b = wl.make_prefill_attention(ctx, ql, num_heads=8, num_kv_heads=2, head_dim=128,
+                                  block_size=16, dtype="f16", seed=9)
+    ref = _oracle_prefill(b)
+    t = upload(b, cuda)
+    bt = t["bt"].clone()
+    bt[1, 15] = b.num_blocks + 3  # tokens 240..255 of sequence 1
+    t["bt"] = bt
+    out = to_f64(_gpu_prefill(b, t, out_dtype="f32"))
+    qsl = b.meta["query_start_loc"]
+    pos1 = 300 - 60 + np.arange(60)
+    rows1 = np.arange(qsl[1], qsl[2])
+    reach = pos1 >= 240
+    assert np.isnan(out[rows1[reach]]).all()
+    assert max_err(out[rows1[~reach]], ref[rows1[~reach]]) <= TIGHT["f16"]
+    others = np.r_[qsl[0]:qsl[1], qsl[2]:qsl[4]]
+    assert max_err(out[others], ref[others]) <= TIGHT["f16"]
+    # a context shorter than the sequence's query count, and one past max_context_len
+    t = upload(b, cuda)
+    cl = t["cl"].clone()
+    cl[2] = 40  # q_len 50 > 40
+    cl[3] = b.max_context_len + 1
+    t["cl"] = cl
+    out = to_f64(_gpu_prefill(b, t, out_dtype="f32"))
+    assert np.isnan(out[qsl[2]:qsl[4]]).all()
+    assert max_err(out[qsl[0]:qsl[2]], ref[qsl[0]:qsl[2]]) <= TIGHT["f16"]
+    torch.cuda.synchronize()
+
+
+def test_prefill_full_workload_sampled(cuda):
+    """The prompt workload at full size (32 prompts of 1024..8192 tokens):
+    the bulk write of every prompt token through slot_mapping, then causal
+    attention of every prompt token; 96 sampled (token, head) rows against
+    the oracle's attention over the history that row sees."""
+    import torch
+
+    import paged_kv_decode_13_amd as pkv
+
+    b = wl.add_prompt_queries(wl.make_prefill_config("prefill_bf16"), seed=11)
+    t = upload(b, cuda)
+    pkv.paged_kv_write(t["nk"], t["nv"], t["kc"], t["vc"], t["slots"])
+    out = _gpu_prefill(b, t).cpu()
+    torch.cuda.synchronize()
+    kc, vc = b.key_cache.copy(), b.value_cache.copy()
+    oracle.paged_kv_write(b.new_key, b.new_value, kc, vc, b.slot_mapping)
+    qsl = b.meta["query_start_loc"]
+    rng = np.random.default_rng(4)
+    g = b.num_heads // b.num_kv_heads
+    q = oracle.to_float64(b.meta["prompt_query"], "bf16")
+    worst = 0.0
+    for s_ in rng.choice(b.num_seqs, 8, replace=False):
+        ctx = int(b.context_lens[s_])
+        for kvh in rng.choice(b.num_kv_heads, 2, replace=False):
+            keys, vals = oracle.paged_gather(kc, vc, b.block_tables[s_], ctx, int(kvh), "bf16")
+            for pos in list(rng.choice(ctx, 5, replace=False)) + [ctx - 1]:
+                h = int(kvh) * g + int(rng.integers(g))
+                row = int(qsl[s_]) + int(pos)
+                ref = oracle.attention(q[row, h], keys[:pos + 1], vals[:pos + 1], b.scale)
+                got = out[row, h].float().numpy().astype(np.float64)
+                worst = max(worst, float(np.max(np.abs(got - ref))))
+    print(f"\n[prefill_bf16] sampled max|err| {worst:.3e}", flush=True)
+    assert worst <= TOL["bf16"]
