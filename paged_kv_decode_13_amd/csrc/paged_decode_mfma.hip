@@ -1,16 +1,17 @@
-// Fused paged decode attention with the score product on the matrix cores
-// (gfx950 v_mfma_f32_16x16x32_{bf16,f16}), for 16-bit caches and head_dim 128.
+// Fused paged decode attention with both products on the matrix cores
+// (gfx950 v_mfma_f32_16x16x32_{bf16,f16}), head_dim 128, over 16-bit or
+// E4M3 caches.
 //
 // Same computation as the VALU kernel (pages on PagedAttention:
 // "实现教学版 PagedAttention：从 block table 读取历史 KV cache", sections
 // "从逻辑 token 到物理 block" and "从 gather 后的 K/V 做 attention";
 // "从正确到更快：PagedAttention 的优化路线", sections "高性能 PagedAttention 的核心
-// 思想" and "attention kernel 真正在做什么").  With a query-head group the
-// score step of a 16-token tile is a small dense product
-//     S[16 tokens x 16] = K_tile[16 x 128] . Q^T[128 x 16]
-// whose 16 columns carry the group's heads (replicated when G < 4; two
-// products of 4 heads each when G = 8).  Four MFMAs (k = 32 each) per tile
-// replace the dot-product and lane-reduction work of the VALU kernel.
+// 思想" and "attention kernel 真正在做什么").  With a query-head group both
+// steps of a 16-token tile are small dense products whose 16 columns carry
+// the group's heads (column c: head c % G):
+//     S^T[16 tokens x 16] = K_tile[16 x 128] . Q^T[128 x 16]
+//     O^T[128 x 16]      += V^T[128 x 32 tokens] . P^T[32 tokens x 16]
+// (the second over a pair of tiles, k = 32).
 //
 // Work distribution: a persistent grid (as many workgroups as fit on the
 // chip) draws work units (sequence, KV partition, KV head) one at a time from
@@ -23,56 +24,37 @@
 //
 // Lane roles inside a wave (lane = 16 q + c):
 //  - K and V rows are loaded whole: load instruction i gives lane (q, c)
-//    16-byte chunk c of token 4q + i, so each instruction reads four complete
-//    256-byte rows.  (Reading the MFMA operand layout straight from HBM --
-//    64 bytes of 16 different rows per instruction -- measured 24% slower.)
+//    chunk c (head dims 8c..8c+7) of token 4q + i, so each instruction reads
+//    four complete rows.  (Reading the MFMA operand layout straight from
+//    HBM -- 64 bytes of 16 different rows per instruction -- measured 24%
+//    slower.)
 //  - K operand: the tile's K rows are transposed through a wave-private LDS
 //    tile so that lane (q, c) holds token c, chunks 4j + q (j = 0..3).  The
 //    query operand uses the same chunk order, so the contraction pairs
 //    equal head-dim indices.
-//  - Scores come back as rows 4q + r (r = 0..3) of the tile for head c % 4
-//    (+4 for the second product): lane (q, c) owns tokens 4q..4q+3.
-//  - V stays in the loaded row order: lane (q, c) holds chunk c of tokens
-//    4q + r, the same tokens whose scores it holds; the
-//    other heads' probabilities come from the lanes of its quad (DPP quad
-//    broadcast).  The running softmax is kept per lane and per row group q
-//    and merged at the end, so the tile loop needs no cross-lane max.
-//  - The loads of a wave's next tile are issued before the current tile is
-//    computed (two register sets), so HBM requests stay in flight while the
-//    wave computes.
+//  - Scores come back as rows 4q + r (r = 0..3) of the tile for column c:
+//    lane (q, c) owns tokens 4q..4q+3, which is the B-operand layout of the
+//    value product, and V^T is formed from the lane's own V registers (see
+//    the kernel).
+//  - A wave issues the loads of two tiles, then computes them; three waves
+//    per SIMD keep HBM requests in flight while others compute.
 #include <math.h>
+
+#include <type_traits>
 
 #include "pkv_decode_common.h"
 #include "pkv_mfma.h"
 
+// Tiles whose loads a wave issues at once (even: tiles are computed in
+// pairs); the register budget of three waves per SIMD allows two
 #ifndef PKV_TILES_PER_STEP
 #define PKV_TILES_PER_STEP 2
 #endif
-// E4M3 caches: a tile is half the bytes, so twice the tiles per step keep
-// the same bytes in flight
 #ifndef PKV_TILES_PER_STEP_E4M3
-#define PKV_TILES_PER_STEP_E4M3 4
+#define PKV_TILES_PER_STEP_E4M3 2
 #endif
 
 namespace pkv {
-
-// Value of head slot `hl` (0 <= hl < HS) held by the lanes of this lane's quad:
-// lane c of a quad carries head slot c % HS.
-template <int HS>
-__device__ __forceinline__ float head_bcast(float x, int hl) {
-    if constexpr (HS == 1) {
-        return x;
-    } else if constexpr (HS == 2) {
-        return hl == 0 ? dpp<0xA0>(x) : dpp<0xF5>(x);  // quad_perm [0,0,2,2] / [1,1,3,3]
-    } else {
-        switch (hl) {
-            case 0: return dpp<0x00>(x);  // quad_perm [0,0,0,0]
-            case 1: return dpp<0x55>(x);  // [1,1,1,1]
-            case 2: return dpp<0xAA>(x);  // [2,2,2,2]
-            default: return dpp<0xFF>(x); // [3,3,3,3]
-        }
-    }
-}
 
 // Loaded rows of one 16-token tile: 16-byte chunks of 16-bit rows, or
 // 8-byte chunks (eight E4M3 codes, the same head dims) of quantised rows.
@@ -89,24 +71,22 @@ struct TileRegsT<true> {
     uint32_t vmask;
 };
 
-// Eight E4M3 codes -> the same eight values in the 16-bit compute type
-// (exact: E4M3 values are representable in binary16 and bfloat16).
+// Two E4M3 codes (bytes 0, 1 of `w`, or bytes 2, 3 with HIGH) -> the packed
+// 16-bit pair of the same values (exact: E4M3 values are representable in
+// binary16 and bfloat16); one instruction (scale 1: the plain value).
+template <int DT, bool HIGH>
+__device__ __forceinline__ uint32_t e4m3_pair(uint32_t w) {
+    if constexpr (DT == kBF16)
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, HIGH));
+    else
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.f, HIGH));
+}
+
+// Eight E4M3 codes -> the same eight values in the 16-bit compute type.
 template <int DT>
 __device__ __forceinline__ u32x4 widen_e4m3(const u32x2 w) {
-    // one instruction per pair (scale 1: the plain value)
-    u32x4 r;
-    if constexpr (DT == kBF16) {
-        r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.f, false));
-        r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.f, true));
-        r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.f, false));
-        r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.f, true));
-    } else {
-        r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.x, 1.f, false));
-        r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.x, 1.f, true));
-        r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.y, 1.f, false));
-        r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.y, 1.f, true));
-    }
-    return r;
+    return u32x4{e4m3_pair<DT, false>(w.x), e4m3_pair<DT, true>(w.x), e4m3_pair<DT, false>(w.y),
+                 e4m3_pair<DT, true>(w.y)};
 }
 
 // Unit order: all full partitions of the batch first, then the partial last
@@ -146,6 +126,70 @@ __device__ __forceinline__ void build_unit_order(const DecodeArgs &a, int *s_pf,
     __syncthreads();
 }
 
+// Units are handed out one at a time from a counter in the workspace, so a
+// workgroup that drew short units simply takes more: with a static
+// assignment the chip idles while the unluckiest workgroups finish.  Every
+// workgroup ends with exactly one failed draw; the draw that sees the last
+// ticket of the launch (total + grid - 1) resets the counter to zero for the
+// next call on this workspace.  Decodes the unit into (sequence, partition,
+// KV head); false once the units are exhausted.  Starts with a barrier, so
+// the previous unit's epilogue is done with LDS.
+template <bool PFX>
+__device__ __forceinline__ bool draw_unit(const DecodeArgs &a, const int *s_pf, const int *s_pp,
+                                          const int *s_ctx, int *s_unit, Unit &u) {
+    const int total_full = s_pf[a.num_seqs];
+    const int total_units = (total_full + s_pp[a.num_seqs]) * a.num_kv_heads;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned got = atomicAdd(a.work_counter, 1u);
+        if (got == (unsigned)total_units + gridDim.x - 1u) atomicExch(a.work_counter, 0u);
+        *s_unit = (int)got;
+    }
+    __syncthreads();
+    const int unit = *s_unit;
+    if (unit >= total_units) return false;
+    u.kvh = unit % a.num_kv_heads;
+    const int sp = unit / a.num_kv_heads;
+    if (sp < total_full) {
+        u.s = search_le(s_pf, a.num_seqs, sp);
+        u.p = sp - s_pf[u.s];
+    } else {
+        u.s = search_le(s_pp, a.num_seqs, sp - total_full);
+        u.p = seq_full<PFX>(a, s_ctx[u.s]);
+    }
+    u.ctx = s_ctx[u.s];
+    u.bad_len = bad_context(a, u.ctx);
+    u.tok_begin = first_token<PFX>(a) + u.p * a.partition_size;
+    u.tok_end = u.bad_len ? 0 : min(u.ctx, u.tok_begin + a.partition_size);
+    u.nparts = seq_parts<PFX>(a, u.ctx);
+    u.empty = false;
+    return true;
+}
+
+// The value product.  Two consecutive 16-token tiles form a 32-token pair,
+// and for each of eight head-dim blocks dt
+//     O^T[16 x 16] += V^T[16 x 32 tokens] . P^T[32 tokens x 16]
+// is one k = 32 MFMA (twice: the probabilities enter as a two-term split
+// hi + lo, so about 16 (bf16) or 21 (fp16) bits of each p reach the fp32
+// accumulators).  The 16 columns carry the group's heads (column c: head
+// c % G), so one score product per tile covers every group size up to 8,
+// and the accumulators are 32 floats per lane whatever G is.
+//  - The score MFMA leaves lane (q, c) the probabilities of tokens 4q..4q+3
+//    of each tile for column c, which is already the layout of the B
+//    operand (k = 8q + e: tile A's token 4q + e for e < 4, tile B's 4q + e - 4
+//    after): P^T needs no data movement.
+//  - Row i of block dt's A operand is head dim 8i + dt.  Lane (q, c) then
+//    needs dim 8c + dt of tokens 4q..4q+3 of both tiles -- values it loaded
+//    itself (its V chunk c is dims 8c..8c+7 of exactly those tokens) -- so
+//    V^T is formed in registers with one v_perm per operand register and
+//    never touches LDS.  The accumulator of block dt holds dims
+//    8 (4q + r) + dt: lane (q, c) ends with dims 32q..32q+31 of column c.
+//  - One reference max per column, shared by the four row groups q (two
+//    lane swaps per pair), so every probability of a column is relative
+//    to the same max and the value product can sum over all 32 tokens; the
+//    lazy rule (move only when passed by more than 2^kMaxSlack) keeps
+//    rescales rare.
+//
 // Three waves per SIMD (<= 168 VGPRs) keep enough loads in flight; the
 // allocator is held to that budget.
 //
@@ -153,123 +197,73 @@ __device__ __forceinline__ void build_unit_order(const DecodeArgs &a, int *s_pf,
 // always writes partials (slots part_base.. of part_stride), for the
 // shared-prefix path; the plain instantiation never reads those fields.
 // KV8: the caches hold E4M3 codes (128-byte rows) with per-KV-head scales;
-// DT is then the type of the query and the output.  K is widened to DT
-// before the score MFMA, V to fp32 before the value product; k_scale joins
-// the score scale and v_scale multiplies the result.
+// DT is then the type of the query and the output.  K and V are widened to
+// DT (exact) for the MFMAs; k_scale joins the score scale and v_scale
+// multiplies the result.
 template <int DT, int G, bool PFX, bool KV8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8)))
 void paged_decode_mfma_kernel(DecodeArgs a) {
     constexpr int D = 128;
     constexpr int ROW_BYTES = D * 2;
     constexpr int TILE = 16;
-    constexpr int HS = G < 4 ? G : 4;  // heads per score product
-    constexpr int NSET = G / HS;       // score products per tile
-    constexpr bool kQopInLds = NSET > 1;
     constexpr int KV_ROW = KV8 ? D : D * 2;     // bytes of one cached row
     constexpr int KV_CHUNK = KV8 ? 8 : 16;      // bytes of one lane's chunk
     using TileRegs = TileRegsT<KV8>;
+    constexpr int TPS = KV8 ? PKV_TILES_PER_STEP_E4M3 : PKV_TILES_PER_STEP;
+    static_assert(TPS % 2 == 0, "tiles go in pairs");
+    // one wave's LDS region: the K rows of the tile being scored (the score
+    // operand transpose), then the wave's accumulators for the epilogue
+    constexpr int kRegion = TILE * ROW_BYTES;
+    static_assert(G * D * 4 <= kRegion, "accumulators fit the wave's region");
 
     extern __shared__ int s_dyn[];     // full-unit prefix [B + 1], partial-unit prefix [B + 1], lengths [B]
     __shared__ int s_pages[kSegPages];
     __shared__ int s_bad;
     __shared__ float s_m[kNumWaves][G];
     __shared__ float s_l[kNumWaves][G];
-    __shared__ float s_acc[kNumWaves][G][D];
-    __shared__ __attribute__((aligned(16))) char s_ktile[kNumWaves][TILE * ROW_BYTES];
-    __shared__ u32x4 s_qop[kQopInLds ? NSET : 1][4][kWave];
+    __shared__ __attribute__((aligned(16))) char s_region[kNumWaves][kRegion];
 
     int *s_pf = s_dyn;
     int *s_pp = s_dyn + a.num_seqs + 1;
     int *s_ctx = s_dyn + 2 * (a.num_seqs + 1);
     build_unit_order<PFX>(a, s_pf, s_pp, s_ctx, s_pages);
-    const int total_full = s_pf[a.num_seqs];
-    const int total_units = (total_full + s_pp[a.num_seqs]) * a.num_kv_heads;
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    // wave-uniform (scalar) so that the tile loop is a scalar loop
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int q = lane >> 4;  // row group: tokens 4q..4q+3 of a tile
-    const int c = lane & 15;  // column: head slot c % HS; V chunk c
+    const int c = lane & 15;  // column (head c % G); K and V chunk c
 
     const char *kbase = reinterpret_cast<const char *>(a.key_cache);
     const char *vbase = reinterpret_cast<const char *>(a.value_cache);
     const int bs = a.block_size;
     const int lbs = a.log2_block_size;
     const int64_t tok_stride = (int64_t)a.num_kv_heads * KV_ROW;  // bytes between slots
-    const float sl2_q = a.scale_log2e;
-    char *ktile = s_ktile[wave];
+    char *kt = s_region[wave];
 
-    // Units are handed out one at a time from a counter in the workspace, so
-    // a workgroup that drew short units simply takes more: with a static
-    // assignment the chip idles while the unluckiest workgroups finish.
-    // Every workgroup ends with exactly one failed draw; the draw that sees
-    // the last ticket of the launch (total + grid - 1) resets the counter to
-    // zero for the next call on this workspace.
     __shared__ int s_unit;
-    for (;;) {
-        __syncthreads();  // previous unit's epilogue is done with LDS
-        if (threadIdx.x == 0) {
-            const unsigned got = atomicAdd(a.work_counter, 1u);
-            if (got == (unsigned)total_units + gridDim.x - 1u) atomicExch(a.work_counter, 0u);
-            s_unit = (int)got;
-        }
-        __syncthreads();
-        const int unit = s_unit;
-        if (unit >= total_units) break;
-        // unit -> (sequence, partition, KV head)
-        Unit u;
-        u.kvh = unit % a.num_kv_heads;
-        const int sp = unit / a.num_kv_heads;
-        if (sp < total_full) {
-            u.s = search_le(s_pf, a.num_seqs, sp);
-            u.p = sp - s_pf[u.s];
-        } else {
-            u.s = search_le(s_pp, a.num_seqs, sp - total_full);
-            u.p = seq_full<PFX>(a, s_ctx[u.s]);
-        }
-        u.ctx = s_ctx[u.s];
-        u.bad_len = bad_context(a, u.ctx);
-        u.tok_begin = first_token<PFX>(a) + u.p * a.partition_size;
-        u.tok_end = u.bad_len ? 0 : min(u.ctx, u.tok_begin + a.partition_size);
-        u.nparts = seq_parts<PFX>(a, u.ctx);
-        u.empty = false;
-
+    Unit u;
+    while (draw_unit<PFX>(a, s_pf, s_pp, s_ctx, &s_unit, u)) {
         if (tid == 0) s_bad = 0;
 
-        // query operand: head (set*HS + c%HS), chunks 4j + q.  It is the
-        // same for every wave; with two score products (G = 8) it is parked
-        // in LDS (wave 0 writes it before the first barrier below) to keep
-        // the register count at three waves per SIMD.
+        // query operand: head h0 + c % G, chunks 4j + q
         const int h0 = u.kvh * G;
-        u32x4 qop[NSET][4];
-        if (!kQopInLds || wave == 0) {
-            const char *qb = reinterpret_cast<const char *>(a.query);
+        u32x4 qop[4];
+        {
+            const char *row = reinterpret_cast<const char *>(a.query) +
+                              ((int64_t)u.s * a.num_heads + h0 + c % G) * ROW_BYTES;
 #pragma unroll
-            for (int set = 0; set < NSET; ++set) {
-                const int h = h0 + set * HS + (c % HS);
-                const char *row = qb + ((int64_t)u.s * a.num_heads + h) * ROW_BYTES;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    qop[set][j] = load16(row + (4 * j + q) * 16);
-                    if constexpr (kQopInLds) s_qop[set][j][lane] = qop[set][j];
-                }
-            }
+            for (int j = 0; j < 4; ++j) qop[j] = load16(row + (4 * j + q) * 16);
         }
 
-        float m[NSET], l[NSET], acc[G][8];
+        float m = -INFINITY;  // reference max of column c (equal in the four row groups)
+        float lsum = 0.f;     // this lane's share of column c's normaliser
+        f32x4_t acc[8];       // block dt: dims 8 (4q + r) + dt of column c
 #pragma unroll
-        for (int set = 0; set < NSET; ++set) {
-            m[set] = -INFINITY;
-            l[set] = 0.f;
-        }
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
+        for (int dt = 0; dt < 8; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
         const int64_t kvh_off = (int64_t)u.kvh * KV_ROW;
-        float sl2 = sl2_q;
+        float sl2 = a.scale_log2e;
         if constexpr (KV8) sl2 *= a.k_scale[u.kvh];
 
         for (int seg = u.tok_begin; seg < u.tok_end; seg += kSegPages << lbs) {
@@ -279,176 +273,203 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
             stage_pages(a, u, seg >> lbs, npages, s_pages, &s_bad);
             __syncthreads();
 
-            // token -> byte offset of its row in the pool.  Loads are issued
-            // unconditionally so the compiler can count outstanding loads
-            // exactly and keep the next tile's loads in flight: a token past
-            // the segment or on a bad page id reads a row of page 0 (always
-            // in the pool) and is flagged invalid; invalid V rows are zeroed
-            // where they are consumed and invalid scores are masked.
-            auto row_of = [&](int t, bool &valid) -> int64_t {
+            // Byte offset of this lane's chunk of token t0 + 4q, the first of
+            // its four consecutive tokens (t0 is a multiple of 4 and pages
+            // hold >= 4 tokens, so the four share a page and lie one
+            // tok_stride apart).  A token past the segment or on a bad page id
+            // reads a row of page 0 (always in the pool) and is flagged
+            // invalid in `vmask` (its V zeroed; its score masked, or the
+            // output made NaN by the bad-page flag).
+            auto tile_base = [&](int t0, uint32_t &vmask) -> int64_t {
+                const int t = t0 + 4 * q;
                 const int pb = s_pages[min((t - seg) >> lbs, npages - 1)];
-                valid = (t < seg_end) & (pb >= 0);
-                const int64_t page = valid ? pb : 0;
-                return (page * bs + (t & (bs - 1))) * tok_stride + kvh_off;
+                const int n_ok = pb >= 0 ? min(max(seg_end - t, 0), 4) : 0;
+                vmask = (1u << n_ok) - 1u;
+                const int64_t page = pb >= 0 ? pb : 0;
+                return (page * bs + (t & (bs - 1))) * tok_stride + kvh_off + c * KV_CHUNK;
             };
-            auto load_tile = [&](TileRegs &r, int t0) {
-                r.vmask = 0;
+            auto load_k = [&](TileRegs &r, int t0) {
+                uint32_t unused;
+                const char *p = kbase + tile_base(t0, unused);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    bool ok;
-                    const int64_t row = row_of(t0 + 4 * q + i, ok) + c * KV_CHUNK;
-                    if constexpr (KV8) {
-                        r.k[i] = load8_stream(kbase + row);
-                        r.v[i] = load8_stream(vbase + row);
-                    } else {
-                        r.k[i] = load16_stream(kbase + row);
-                        r.v[i] = load16_stream(vbase + row);
-                    }
-                    r.vmask |= ok ? (1u << i) : 0u;
+                    if constexpr (KV8) r.k[i] = load8_stream(p + i * tok_stride);
+                    else r.k[i] = load16_stream(p + i * tok_stride);
                 }
             };
-            auto compute_tile = [&](const TileRegs &r, int t0) {
-                // K rows arrive whole (16 lanes per 256-byte row); the score
-                // MFMA wants lane (q, c) to hold token c, chunks 4j + q.
-                // Transpose through this wave's LDS tile, 16-byte chunks
-                // XOR-swizzled by token so that writes and reads are free of
-                // bank conflicts.  Rows are private to the wave and LDS
-                // operations of one wave complete in order: no barrier.
+            auto load_v = [&](TileRegs &r, int t0) {
+                const char *p = vbase + tile_base(t0, r.vmask);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if constexpr (KV8) r.v[i] = load8_stream(p + i * tok_stride);
+                    else r.v[i] = load16_stream(p + i * tok_stride);
+                }
+            };
+            // S^T of one tile: K rows -> LDS (16-byte chunks XOR-swizzled by
+            // token), read back so that lane (q, c) holds token c, chunks
+            // 4j + q; four MFMAs against the query operand.  Rows are private
+            // to the wave and its LDS operations complete in order.
+            auto tile_scores = [&](const TileRegs &r) -> f32x4_t {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int tt = 4 * q + i;
                     u32x4 krow;
                     if constexpr (KV8) krow = widen_e4m3<DT>(r.k[i]); else krow = r.k[i];
-                    *reinterpret_cast<u32x4 *>(ktile + tt * ROW_BYTES + ((c ^ tt) & 15) * 16) = krow;
+                    *reinterpret_cast<u32x4 *>(kt + tt * ROW_BYTES + ((c ^ tt) & 15) * 16) = krow;
                 }
-                u32x4 kop[4];
+                asm volatile("" ::: "memory");
+                f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    kop[j] = *reinterpret_cast<const u32x4 *>(ktile + c * ROW_BYTES + (((4 * j + q) ^ c) & 15) * 16);
-                // The reference max of a lane's row group moves only when a
-                // score passes it by more than kMaxSlack, so the accumulator
-                // rescale (a multiply per accumulator) is skipped in nearly
-                // every tile; the merges weight each state by its own
-                // (max, normaliser), so any reference gives the same result.
-                float p[NSET][4], alpha[NSET];
-                bool bump_any = false;
-#pragma unroll
-                for (int set = 0; set < NSET; ++set) {
-                    f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        sacc = mfma_16x16x32<DT>(kop[j], kQopInLds ? s_qop[set][j][lane] : qop[set][j], sacc);
-                    float sv[4];
-                    float mt = -INFINITY;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        sv[i] = (t0 + 4 * q + i < seg_end) ? sacc[i] * sl2 : -INFINITY;
-                        mt = fmaxf(mt, sv[i]);
-                    }
-                    const bool bump = mt > m[set] + kMaxSlack;  // m = -inf: any valid score
-                    alpha[set] = !bump ? 1.f : (m[set] == -INFINITY ? 0.f : fast_exp2(m[set] - mt));
-                    m[set] = bump ? mt : m[set];
-                    bump_any |= bump;
-                    // m = -inf only while the row group has seen no valid
-                    // score: then every score here is masked and 2^(-inf) = 0
-                    const float mref = m[set] == -INFINITY ? 0.f : m[set];
-                    float ps = 0.f;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        p[set][i] = fast_exp2(sv[i] - mref);
-                        ps += p[set][i];
-                    }
-                    l[set] = l[set] * alpha[set] + ps;
+                for (int j = 0; j < 4; ++j) {
+                    const u32x4 kop =
+                        *reinterpret_cast<const u32x4 *>(kt + c * ROW_BYTES + (((4 * j + q) ^ c) & 15) * 16);
+                    sacc = mfma_16x16x32<DT>(kop, qop[j], sacc);
                 }
-                if (__builtin_amdgcn_ballot_w64(bump_any)) {
-#pragma unroll
-                    for (int g = 0; g < G; ++g) {
-                        const float ag = head_bcast<HS>(alpha[g / HS], g % HS);
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) acc[g][e] *= ag;
-                    }
-                }
+                asm volatile("" ::: "memory");
+                return sacc;
+            };
+            // softmax and value product of the pair (tiles A, B at t0, t0 + 16)
+            // whose scores are sa, sb
+            auto pair_values = [&](const f32x4_t sa, const f32x4_t sb, const TileRegs &ra,
+                                   const TileRegs &rb, int t0) {
+                float sc[8];  // tokens t0 + 4q + i (i < 4), t0 + 16 + 4q + i - 4 (i >= 4)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    float vf[8];
-                    if constexpr (KV8) {
-                        const u32x2 vw = (r.vmask >> i) & 1u ? r.v[i] : u32x2{0, 0};
-                        e4m3x4_to_f32(vw.x, vf);
-                        e4m3x4_to_f32(vw.y, vf + 4);
-                    } else {
-                        unpack16<DT>((r.vmask >> i) & 1u ? r.v[i] : u32x4{0, 0, 0, 0}, vf);
+                    sc[i] = sa[i] * sl2;
+                    sc[4 + i] = sb[i] * sl2;
+                }
+                if (t0 + 2 * TILE > seg_end) {  // wave-uniform: only at the end of a segment
+                    asm volatile("" ::: "memory");
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        sc[i] = (t0 + 4 * q + i < seg_end) ? sc[i] : -INFINITY;
+                        sc[4 + i] = (t0 + TILE + 4 * q + i < seg_end) ? sc[4 + i] : -INFINITY;
+                    }
+                }
+                float mx = sc[0];
+#pragma unroll
+                for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sc[i]);
+                mx = rowgroup_max(mx);
+                const bool bump = mx > m + kMaxSlack;  // m = -inf: any valid score
+                if (__builtin_amdgcn_ballot_w64(bump)) {
+                    const float alpha = !bump ? 1.f : (m == -INFINITY ? 0.f : fast_exp2(m - mx));
+                    m = bump ? mx : m;
+                    lsum *= alpha;
+#pragma unroll
+                    for (int dt = 0; dt < 8; ++dt) acc[dt] *= alpha;
+                }
+                // m = -inf only while the column has seen no valid score:
+                // every score here is then masked and 2^(-inf - 0) = 0
+                const float mref = m == -INFINITY ? 0.f : m;
+                float ps = 0.f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    sc[i] = fast_exp2(sc[i] - mref);
+                    ps += sc[i];
+                }
+                lsum += ps;
+                u32x4 ph, pl;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    uint32_t hi, lo;
+                    split_pack<DT>(sc[2 * w], sc[2 * w + 1], hi, lo);
+                    ph[w] = hi;
+                    pl[w] = lo;
+                }
+
+                // value operands: this lane's V rows (tokens 4q + i of tiles A
+                // and B, dims 8c..8c+7); invalid rows (past the segment, bad
+                // page) become zeros, since a zero probability times a NaN
+                // row would still be NaN
+                using VRow = std::conditional_t<KV8, u32x2, u32x4>;
+                VRow va[4], vb[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    va[i] = ra.v[i];
+                    vb[i] = rb.v[i];
+                }
+                if (__builtin_amdgcn_ballot_w64((ra.vmask & rb.vmask) != 0xFu)) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        va[i] = (ra.vmask >> i) & 1u ? va[i] : VRow{};
+                        vb[i] = (rb.vmask >> i) & 1u ? vb[i] : VRow{};
+                    }
+                }
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    // word w of each row (dims 8c + 2w, + 1) in 16-bit form
+                    uint32_t xa[4], xb[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        if constexpr (KV8) {
+                            xa[i] = (w & 1) ? e4m3_pair<DT, true>(w < 2 ? va[i].x : va[i].y)
+                                            : e4m3_pair<DT, false>(w < 2 ? va[i].x : va[i].y);
+                            xb[i] = (w & 1) ? e4m3_pair<DT, true>(w < 2 ? vb[i].x : vb[i].y)
+                                            : e4m3_pair<DT, false>(w < 2 ? vb[i].x : vb[i].y);
+                        } else {
+                            xa[i] = va[i][w];
+                            xb[i] = vb[i][w];
+                        }
                     }
 #pragma unroll
-                    for (int g = 0; g < G; ++g) {
-                        const float pg = head_bcast<HS>(p[g / HS][i], g % HS);
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(pg, vf[e], acc[g][e]);
+                    for (int odd = 0; odd < 2; ++odd) {
+                        // dim 8c + 2w + odd: v_perm pairs the 16-bit halves
+                        // of two tokens
+                        const int dt = 2 * w + odd;
+                        const uint32_t sel = odd ? 0x07060302u : 0x05040100u;
+                        u32x4 vop;
+                        vop[0] = __builtin_amdgcn_perm(xa[1], xa[0], sel);
+                        vop[1] = __builtin_amdgcn_perm(xa[3], xa[2], sel);
+                        vop[2] = __builtin_amdgcn_perm(xb[1], xb[0], sel);
+                        vop[3] = __builtin_amdgcn_perm(xb[3], xb[2], sel);
+                        acc[dt] = mfma_16x16x32<DT>(vop, ph, acc[dt]);
+                        acc[dt] = mfma_16x16x32<DT>(vop, pl, acc[dt]);
                     }
                 }
             };
 
-            // Each wave step issues the loads of TPS consecutive tiles at
-            // once and then computes them in order, so up to TPS * 8 KiB of
-            // HBM requests per wave are in flight while earlier tiles are
-            // computed.  Straight-line code: the compiler waits for exactly
-            // the loads a tile needs.  A tile past the segment is all
-            // invalid and computes to no change.
-            constexpr int TPS = KV8 ? (G == 8 ? 2 : PKV_TILES_PER_STEP_E4M3)
-                                    : (G == 8 ? 1 : PKV_TILES_PER_STEP);  // register budget
             constexpr int STEP = kNumWaves * TILE * TPS;
+            // Each wave step issues the loads of TPS consecutive tiles at
+            // once, then computes them pair by pair.  A tile past the
+            // segment is all invalid and computes to no change.
             for (int t = seg + wave * TILE * TPS; t < seg_end; t += STEP) {
                 TileRegs r[TPS];
 #pragma unroll
-                for (int i = 0; i < TPS; ++i) load_tile(r[i], t + i * TILE);
-                // keep every load of the step ahead of the compute: left
-                // alone, the scheduler sinks each load next to its use and
-                // the wave then waits on one load at a time
+                for (int i = 0; i < TPS; ++i) {
+                    load_k(r[i], t + i * TILE);
+                    load_v(r[i], t + i * TILE);
+                }
+                // keep every load of the step ahead of the compute
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int i = 0; i < TPS; ++i) compute_tile(r[i], t + i * TILE);
-            }
-        }
-
-        // merge the four row groups q of this wave (lanes c, c+16, c+32, c+48)
-        float f[NSET];
-#pragma unroll
-        for (int set = 0; set < NSET; ++set) {
-            float M = fmaxf(m[set], __shfl_xor(m[set], 16));
-            M = fmaxf(M, __shfl_xor(M, 32));
-            f[set] = (M == -INFINITY) ? 0.f : fast_exp2(m[set] - M);
-            float L = l[set] * f[set];
-            L += __shfl_xor(L, 16);
-            L += __shfl_xor(L, 32);
-            m[set] = M;
-            l[set] = L;
-        }
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const float fg = head_bcast<HS>(f[g / HS], g % HS);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float x = acc[g][e] * fg;
-                x += __shfl_xor(x, 16);
-                x += __shfl_xor(x, 32);
-                acc[g][e] = x;
-            }
-        }
-        if (q == 0) {
-#pragma unroll
-            for (int g = 0; g < G; ++g)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) s_acc[wave][g][c * 8 + e] = acc[g][e];
-            if (c < HS) {
-#pragma unroll
-                for (int set = 0; set < NSET; ++set) {
-                    s_m[wave][set * HS + c] = m[set];
-                    s_l[wave][set * HS + c] = l[set];
+                for (int i = 0; i < TPS; i += 2) {
+                    const f32x4_t sa = tile_scores(r[i]);
+                    const f32x4_t sb = tile_scores(r[i + 1]);
+                    pair_values(sa, sb, r[i], r[i + 1], t + i * TILE);
                 }
             }
         }
+
+        // the column's normaliser is the sum over the four row groups; lanes
+        // (q, c < G) hold head c's dims 32q + 8r + dt in acc[dt][r]
+        const float L = rowgroup_sum(lsum);
+        float *wacc = reinterpret_cast<float *>(kt);
+        if (c < G) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float *dst = wacc + c * D + 32 * q + 8 * r;
+                *reinterpret_cast<f32x4_t *>(dst) = f32x4_t{acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
+                *reinterpret_cast<f32x4_t *>(dst + 4) = f32x4_t{acc[4][r], acc[5][r], acc[6][r], acc[7][r]};
+            }
+            if (q == 0) {
+                s_m[wave][c] = m;
+                s_l[wave][c] = L;
+            }
+        }
         __syncthreads();
-        unit_epilogue<DT, D, G, PFX>(a, u, u.bad_len || s_bad != 0, s_m, s_l, s_acc,
-                                     KV8 ? a.v_scale[u.kvh] : 1.f);
+        unit_epilogue<DT, D, G, PFX, kRegion / 4>(a, u, u.bad_len || s_bad != 0, s_m, s_l,
+                                                         reinterpret_cast<const float *>(&s_region[0][0]),
+                                                         KV8 ? a.v_scale[u.kvh] : 1.f);
     }
 }
 

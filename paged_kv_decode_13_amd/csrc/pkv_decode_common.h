@@ -134,11 +134,12 @@ __device__ __forceinline__ void store_out(const DecodeArgs &a, int64_t idx, floa
 
 // Merge the per-wave states (running max m, normaliser l, unnormalised
 // accumulator) of one unit and store either the final output (one partition)
-// or the partition's normalised partial with its (m, l).
-template <int DT, int D, int G, bool PFX = false>
+// or the partition's normalised partial with its (m, l).  Wave w's
+// accumulator of head g is s_acc[w * WS + g * D + 0 .. D - 1].
+template <int DT, int D, int G, bool PFX = false, int WS = G * D>
 __device__ __forceinline__ void unit_epilogue(const DecodeArgs &a, const Unit &u, bool bad,
                                               const float (*s_m)[G], const float (*s_l)[G],
-                                              const float (*s_acc)[G][D], float vscale = 1.f) {
+                                              const float *s_acc, float vscale = 1.f) {
     const int h0 = u.kvh * G;
     for (int i = threadIdx.x; i < G * D; i += kThreads) {
         const int g = i / D;
@@ -151,7 +152,7 @@ __device__ __forceinline__ void unit_epilogue(const DecodeArgs &a, const Unit &u
         for (int w = 0; w < kNumWaves; ++w) {
             const float f = (M == -INFINITY) ? 0.f : fast_exp2(s_m[w][g] - M);
             L += s_l[w][g] * f;
-            O += s_acc[w][g][d] * f;
+            O += s_acc[w * WS + g * D + d] * f;
         }
         const int h = h0 + g;
         if constexpr (PFX) {

@@ -24,4 +24,44 @@ __device__ __forceinline__ f32x4_t mfma_16x16x32(const u32x4 a, const u32x4 b, f
                                                       __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
 
+// Max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the four row
+// groups of an MFMA column) with the gfx950 lane-swap instructions: each
+// swap hands a lane its partner's value, so both steps stay on the VALU with
+// no LDS round trip, and every lane of the four ends with the same result.
+__device__ __forceinline__ float rowgroup_max(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rowgroup_sum(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Two probabilities -> packed 16-bit pairs (hi, lo) with hi + lo = p to
+// about 16 (bf16: hardware round-to-nearest-even both times) or 21 (fp16:
+// hardware pack with round toward zero; the remainder carries the rest)
+// significant bits.
+template <int DT>
+__device__ __forceinline__ void split_pack(float p0, float p1, uint32_t &hi, uint32_t &lo) {
+    if constexpr (DT == kBF16) {
+        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+        const bf16x2_t h = {(__bf16)p0, (__bf16)p1};
+        hi = __builtin_bit_cast(uint32_t, h);
+        const float r0 = p0 - __uint_as_float(hi << 16);
+        const float r1 = p1 - __uint_as_float(hi & 0xffff0000u);
+        const bf16x2_t l = {(__bf16)r0, (__bf16)r1};
+        lo = __builtin_bit_cast(uint32_t, l);
+    } else {
+        const auto h = __builtin_amdgcn_cvt_pkrtz(p0, p1);
+        hi = __builtin_bit_cast(uint32_t, h);
+        const float r0 = p0 - (float)h[0];
+        const float r1 = p1 - (float)h[1];
+        lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(r0, r1));
+    }
+}
+
 }  // namespace pkv

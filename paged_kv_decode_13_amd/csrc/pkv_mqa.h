@@ -15,7 +15,7 @@
 //    so the product keeps about 16 (bf16) or 21 (fp16) bits of p and the
 //    accumulation is fp32.
 //  - One reference max per row, shared by the row's four lane groups (two
-//    lane shuffles per chunk), so every probability of a chunk is relative to
+//    lane swaps per chunk), so every probability of a chunk is relative to
 //    the same max and the value product can sum across lane groups.  It
 //    moves only when passed by more than 2^kMaxSlack, so the accumulators
 //    are rarely rescaled.
@@ -44,29 +44,6 @@ struct MqaLds {
 // so that the transposing writes (rows 8c + e) and the operand reads (rows
 // 16 dt + i) both spread over the LDS banks.
 __device__ __forceinline__ int vt_swz(int d, int col) { return col ^ ((d ^ (d >> 3)) & 7); }
-
-// Two probabilities -> packed 16-bit pairs (hi, lo) with hi + lo = p to
-// about 16 (bf16: hardware round-to-nearest-even both times) or 21 (fp16:
-// hardware pack with round toward zero; the remainder carries the rest)
-// significant bits.
-template <int DT>
-__device__ __forceinline__ void split_pack(float p0, float p1, uint32_t &hi, uint32_t &lo) {
-    if constexpr (DT == kBF16) {
-        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-        const bf16x2_t h = {(__bf16)p0, (__bf16)p1};
-        hi = __builtin_bit_cast(uint32_t, h);
-        const float r0 = p0 - __uint_as_float(hi << 16);
-        const float r1 = p1 - __uint_as_float(hi & 0xffff0000u);
-        const bf16x2_t l = {(__bf16)r0, (__bf16)r1};
-        lo = __builtin_bit_cast(uint32_t, l);
-    } else {
-        const auto h = __builtin_amdgcn_cvt_pkrtz(p0, p1);
-        hi = __builtin_bit_cast(uint32_t, h);
-        const float r0 = p0 - (float)h[0];
-        const float r1 = p1 - (float)h[1];
-        lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(r0, r1));
-    }
-}
 
 // Stage the four tokens 4 lg .. 4 lg + 3 of a chunk that this thread loaded
 // (16-byte chunk lc of each row): K rows into kt, V transposed into vt.  V
@@ -154,8 +131,7 @@ __device__ __forceinline__ void mqa_chunk(const char *kt, const char *vt, const 
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) mx = fmaxf(mx, sc[tt][rr]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = rowgroup_max(mx);
     // m = -inf until the row has seen a valid token
     const bool bump = mx > st.m + kMaxSlack;
     if (__builtin_amdgcn_ballot_w64(bump)) {
@@ -197,10 +173,7 @@ __device__ __forceinline__ void mqa_chunk(const char *kt, const char *vt, const 
 }
 
 // The row's normaliser: the sum of the four lane groups' shares.
-__device__ __forceinline__ float mqa_row_sum(const MqaRowState &st) {
-    float L = st.lsum + __shfl_xor(st.lsum, 16);
-    return L + __shfl_xor(L, 32);
-}
+__device__ __forceinline__ float mqa_row_sum(const MqaRowState &st) { return rowgroup_sum(st.lsum); }
 
 // Workgroup id -> unit so that consecutive units share an XCD (consecutive
 // workgroup ids are dealt to the 8 XCDs in turn); a bijection on [0, n).
