@@ -206,13 +206,10 @@ __global__ __launch_bounds__(kThreads) void paged_decode_valu_kernel(DecodeArgs 
     unit_epilogue<DT, D, G>(a, up, up.bad_len || s_bad != 0, s_m, s_l, &s_acc[0][0][0]);
 }
 
-// Log-sum-exp merge of the partitions of one (sequence, query head):
-// with partition p holding normalised output o_p, running max m_p and
-// normaliser l_p (exp2 domain), out = sum_p w_p o_p / sum_p w_p,
-// w_p = l_p * 2^(m_p - max_q m_q).
+// Log-sum-exp merge of the partitions of one (sequence, query head), one
+// workgroup each (sequences with one partition were written directly).
 template <int DT, int D>
-__global__ __launch_bounds__(kWave) void lse_merge_kernel(DecodeArgs a) {
-    constexpr int PER_LANE = D / kWave;
+__global__ __launch_bounds__(kThreads) void lse_merge_kernel(DecodeArgs a) {
     const int s = blockIdx.x / a.num_heads;
     const int h = blockIdx.x % a.num_heads;
     const int ctx = a.context_lens[s];
@@ -220,24 +217,8 @@ __global__ __launch_bounds__(kWave) void lse_merge_kernel(DecodeArgs a) {
     int nparts = (ctx + a.partition_size - 1) / a.partition_size;
     if (nparts <= 1) return;                       // written directly
     nparts = min(nparts, a.num_partitions);
-    const int64_t base = ((int64_t)s * a.num_heads + h) * a.num_partitions;
-    const int lane = threadIdx.x;
-
-    float M = -INFINITY;
-    for (int p = 0; p < nparts; ++p) M = fmaxf(M, a.part_ml[(base + p) * 2]);
-    float L = 0.f, O[PER_LANE];
-#pragma unroll
-    for (int j = 0; j < PER_LANE; ++j) O[j] = 0.f;
-    for (int p = 0; p < nparts; ++p) {
-        const float w = a.part_ml[(base + p) * 2 + 1] * fast_exp2(a.part_ml[(base + p) * 2] - M);
-        L += w;
-#pragma unroll
-        for (int j = 0; j < PER_LANE; ++j) O[j] = fmaf(w, a.part_out[(base + p) * D + lane + j * kWave], O[j]);
-    }
-    const float inv = 1.f / L;
-#pragma unroll
-    for (int j = 0; j < PER_LANE; ++j)
-        store_out<DT>(a, ((int64_t)s * a.num_heads + h) * D + lane + j * kWave, O[j] * inv);
+    const int64_t row = (int64_t)s * a.num_heads + h;
+    merge_partials<DT, D>(a, row * a.num_partitions, nparts, row * D);
 }
 
 template <int DT, int D, int G>
@@ -263,7 +244,7 @@ template <int DT, int D>
 static hipError_t launch_merge(const DecodeArgs &a, hipStream_t stream) {
     if (a.num_partitions <= 1) return hipSuccess;
     const int64_t rows = (int64_t)a.num_seqs * a.num_heads;
-    hipLaunchKernelGGL((lse_merge_kernel<DT, D>), dim3((unsigned)rows), dim3(kWave), 0, stream, a);
+    hipLaunchKernelGGL((lse_merge_kernel<DT, D>), dim3((unsigned)rows), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -53,6 +53,12 @@
 #ifndef PKV_TILES_PER_STEP_E4M3
 #define PKV_TILES_PER_STEP_E4M3 2
 #endif
+#ifndef PKV_WG_PER_CU
+#define PKV_WG_PER_CU 2
+#endif
+#ifndef PKV_WG_PER_CU_E4M3
+#define PKV_WG_PER_CU_E4M3 8
+#endif
 
 namespace pkv {
 
@@ -126,6 +132,32 @@ __device__ __forceinline__ void build_unit_order(const DecodeArgs &a, int *s_pf,
     __syncthreads();
 }
 
+// Unit index -> (sequence, partition, KV head) and its token range, from the
+// prefix sums of build_unit_order (KV head fastest, full partitions first).
+// The fields are wave-uniform; readfirstlane keeps them in scalar registers.
+template <bool PFX>
+__device__ __forceinline__ void decode_unit(const DecodeArgs &a, const int *s_pf, const int *s_pp,
+                                            const int *s_ctx, int unit, Unit &u) {
+    const int total_full = s_pf[a.num_seqs];
+    u.kvh = unit % a.num_kv_heads;
+    const int sp = unit / a.num_kv_heads;
+    if (sp < total_full) {
+        u.s = search_le(s_pf, a.num_seqs, sp);
+        u.p = sp - s_pf[u.s];
+    } else {
+        u.s = search_le(s_pp, a.num_seqs, sp - total_full);
+        u.p = seq_full<PFX>(a, s_ctx[u.s]);
+    }
+    u.s = __builtin_amdgcn_readfirstlane(u.s);
+    u.p = __builtin_amdgcn_readfirstlane(u.p);
+    u.ctx = __builtin_amdgcn_readfirstlane(s_ctx[u.s]);
+    u.bad_len = bad_context(a, u.ctx);
+    u.tok_begin = first_token<PFX>(a) + u.p * a.partition_size;
+    u.tok_end = u.bad_len ? 0 : min(u.ctx, u.tok_begin + a.partition_size);
+    u.nparts = seq_parts<PFX>(a, u.ctx);
+    u.empty = false;
+}
+
 // Units are handed out one at a time from a counter in the workspace, so a
 // workgroup that drew short units simply takes more: with a static
 // assignment the chip idles while the unluckiest workgroups finish.  Every
@@ -148,21 +180,7 @@ __device__ __forceinline__ bool draw_unit(const DecodeArgs &a, const int *s_pf, 
     __syncthreads();
     const int unit = *s_unit;
     if (unit >= total_units) return false;
-    u.kvh = unit % a.num_kv_heads;
-    const int sp = unit / a.num_kv_heads;
-    if (sp < total_full) {
-        u.s = search_le(s_pf, a.num_seqs, sp);
-        u.p = sp - s_pf[u.s];
-    } else {
-        u.s = search_le(s_pp, a.num_seqs, sp - total_full);
-        u.p = seq_full<PFX>(a, s_ctx[u.s]);
-    }
-    u.ctx = s_ctx[u.s];
-    u.bad_len = bad_context(a, u.ctx);
-    u.tok_begin = first_token<PFX>(a) + u.p * a.partition_size;
-    u.tok_end = u.bad_len ? 0 : min(u.ctx, u.tok_begin + a.partition_size);
-    u.nparts = seq_parts<PFX>(a, u.ctx);
-    u.empty = false;
+    decode_unit<PFX>(a, s_pf, s_pp, s_ctx, unit, u);
     return true;
 }
 
@@ -215,6 +233,9 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
     // operand transpose), then the wave's accumulators for the epilogue
     constexpr int kRegion = TILE * ROW_BYTES;
     static_assert(G * D * 4 <= kRegion, "accumulators fit the wave's region");
+    // With more tiles per step the query operand moves to LDS to free its
+    // 16 registers for loads in flight
+    constexpr bool kQopLds = TPS > 2;
 
     extern __shared__ int s_dyn[];     // full-unit prefix [B + 1], partial-unit prefix [B + 1], lengths [B]
     __shared__ int s_pages[kSegPages];
@@ -222,6 +243,7 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
     __shared__ float s_m[kNumWaves][G];
     __shared__ float s_l[kNumWaves][G];
     __shared__ __attribute__((aligned(16))) char s_region[kNumWaves][kRegion];
+    __shared__ u32x4 s_qop[kQopLds ? 4 : 1][kWave];
 
     int *s_pf = s_dyn;
     int *s_pp = s_dyn + a.num_seqs + 1;
@@ -248,12 +270,17 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
 
         // query operand: head h0 + c % G, chunks 4j + q
         const int h0 = u.kvh * G;
-        u32x4 qop[4];
+        u32x4 qop[4];  // in registers, or parked in LDS (kQopLds) and read per tile
         {
             const char *row = reinterpret_cast<const char *>(a.query) +
                               ((int64_t)u.s * a.num_heads + h0 + c % G) * ROW_BYTES;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) qop[j] = load16(row + (4 * j + q) * 16);
+            for (int j = 0; j < 4; ++j) {
+                qop[j] = load16(row + (4 * j + q) * 16);
+                // every wave of the unit holds the same operand: wave 0 parks
+                // it before the segment loop's first barrier
+                if (kQopLds && wave == 0) s_qop[j][lane] = qop[j];
+            }
         }
 
         float m = -INFINITY;  // reference max of column c (equal in the four row groups)
@@ -310,20 +337,25 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
             // 4j + q; four MFMAs against the query operand.  Rows are private
             // to the wave and its LDS operations complete in order.
             auto tile_scores = [&](const TileRegs &r) -> f32x4_t {
+                // E4M3 rows stay 8-bit in LDS (8-byte chunks, 128-byte rows)
+                // and are widened after the read, one operand at a time
+                constexpr int LROW = KV8 ? D : ROW_BYTES;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int tt = 4 * q + i;
-                    u32x4 krow;
-                    if constexpr (KV8) krow = widen_e4m3<DT>(r.k[i]); else krow = r.k[i];
-                    *reinterpret_cast<u32x4 *>(kt + tt * ROW_BYTES + ((c ^ tt) & 15) * 16) = krow;
+                    char *dst = kt + tt * LROW + ((c ^ tt) & 15) * KV_CHUNK;
+                    if constexpr (KV8) *reinterpret_cast<u32x2 *>(dst) = r.k[i];
+                    else *reinterpret_cast<u32x4 *>(dst) = r.k[i];
                 }
                 asm volatile("" ::: "memory");
                 f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const u32x4 kop =
-                        *reinterpret_cast<const u32x4 *>(kt + c * ROW_BYTES + (((4 * j + q) ^ c) & 15) * 16);
-                    sacc = mfma_16x16x32<DT>(kop, qop[j], sacc);
+                    const char *src = kt + c * LROW + (((4 * j + q) ^ c) & 15) * KV_CHUNK;
+                    u32x4 kop;
+                    if constexpr (KV8) kop = widen_e4m3<DT>(*reinterpret_cast<const u32x2 *>(src));
+                    else kop = *reinterpret_cast<const u32x4 *>(src);
+                    sacc = mfma_16x16x32<DT>(kop, kQopLds ? s_qop[j][lane] : qop[j], sacc);
                 }
                 asm volatile("" ::: "memory");
                 return sacc;
@@ -473,10 +505,10 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
     }
 }
 
-// Persistent grid: as many workgroups as are resident at once (queried once
-// per kernel and LDS size), capped by the number of units.
+// Persistent grid: as many workgroups as are resident at once (occupancy
+// query), at most max_per_cu per CU, capped by the number of units.
 template <typename K>
-static hipError_t launch_persistent(K kernel, const DecodeArgs &a, hipStream_t stream) {
+static hipError_t launch_persistent(K kernel, const DecodeArgs &a, int max_per_cu, hipStream_t stream) {
     const size_t dyn = (size_t)(3 * a.num_seqs + 2) * sizeof(int);
     int dev = 0, cus = 0, per_cu = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -485,6 +517,7 @@ static hipError_t launch_persistent(K kernel, const DecodeArgs &a, hipStream_t s
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(kernel),
                                                          kThreads, dyn);
     if (e != hipSuccess) return e;
+    if (per_cu > max_per_cu) per_cu = max_per_cu;
     int64_t grid = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
     const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * a.num_partitions;  // upper bound
     if (grid > units) grid = units;
@@ -492,13 +525,19 @@ static hipError_t launch_persistent(K kernel, const DecodeArgs &a, hipStream_t s
     return hipGetLastError();
 }
 
+// Resident workgroups per CU.  Past a point more requests in flight only
+// queue at HBM: with 16-bit caches two workgroups per CU (up to 128 KiB of
+// loads in flight per CU) already reach the bandwidth the access pattern
+// allows, and a third one measured 1-4% slower; an E4M3 step carries half
+// the bytes, so that path keeps every resident workgroup.
 template <int DT, bool PFX, bool KV8 = false>
 static hipError_t launch_group(const DecodeArgs &a, hipStream_t stream) {
+    const int cap = KV8 ? PKV_WG_PER_CU_E4M3 : PKV_WG_PER_CU;
     switch (a.num_heads / a.num_kv_heads) {
-        case 1: return launch_persistent(paged_decode_mfma_kernel<DT, 1, PFX, KV8>, a, stream);
-        case 2: return launch_persistent(paged_decode_mfma_kernel<DT, 2, PFX, KV8>, a, stream);
-        case 4: return launch_persistent(paged_decode_mfma_kernel<DT, 4, PFX, KV8>, a, stream);
-        case 8: return launch_persistent(paged_decode_mfma_kernel<DT, 8, PFX, KV8>, a, stream);
+        case 1: return launch_persistent(paged_decode_mfma_kernel<DT, 1, PFX, KV8>, a, cap, stream);
+        case 2: return launch_persistent(paged_decode_mfma_kernel<DT, 2, PFX, KV8>, a, cap, stream);
+        case 4: return launch_persistent(paged_decode_mfma_kernel<DT, 4, PFX, KV8>, a, cap, stream);
+        case 8: return launch_persistent(paged_decode_mfma_kernel<DT, 8, PFX, KV8>, a, cap, stream);
         default: return hipErrorInvalidValue;
     }
 }

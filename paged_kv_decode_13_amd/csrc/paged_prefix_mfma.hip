@@ -163,36 +163,18 @@ __global__ __launch_bounds__(kThreads) void paged_prefix_mfma_kernel(PrefixArgs 
 // Log-sum-exp merge of every partial slot of one (sequence, query head):
 // the prefix splits, then the suffix partitions.  Writes every output.
 template <int DT>
-__global__ __launch_bounds__(kWave) void prefix_merge_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads) void prefix_merge_kernel(DecodeArgs a) {
     constexpr int D = 128;
-    constexpr int PER_LANE = D / kWave;
     const int s = blockIdx.x / a.num_heads;
     const int h = blockIdx.x % a.num_heads;
-    const int lane = threadIdx.x;
     const int ctx = a.context_lens[s];
-    const int64_t obase = ((int64_t)s * a.num_heads + h) * D;
+    const int64_t row = (int64_t)s * a.num_heads + h;
     if (bad_context(a, ctx) || ctx == 0) {
         const float v = ctx == 0 ? 0.f : __builtin_nanf("");
-#pragma unroll
-        for (int jj = 0; jj < PER_LANE; ++jj) store_out<DT>(a, obase + lane + jj * kWave, v);
+        for (int d = threadIdx.x; d < D; d += kThreads) store_out<DT>(a, row * D + d, v);
         return;
     }
-    const int n = a.part_base + seq_parts<true>(a, ctx);
-    const int64_t base = ((int64_t)s * a.num_heads + h) * a.part_stride;
-    float M = -INFINITY;
-    for (int p = 0; p < n; ++p) M = fmaxf(M, a.part_ml[(base + p) * 2]);
-    float L = 0.f, O[PER_LANE];
-#pragma unroll
-    for (int jj = 0; jj < PER_LANE; ++jj) O[jj] = 0.f;
-    for (int p = 0; p < n; ++p) {
-        const float w = a.part_ml[(base + p) * 2 + 1] * fast_exp2(a.part_ml[(base + p) * 2] - M);
-        L += w;
-#pragma unroll
-        for (int jj = 0; jj < PER_LANE; ++jj) O[jj] = fmaf(w, a.part_out[(base + p) * D + lane + jj * kWave], O[jj]);
-    }
-    const float inv = 1.f / L;
-#pragma unroll
-    for (int jj = 0; jj < PER_LANE; ++jj) store_out<DT>(a, obase + lane + jj * kWave, O[jj] * inv);
+    merge_partials<DT, D>(a, row * a.part_stride, a.part_base + seq_parts<true>(a, ctx), row * D);
 }
 
 template <int DT>
@@ -207,7 +189,7 @@ static hipError_t launch_all(const PrefixArgs &p, const DecodeArgs &a, hipStream
     hipError_t e = launch_paged_decode_mfma_suffix(a, DT, stream);
     if (e != hipSuccess || a.fold_prefix) return e;
     const int64_t rows = (int64_t)a.num_seqs * a.num_heads;
-    hipLaunchKernelGGL(prefix_merge_kernel<DT>, dim3((unsigned)rows), dim3(kWave), 0, stream, a);
+    hipLaunchKernelGGL(prefix_merge_kernel<DT>, dim3((unsigned)rows), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
