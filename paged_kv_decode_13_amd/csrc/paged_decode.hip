@@ -207,9 +207,10 @@ __global__ __launch_bounds__(kThreads) void paged_decode_valu_kernel(DecodeArgs 
 }
 
 // Log-sum-exp merge of the partitions of one (sequence, query head), one
-// workgroup each (sequences with one partition were written directly).
-template <int DT, int D>
-__global__ __launch_bounds__(kThreads) void lse_merge_kernel(DecodeArgs a) {
+// workgroup of NW waves each (sequences with one partition were written
+// directly).
+template <int DT, int D, int NW>
+__global__ __launch_bounds__(NW * kWave) void lse_merge_kernel(DecodeArgs a) {
     const int s = blockIdx.x / a.num_heads;
     const int h = blockIdx.x % a.num_heads;
     const int ctx = a.context_lens[s];
@@ -218,7 +219,7 @@ __global__ __launch_bounds__(kThreads) void lse_merge_kernel(DecodeArgs a) {
     if (nparts <= 1) return;                       // written directly
     nparts = min(nparts, a.num_partitions);
     const int64_t row = (int64_t)s * a.num_heads + h;
-    merge_partials<DT, D>(a, row * a.num_partitions, nparts, row * D);
+    merge_partials<DT, D, NW>(a, row * a.num_partitions, nparts, row * D);
 }
 
 template <int DT, int D, int G>
@@ -244,7 +245,10 @@ template <int DT, int D>
 static hipError_t launch_merge(const DecodeArgs &a, hipStream_t stream) {
     if (a.num_partitions <= 1) return hipSuccess;
     const int64_t rows = (int64_t)a.num_seqs * a.num_heads;
-    hipLaunchKernelGGL((lse_merge_kernel<DT, D>), dim3((unsigned)rows), dim3(kThreads), 0, stream, a);
+    if (a.num_partitions >= kMergeWideFrom)
+        hipLaunchKernelGGL((lse_merge_kernel<DT, D, kNumWaves>), dim3((unsigned)rows), dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL((lse_merge_kernel<DT, D, 1>), dim3((unsigned)rows), dim3(kWave), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -162,8 +162,8 @@ __global__ __launch_bounds__(kThreads) void paged_prefix_mfma_kernel(PrefixArgs 
 
 // Log-sum-exp merge of every partial slot of one (sequence, query head):
 // the prefix splits, then the suffix partitions.  Writes every output.
-template <int DT>
-__global__ __launch_bounds__(kThreads) void prefix_merge_kernel(DecodeArgs a) {
+template <int DT, int NW>
+__global__ __launch_bounds__(NW * kWave) void prefix_merge_kernel(DecodeArgs a) {
     constexpr int D = 128;
     const int s = blockIdx.x / a.num_heads;
     const int h = blockIdx.x % a.num_heads;
@@ -171,10 +171,10 @@ __global__ __launch_bounds__(kThreads) void prefix_merge_kernel(DecodeArgs a) {
     const int64_t row = (int64_t)s * a.num_heads + h;
     if (bad_context(a, ctx) || ctx == 0) {
         const float v = ctx == 0 ? 0.f : __builtin_nanf("");
-        for (int d = threadIdx.x; d < D; d += kThreads) store_out<DT>(a, row * D + d, v);
+        for (int d = threadIdx.x; d < D; d += NW * kWave) store_out<DT>(a, row * D + d, v);
         return;
     }
-    merge_partials<DT, D>(a, row * a.part_stride, a.part_base + seq_parts<true>(a, ctx), row * D);
+    merge_partials<DT, D, NW>(a, row * a.part_stride, a.part_base + seq_parts<true>(a, ctx), row * D);
 }
 
 template <int DT>
@@ -189,7 +189,10 @@ static hipError_t launch_all(const PrefixArgs &p, const DecodeArgs &a, hipStream
     hipError_t e = launch_paged_decode_mfma_suffix(a, DT, stream);
     if (e != hipSuccess || a.fold_prefix) return e;
     const int64_t rows = (int64_t)a.num_seqs * a.num_heads;
-    hipLaunchKernelGGL(prefix_merge_kernel<DT>, dim3((unsigned)rows), dim3(kThreads), 0, stream, a);
+    if (a.part_stride >= kMergeWideFrom)
+        hipLaunchKernelGGL((prefix_merge_kernel<DT, kNumWaves>), dim3((unsigned)rows), dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL((prefix_merge_kernel<DT, 1>), dim3((unsigned)rows), dim3(kWave), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -205,51 +205,62 @@ __device__ __forceinline__ void unit_epilogue(const DecodeArgs &a, const Unit &u
 // Log-sum-exp join of the n partial results in slots base .. base + n - 1
 // (normalised output o_p, max m_p and normaliser l_p in the exp2 domain):
 // out = sum_p w_p o_p / sum_p w_p with w_p = l_p 2^(m_p - max_q m_q), stored at
-// out[out_idx .. + D).  One workgroup: all threads find the max, then wave w
-// joins partials w, w + 4, ... (lane: dims lane + 64 j), several partials'
-// loads in flight at once, and the four waves' sums are added in LDS.  A NaN
-// max (bad page) makes its weight and so the output NaN.
-template <int DT, int D>
+// out[out_idx .. + D).  A workgroup of NW waves: all threads find the max,
+// then wave w joins partials w, w + NW, ... (lane: dims lane + 64 j) with
+// several partials' loads in flight, and with NW > 1 the waves' sums are
+// added in LDS.  A NaN max (bad page) makes its weight and so the output
+// NaN.
+template <int DT, int D, int NW>
 __device__ __forceinline__ void merge_partials(const DecodeArgs &a, int64_t base, int n, int64_t out_idx) {
     constexpr int PL = D / kWave;
-    __shared__ float s_red[kNumWaves];
-    __shared__ float s_lw[kNumWaves];
-    __shared__ float s_ow[kNumWaves][D];
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
-    float mx = -INFINITY;
-    for (int p = tid; p < n; p += kThreads) mx = fmaxf(mx, a.part_ml[(base + p) * 2]);
-    mx = group_max<kWave>(mx);
-    if (lane == 0) s_red[wave] = mx;
-    __syncthreads();
-    float M = s_red[0];
+    float M = -INFINITY;
+    for (int p = tid; p < n; p += NW * kWave) M = fmaxf(M, a.part_ml[(base + p) * 2]);
+    M = group_max<kWave>(M);
+    if constexpr (NW > 1) {
+        __shared__ float s_red[NW];
+        if (lane == 0) s_red[wave] = M;
+        __syncthreads();
+        M = s_red[0];
 #pragma unroll
-    for (int w = 1; w < kNumWaves; ++w) M = fmaxf(M, s_red[w]);
+        for (int w = 1; w < NW; ++w) M = fmaxf(M, s_red[w]);
+    }
     float L = 0.f, O[PL];
 #pragma unroll
     for (int j = 0; j < PL; ++j) O[j] = 0.f;
-#pragma unroll 4
-    for (int p = wave; p < n; p += kNumWaves) {
+#pragma unroll 8
+    for (int p = wave; p < n; p += NW) {
         const float w = a.part_ml[(base + p) * 2 + 1] * fast_exp2(a.part_ml[(base + p) * 2] - M);
         L += w;
 #pragma unroll
         for (int j = 0; j < PL; ++j) O[j] = fmaf(w, a.part_out[(base + p) * D + lane + j * kWave], O[j]);
     }
+    if constexpr (NW == 1) {
 #pragma unroll
-    for (int j = 0; j < PL; ++j) s_ow[wave][lane + j * kWave] = O[j];
-    if (lane == 0) s_lw[wave] = L;
-    __syncthreads();
-    for (int d = tid; d < D; d += kThreads) {
-        float o = 0.f, l = 0.f;
+        for (int j = 0; j < PL; ++j) store_out<DT>(a, out_idx + lane + j * kWave, O[j] / L);
+    } else {
+        __shared__ float s_lw[NW];
+        __shared__ float s_ow[NW][D];
 #pragma unroll
-        for (int w = 0; w < kNumWaves; ++w) {
-            o += s_ow[w][d];
-            l += s_lw[w];
+        for (int j = 0; j < PL; ++j) s_ow[wave][lane + j * kWave] = O[j];
+        if (lane == 0) s_lw[wave] = L;
+        __syncthreads();
+        for (int d = tid; d < D; d += NW * kWave) {
+            float o = 0.f, l = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                o += s_ow[w][d];
+                l += s_lw[w];
+            }
+            store_out<DT>(a, out_idx + d, o / l);
         }
-        store_out<DT>(a, out_idx + d, o / l);
     }
 }
+// Waves per merge workgroup: one while a row has few partials; four once
+// it has many, so that each wave's loads fit in a couple of round trips.
+constexpr int kMergeWideFrom = 32;
 
 // MFMA decode kernel launcher (16-bit caches, head_dim 128); the merge
 // kernel is launched by the caller.
