@@ -34,11 +34,14 @@ namespace pkv {
 constexpr int kPfxMaxSplitTokens = 2048;  // matches the host-side plan
 constexpr int kPfxMaxSplitPages = kPfxMaxSplitTokens / 4;
 
+// Three workgroups per CU (<= 168 VGPRs, one 32 KiB LDS chunk buffer each).
 template <int DT>
-__global__ __launch_bounds__(kThreads) void paged_prefix_mfma_kernel(PrefixArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8)))
+void paged_prefix_mfma_kernel(PrefixArgs a) {
     constexpr int D = 128;
     constexpr int ROW = kMqaRowBytes;
-    __shared__ __attribute__((aligned(16))) MqaLds s_buf;
+    __shared__ __attribute__((aligned(16))) char s_k[kMqaChunk * kMqaRowBytes];  // K rows of a chunk
+    __shared__ __attribute__((aligned(16))) char s_vt[128 * kMqaVtRow];           // V^T of a chunk
     __shared__ int s_pages[kPfxMaxSplitPages];
     __shared__ int s_badtok;
 
@@ -126,23 +129,21 @@ __global__ __launch_bounds__(kThreads) void paged_prefix_mfma_kernel(PrefixArgs 
     MqaRowState st;
     mqa_init(st);
 
-    // Chunk n is computed from LDS buffer n % 2 while chunk n + 1 is in
-    // flight in registers; loads are unconditional (a chunk past the split
-    // reads page-0 rows and stages zeros) so that the compiler counts
-    // outstanding loads exactly.
+    // Chunk n is computed from the LDS buffer while chunk n + 1 is in flight
+    // in registers (two barriers per chunk); loads are unconditional (a
+    // chunk past the split reads page-0 rows and stages zeros) so that the
+    // compiler counts outstanding loads exactly.
     const int nch = (tok_end - tok_begin + kMqaChunk - 1) / kMqaChunk;
     u32x4 kr[4], vr[4];
     uint32_t ok = load_chunk(tok_begin, kr, vr);
-    mqa_store_chunk(s_buf.k[0], s_buf.vt[0], lc, lg, kr, vr, ok);
-    __syncthreads();
     for (int n = 0; n < nch; ++n) {
         const int t0 = tok_begin + n * kMqaChunk;
+        mqa_store_chunk(s_k, s_vt, lc, lg, kr, vr, ok);
+        __syncthreads();
         ok = load_chunk(t0 + kMqaChunk, kr, vr);
         // keep the next chunk's loads ahead of this chunk's compute
         __builtin_amdgcn_sched_barrier(0);
-        mqa_chunk<DT>(s_buf.k[n & 1], s_buf.vt[n & 1], qop, j, q, t0, lim, t0 + kMqaChunk > wlim,
-                      a.scale_log2e, st);
-        mqa_store_chunk(s_buf.k[(n + 1) & 1], s_buf.vt[(n + 1) & 1], lc, lg, kr, vr, ok);
+        mqa_chunk<DT>(s_k, s_vt, qop, j, q, t0, lim, t0 + kMqaChunk > wlim, a.scale_log2e, st);
         __syncthreads();
     }
 

@@ -34,12 +34,6 @@ constexpr int kMqaChunk = 64;                       // tokens per LDS chunk
 constexpr int kMqaRowBytes = 256;                   // one 16-bit K or V row (D = 128)
 constexpr int kMqaVtRow = kMqaChunk * 2;            // bytes of one transposed-V row
 
-// Double-buffered LDS chunk: K rows and transposed V.
-struct MqaLds {
-    char k[2][kMqaChunk * kMqaRowBytes];
-    char vt[2][128 * kMqaVtRow];
-};
-
 // 16-byte column of transposed-V row d that holds column `col`: XOR swizzle
 // so that the transposing writes (rows 8c + e) and the operand reads (rows
 // 16 dt + i) both spread over the LDS banks.
