@@ -371,11 +371,15 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
                     sc[4 + i] = sb[i] * sl2;
                 }
                 if (t0 + 2 * TILE > seg_end) {  // wave-uniform: only at the end of a segment
-                    asm volatile("" ::: "memory");
+                    // tokens of this lane before the end; the count passes
+                    // through an empty asm inside the branch, so the compares
+                    // cannot be hoisted out of it
+                    int nv = seg_end - (t0 + 4 * q);
+                    asm volatile("" : "+v"(nv));
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        sc[i] = (t0 + 4 * q + i < seg_end) ? sc[i] : -INFINITY;
-                        sc[4 + i] = (t0 + TILE + 4 * q + i < seg_end) ? sc[4 + i] : -INFINITY;
+                        sc[i] = (i < nv) ? sc[i] : -INFINITY;
+                        sc[4 + i] = (TILE + i < nv) ? sc[4 + i] : -INFINITY;
                     }
                 }
                 float mx = sc[0];

@@ -113,13 +113,16 @@ __device__ __forceinline__ void mqa_chunk(const char *kt, const char *vt, const 
         for (int rr = 0; rr < 4; ++rr) sc[tt][rr] = sacc[rr] * sl2;
     }
     if (masked) {
-        // the empty asm keeps this a branch: full chunks skip the masking
-        asm volatile("" ::: "memory");
+        // tokens left of this lane's row limit: the count passes through an
+        // empty asm inside the branch, so the compares cannot be hoisted
+        // out of it and full chunks skip the masking
+        int nv = lim - (t0 + 4 * q);
+        asm volatile("" : "+v"(nv));
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr)
-                sc[tt][rr] = (t0 + tt * 16 + 4 * q + rr < lim) ? sc[tt][rr] : -INFINITY;
+                sc[tt][rr] = (tt * 16 + rr < nv) ? sc[tt][rr] : -INFINITY;
     }
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
