@@ -11,13 +11,13 @@
 // query i at position p = ctx - q_len + i attends to tokens 0..p through the
 // sequence's block table.
 //
-// Work unit = (sequence, KV head, tile of 64 query rows); a query row is one
-// (query token, head of the group) pair, so a tile holds 64 / G consecutive
-// query tokens.  Each unit streams the visible history [0, last position of
-// the tile] through the chunk machinery of pkv_mqa.h (64 tokens at a time,
-// K row-wise and V transposed in LDS, scores and values as MFMA products);
-// each row masks the tokens past its own position, so only the chunks on the
-// tile's diagonal carry masking work.  Page ids are staged in LDS 512 at a
+// Work unit = (sequence, KV head, tile of kPflRows = 128 query rows, 32 per
+// wave); a query row is one (query token, head of the group) pair, so a tile
+// holds 128 / G consecutive query tokens.  Each unit streams the visible
+// history [0, last position of the tile] through the chunk machinery of
+// pkv_mqa.h (64 tokens at a time, K row-wise and V transposed in LDS, scores
+// and values as MFMA products); each row masks the tokens past its own
+// position, so only the chunks on the tile's diagonal carry masking work.  Page ids are staged in LDS 512 at a
 // time.  The output is written directly (no partials): a unit sees all of
 // its rows' history.
 //
@@ -32,24 +32,28 @@
 namespace pkv {
 
 constexpr int kPflSegPages = 512;  // page ids staged in LDS at a time
+constexpr int kPflRows = kNumWaves * 16 * kPrefillBlocks;  // query rows per tile
 
 
 
-// 64-row tiles of a sequence; 0 when its query range lies outside
+// Row tiles of a sequence; 0 when its query range lies outside
 // [0, total_queries] (such rows are never read or written).
 __device__ __forceinline__ int prefill_tiles(const PrefillArgs &a, int s, int &q0, int &q_len) {
     q0 = a.query_start_loc[s];
     const int q1 = a.query_start_loc[s + 1];
     q_len = q1 - q0;
     if (q0 < 0 || q1 > a.total_queries || q_len <= 0) return 0;
-    return ((q_len << a.log2_group) + kMqaRows - 1) / kMqaRows;
+    return ((q_len << a.log2_group) + kPflRows - 1) / kPflRows;
 }
 
-// Three workgroups per CU (<= 168 VGPRs, 35 KiB of LDS each) hide the
-// chunk loads' latency better than two with double-buffered LDS (measured
-// 10.9 against 12.8 ms on the 32-prompt workload).
+// One 35 KiB LDS chunk buffer per workgroup, so that LDS never limits the
+// workgroups per CU: with one 16-row block per wave three fit (<= 168
+// VGPRs) and hid the chunk loads' latency better than two with
+// double-buffered LDS (10.9 against 12.8 ms on the 32-prompt workload); two
+// blocks per wave at two workgroups per CU took it to 9.5 ms.
 template <int DT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8)))
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(mqa_waves_per_simd(kPrefillBlocks), 8)))
 void paged_prefill_mfma_kernel(PrefillArgs a) {
     constexpr int D = 128;
     constexpr int ROW = kMqaRowBytes;
@@ -94,34 +98,40 @@ void paged_prefill_mfma_kernel(PrefillArgs a) {
     const bool bad = ctx < 0 || ctx > a.max_context_len ||
                      (int64_t)ctx > (int64_t)a.max_blocks_per_seq * bs || q_len > ctx;
 
-    // this lane's row: query token i of the sequence, head g of the group
+    // this lane's rows, one per column block b: query token i of the
+    // sequence, head g of the group
+    constexpr int NB = kPrefillBlocks;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int j = lane & 15;
     const int q = lane >> 4;
     const int G = 1 << a.log2_group;
     const int nrows = q_len << a.log2_group;
-    const int r = tile * kMqaRows + wave * kMqaWaveRows + j;
-    const bool row_ok = r < nrows;
-    const int i = row_ok ? (r >> a.log2_group) : 0;
-    const int h = kvh * G + (r & (G - 1));
     // the tile's last query sees the most: the unit's token range
-    const int i_last = min(q_len - 1, (tile * kMqaRows + kMqaRows - 1) >> a.log2_group);
+    const int i_last = min(q_len - 1, (tile * kPflRows + kPflRows - 1) >> a.log2_group);
     const int tok_end = bad ? 0 : ctx - q_len + i_last + 1;
-    const int lim = row_ok ? ctx - q_len + i + 1 : tok_end;  // padding rows compute, never store
-    int wlim = lim;
+    bool row_ok[NB];
+    int lim[NB];
+    int64_t qrow[NB];
+    u32x4 qop[NB][4];
+    int wlim = INT_MAX;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        const int r = tile * kPflRows + wave * 16 * NB + b * 16 + j;
+        row_ok[b] = r < nrows;
+        const int i = row_ok[b] ? (r >> a.log2_group) : 0;
+        const int h = kvh * G + (r & (G - 1));
+        lim[b] = row_ok[b] ? ctx - q_len + i + 1 : tok_end;  // padding rows compute, never store
+        wlim = min(wlim, lim[b]);
+        qrow[b] = ((int64_t)(q0 + i) * a.num_heads + h) * D;
+        const char *row = reinterpret_cast<const char *>(a.query) + qrow[b] * 2;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            qop[b][kk] = row_ok[b] ? load16(row + (4 * kk + q) * 16) : u32x4{0, 0, 0, 0};
+    }
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) wlim = min(wlim, __shfl_xor(wlim, off));
     wlim = __builtin_amdgcn_readfirstlane(wlim);
-
-    const int64_t qrow = ((int64_t)(q0 + i) * a.num_heads + h) * D;
-    u32x4 qop[4];
-    {
-        const char *row = reinterpret_cast<const char *>(a.query) + qrow * 2;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-            qop[kk] = row_ok ? load16(row + (4 * kk + q) * 16) : u32x4{0, 0, 0, 0};
-    }
 
     // staging roles as in the shared-prefix kernel
     const int lc = tid & 15;
@@ -132,8 +142,9 @@ void paged_prefill_mfma_kernel(PrefillArgs a) {
     const int64_t lane_off = (int64_t)kvh * ROW + lc * 16;
     const int32_t *table = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
 
-    MqaRowState st;
-    mqa_init(st);
+    MqaRowState st[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) mqa_init(st[b]);
 
     for (int seg = 0; seg < tok_end; seg += kPflSegPages << lbs) {
         const int seg_end = min(tok_end, seg + (kPflSegPages << lbs));
@@ -177,21 +188,23 @@ void paged_prefill_mfma_kernel(PrefillArgs a) {
             __syncthreads();
             ok = load_chunk(t0 + kMqaChunk, kr, vr);
             __builtin_amdgcn_sched_barrier(0);
-            mqa_chunk<DT>(s_k, s_vt, qop, j, q, t0, lim, t0 + kMqaChunk > wlim, a.scale_log2e, st);
+            mqa_chunk<DT, NB>(s_k, s_vt, qop, j, q, t0, lim, t0 + kMqaChunk > wlim, a.scale_log2e, st);
             __syncthreads();
         }
     }
 
-    const float L = mqa_row_sum(st);
-    if (row_ok) {
-        const bool nan = bad || s_badtok < lim;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        const float L = mqa_row_sum(st[b]);
+        if (!row_ok[b]) continue;
+        const bool nan = bad || s_badtok < lim[b];
         const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
-            const int64_t o = qrow + 16 * dt + 4 * q;
+            const int64_t o = qrow[b] + 16 * dt + 4 * q;
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
-                const float v = nan ? __builtin_nanf("") : st.acc[dt][rr] * inv;
+                const float v = nan ? __builtin_nanf("") : st[b].acc[dt][rr] * inv;
                 if (a.out_f32)
                     reinterpret_cast<float *>(a.out)[o + rr] = v;
                 else
@@ -205,7 +218,7 @@ template <int DT>
 static hipError_t launch_dt(const PrefillArgs &a, hipStream_t stream) {
     // upper bound of the units: each sequence's last tile may be partial
     const int64_t rows = ((int64_t)a.total_queries << a.log2_group);
-    const int64_t units = ((rows + kMqaRows - 1) / kMqaRows + a.num_seqs) * a.num_kv_heads;
+    const int64_t units = ((rows + kPflRows - 1) / kPflRows + a.num_seqs) * a.num_kv_heads;
     if (units == 0) return hipSuccess;
     const size_t dyn = (size_t)(a.num_seqs + 1) * sizeof(int);
     hipLaunchKernelGGL(paged_prefill_mfma_kernel<DT>, dim3((unsigned)units), dim3(kThreads), dyn,

@@ -14,9 +14,9 @@
 // table 读取历史 KV cache", section "从 gather 后的 K/V 做 attention") over
 // tables whose first prefix_len / block_size entries are the shared pages.
 //
-// Work unit = (KV head, prefix split, block of 64 query rows); a query row
-// is one (sequence, head of the group) pair, rows ordered sequence-major, so
-// the 16 rows of one wave span several sequences.  The 64-token chunks of
+// Work unit = (KV head, prefix split, block of kPrefixRowsPerBlock query
+// rows); a query row is one (sequence, head of the group) pair, rows ordered
+// sequence-major, so the 16 rows of one wave span several sequences.  The 64-token chunks of
 // the split go through the LDS machinery of pkv_mqa.h (K row-wise, V
 // transposed, scores and values as MFMA products, a shared reference max
 // per row); the next chunk's loads are in flight while the current one is
@@ -34,9 +34,11 @@ namespace pkv {
 constexpr int kPfxMaxSplitTokens = 2048;  // matches the host-side plan
 constexpr int kPfxMaxSplitPages = kPfxMaxSplitTokens / 4;
 
-// Three workgroups per CU (<= 168 VGPRs, one 32 KiB LDS chunk buffer each).
+// One 16-row block per wave, three workgroups per CU (<= 168 VGPRs, one
+// 32 KiB LDS chunk buffer each).
 template <int DT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8)))
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(mqa_waves_per_simd(kPrefixBlocks), 8)))
 void paged_prefix_mfma_kernel(PrefixArgs a) {
     constexpr int D = 128;
     constexpr int ROW = kMqaRowBytes;
@@ -60,26 +62,32 @@ void paged_prefix_mfma_kernel(PrefixArgs a) {
 
     const int tid = threadIdx.x;
 
-    // this lane's query row (MFMA column j) and how far into the prefix it
-    // sees; its loads are issued before the page-id staging so that the two
-    // round trips overlap
+    // this lane's query rows (MFMA column j of each column block b) and how
+    // far into the prefix they see; their loads are issued before the
+    // page-id staging so that the two round trips overlap
+    constexpr int NB = kPrefixBlocks;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int j = lane & 15;
     const int q = lane >> 4;
     const int G = 1 << a.log2_group;
     const int nrows = a.num_seqs << a.log2_group;
-    const int r = rb * kMqaRows + wave * kMqaWaveRows + j;
-    const bool row_ok = r < nrows;
-    const int s = row_ok ? (r >> a.log2_group) : 0;
-    const int h = kvh * G + (r & (G - 1));
-    const int ctx = row_ok ? a.context_lens[s] : tok_end;  // padding rows compute, never store
-    u32x4 qop[4];
-    {
-        const char *row = reinterpret_cast<const char *>(a.query) + ((int64_t)s * a.num_heads + h) * ROW;
+    bool row_ok[NB];
+    int64_t hrow[NB];  // (sequence, query head) row of the output and partials
+    int ctx[NB];
+    u32x4 qop[NB][4];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        const int r = rb * kPrefixRowsPerBlock + wave * 16 * NB + b * 16 + j;
+        row_ok[b] = r < nrows;
+        const int s = row_ok[b] ? (r >> a.log2_group) : 0;
+        const int h = kvh * G + (r & (G - 1));
+        hrow[b] = (int64_t)s * a.num_heads + h;
+        ctx[b] = row_ok[b] ? a.context_lens[s] : tok_end;  // padding rows compute, never store
+        const char *row = reinterpret_cast<const char *>(a.query) + hrow[b] * ROW;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
-            qop[kk] = row_ok ? load16(row + (4 * kk + q) * 16) : u32x4{0, 0, 0, 0};
+            qop[b][kk] = row_ok[b] ? load16(row + (4 * kk + q) * 16) : u32x4{0, 0, 0, 0};
     }
 
     if (tid == 0) s_badtok = INT_MAX;
@@ -94,8 +102,13 @@ void paged_prefix_mfma_kernel(PrefixArgs a) {
     }
     __syncthreads();
 
-    const int lim = min(max(ctx, 0), tok_end);  // tokens t < lim are this row's
-    int wlim = lim;  // smallest limit over the wave's rows
+    int lim[NB];  // tokens t < lim are the row's
+    int wlim = INT_MAX;  // smallest limit over the wave's rows
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        lim[b] = min(max(ctx[b], 0), tok_end);
+        wlim = min(wlim, lim[b]);
+    }
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) wlim = min(wlim, __shfl_xor(wlim, off));
     wlim = __builtin_amdgcn_readfirstlane(wlim);
@@ -126,8 +139,9 @@ void paged_prefix_mfma_kernel(PrefixArgs a) {
         return ok ? 0xFu : 0u;
     };
 
-    MqaRowState st;
-    mqa_init(st);
+    MqaRowState st[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) mqa_init(st[b]);
 
     // Chunk n is computed from the LDS buffer while chunk n + 1 is in flight
     // in registers (two barriers per chunk); loads are unconditional (a
@@ -143,19 +157,21 @@ void paged_prefix_mfma_kernel(PrefixArgs a) {
         ok = load_chunk(t0 + kMqaChunk, kr, vr);
         // keep the next chunk's loads ahead of this chunk's compute
         __builtin_amdgcn_sched_barrier(0);
-        mqa_chunk<DT>(s_k, s_vt, qop, j, q, t0, lim, t0 + kMqaChunk > wlim, a.scale_log2e, st);
+        mqa_chunk<DT, NB>(s_k, s_vt, qop, j, q, t0, lim, t0 + kMqaChunk > wlim, a.scale_log2e, st);
         __syncthreads();
     }
 
-    const float L = mqa_row_sum(st);
-    if (row_ok) {
-        const int64_t slot = ((int64_t)s * a.num_heads + h) * a.part_stride + split;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        const float L = mqa_row_sum(st[b]);
+        if (!row_ok[b]) continue;
+        const int64_t slot = hrow[b] * a.part_stride + split;
         const float inv = L > 0.f ? 1.f / L : 0.f;
         float *po = a.part_out + slot * D + 4 * q;
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4_t *>(po + 16 * dt) = st.acc[dt] * inv;
+        for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4_t *>(po + 16 * dt) = st[b].acc[dt] * inv;
         if (q == 0) {
-            a.part_ml[slot * 2] = s_badtok < lim ? __builtin_nanf("") : st.m;
+            a.part_ml[slot * 2] = s_badtok < lim[b] ? __builtin_nanf("") : st[b].m;
             a.part_ml[slot * 2 + 1] = L;
         }
     }

@@ -37,9 +37,9 @@ int32_t num_partitions(int32_t max_context_len, int32_t partition_size) {
     return (int32_t)(((int64_t)max_context_len + partition_size - 1) / partition_size);
 }
 
-// Shared-prefix plan: 64-query-row blocks per KV head, and the prefix cut
-// into splits of whole 64-token chunks (at most 2048 tokens each) so that
-// about kPrefixTargetUnits workgroups share the prefix work.
+// Shared-prefix plan: blocks of kPrefixRowsPerBlock query rows per KV head, and
+// the prefix cut into splits of whole 64-token chunks (at most 2048 tokens
+// each) so that about kPrefixTargetUnits workgroups share the prefix work.
 constexpr int32_t kPrefixChunk = 64;
 constexpr int32_t kPrefixMaxSplitChunks = 32;
 #ifndef PKV_PFX_TARGET_UNITS
@@ -56,7 +56,7 @@ PrefixPlan prefix_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads
                        int32_t max_context_len, int32_t prefix_len, int32_t partition_size) {
     PrefixPlan p;
     const int64_t rows = (int64_t)num_seqs * (num_heads / num_kv_heads);
-    p.row_blocks = (int32_t)((rows + 63) / 64);
+    p.row_blocks = (int32_t)((rows + pkv::kPrefixRowsPerBlock - 1) / pkv::kPrefixRowsPerBlock);
     p.num_splits = 0;
     p.split_tokens = kPrefixChunk;
     if (prefix_len > 0) {

@@ -1,7 +1,9 @@
 // Chunk machinery shared by the multi-query MFMA kernels (the shared-prefix
-// kernel and the prefill kernel): a workgroup of four waves holds 64 query
-// rows (16 per wave, one MFMA column block) and streams the K/V rows of one
-// KV head through LDS 64 tokens at a time, 16-bit caches, head_dim 128.
+// kernel and the prefill kernel): a workgroup of four waves holds
+// 4 x 16 x NB query rows (NB MFMA column blocks of 16 rows per wave) and
+// streams the K/V rows of one KV head through LDS 64 tokens at
+// a time, 16-bit caches, head_dim 128.  Every K or V operand a wave reads
+// from LDS feeds the MFMAs of all its column blocks.
 //
 //  - K keeps its row layout in LDS (16-byte chunks XOR-swizzled by token);
 //    the score MFMA reads lane (i, q) = token i, head-dim chunk 4kk + q, and
@@ -28,8 +30,9 @@
 
 namespace pkv {
 
-constexpr int kMqaWaveRows = 16;                    // query rows per wave
-constexpr int kMqaRows = kNumWaves * kMqaWaveRows;  // query rows per workgroup
+// Register budget of a kernel with NB column blocks per wave: three waves
+// per SIMD with one block, two with two.
+constexpr int mqa_waves_per_simd(int nb) { return nb == 1 ? 3 : 2; }
 constexpr int kMqaChunk = 64;                       // tokens per LDS chunk
 constexpr int kMqaRowBytes = 256;                   // one 16-bit K or V row (D = 128)
 constexpr int kMqaVtRow = kMqaChunk * 2;            // bytes of one transposed-V row
@@ -92,79 +95,101 @@ __device__ __forceinline__ void mqa_init(MqaRowState &st) {
 }
 
 // One 64-token chunk (tokens t0 .. t0 + 63 staged in kt / vt) for this
-// wave's 16 rows.  Row j sees tokens t < lim; `masked` (wave-uniform) says
-// some token of the chunk lies past some row's limit.
-template <int DT>
-__device__ __forceinline__ void mqa_chunk(const char *kt, const char *vt, const u32x4 (&qop)[4],
-                                          int j, int q, int t0, int lim, bool masked, float sl2,
-                                          MqaRowState &st) {
-    float sc[4][4];  // [16-token tile][r]: token tile*16 + 4q + r, row j
-    float mx = -INFINITY;
+// wave's NB column blocks of 16 rows.  Row j of block b sees tokens
+// t < lim[b]; `masked` (wave-uniform) says some token of the chunk lies past
+// some row's limit.
+template <int DT, int NB>
+__device__ __forceinline__ void mqa_chunk(const char *kt, const char *vt, const u32x4 (&qop)[NB][4],
+                                          int j, int q, int t0, const int (&lim)[NB], bool masked,
+                                          float sl2, MqaRowState (&st)[NB]) {
+    float sc[NB][4][4];  // [block][16-token tile][r]: token tile*16 + 4q + r, row j
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
-        f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+        f32x4_t sacc[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) sacc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             const u32x4 kop = *reinterpret_cast<const u32x4 *>(
                 kt + (tt * 16 + j) * kMqaRowBytes + (((4 * kk + q) ^ j) & 15) * 16);
-            sacc = mfma_16x16x32<DT>(kop, qop[kk], sacc);
+#pragma unroll
+            for (int b = 0; b < NB; ++b) sacc[b] = mfma_16x16x32<DT>(kop, qop[b][kk], sacc[b]);
         }
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) sc[tt][rr] = sacc[rr] * sl2;
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) sc[b][tt][rr] = sacc[b][rr] * sl2;
     }
     if (masked) {
-        // tokens left of this lane's row limit: the count passes through an
-        // empty asm inside the branch, so the compares cannot be hoisted
-        // out of it and full chunks skip the masking
-        int nv = lim - (t0 + 4 * q);
-        asm volatile("" : "+v"(nv));
+        // tokens left of this lane's row limits: the counts pass through an
+        // empty asm inside the branch, so the compares cannot be hoisted out
+        // of it and full chunks skip the masking
+        int nv[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            nv[b] = lim[b] - (t0 + 4 * q);
+            asm volatile("" : "+v"(nv[b]));
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr)
+                    sc[b][tt][rr] = (tt * 16 + rr < nv[b]) ? sc[b][tt][rr] : -INFINITY;
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        float mx = -INFINITY;
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr)
-                sc[tt][rr] = (tt * 16 + rr < nv) ? sc[tt][rr] : -INFINITY;
-    }
+            for (int rr = 0; rr < 4; ++rr) mx = fmaxf(mx, sc[b][tt][rr]);
+        mx = rowgroup_max(mx);
+        // m = -inf until the row has seen a valid token
+        const bool bump = mx > st[b].m + kMaxSlack;
+        if (__builtin_amdgcn_ballot_w64(bump)) {
+            const float alpha = !bump ? 1.f : (st[b].m == -INFINITY ? 0.f : fast_exp2(st[b].m - mx));
+            st[b].m = bump ? mx : st[b].m;
+            st[b].lsum *= alpha;
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) mx = fmaxf(mx, sc[tt][rr]);
-    mx = rowgroup_max(mx);
-    // m = -inf until the row has seen a valid token
-    const bool bump = mx > st.m + kMaxSlack;
-    if (__builtin_amdgcn_ballot_w64(bump)) {
-        const float alpha = !bump ? 1.f : (st.m == -INFINITY ? 0.f : fast_exp2(st.m - mx));
-        st.m = bump ? mx : st.m;
-        st.lsum *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) st.acc[dt] *= alpha;
-    }
-    // a row with m = -inf has only masked scores here: 2^(-inf - 0) = 0
-    const float mref = st.m == -INFINITY ? 0.f : st.m;
-    float ps = 0.f;
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            sc[tt][rr] = fast_exp2(sc[tt][rr] - mref);
-            ps += sc[tt][rr];
+            for (int dt = 0; dt < 8; ++dt) st[b].acc[dt] *= alpha;
         }
-    st.lsum += ps;
+        // a row with m = -inf has only masked scores here: 2^(-inf - 0) = 0
+        const float mref = st[b].m == -INFINITY ? 0.f : st[b].m;
+        float ps = 0.f;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                sc[b][tt][rr] = fast_exp2(sc[b][tt][rr] - mref);
+                ps += sc[b][tt][rr];
+            }
+        st[b].lsum += ps;
+    }
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
         // B operand: tokens (tile 2bb, 4q + e) for e < 4, (tile 2bb+1, 4q + e - 4) after
-        uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
-        split_pack<DT>(sc[2 * bb][0], sc[2 * bb][1], h0, l0);
-        split_pack<DT>(sc[2 * bb][2], sc[2 * bb][3], h1, l1);
-        split_pack<DT>(sc[2 * bb + 1][0], sc[2 * bb + 1][1], h2, l2);
-        split_pack<DT>(sc[2 * bb + 1][2], sc[2 * bb + 1][3], h3, l3);
-        const u32x4 ph = {h0, h1, h2, h3};
-        const u32x4 pl = {l0, l1, l2, l3};
+        u32x4 ph[NB], pl[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
+            split_pack<DT>(sc[b][2 * bb][0], sc[b][2 * bb][1], h0, l0);
+            split_pack<DT>(sc[b][2 * bb][2], sc[b][2 * bb][3], h1, l1);
+            split_pack<DT>(sc[b][2 * bb + 1][0], sc[b][2 * bb + 1][1], h2, l2);
+            split_pack<DT>(sc[b][2 * bb + 1][2], sc[b][2 * bb + 1][3], h3, l3);
+            ph[b] = u32x4{h0, h1, h2, h3};
+            pl[b] = u32x4{l0, l1, l2, l3};
+        }
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
             const int d = 16 * dt + j;
             const u32x4 vop = *reinterpret_cast<const u32x4 *>(vt + d * kMqaVtRow + vt_swz(d, bb * 4 + q) * 16);
-            st.acc[dt] = mfma_16x16x32<DT>(vop, ph, st.acc[dt]);
-            st.acc[dt] = mfma_16x16x32<DT>(vop, pl, st.acc[dt]);
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                st[b].acc[dt] = mfma_16x16x32<DT>(vop, ph[b], st[b].acc[dt]);
+                st[b].acc[dt] = mfma_16x16x32<DT>(vop, pl[b], st[b].acc[dt]);
+            }
         }
     }
 }
