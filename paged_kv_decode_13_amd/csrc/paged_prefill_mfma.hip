@@ -59,7 +59,7 @@ void paged_prefill_mfma_kernel(PrefillArgs a) {
     constexpr int ROW = kMqaRowBytes;
     extern __shared__ int s_tpre[];  // [B + 1]: exclusive prefix sum of tiles
     __shared__ __attribute__((aligned(16))) char s_k[kMqaChunk * kMqaRowBytes];  // K rows of a chunk
-    __shared__ __attribute__((aligned(16))) char s_vt[128 * kMqaVtRow];           // V^T of a chunk
+    __shared__ __attribute__((aligned(16))) char s_v[kMqaChunk * kMqaVRow];        // V rows of a chunk
     __shared__ int s_pages[kPflSegPages];
     __shared__ int s_scan[kThreads];
     __shared__ int s_badtok;
@@ -184,11 +184,11 @@ void paged_prefill_mfma_kernel(PrefillArgs a) {
         uint32_t ok = load_chunk(seg, kr, vr);
         for (int n = 0; n < nch; ++n) {
             const int t0 = seg + n * kMqaChunk;
-            mqa_store_chunk(s_k, s_vt, lc, lg, kr, vr, ok);
+            mqa_store_chunk(s_k, s_v, lc, lg, kr, vr, ok);
             __syncthreads();
             ok = load_chunk(t0 + kMqaChunk, kr, vr);
             __builtin_amdgcn_sched_barrier(0);
-            mqa_chunk<DT, NB>(s_k, s_vt, qop, j, q, t0, lim, t0 + kMqaChunk > wlim, a.scale_log2e, st);
+            mqa_chunk<DT, NB>(s_k, s_v, qop, j, q, t0, lim, t0 + kMqaChunk > wlim, a.scale_log2e, st);
             __syncthreads();
         }
     }

@@ -43,7 +43,7 @@ void paged_prefix_mfma_kernel(PrefixArgs a) {
     constexpr int D = 128;
     constexpr int ROW = kMqaRowBytes;
     __shared__ __attribute__((aligned(16))) char s_k[kMqaChunk * kMqaRowBytes];  // K rows of a chunk
-    __shared__ __attribute__((aligned(16))) char s_vt[128 * kMqaVtRow];           // V^T of a chunk
+    __shared__ __attribute__((aligned(16))) char s_v[kMqaChunk * kMqaVRow];        // V rows of a chunk
     __shared__ int s_pages[kPfxMaxSplitPages];
     __shared__ int s_badtok;
 
@@ -152,12 +152,12 @@ void paged_prefix_mfma_kernel(PrefixArgs a) {
     uint32_t ok = load_chunk(tok_begin, kr, vr);
     for (int n = 0; n < nch; ++n) {
         const int t0 = tok_begin + n * kMqaChunk;
-        mqa_store_chunk(s_k, s_vt, lc, lg, kr, vr, ok);
+        mqa_store_chunk(s_k, s_v, lc, lg, kr, vr, ok);
         __syncthreads();
         ok = load_chunk(t0 + kMqaChunk, kr, vr);
         // keep the next chunk's loads ahead of this chunk's compute
         __builtin_amdgcn_sched_barrier(0);
-        mqa_chunk<DT, NB>(s_k, s_vt, qop, j, q, t0, lim, t0 + kMqaChunk > wlim, a.scale_log2e, st);
+        mqa_chunk<DT, NB>(s_k, s_v, qop, j, q, t0, lim, t0 + kMqaChunk > wlim, a.scale_log2e, st);
         __syncthreads();
     }
 

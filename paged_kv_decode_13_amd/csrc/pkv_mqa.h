@@ -9,10 +9,15 @@
 //    the score MFMA reads lane (i, q) = token i, head-dim chunk 4kk + q, and
 //    the query operand uses the same chunk order:
 //        S^T[16 tokens x 16 rows] = K[16 x 128] . Q^T[128 x 16].
-//  - V is transposed while it is staged (V^T[d][token], tokens of a 32-token
-//    block interleaved so that one 16-byte read gives a lane the eight tokens
-//    whose probabilities it already holds):
+//  - V also keeps its row layout in LDS, rows padded to 288 bytes, and the
+//    value MFMA reads it transposed with the gfx950 LDS transpose load
+//    (ds_read_b64_tr_b16: within each 16-lane group, output lane 4a + b
+//    receives element b of the 8-byte pieces that lanes a, a + 4, a + 8,
+//    a + 12 point at), so a lane gathers the eight tokens whose
+//    probabilities it already holds from two such loads:
 //        O^T[16 d x 16 rows] += V^T[16 x 32 tokens] . P^T[32 x 16].
+//    The padding puts rows 32 bytes apart in the banks: both the 16-byte
+//    row stores and the transposed loads are free of bank conflicts.
 //    The probabilities enter the 16-bit MFMA as a two-term split p = hi + lo,
 //    so the product keeps about 16 (bf16) or 21 (fp16) bits of p and the
 //    accumulation is fp32.
@@ -35,18 +40,23 @@ namespace pkv {
 constexpr int mqa_waves_per_simd(int nb) { return nb == 1 ? 3 : 2; }
 constexpr int kMqaChunk = 64;                       // tokens per LDS chunk
 constexpr int kMqaRowBytes = 256;                   // one 16-bit K or V row (D = 128)
-constexpr int kMqaVtRow = kMqaChunk * 2;            // bytes of one transposed-V row
+constexpr int kMqaVRow = kMqaRowBytes + 32;        // padded V row in LDS
 
-// 16-byte column of transposed-V row d that holds column `col`: XOR swizzle
-// so that the transposing writes (rows 8c + e) and the operand reads (rows
-// 16 dt + i) both spread over the LDS banks.
-__device__ __forceinline__ int vt_swz(int d, int col) { return col ^ ((d ^ (d >> 3)) & 7); }
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+// Transposed 8-byte LDS load (see the header comment) of the piece at `p`.
+__device__ __forceinline__ u32x2 lds_read_tr16(const char *p) {
+    const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4_t *)(p));
+    return __builtin_bit_cast(u32x2, v);
+}
 
 // Stage the four tokens 4 lg .. 4 lg + 3 of a chunk that this thread loaded
-// (16-byte chunk lc of each row): K rows into kt, V transposed into vt.  V
-// of tokens that are not valid (bit k of `okmask` clear: past the range or
-// on a bad page) is staged as zeros -- a zero probability times a NaN row
-// would still be NaN -- and their scores are masked by the caller.
+// (16-byte chunk lc of each row): K rows into kt (chunks XOR-swizzled by
+// token), V rows into vt (padded rows).  V of tokens that are not valid
+// (bit k of `okmask` clear: past the range or on a bad page) is staged as
+// zeros -- a zero probability times a NaN row would still be NaN -- and
+// their scores are masked by the caller.
 __device__ __forceinline__ void mqa_store_chunk(char *kt, char *vt, int lc, int lg,
                                                 const u32x4 (&kr)[4], const u32x4 (&vin)[4],
                                                 uint32_t okmask) {
@@ -60,24 +70,9 @@ __device__ __forceinline__ void mqa_store_chunk(char *kt, char *vt, int lc, int 
 #pragma unroll
         for (int i = 0; i < 4; ++i) vr[i] = (okmask >> i) & 1u ? vr[i] : u32x4{0, 0, 0, 0};
     }
-    // tokens 4 lg .. +3 sit in block lg / 8 (32 tokens), tile (lg / 4) & 1
-    // of the block, row group lg & 3 of the tile
-    const int col = ((lg >> 3) << 2) | (lg & 3);
-    const int half = (lg >> 2) & 1;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        // word w of a row holds head dims 8 lc + 2w (low half) and + 1 (high
-        // half); gather each across the four tokens: v_perm picks 16-bit
-        // halves of two registers
-        uint2 ev, od;
-        ev.x = __builtin_amdgcn_perm(vr[1][w], vr[0][w], 0x05040100u);
-        ev.y = __builtin_amdgcn_perm(vr[3][w], vr[2][w], 0x05040100u);
-        od.x = __builtin_amdgcn_perm(vr[1][w], vr[0][w], 0x07060302u);
-        od.y = __builtin_amdgcn_perm(vr[3][w], vr[2][w], 0x07060302u);
-        const int d0 = 8 * lc + 2 * w;
-        *reinterpret_cast<uint2 *>(vt + d0 * kMqaVtRow + vt_swz(d0, col) * 16 + half * 8) = ev;
-        *reinterpret_cast<uint2 *>(vt + (d0 + 1) * kMqaVtRow + vt_swz(d0 + 1, col) * 16 + half * 8) = od;
-    }
+    for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<u32x4 *>(vt + (4 * lg + i) * kMqaVRow + lc * 16) = vr[i];
 }
 
 // Running state of one query row (lane j of each lane group q).
@@ -181,10 +176,16 @@ __device__ __forceinline__ void mqa_chunk(const char *kt, const char *vt, const 
             ph[b] = u32x4{h0, h1, h2, h3};
             pl[b] = u32x4{l0, l1, l2, l3};
         }
+        // A operand V^T[16 dt + j][token]: source lane j of row group q
+        // points at head dims 16 dt + 4 (j & 3) .. + 3 of token
+        // 32 bb + 16 h + 4 q + (j >> 2); the load for h = 0 gives the
+        // lane's tokens of tile 2 bb, h = 1 those of tile 2 bb + 1
+        const char *vrow = vt + (32 * bb + 4 * q + (j >> 2)) * kMqaVRow + 8 * (j & 3);
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
-            const int d = 16 * dt + j;
-            const u32x4 vop = *reinterpret_cast<const u32x4 *>(vt + d * kMqaVtRow + vt_swz(d, bb * 4 + q) * 16);
+            const u32x2 v0 = lds_read_tr16(vrow + 32 * dt);
+            const u32x2 v1 = lds_read_tr16(vrow + 16 * kMqaVRow + 32 * dt);
+            const u32x4 vop = u32x4{v0[0], v0[1], v1[0], v1[1]};
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
                 st[b].acc[dt] = mfma_16x16x32<DT>(vop, ph[b], st[b].acc[dt]);
