@@ -10,7 +10,10 @@ paged_kv_decode_13_amd/workloads.py) uploaded to HBM before the timed region.
 Prints ONE JSON line on stdout.  ``value`` is the effective KV-read bandwidth
 of the whole step: sum(ctx) * num_kv_heads * head_dim * 2 * bytes / step time.
 ``roofline`` rates the decode call alone (HIP events on the launch stream)
-against the 8 TB/s HBM peak.  ``cpu_baseline`` is the fp64 oracle timed on a
+against the 8 TB/s HBM peak.  ``cold`` repeats the step with L2 and the MALL
+flushed before each one (a 1 GiB read-modify-write outside the events);
+``stream_read`` times a plain contiguous read (libpkvstream.so) as the
+achievable-read yardstick.  ``cpu_baseline`` is the fp64 oracle timed on a
 bounded sample of the same batch on the host cores.
 
 Usage: python bench.py [--steps K] [--warmup W] [--config gqa_bf16]
@@ -33,6 +36,8 @@ if REPO not in sys.path:
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published
 METRIC = "effective KV-read HBM GB/s (% of MI355X peak) + decode tokens/s, paged attention"
 SHARED_PREFIX_PARTITION = 512
+COLD_FLUSH_BYTES = 1 << 30   # > L2 (4 MiB per XCD) + MALL (256 MiB)
+STREAM_READ_BYTES = 2 << 30  # contiguous buffer of the streaming-read yardstick
 
 
 def log(msg: str) -> None:
@@ -83,7 +88,13 @@ def upload(batch, dev):
     return t
 
 
-def time_steps(batch, t, partition_size: int, steps: int, warmup: int, shared_prefix: bool = False):
+def _pct(xs, p: float) -> float:
+    xs = sorted(xs)
+    return xs[min(len(xs) - 1, int(p * len(xs)))]
+
+
+def time_steps(batch, t, partition_size: int, steps: int, warmup: int, shared_prefix: bool = False,
+               cold_steps: int = 0):
     import torch
 
     import paged_kv_decode_13_amd as pkv
@@ -146,15 +157,79 @@ def time_steps(batch, t, partition_size: int, steps: int, warmup: int, shared_pr
     step_ms = [e[0].elapsed_time(e[2]) for e in evs]
     write_ms = [e[0].elapsed_time(e[1]) for e in evs]
     decode_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    return {
+    res = {
         "ms_per_step": start.elapsed_time(end) / steps,
         "wall_ms_per_step": 1e3 * wall / steps,
         "write_ms": statistics.mean(write_ms),
         "decode_ms": statistics.mean(decode_ms),
         "decode_ms_median": statistics.median(decode_ms),
-        "step_ms_p99": sorted(step_ms)[min(len(step_ms) - 1, int(0.99 * len(step_ms)))],
+        "step_ms_p99": _pct(step_ms, 0.99),
         "out": out,
     }
+    if cold_steps > 0:
+        # cold caches: a 1 GiB read-modify-write before each step evicts L2
+        # and the MALL (tables, workspace, query, recently read pages); it
+        # sits outside the events, on the same stream
+        scratch = torch.zeros(COLD_FLUSH_BYTES // 4, dtype=torch.int32, device=t["q"].device)
+        cevs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(cold_steps)]
+        for e in cevs:
+            scratch.add_(1)
+            e[0].record()
+            write()
+            e[1].record()
+            decode()
+            e[2].record()
+        torch.cuda.synchronize()
+        del scratch
+        c_step = [e[0].elapsed_time(e[2]) for e in cevs]
+        c_dec = [e[1].elapsed_time(e[2]) for e in cevs]
+        res["cold"] = {
+            "steps": cold_steps,
+            "flush_bytes": COLD_FLUSH_BYTES,
+            "step_ms_median": statistics.median(c_step),
+            "step_ms_p99": _pct(c_step, 0.99),
+            "decode_ms_median": statistics.median(c_dec),
+            "decode_ms_p99": _pct(c_dec, 0.99),
+        }
+    return res
+
+
+def stream_read(dev, nbytes: int = STREAM_READ_BYTES, reps: int = 10, warmup: int = 3) -> dict:
+    """The plain streaming-read kernel (libpkvstream.so) over one contiguous
+    buffer: what a simple stream achieves on this GPU, timed with HIP events
+    on the launch stream."""
+    import ctypes
+
+    import torch
+
+    from paged_kv_decode_13_amd import build as pkv_build
+
+    if not os.path.exists(pkv_build.STREAM_LIB_PATH):
+        raise RuntimeError(f"{pkv_build.STREAM_LIB_PATH} is missing; run build() first")
+    lib = ctypes.CDLL(pkv_build.STREAM_LIB_PATH)
+    lib.pkv_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    lib.pkv_stream_read.restype = ctypes.c_int
+    buf = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+    def once():
+        rc = lib.pkv_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), stream)
+        if rc != 0:
+            raise RuntimeError(f"pkv_stream_read failed with status {rc}")
+
+    for _ in range(warmup):
+        once()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        once()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / reps
+    del buf
+    return {"kernel": "stream_read_kernel (contiguous, 16-byte non-temporal loads)",
+            "bytes": nbytes, "ms": round(ms, 5), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 2)}
 
 
 def cpu_baseline(batch, target_s: float):
@@ -358,6 +433,10 @@ def main() -> int:
                          "prefix read once per KV head for the batch)")
     ap.add_argument("--mode", default="decode", choices=["decode", "write", "copy", "prefill"])
     ap.add_argument("--copy-mb", type=int, default=1024)
+    ap.add_argument("--cold-steps", type=int, default=20,
+                    help="steps timed again with L2/MALL flushed before each (0: skip)")
+    ap.add_argument("--no-stream-read", action="store_true",
+                    help="skip the streaming-read yardstick")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -380,10 +459,10 @@ def main() -> int:
     import paged_kv_decode_13_amd as pkv
     from paged_kv_decode_13_amd import workloads as wl
 
-    if not os.path.exists(pkv.library_path()):
-        from paged_kv_decode_13_amd import build
+    from paged_kv_decode_13_amd import build as pkv_build
 
-        build.build()
+    if not (os.path.exists(pkv.library_path()) and os.path.exists(pkv_build.STREAM_LIB_PATH)):
+        pkv_build.build()
     dev = torch.device("cuda:0")
     t0 = time.time()
     if args.config in wl.PREFILL_NAMES:
@@ -426,7 +505,7 @@ def main() -> int:
                 f"({gbs:7.1f} GB/s, {100 * gbs / HBM_PEAK_GBS:5.1f}% of peak), "
                 f"write {r['write_ms']*1e3:6.1f} us")
 
-    r = time_steps(batch, t, ps, args.steps, args.warmup, shared)
+    r = time_steps(batch, t, ps, args.steps, args.warmup, shared, cold_steps=args.cold_steps)
     log(f"[bench] timed {args.steps} steps: {r['ms_per_step']:.4f} ms/step "
         f"(decode {r['decode_ms']:.4f} ms, write {r['write_ms']:.4f} ms)")
 
@@ -490,6 +569,17 @@ def main() -> int:
             "traffic": traffic,
         },
     }
+    if "cold" in r:
+        c = dict(r["cold"])
+        c["decode_gbs_median"] = round(alg_bytes / (c["decode_ms_median"] * 1e-3) / 1e9, 2)
+        c["value_median"] = round(kv_bytes / (c["step_ms_median"] * 1e-3) / 1e9, 2)
+        line["cold"] = {k: (round(v, 5) if isinstance(v, float) else v) for k, v in c.items()}
+    if not args.no_stream_read:
+        sr = stream_read(dev)
+        sr["decode_frac_of_stream"] = round(achieved / sr["gbs"], 4)
+        line["stream_read"] = sr
+        log(f"[bench] stream read {sr['gbs']:.1f} GB/s; decode call at "
+            f"{100 * sr['decode_frac_of_stream']:.1f}% of it")
     if args.block_size is not None or shared:
         line["config"]["unique_kv_bytes"] = batch.kv_bytes_unique()
     if shared:

@@ -252,3 +252,29 @@ def test_no_oracle_in_product_path():
                 text = open(os.path.join(root, f), encoding="utf-8").read()
                 assert not re.search(r"^\s*(import|from)\s+oracle", text, flags=re.M), f
                 assert "liboracle" not in text, f
+
+
+def test_stream_read_library():
+    """libpkvstream.so (the streaming-read yardstick the benchmark times)
+    exports what its header declares and rejects bad arguments before any
+    launch."""
+    from paged_kv_decode_13_amd import build
+
+    if not os.path.exists(build.STREAM_LIB_PATH):
+        build.build()
+    header = open(os.path.join(REPO, "include", "pkv_stream.h"), encoding="utf-8").read()
+    header = re.sub(r"/\*.*?\*/", "", header, flags=re.S)
+    declared = set(re.findall(r"^\s*int\s+(\w+)\s*\(", header, flags=re.M))
+    assert declared == {"pkv_stream_read"}
+    out = subprocess.run(["nm", "-D", "--defined-only", build.STREAM_LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    assert "pkv_stream_read" in set(re.findall(r" T (\w+)$", out, flags=re.M))
+    lib = ctypes.CDLL(build.STREAM_LIB_PATH)
+    f = lib.pkv_stream_read
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    assert f(None, 1024, A, None) == -1      # null source
+    assert f(A, 1024, None, None) == -1      # null sink
+    assert f(A + 8, 1024, A, None) == -1     # misaligned source
+    assert f(A, 1000, A, None) == -1         # not a multiple of 16
+    assert f(A, 0, A, None) == -1            # empty
