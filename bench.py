@@ -263,6 +263,15 @@ def cpu_baseline(batch, target_s: float):
         secs += time.perf_counter() - t0
         passes += 1
     per_pass = secs / passes
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    cpu_model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {
         "value": round(sample.kv_bytes_logical() / per_pass / 1e9, 4),
         "unit": "GB/s",
@@ -272,6 +281,7 @@ def cpu_baseline(batch, target_s: float):
                    f"{sample.total_tokens} context tokens), fp64 gather + softmax attention, "
                    f"{passes} passes in {secs:.1f} s"),
         "tokens_per_s": round(sample.num_seqs / per_pass, 3),
+        "cpu_model": cpu_model,
     }
 
 

@@ -162,6 +162,11 @@ __device__ __forceinline__ void mqa_chunk(const char *kt, const char *vt, const 
             }
         st[b].lsum += ps;
     }
+    // The value MFMAs run at raised wave priority: the SIMD then issues them
+    // as soon as they are ready and fills the matrix pipe's busy cycles with
+    // the other resident wave's softmax (prefill 9.35 -> 8.99 ms on the
+    // 32-prompt workload; priority over the score MFMAs as well: no gain).
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
         // B operand: tokens (tile 2bb, 4q + e) for e < 4, (tile 2bb+1, 4q + e - 4) after
@@ -193,6 +198,7 @@ __device__ __forceinline__ void mqa_chunk(const char *kt, const char *vt, const 
             }
         }
     }
+    __builtin_amdgcn_s_setprio(0);
 }
 
 // The row's normaliser: the sum of the four lane groups' shares.
