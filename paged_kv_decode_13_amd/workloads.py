@@ -324,6 +324,67 @@ def make_batch(context_lens, *, num_heads: int, num_kv_heads: int, head_dim: int
     return batch
 
 
+def make_decode_steps(context_lens, steps: int, *, num_heads: int, num_kv_heads: int,
+                      head_dim: int, block_size: int, dtype: str, seed: int,
+                      kv_dtype: str | None = None, partition_size: int = 0):
+    """Inputs of ``steps`` consecutive decode steps of an engine loop: every
+    sequence appends one token per step.  The token at position p goes to
+    slot table[p // block_size] * block_size + p % block_size, and a sequence
+    whose next position opens a page first takes a fresh page id from a
+    shuffled free list (extra pages, NaN-filled until written), as a block
+    allocator would; the table grows accordingly.
+
+    Returns ``(batch, per_step)``: ``batch`` holds the initial pool and
+    tables (already widened to the final length), and each ``per_step``
+    entry holds that step's ``query``, ``new_key``, ``new_value``,
+    ``slot_mapping`` and the ``block_tables`` / ``context_lens`` after its
+    token is appended (what the decode of that step reads)."""
+    ctx0 = np.asarray(context_lens, dtype=np.int64).reshape(-1)
+    batch = make_batch(ctx0, num_heads=num_heads, num_kv_heads=num_kv_heads, head_dim=head_dim,
+                       block_size=block_size, dtype=dtype, seed=seed, poison=True,
+                       partition_size=partition_size, name="decode_steps", kv_dtype=kv_dtype)
+    cdt = batch.cache_dtype
+    final = ctx0 + steps
+    width = max(1, int(((final + block_size - 1) // block_size).max()))
+    spare = batch.poison_block
+    tables = np.full((ctx0.size, width), spare, np.int32)
+    tables[:, :batch.block_tables.shape[1]] = batch.block_tables
+    # pages the steps open, appended to the pool, NaN until written
+    opened = int(sum(((f + block_size - 1) // block_size) - ((c + block_size - 1) // block_size)
+                     for c, f in zip(ctx0, final)))
+    nb0 = batch.key_cache.shape[0]
+    extra = np.full((opened,) + batch.key_cache.shape[1:], nan_value(cdt), storage_dtype(cdt))
+    batch.key_cache = np.concatenate([batch.key_cache, extra])
+    batch.value_cache = np.concatenate([batch.value_cache, extra.copy()])
+    batch.meta["num_blocks"] = nb0 + opened
+    batch.block_tables = tables.copy()
+    ss = np.random.SeedSequence([seed, 17])
+    s_free, s_steps = ss.spawn(2)
+    free = list(np.random.Generator(np.random.PCG64(s_free)).permutation(
+        np.arange(nb0, nb0 + opened, dtype=np.int32)))
+    ctx = ctx0.copy()
+    b = ctx.size
+    per_step = []
+    for k, sk in enumerate(s_steps.spawn(steps)):
+        s_q, s_nk, s_nv = sk.spawn(3)
+        slots = np.empty(b, np.int64)
+        for s in range(b):
+            pos = int(ctx[s])
+            if pos % block_size == 0:
+                tables[s, pos // block_size] = free.pop()
+            slots[s] = _row_index(tables, s, pos, block_size)
+            ctx[s] += 1
+        per_step.append({
+            "query": _random_storage(s_q, (b, num_heads, head_dim), dtype),
+            "new_key": _random_storage(s_nk, (b, num_kv_heads, head_dim), dtype),
+            "new_value": _random_storage(s_nv, (b, num_kv_heads, head_dim), dtype),
+            "slot_mapping": slots,
+            "block_tables": tables.copy(),
+            "context_lens": ctx.astype(np.int32),
+        })
+    return batch, per_step
+
+
 # ----------------------------------------------------------------------------
 # the five named workloads
 

@@ -622,6 +622,51 @@ def pin_write():
     assert np.array_equal(kc16[3, 1], bits[0]) and np.count_nonzero(kc16) == 4
 
 
+def pin_multistep_engine():
+    """An engine loop of decode steps ([P2] "写入 slot 和读取 block table 必须一致"
+    and "PagedAttention 如何接入 mini vLLM"): each step writes every sequence's
+    new token at its slot -- a fresh page whenever the position opens one --
+    and then decodes.  At every step the paged result must equal attention
+    over the contiguous history grown by appending the same rows, and after
+    the last step the pool holds exactly the initial rows plus the written
+    ones."""
+    from paged_kv_decode_13_amd import workloads as wl
+
+    for dtype, bs in (("f32", 4), ("f16", 4), ("bf16", 8)):
+        batch, steps = wl.make_decode_steps([0, 1, 3, 4, 9, 17], 13, num_heads=8, num_kv_heads=2,
+                                            head_dim=16, block_size=bs, dtype=dtype, seed=31)
+        kc, vc = batch.key_cache.copy(), batch.value_cache.copy()
+        kc0, vc0 = kc.copy(), vc.copy()
+        dec = lambda a: oracle.to_float64(a, dtype)  # noqa: E731
+        # contiguous histories from the initial pool, by plain indexing
+        hist_k, hist_v = [], []
+        for s, c in enumerate(batch.context_lens):
+            rows = [(batch.block_tables[s, t // bs], t % bs) for t in range(int(c))]
+            hist_k.append([dec(kc0[pb, off]) for pb, off in rows])
+            hist_v.append([dec(vc0[pb, off]) for pb, off in rows])
+        written = []
+        for st in steps:
+            oracle.paged_kv_write(st["new_key"], st["new_value"], kc, vc, st["slot_mapping"])
+            written.extend(int(x) for x in st["slot_mapping"])
+            out = oracle.paged_decode(st["query"], kc, vc, st["block_tables"], st["context_lens"], bs,
+                                      batch.scale, dtype)
+            for s in range(batch.num_seqs):
+                hist_k[s].append(dec(st["new_key"][s]))
+                hist_v[s].append(dec(st["new_value"][s]))
+                assert len(hist_k[s]) == int(st["context_lens"][s])
+                ref = _sdpa(dec(st["query"][s]), np.stack(hist_k[s]), np.stack(hist_v[s]), batch.scale,
+                            enable_gqa=True)
+                assert np.max(np.abs(out[s] - ref)) < 1e-12, (dtype, s)
+        # the pool: initial rows plus exactly the written rows
+        exp_k, exp_v = kc0.reshape(-1, *kc0.shape[2:]).copy(), vc0.reshape(-1, *vc0.shape[2:]).copy()
+        for st in steps:
+            exp_k[st["slot_mapping"]] = st["new_key"]
+            exp_v[st["slot_mapping"]] = st["new_value"]
+        assert len(set(written)) == len(written)  # no slot is handed out twice
+        assert np.array_equal(kc.reshape(exp_k.shape).view(np.uint8), exp_k.view(np.uint8))
+        assert np.array_equal(vc.reshape(exp_v.shape).view(np.uint8), exp_v.view(np.uint8))
+
+
 QUICK_PINS = [
     pin_printed_mapping,
     pin_batch_example_tables,
@@ -644,6 +689,7 @@ QUICK_PINS = [
     pin_e4m3_write,
     pin_e4m3_decode_attention,
     pin_write,
+    pin_multistep_engine,
 ]
 
 
