@@ -10,7 +10,8 @@ paged_kv_decode_13_amd/workloads.py) uploaded to HBM before the timed region.
 Prints ONE JSON line on stdout.  ``value`` is the effective KV-read bandwidth
 of the whole step: sum(ctx) * num_kv_heads * head_dim * 2 * bytes / step time.
 ``roofline`` rates the decode call alone (HIP events on the launch stream)
-against the 8 TB/s HBM peak.  ``cold`` repeats the step with L2 and the MALL
+against the 8 TB/s HBM peak.  ``graph`` times the same step replayed from
+a captured HIP graph (no host launch gaps).  ``cold`` repeats the step with L2 and the MALL
 flushed before each one (a 1 GiB read-modify-write outside the events);
 ``stream_read`` times a plain contiguous read (libpkvstream.so) as the
 achievable-read yardstick.  ``cpu_baseline`` is the fp64 oracle timed on a
@@ -94,7 +95,7 @@ def _pct(xs, p: float) -> float:
 
 
 def time_steps(batch, t, partition_size: int, steps: int, warmup: int, shared_prefix: bool = False,
-               cold_steps: int = 0):
+               cold_steps: int = 0, graph: bool = False):
     import torch
 
     import paged_kv_decode_13_amd as pkv
@@ -166,6 +167,24 @@ def time_steps(batch, t, partition_size: int, steps: int, warmup: int, shared_pr
         "step_ms_p99": _pct(step_ms, 0.99),
         "out": out,
     }
+    if graph:
+        # the same step captured once in a HIP graph and replayed: no host
+        # launch gaps between the write, the decode and the merge
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            write()
+            decode()
+        for _ in range(max(1, warmup)):
+            g.replay()
+        torch.cuda.synchronize()
+        gs, ge = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        gs.record()
+        for _ in range(steps):
+            g.replay()
+        ge.record()
+        torch.cuda.synchronize()
+        res["graph_ms_per_step"] = gs.elapsed_time(ge) / steps
+        del g
     if cold_steps > 0:
         # cold caches: a 1 GiB read-modify-write before each step evicts L2
         # and the MALL (tables, workspace, query, recently read pages); it
@@ -447,6 +466,8 @@ def main() -> int:
                     help="steps timed again with L2/MALL flushed before each (0: skip)")
     ap.add_argument("--no-stream-read", action="store_true",
                     help="skip the streaming-read yardstick")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip timing the step replayed from a captured HIP graph")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -515,7 +536,8 @@ def main() -> int:
                 f"({gbs:7.1f} GB/s, {100 * gbs / HBM_PEAK_GBS:5.1f}% of peak), "
                 f"write {r['write_ms']*1e3:6.1f} us")
 
-    r = time_steps(batch, t, ps, args.steps, args.warmup, shared, cold_steps=args.cold_steps)
+    r = time_steps(batch, t, ps, args.steps, args.warmup, shared, cold_steps=args.cold_steps,
+                   graph=not args.no_graph)
     log(f"[bench] timed {args.steps} steps: {r['ms_per_step']:.4f} ms/step "
         f"(decode {r['decode_ms']:.4f} ms, write {r['write_ms']:.4f} ms)")
 
@@ -579,6 +601,12 @@ def main() -> int:
             "traffic": traffic,
         },
     }
+    if "graph_ms_per_step" in r:
+        line["graph"] = {
+            "ms_per_step": round(r["graph_ms_per_step"], 5),
+            "value": round(kv_bytes / (r["graph_ms_per_step"] * 1e-3) / 1e9, 2),
+            "decode_tokens_per_s": round(batch.num_seqs / (r["graph_ms_per_step"] * 1e-3), 1),
+        }
     if "cold" in r:
         c = dict(r["cold"])
         c["decode_gbs_median"] = round(alg_bytes / (c["decode_ms_median"] * 1e-3) / 1e9, 2)
