@@ -45,12 +45,42 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def source_digest() -> str:
+def code_text(text: str) -> str:
+    """Source text without comments and with whitespace runs collapsed:
+    what the compiler sees, so comment edits keep the digest."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif text[i] in "\"'":
+            q, j = text[i], i + 1
+            while j < n and text[j] != q:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(text[i])
+            i += 1
+    return " ".join("".join(out).split())
+
+
+def source_digest(files: dict | None = None) -> str:
+    """Digest of the kernel sources' code (comments and layout ignored);
+    ``files`` maps file name -> text, default: the csrc directory."""
+    if files is None:
+        csrc = os.path.join(REPO, "paged_kv_decode_13_amd", "csrc")
+        files = {}
+        for f in sorted(os.listdir(csrc)):
+            with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+                files[f] = fh.read()
     h = hashlib.sha256()
-    csrc = os.path.join(REPO, "paged_kv_decode_13_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+    for f in sorted(files):
+        h.update(f.encode() + b"\0" + code_text(files[f]).encode())
     return h.hexdigest()[:16]
 
 

@@ -15,11 +15,11 @@
 // wave); a query row is one (query token, head of the group) pair, so a tile
 // holds 128 / G consecutive query tokens.  Each unit streams the visible
 // history [0, last position of the tile] through the chunk machinery of
-// pkv_mqa.h (64 tokens at a time, K row-wise and V transposed in LDS, scores
-// and values as MFMA products); each row masks the tokens past its own
-// position, so only the chunks on the tile's diagonal carry masking work.  Page ids are staged in LDS 512 at a
-// time.  The output is written directly (no partials): a unit sees all of
-// its rows' history.
+// pkv_mqa.h (64 tokens at a time, K and V rows in LDS, scores and values as
+// MFMA products); each row masks the tokens past its own position, so only
+// the chunks on the tile's diagonal carry masking work.  Page ids are staged
+// in LDS 512 at a time.  The output is written directly (no partials): a
+// unit sees all of its rows' history.
 //
 // Unit order: a sequence's tiles of one KV head are consecutive and share an
 // XCD (they read the same history through one L2), the tiles with the
@@ -46,11 +46,12 @@ __device__ __forceinline__ int prefill_tiles(const PrefillArgs &a, int s, int &q
     return ((q_len << a.log2_group) + kPflRows - 1) / kPflRows;
 }
 
-// One 35 KiB LDS chunk buffer per workgroup, so that LDS never limits the
-// workgroups per CU: with one 16-row block per wave three fit (<= 168
-// VGPRs) and hid the chunk loads' latency better than two with
-// double-buffered LDS (10.9 against 12.8 ms on the 32-prompt workload); two
-// blocks per wave at two workgroups per CU took it to 9.5 ms.
+// One 37 KiB LDS chunk buffer per workgroup.  With one 16-row block per
+// wave three workgroups fit per CU (<= 168 VGPRs) and hid the chunk loads'
+// latency better than two with double-buffered LDS (10.9 against 12.8 ms on
+// the 32-prompt workload); two blocks per wave at two workgroups per CU
+// took it to 9.5 ms, and a second LDS buffer there (one barrier per chunk)
+// measured 1.5% slower.
 template <int DT>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(mqa_waves_per_simd(kPrefillBlocks), 8)))
@@ -178,8 +179,7 @@ void paged_prefill_mfma_kernel(PrefillArgs a) {
         };
         const int nch = (seg_end - seg + kMqaChunk - 1) / kMqaChunk;
         // chunk n is computed from the LDS buffer while chunk n + 1 is in
-        // flight in registers; one buffer (two barriers per chunk) keeps the
-        // workgroup at 35 KiB of LDS, so three fit per CU
+        // flight in registers (one buffer, two barriers per chunk)
         u32x4 kr[4], vr[4];
         uint32_t ok = load_chunk(seg, kr, vr);
         for (int n = 0; n < nch; ++n) {

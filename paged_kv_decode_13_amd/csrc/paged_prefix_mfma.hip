@@ -16,11 +16,11 @@
 //
 // Work unit = (KV head, prefix split, block of kPrefixRowsPerBlock query
 // rows); a query row is one (sequence, head of the group) pair, rows ordered
-// sequence-major, so the 16 rows of one wave span several sequences.  The 64-token chunks of
-// the split go through the LDS machinery of pkv_mqa.h (K row-wise, V
-// transposed, scores and values as MFMA products, a shared reference max
-// per row); the next chunk's loads are in flight while the current one is
-// computed.
+// sequence-major, so the 16 rows of one wave span several sequences.  The
+// 64-token chunks of the split go through the LDS machinery of pkv_mqa.h (K
+// and V rows in LDS, V read back transposed, scores and values as MFMA
+// products, a shared reference max per row); the next chunk's loads are in
+// flight while the current one is computed.
 //
 // Workgroups of one (KV head, split) read the same chunks; the launch order
 // places them on the same XCD so the chunk is fetched from HBM once per L2.
