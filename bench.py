@@ -326,9 +326,10 @@ def cpu_baseline(batch, target_s: float):
         "unit": "GB/s",
         "cores": oracle.max_threads(),
         "kind": "oracle",
-        "sample": (f"every {step}th sequence of the same batch ({sample.num_seqs} sequences, "
-                   f"{sample.total_tokens} context tokens), fp64 gather + softmax attention, "
-                   f"{passes} passes in {secs:.1f} s"),
+        "sample": ((f"every {step}th sequence of the same batch" if step > 1 else
+                    "the whole batch") +
+                   f" ({sample.num_seqs} sequences, {sample.total_tokens} context tokens), "
+                   f"fp64 gather + softmax attention, {passes} passes in {secs:.1f} s"),
         "tokens_per_s": round(sample.num_seqs / per_pass, 3),
         "cpu_model": cpu_model,
     }
