@@ -44,6 +44,7 @@
 
 #include "pkv_decode_common.h"
 #include "pkv_mfma.h"
+#include "pkv_prefix_unit.h"
 
 // Tiles whose loads a wave issues at once (even: tiles are computed in
 // pairs); the register budget of three waves per SIMD allows two
@@ -162,19 +163,19 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs &a, const int *s_pf
 // workgroup that drew short units simply takes more: with a static
 // assignment the chip idles while the unluckiest workgroups finish.  Every
 // workgroup ends with exactly one failed draw; the draw that sees the last
-// ticket of the launch (total + grid - 1) resets the counter to zero for the
-// next call on this workspace.  Decodes the unit into (sequence, partition,
+// ticket of the launch (total + drawers - 1, drawers = the workgroups that
+// draw) resets the counter to zero for the next call on this workspace.  Decodes the unit into (sequence, partition,
 // KV head); false once the units are exhausted.  Starts with a barrier, so
 // the previous unit's epilogue is done with LDS.
 template <bool PFX>
 __device__ __forceinline__ bool draw_unit(const DecodeArgs &a, const int *s_pf, const int *s_pp,
-                                          const int *s_ctx, int *s_unit, Unit &u) {
+                                          const int *s_ctx, int *s_unit, Unit &u, int drawers) {
     const int total_full = s_pf[a.num_seqs];
     const int total_units = (total_full + s_pp[a.num_seqs]) * a.num_kv_heads;
     __syncthreads();
     if (threadIdx.x == 0) {
         const unsigned got = atomicAdd(a.work_counter, 1u);
-        if (got == (unsigned)total_units + gridDim.x - 1u) atomicExch(a.work_counter, 0u);
+        if (got == (unsigned)total_units + (unsigned)drawers - 1u) atomicExch(a.work_counter, 0u);
         *s_unit = (int)got;
     }
     __syncthreads();
@@ -218,32 +219,55 @@ __device__ __forceinline__ bool draw_unit(const DecodeArgs &a, const int *s_pf, 
 // DT is then the type of the query and the output.  K and V are widened to
 // DT (exact) for the MFMAs; k_scale joins the score scale and v_scale
 // multiplies the result.
+// Tiles whose loads a wave issues at once, and whether the query operand
+// then moves to LDS (more tiles per step) to free its 16 registers for
+// loads in flight.
+template <bool KV8>
+constexpr int tiles_per_step() { return KV8 ? PKV_TILES_PER_STEP_E4M3 : PKV_TILES_PER_STEP; }
+template <bool KV8>
+constexpr bool qop_in_lds() { return tiles_per_step<KV8>() > 2; }
+
+// One wave's LDS region: the K rows of the 16-token tile being scored (the
+// score operand transpose), then the wave's accumulators for the epilogue.
+constexpr int kDecodeRegion = 16 * 128 * 2;
+
+// LDS of the decode work loop (besides the dynamic unit-order tables).
+template <int G, bool QOP_LDS>
+struct DecodeLds {
+    int pages[kSegPages];
+    int bad;
+    int unit;
+    float m[kNumWaves][G];
+    float l[kNumWaves][G];
+    __attribute__((aligned(16))) char region[kNumWaves][kDecodeRegion];
+    u32x4 qop[QOP_LDS ? 4 : 1][kWave];
+};
+
+// The decode work loop of one workgroup, as a device function over LDS the
+// kernel provides (s_dyn: full-unit prefix [B + 1], partial-unit prefix
+// [B + 1], lengths [B]); drawers = the launch's workgroups that draw units.
 template <int DT, int G, bool PFX, bool KV8>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8)))
-void paged_decode_mfma_kernel(DecodeArgs a) {
+__device__ __forceinline__ void decode_body(const DecodeArgs &a, int *s_dyn,
+                                            DecodeLds<G, qop_in_lds<KV8>()> &L, int drawers) {
     constexpr int D = 128;
     constexpr int ROW_BYTES = D * 2;
     constexpr int TILE = 16;
     constexpr int KV_ROW = KV8 ? D : D * 2;     // bytes of one cached row
     constexpr int KV_CHUNK = KV8 ? 8 : 16;      // bytes of one lane's chunk
     using TileRegs = TileRegsT<KV8>;
-    constexpr int TPS = KV8 ? PKV_TILES_PER_STEP_E4M3 : PKV_TILES_PER_STEP;
+    constexpr int TPS = tiles_per_step<KV8>();
     static_assert(TPS % 2 == 0, "tiles go in pairs");
-    // one wave's LDS region: the K rows of the tile being scored (the score
-    // operand transpose), then the wave's accumulators for the epilogue
-    constexpr int kRegion = TILE * ROW_BYTES;
+    constexpr int kRegion = kDecodeRegion;
+    static_assert(TILE * ROW_BYTES == kRegion, "a region holds one tile of K rows");
     static_assert(G * D * 4 <= kRegion, "accumulators fit the wave's region");
-    // With more tiles per step the query operand moves to LDS to free its
-    // 16 registers for loads in flight
-    constexpr bool kQopLds = TPS > 2;
+    constexpr bool kQopLds = qop_in_lds<KV8>();
 
-    extern __shared__ int s_dyn[];     // full-unit prefix [B + 1], partial-unit prefix [B + 1], lengths [B]
-    __shared__ int s_pages[kSegPages];
-    __shared__ int s_bad;
-    __shared__ float s_m[kNumWaves][G];
-    __shared__ float s_l[kNumWaves][G];
-    __shared__ __attribute__((aligned(16))) char s_region[kNumWaves][kRegion];
-    __shared__ u32x4 s_qop[kQopLds ? 4 : 1][kWave];
+    int *s_pages = L.pages;
+    int &s_bad = L.bad;
+    float (*s_m)[G] = L.m;
+    float (*s_l)[G] = L.l;
+    char (*s_region)[kRegion] = L.region;
+    u32x4 (*s_qop)[kWave] = L.qop;
 
     int *s_pf = s_dyn;
     int *s_pp = s_dyn + a.num_seqs + 1;
@@ -263,9 +287,8 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
     const int64_t tok_stride = (int64_t)a.num_kv_heads * KV_ROW;  // bytes between slots
     char *kt = s_region[wave];
 
-    __shared__ int s_unit;
     Unit u;
-    while (draw_unit<PFX>(a, s_pf, s_pp, s_ctx, &s_unit, u)) {
+    while (draw_unit<PFX>(a, s_pf, s_pp, s_ctx, &L.unit, u, drawers)) {
         if (tid == 0) s_bad = 0;
 
         // query operand: head h0 + c % G, chunks 4j + q
@@ -509,6 +532,34 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
     }
 }
 
+template <int DT, int G, bool PFX, bool KV8>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8)))
+void paged_decode_mfma_kernel(DecodeArgs a) {
+    extern __shared__ int s_dyn[];
+    __shared__ DecodeLds<G, qop_in_lds<KV8>()> lds;
+    decode_body<DT, G, PFX, KV8>(a, s_dyn, lds, gridDim.x);
+}
+
+// Shared-prefix decode in one launch: workgroups [0, prefix_wgs) each run one
+// prefix unit (units of one (KV head, split) on one XCD), the others are the
+// persistent suffix grid.  The prefix units are latency-bound and the suffix
+// streams from HBM, so the two overlap; their LDS is one union.  Every suffix
+// partition writes a partial; a merge kernel joins them with the prefix's.
+template <int DT, int G>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8)))
+void paged_prefix_fused_kernel(DecodeArgs a, PrefixArgs p, int prefix_wgs) {
+    extern __shared__ int s_dyn[];
+    __shared__ union {
+        DecodeLds<G, qop_in_lds<false>()> d;
+        PrefixLds x;
+    } lds;
+    if ((int)blockIdx.x < prefix_wgs) {
+        prefix_unit<DT>(p, xcd_unit(blockIdx.x, prefix_wgs), lds.x);
+        return;
+    }
+    decode_body<DT, G, true, false>(a, s_dyn, lds.d, (int)gridDim.x - prefix_wgs);
+}
+
 // Persistent grid: as many workgroups as are resident at once (occupancy
 // query), at most max_per_cu per CU, capped by the number of units.
 template <typename K>
@@ -555,6 +606,49 @@ hipError_t launch_paged_decode_mfma(const DecodeArgs &a, int dtype, hipStream_t 
 hipError_t launch_paged_decode_mfma_e4m3(const DecodeArgs &a, int dtype, hipStream_t stream) {
     if (dtype == kBF16) return launch_group<kBF16, false, true>(a, stream);
     if (dtype == kF16) return launch_group<kF16, false, true>(a, stream);
+    return hipErrorInvalidValue;
+}
+
+// The fused shared-prefix launch: prefix_units workgroups for the prefix,
+// then the persistent suffix grid (as many as are resident, at most
+// PKV_WG_PER_CU per CU, capped by the suffix units).
+template <int DT, int G>
+static hipError_t launch_fused(const PrefixArgs &p, const DecodeArgs &a, int64_t prefix_units,
+                               hipStream_t stream) {
+    auto kernel = paged_prefix_fused_kernel<DT, G>;
+    const size_t dyn = (size_t)(3 * a.num_seqs + 2) * sizeof(int);
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(kernel),
+                                                         kThreads, dyn);
+    if (e != hipSuccess) return e;
+    if (per_cu > PKV_WG_PER_CU) per_cu = PKV_WG_PER_CU;
+    int64_t grid = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
+    const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * a.num_partitions;  // upper bound
+    if (grid > units) grid = units;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)(prefix_units + grid)), dim3(kThreads), dyn, stream, a, p,
+                       (int)prefix_units);
+    return hipGetLastError();
+}
+
+template <int DT>
+static hipError_t launch_fused_group(const PrefixArgs &p, const DecodeArgs &a, hipStream_t stream) {
+    const int64_t prefix_units = (int64_t)p.row_blocks * p.num_splits * p.num_kv_heads;
+    switch (a.num_heads / a.num_kv_heads) {
+        case 1: return launch_fused<DT, 1>(p, a, prefix_units, stream);
+        case 2: return launch_fused<DT, 2>(p, a, prefix_units, stream);
+        case 4: return launch_fused<DT, 4>(p, a, prefix_units, stream);
+        case 8: return launch_fused<DT, 8>(p, a, prefix_units, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_paged_prefix_fused(const PrefixArgs &p, const DecodeArgs &a, int dtype,
+                                     hipStream_t stream) {
+    if (dtype == kBF16) return launch_fused_group<kBF16>(p, a, stream);
+    if (dtype == kF16) return launch_fused_group<kF16>(p, a, stream);
     return hipErrorInvalidValue;
 }
 

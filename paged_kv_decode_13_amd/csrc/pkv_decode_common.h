@@ -269,5 +269,9 @@ hipError_t launch_paged_decode_mfma(const DecodeArgs &a, int dtype, hipStream_t 
 hipError_t launch_paged_decode_mfma_e4m3(const DecodeArgs &a, int dtype, hipStream_t stream);
 // The same over tokens [token_begin, ctx), partials only (shared-prefix path).
 hipError_t launch_paged_decode_mfma_suffix(const DecodeArgs &a, int dtype, hipStream_t stream);
+// The shared-prefix units and that suffix decode in one launch (partials
+// only; the caller merges).
+hipError_t launch_paged_prefix_fused(const PrefixArgs &p, const DecodeArgs &a, int dtype,
+                                     hipStream_t stream);
 
 }  // namespace pkv

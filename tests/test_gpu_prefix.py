@@ -95,6 +95,10 @@ def test_prefix_out_of_range_contents(cuda):
 
 
 def test_prefix_deterministic_and_counter_left_zero(cuda):
+    """Three calls on one workspace with two suffix partitions per sequence,
+    i.e. through the launch that runs the prefix units beside the persistent
+    suffix grid: identical outputs, and the work counter back at zero after
+    each call."""
     import torch
 
     import paged_kv_decode_13_amd as pkv
