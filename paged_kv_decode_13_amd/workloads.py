@@ -13,10 +13,10 @@ type round-to-nearest-even):
                blocks, table = 10 ids of a seeded permutation, fp32, plus one
                new token written through slot_mapping;
   mha_fp16     32 seqs, 32/32 heads, head_dim 128, block 16, contexts uniform
-               in [1, 4096], fp16; 512-token KV partitions;
+               in [1, 4096], fp16; 384-token KV partitions;
   gqa_bf16     256 seqs, 32/8 heads, head_dim 128, block 16, contexts
                log-uniform in [128, 16000], bf16, one new token per sequence;
-               2048-token KV partitions;
+               2560-token KV partitions;
   long_bf16    4 seqs x 32768, 64/8 heads, head_dim 128, block 32, bf16,
                512-token KV partitions;
   prefix_fp16  128 seqs sharing one 2048-token prefix (same physical pages)
@@ -557,14 +557,14 @@ def make_config(name: str, *, block_size: int | None = None, seed: int | None = 
     if name == "mha_fp16":
         ctx = rng.integers(1, 4096, size=32, endpoint=True)
         return make_batch(ctx, num_heads=32, num_kv_heads=32, head_dim=128, block_size=16,
-                          dtype="f16", seed=seed, poison=poison, partition_size=512,
+                          dtype="f16", seed=seed, poison=poison, partition_size=384,
                           name=name, values=values)
     if name in ("gqa_bf16", "gqa_fp8"):
         ctx = np.floor(np.exp(rng.uniform(math.log(128), math.log(16000), size=256)))
         ctx = np.clip(ctx, 128, 16000).astype(np.int64)
         return make_batch(ctx, num_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
                           dtype="bf16", seed=seed, write_new_token=True, poison=poison,
-                          partition_size=4096 if name == "gqa_fp8" else 2048, name=name,
+                          partition_size=4096 if name == "gqa_fp8" else 2560, name=name,
                           values=values, kv_dtype="e4m3" if name == "gqa_fp8" else None)
     if name == "long_bf16":
         return make_batch(np.full(4, 32768), num_heads=64, num_kv_heads=8, head_dim=128,
