@@ -135,3 +135,22 @@ def test_prefix_full_config(cuda, bs):
     assert max_err(out, ref) <= TOL["f16"], max_err(out, ref)
     out = to_f64(gpu_prefix_step(b, upload(b, cuda), out_dtype="f32", partition_size=0))
     assert max_err(out, ref) <= TIGHT["f16"], max_err(out, ref)
+
+
+def test_prefix_more_units_than_fit_beside_the_suffix_grid(cuda):
+    """768 sequences sharing a 1024-token prefix with 128-token suffix
+    partitions: 48 row blocks x 8 KV heads = 384 prefix units share the
+    launch with the persistent suffix grid, more than the CUs can hold beside
+    it, so part of the suffix grid starts only as prefix units finish.
+    Includes sequences shorter than the prefix and empty ones."""
+    rng = np.random.default_rng(7681)
+    prefix = 1024
+    ctx = prefix + rng.integers(0, 300, size=768, endpoint=True)
+    ctx[:8] = [0, 1, 500, prefix - 1, prefix, prefix + 1, prefix + 128, prefix + 129]
+    b = wl.make_prefix_batch(ctx, prefix, num_heads=32, num_kv_heads=8, head_dim=128,
+                             block_size=16, dtype="f16", seed=7681, partition_size=128)
+    ref = oracle_prefix_step(b)
+    out = to_f64(gpu_prefix_step(b, upload(b, cuda), out_dtype="f32"))
+    assert max_err(out, ref) <= TIGHT["f16"], max_err(out, ref)
+    out = to_f64(gpu_prefix_step(b, upload(b, cuda)))
+    assert rounded_out_ok(out, ref, "f16"), max_err(out, ref)
