@@ -1,5 +1,6 @@
 """The decode step (slot write + decode attention, split partitions and the
-log-sum-exp merge included) captured in a HIP graph and replayed (MI355X).
+log-sum-exp merge included), and the shared-prefix call, captured in a HIP
+graph and replayed (MI355X).
 
 The library allocates nothing and clears nothing with memset (the unit
 counter of the persistent kernel resets itself at the end of every launch),
@@ -75,6 +76,59 @@ def test_decode_step_replays_in_graph(cuda, kv):
         t["q"].copy_(torch.from_numpy(
             wl.encode(rng.standard_normal(batch.query.size).astype(np.float32), "bf16")
             .reshape(batch.query.shape)).view(torch.bfloat16).to(dev))
+        step()
+        torch.cuda.synchronize()
+        eager = out.clone()
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), i
+
+
+def test_shared_prefix_call_replays_in_graph(cuda):
+    """The shared-prefix call with two suffix partitions per sequence (prefix
+    units and the suffix decode in one launch, then the merge) captured and
+    replayed: every replay bit for bit equal to an eager call."""
+    import torch
+
+    import paged_kv_decode_13_amd as pkv
+
+    prefix = 2048
+    b = wl.make_prefix_batch([0, 1, prefix - 1, prefix, prefix + 1, prefix + 600, prefix + 952,
+                              prefix + 52] * 4, prefix, num_heads=32, num_kv_heads=8,
+                             head_dim=128, block_size=16, dtype="f16", seed=78,
+                             partition_size=512)
+    print(f"\n[graph] shared prefix: {b.num_seqs} seqs", flush=True)
+    dev = cuda
+    t = upload(b, dev)
+    pt = torch.from_numpy(b.meta["prefix_table"]).to(dev)
+    out = torch.empty((b.num_seqs, b.num_heads, b.head_dim), dtype=torch.float32, device=dev)
+    need = pkv.paged_prefix_decode_workspace_size(b.num_seqs, b.num_heads, b.num_kv_heads,
+                                                  b.head_dim, b.max_context_len, prefix, 512)
+    ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
+
+    def step():
+        pkv.paged_prefix_decode_attention(t["q"], t["kc"], t["vc"], pt, prefix, t["bt"], t["cl"],
+                                          b.block_size, b.scale, max_context_len=b.max_context_len,
+                                          partition_size=512, out=out, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref = oracle.paged_prefix_decode(b.query, b.key_cache, b.value_cache, b.meta["prefix_table"],
+                                     prefix, b.block_tables, b.context_lens, b.block_size, b.scale,
+                                     b.dtype)
+    assert max_err(to_f64(out), ref) <= TIGHT["f16"]
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(4)
+    for i in range(4):
+        t["q"].copy_(torch.from_numpy(
+            wl.encode(rng.standard_normal(b.query.size).astype(np.float32), "f16")
+            .reshape(b.query.shape)).view(torch.float16).to(dev))
         step()
         torch.cuda.synchronize()
         eager = out.clone()
