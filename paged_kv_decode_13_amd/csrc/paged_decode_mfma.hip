@@ -213,8 +213,9 @@ __device__ __forceinline__ bool draw_unit(const DecodeArgs &a, const int *s_pf, 
 // allocator is held to that budget.
 //
 // PFX: the launch covers tokens [token_begin, ctx) of each sequence and
-// always writes partials (slots part_base.. of part_stride), for the
-// shared-prefix path; the plain instantiation never reads those fields.
+// writes partials (slots part_base.. of part_stride), for the shared-prefix
+// path, unless direct_out (no prefix, one partition per suffix); the plain
+// instantiation never reads those fields.
 // KV8: the caches hold E4M3 codes (128-byte rows) with per-KV-head scales;
 // DT is then the type of the query and the output.  K and V are widened to
 // DT (exact) for the MFMAs; k_scale joins the score scale and v_scale

@@ -2,8 +2,8 @@
 // batch shares is read once per KV head for all the batch's query rows, and
 // the score and value products over it become dense matrix products on the
 // matrix cores.  The rest of each history runs through the paged decode
-// kernel, whose epilogue joins the prefix's partial results by log-sum-exp
-// when each suffix is one partition; otherwise a merge kernel joins them.
+// loop in the same launch (paged_prefix_fused_kernel, beside the prefix
+// units), and a merge kernel joins the partial results by log-sum-exp.
 //
 // Pages on PagedAttention: "算子与编译器：推理 Attention 与 KV Kernel",
 // section "4.1 为什么页面化会改变 kernel 设计" (decode reads page tables,
@@ -28,17 +28,6 @@
 
 namespace pkv {
 
-// One 16-row block per wave, three workgroups per CU (<= 168 VGPRs, one
-// 32 KiB LDS chunk buffer each); workgroup id -> unit so that the units of
-// one (KV head, split) share an XCD.
-template <int DT>
-__global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(mqa_waves_per_simd(kPrefixBlocks), 8)))
-void paged_prefix_mfma_kernel(PrefixArgs a) {
-    __shared__ PrefixLds lds;
-    prefix_unit<DT>(a, xcd_unit(blockIdx.x, gridDim.x), lds);
-}
-
 // Log-sum-exp merge of every partial slot of one (sequence, query head):
 // the prefix splits, then the suffix partitions.  Writes every output.
 template <int DT, int NW>
@@ -56,27 +45,16 @@ __global__ __launch_bounds__(NW * kWave) void prefix_merge_kernel(DecodeArgs a) 
     merge_partials<DT, D, NW>(a, row * a.part_stride, a.part_base + seq_parts<true>(a, ctx), row * D);
 }
 
-// With several suffix partitions a merge kernel joins every partial, so the
-// prefix units and the suffix decode share one launch (they overlap); with
-// one suffix partition per sequence the suffix epilogue joins the prefix's
-// partials itself, so the prefix kernel runs first and no merge follows.
+// With a shared prefix, its units and the suffix decode share one launch
+// (they overlap: the prefix work is latency-bound, the suffix streams) and
+// the merge joins every partial; without one, the suffix decode alone,
+// storing the output itself when each suffix is one partition.
 template <int DT>
 static hipError_t launch_all(const PrefixArgs &p, const DecodeArgs &a, hipStream_t stream) {
     const int64_t units = (int64_t)p.row_blocks * p.num_splits * p.num_kv_heads;
-    hipError_t e;
-    if (units > 0 && !a.fold_prefix) {
-        e = launch_paged_prefix_fused(p, a, DT, stream);
-        if (e != hipSuccess) return e;
-    } else {
-        if (units > 0) {
-            hipLaunchKernelGGL(paged_prefix_mfma_kernel<DT>, dim3((unsigned)units), dim3(kThreads), 0,
-                               stream, p);
-            e = hipGetLastError();
-            if (e != hipSuccess) return e;
-        }
-        e = launch_paged_decode_mfma_suffix(a, DT, stream);
-        if (e != hipSuccess || a.fold_prefix) return e;
-    }
+    hipError_t e = units > 0 ? launch_paged_prefix_fused(p, a, DT, stream)
+                             : launch_paged_decode_mfma_suffix(a, DT, stream);
+    if (e != hipSuccess || a.direct_out) return e;
     const int64_t rows = (int64_t)a.num_seqs * a.num_heads;
     if (a.part_stride >= kMergeWideFrom)
         hipLaunchKernelGGL((prefix_merge_kernel<DT, kNumWaves>), dim3((unsigned)rows), dim3(kThreads), 0, stream, a);

@@ -199,7 +199,7 @@ pkv_status paged_decode_attention(void *out, const void *query, const void *key_
     a.token_begin = 0;
     a.part_stride = parts;
     a.part_base = 0;
-    a.fold_prefix = 0;
+    a.direct_out = 0;
     hipError_t e = pkv::launch_paged_decode(a, (int)dtype, head_dim,
                                             reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
@@ -315,7 +315,10 @@ pkv_status paged_prefix_decode_attention(
     a.token_begin = prefix_len;
     a.part_stride = (int32_t)slots;
     a.part_base = plan.num_splits;
-    a.fold_prefix = plan.suffix_parts == 1 ? 1 : 0;
+    // With a prefix, the prefix units and the suffix decode share one launch
+    // and a merge joins every partial; with none, a one-partition suffix
+    // stores its output directly.
+    a.direct_out = plan.suffix_parts == 1 && plan.num_splits == 0 ? 1 : 0;
     hipError_t e = pkv::launch_paged_prefix_decode(p, a, (int)dtype, reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }

@@ -155,42 +155,13 @@ __device__ __forceinline__ void unit_epilogue(const DecodeArgs &a, const Unit &u
             O += s_acc[w * WS + g * D + d] * f;
         }
         const int h = h0 + g;
-        if constexpr (PFX) {
-            if (a.fold_prefix) {
-                // One partition per suffix: join the shared prefix's partials
-                // (written by the prefix kernel earlier on this stream) here
-                // and store the output; no merge kernel follows.
-                const int64_t base = ((int64_t)u.s * a.num_heads + h) * a.part_stride;
-                float Mx = M;
-                bool poisoned = bad;  // a bad prefix page marks its partial's max NaN
-                for (int p = 0; p < a.part_base; ++p) {
-                    const float mp = a.part_ml[(base + p) * 2];
-                    poisoned |= mp != mp;
-                    Mx = fmaxf(Mx, mp);
-                }
-                float res = 0.f;  // nothing seen (empty context) -> zeros
-                if (poisoned) {
-                    res = __builtin_nanf("");
-                } else if (Mx != -INFINITY) {
-                    const float f = (M == -INFINITY) ? 0.f : fast_exp2(M - Mx);
-                    float Lt = L * f, Ot = O * f;
-                    for (int p = 0; p < a.part_base; ++p) {
-                        const float w = a.part_ml[(base + p) * 2 + 1] * fast_exp2(a.part_ml[(base + p) * 2] - Mx);
-                        Lt += w;
-                        Ot = fmaf(w, a.part_out[(base + p) * D + d], Ot);
-                    }
-                    res = Ot / Lt;
-                }
-                store_out<DT>(a, ((int64_t)u.s * a.num_heads + h) * D + d, res);
-                continue;
-            }
-        }
         float res = L > 0.f ? O / L * vscale : 0.f;  // empty context -> zeros
         if (bad) res = __builtin_nanf("");
-        if (!PFX && u.nparts == 1) {
+        // a suffix launch stores the output only with no prefix to join
+        if ((!PFX || a.direct_out) && u.nparts == 1) {
             store_out<DT>(a, ((int64_t)u.s * a.num_heads + h) * D + d, res);
         } else {
-            // a prefix launch always writes partials, after the prefix's slots
+            // a suffix launch writes its partials after the prefix's slots
             const int64_t slot = PFX ? ((int64_t)u.s * a.num_heads + h) * a.part_stride + a.part_base + u.p
                                      : ((int64_t)u.s * a.num_heads + h) * a.num_partitions + u.p;
             a.part_out[slot * D + d] = res;

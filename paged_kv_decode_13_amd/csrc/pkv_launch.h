@@ -61,8 +61,8 @@ struct DecodeArgs {
     int32_t token_begin;        // first token read (a page boundary; 0 = whole history)
     int32_t part_stride;        // partial slots per (sequence, head) in the workspace
     int32_t part_base;          // slot of this launch's partition 0
-    int32_t fold_prefix;        // 1: one partition per suffix; the epilogue joins
-                                // slots 0..part_base-1 and stores out (no merge)
+    int32_t direct_out;         // 1: no shared prefix and one partition per suffix:
+                                // the suffix epilogue stores out (no merge)
     const float *k_scale;       // [KVH] E4M3 caches only: cached K = code * k_scale
     const float *v_scale;       // [KVH]
 };
@@ -146,10 +146,11 @@ hipError_t launch_paged_decode(const DecodeArgs &a, int dtype, int head_dim, hip
 // bf16), then the merge when the context is split.
 hipError_t launch_paged_decode_e4m3(const DecodeArgs &a, int dtype, hipStream_t stream);
 
-// Shared-prefix decode (16-bit caches, head_dim 128): the prefix kernel
-// (when num_splits > 0), then the suffix decode over tokens [token_begin,
-// ctx): with fold_prefix its epilogue joins the prefix slots and stores out;
-// otherwise it writes partial slots num_splits.. and a merge kernel follows.
+// Shared-prefix decode (16-bit caches, head_dim 128): with a prefix
+// (num_splits > 0), the prefix units and the suffix decode over tokens
+// [token_begin, ctx) in one launch, writing partial slots, then a merge
+// kernel; with none, the suffix decode alone (direct_out: it stores the
+// output; else partials and the merge).
 hipError_t launch_paged_prefix_decode(const PrefixArgs &p, const DecodeArgs &a, int dtype,
                                       hipStream_t stream);
 

@@ -1,8 +1,8 @@
 // One unit of the shared-prefix score/value work (KV head, prefix split,
 // block of kPrefixRowsPerBlock query rows), written as a device function
-// over an LDS struct the kernel provides: the shared-prefix kernel runs one
-// unit per workgroup, and the fused prefix + suffix kernel runs these units
-// on some of its workgroups (the LDS then shares a union with the decode's).
+// over an LDS struct the kernel provides: the shared-prefix launch runs
+// these units on its first workgroups, beside the suffix decode, and the
+// two share their LDS as a union.
 //
 // Pages on PagedAttention: "算子与编译器：推理 Attention 与 KV Kernel",
 // sections "4.1 为什么页面化会改变 kernel 设计" and "6. Prefix Cache 与
