@@ -582,12 +582,8 @@ def main() -> int:
     workload = args.config if args.block_size is None else f"{args.config}_bs{args.block_size}"
     traffic = load_traffic(workload + ("_shared" if shared else ""))
     if shared:
-        # several suffix partitions: prefix units and suffix decode share one
-        # launch and a merge follows; else the suffix epilogue joins the prefix
-        split = ps and batch.max_context_len - batch.meta["shared_prefix_tokens"] > ps
-        kernel = "paged_prefix_decode_attention call (" + (
-            "prefix units and suffix decode in one kernel + log-sum-exp merge)" if split
-            else "prefix kernel, then the suffix decode joining its partials)")
+        kernel = ("paged_prefix_decode_attention call (prefix units and suffix decode in one "
+                  "kernel + log-sum-exp merge)")
     else:
         kernel = "paged_decode_attention call (decode kernel" + (
             " + log-sum-exp merge)" if ps and batch.max_context_len > ps else ")")
