@@ -154,3 +154,17 @@ def test_prefix_more_units_than_fit_beside_the_suffix_grid(cuda):
     assert max_err(out, ref) <= TIGHT["f16"], max_err(out, ref)
     out = to_f64(gpu_prefix_step(b, upload(b, cuda)))
     assert rounded_out_ok(out, ref, "f16"), max_err(out, ref)
+
+
+def test_prefix_largest_batch(cuda):
+    """The largest batch one call accepts (4096 sequences) through the
+    shared-prefix call: the unit-order tables then fill most of a
+    workgroup's LDS beside the prefix/decode union (one workgroup per CU),
+    and the prefix units far outnumber the resident workgroups."""
+    prefix = 256
+    lens = [(i * 37) % (prefix + 120) for i in range(4096)]
+    b = wl.make_prefix_batch(lens, prefix, num_heads=8, num_kv_heads=2, head_dim=128,
+                             block_size=16, dtype="bf16", seed=4096, partition_size=64)
+    ref = oracle_prefix_step(b)
+    out = to_f64(gpu_prefix_step(b, upload(b, cuda), out_dtype="f32"))
+    assert max_err(out, ref) <= TIGHT["bf16"], max_err(out, ref)
