@@ -40,10 +40,15 @@ int32_t num_partitions(int32_t max_context_len, int32_t partition_size) {
 // Shared-prefix plan: blocks of kPrefixRowsPerBlock query rows per KV head, and
 // the prefix cut into splits of whole 64-token chunks (at most 2048 tokens
 // each) so that about kPrefixTargetUnits workgroups share the prefix work.
+// The prefix units run beside the persistent suffix grid, so they should be
+// few yet short enough to end within the suffix decode: on the 128-sequence,
+// 2048-token-prefix batch (64 units per split) the call took 70.9-71.1 us
+// at 64 units, 66.1-67.5 at 128, 69.6-70.2 at 192, 72.4-72.6 at 256 and
+// 77.5-78.0 at 512.
 constexpr int32_t kPrefixChunk = 64;
 constexpr int32_t kPrefixMaxSplitChunks = 32;
 #ifndef PKV_PFX_TARGET_UNITS
-#define PKV_PFX_TARGET_UNITS 256
+#define PKV_PFX_TARGET_UNITS 128
 #endif
 constexpr int64_t kPrefixTargetUnits = PKV_PFX_TARGET_UNITS;
 

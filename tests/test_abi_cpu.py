@@ -150,11 +150,12 @@ def test_prefix_decode_validation(lib):
 
 def test_prefix_workspace_size(lib):
     # 128 sequences x G = 4: 512 query rows = 8 row blocks per KV head; 64
-    # blocks in all, so the 2048-token prefix is cut into 4 splits of 512
-    # tokens; one suffix slot unsplit, two at partition 512 for 1024 tokens
+    # blocks in all, so the 2048-token prefix is cut into 2 splits of 1024
+    # tokens (about 128 prefix units); one suffix slot unsplit, two at
+    # partition 512 for 1024 tokens
     per = 128 * 32 * 130 * 4
-    assert lib.paged_prefix_decode_workspace_size(128, 32, 8, 128, 3072, 2048, 0) == 256 + 5 * per
-    assert lib.paged_prefix_decode_workspace_size(128, 32, 8, 128, 3072, 2048, 512) == 256 + 6 * per
+    assert lib.paged_prefix_decode_workspace_size(128, 32, 8, 128, 3072, 2048, 0) == 256 + 3 * per
+    assert lib.paged_prefix_decode_workspace_size(128, 32, 8, 128, 3072, 2048, 512) == 256 + 4 * per
     # no prefix: the suffix partitions only
     assert lib.paged_prefix_decode_workspace_size(128, 32, 8, 128, 3072, 0, 1024) == 256 + 3 * per
     # a long prefix is cut into splits of at most 2048 tokens
