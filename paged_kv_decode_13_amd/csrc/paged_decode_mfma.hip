@@ -36,8 +36,8 @@
 //    lane (q, c) owns tokens 4q..4q+3, which is the B-operand layout of the
 //    value product, and V^T is formed from the lane's own V registers (see
 //    the kernel).
-//  - A wave issues the loads of two tiles, then computes them; three waves
-//    per SIMD keep HBM requests in flight while others compute.
+//  - A wave issues the loads of two tiles, then computes them; the other
+//    resident waves keep HBM requests in flight meanwhile.
 #include <math.h>
 
 #include <type_traits>
@@ -54,11 +54,13 @@
 #ifndef PKV_TILES_PER_STEP_E4M3
 #define PKV_TILES_PER_STEP_E4M3 2
 #endif
+// Resident workgroups per CU of the persistent grids.  Past a point more
+// requests in flight only queue at HBM: two workgroups per CU (up to 128
+// KiB of loads in flight per CU with 16-bit caches) already reach what the
+// access pattern allows.  A third measured 1-4% slower on every 16-bit
+// workload and 1.5% slower over E4M3 caches.
 #ifndef PKV_WG_PER_CU
 #define PKV_WG_PER_CU 2
-#endif
-#ifndef PKV_WG_PER_CU_E4M3
-#define PKV_WG_PER_CU_E4M3 8
 #endif
 
 namespace pkv {
@@ -209,8 +211,8 @@ __device__ __forceinline__ bool draw_unit(const DecodeArgs &a, const int *s_pf, 
 //    lazy rule (move only when passed by more than 2^kMaxSlack) keeps
 //    rescales rare.
 //
-// Three waves per SIMD (<= 168 VGPRs) keep enough loads in flight; the
-// allocator is held to that budget.
+// The allocator is held to a three-waves-per-SIMD budget (<= 168 VGPRs);
+// the launch keeps two workgroups per CU (PKV_WG_PER_CU).
 //
 // PFX: the launch covers tokens [token_begin, ctx) of each sequence and
 // writes partials (slots part_base.. of part_stride), for the shared-prefix
@@ -561,39 +563,43 @@ void paged_prefix_fused_kernel(DecodeArgs a, PrefixArgs p, int prefix_wgs) {
     decode_body<DT, G, true, false>(a, s_dyn, lds.d, (int)gridDim.x - prefix_wgs);
 }
 
-// Persistent grid: as many workgroups as are resident at once (occupancy
-// query), at most max_per_cu per CU, capped by the number of units.
+// Workgroups of a persistent grid: as many as are resident at once
+// (occupancy query with `dyn` bytes of dynamic LDS), at most PKV_WG_PER_CU
+// per CU, capped by `units`.  0 on a HIP error (returned in `e`).
 template <typename K>
-static hipError_t launch_persistent(K kernel, const DecodeArgs &a, int max_per_cu, hipStream_t stream) {
-    const size_t dyn = (size_t)(3 * a.num_seqs + 2) * sizeof(int);
+static int64_t resident_grid(K kernel, size_t dyn, int64_t units, hipError_t &e) {
     int dev = 0, cus = 0, per_cu = 0;
-    hipError_t e = hipGetDevice(&dev);
+    e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e == hipSuccess)
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(kernel),
                                                          kThreads, dyn);
-    if (e != hipSuccess) return e;
-    if (per_cu > max_per_cu) per_cu = max_per_cu;
-    int64_t grid = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
+    if (e != hipSuccess) return 0;
+    if (per_cu > PKV_WG_PER_CU) per_cu = PKV_WG_PER_CU;
+    const int64_t grid = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
+    return grid < units ? grid : units;
+}
+
+// Persistent grid: as many workgroups as are resident at once, capped by
+// the number of units.
+template <typename K>
+static hipError_t launch_persistent(K kernel, const DecodeArgs &a, hipStream_t stream) {
+    const size_t dyn = (size_t)(3 * a.num_seqs + 2) * sizeof(int);
     const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * a.num_partitions;  // upper bound
-    if (grid > units) grid = units;
+    hipError_t e;
+    const int64_t grid = resident_grid(kernel, dyn, units, e);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), dyn, stream, a);
     return hipGetLastError();
 }
 
-// Resident workgroups per CU.  Past a point more requests in flight only
-// queue at HBM: with 16-bit caches two workgroups per CU (up to 128 KiB of
-// loads in flight per CU) already reach the bandwidth the access pattern
-// allows, and a third one measured 1-4% slower; an E4M3 step carries half
-// the bytes, so that path keeps every resident workgroup.
 template <int DT, bool PFX, bool KV8 = false>
 static hipError_t launch_group(const DecodeArgs &a, hipStream_t stream) {
-    const int cap = KV8 ? PKV_WG_PER_CU_E4M3 : PKV_WG_PER_CU;
     switch (a.num_heads / a.num_kv_heads) {
-        case 1: return launch_persistent(paged_decode_mfma_kernel<DT, 1, PFX, KV8>, a, cap, stream);
-        case 2: return launch_persistent(paged_decode_mfma_kernel<DT, 2, PFX, KV8>, a, cap, stream);
-        case 4: return launch_persistent(paged_decode_mfma_kernel<DT, 4, PFX, KV8>, a, cap, stream);
-        case 8: return launch_persistent(paged_decode_mfma_kernel<DT, 8, PFX, KV8>, a, cap, stream);
+        case 1: return launch_persistent(paged_decode_mfma_kernel<DT, 1, PFX, KV8>, a, stream);
+        case 2: return launch_persistent(paged_decode_mfma_kernel<DT, 2, PFX, KV8>, a, stream);
+        case 4: return launch_persistent(paged_decode_mfma_kernel<DT, 4, PFX, KV8>, a, stream);
+        case 8: return launch_persistent(paged_decode_mfma_kernel<DT, 8, PFX, KV8>, a, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -611,24 +617,16 @@ hipError_t launch_paged_decode_mfma_e4m3(const DecodeArgs &a, int dtype, hipStre
 }
 
 // The fused shared-prefix launch: prefix_units workgroups for the prefix,
-// then the persistent suffix grid (as many as are resident, at most
-// PKV_WG_PER_CU per CU, capped by the suffix units).
+// then the persistent suffix grid (resident_grid over the suffix units).
 template <int DT, int G>
 static hipError_t launch_fused(const PrefixArgs &p, const DecodeArgs &a, int64_t prefix_units,
                                hipStream_t stream) {
     auto kernel = paged_prefix_fused_kernel<DT, G>;
     const size_t dyn = (size_t)(3 * a.num_seqs + 2) * sizeof(int);
-    int dev = 0, cus = 0, per_cu = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e == hipSuccess)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(kernel),
-                                                         kThreads, dyn);
-    if (e != hipSuccess) return e;
-    if (per_cu > PKV_WG_PER_CU) per_cu = PKV_WG_PER_CU;
-    int64_t grid = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
     const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * a.num_partitions;  // upper bound
-    if (grid > units) grid = units;
+    hipError_t e;
+    const int64_t grid = resident_grid(kernel, dyn, units, e);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kernel, dim3((unsigned)(prefix_units + grid)), dim3(kThreads), dyn, stream, a, p,
                        (int)prefix_units);
     return hipGetLastError();
