@@ -14,9 +14,10 @@
 // (the second over a pair of tiles, k = 32).
 //
 // Work distribution: a persistent grid (as many workgroups as fit on the
-// chip) draws work units (sequence, KV partition, KV head) one at a time from
-// a counter, KV head fastest so that the units reading the same pages run
-// side by side, all full partitions before the shorter last ones.  Each
+// chip) takes work units (sequence, KV partition, KV head) one at a time --
+// the first by workgroup index, the rest from a counter -- KV head fastest
+// so that the units reading the same pages run side by side, all full
+// partitions before the shorter last ones.  Each
 // workgroup first builds, in LDS, the prefix sums of partitions over the
 // sequences of the batch, which map a unit index to its sequence and
 // partition; no workgroup is spent on a partition past the end of its
@@ -161,24 +162,38 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs &a, const int *s_pf
     u.empty = false;
 }
 
-// Units are handed out one at a time from a counter in the workspace, so a
-// workgroup that drew short units simply takes more: with a static
-// assignment the chip idles while the unluckiest workgroups finish.  Every
-// workgroup ends with exactly one failed draw; the draw that sees the last
-// ticket of the launch (total + drawers - 1, drawers = the workgroups that
-// draw) resets the counter to zero for the next call on this workspace.  Decodes the unit into (sequence, partition,
-// KV head); false once the units are exhausted.  Starts with a barrier, so
-// the previous unit's epilogue is done with LDS.
+// Units are handed out from a counter in the workspace, so a workgroup that
+// drew short units simply takes more: with a static assignment the chip
+// idles while the unluckiest workgroups finish.  The first unit of each
+// workgroup is its own index among the `drawers` workgroups that draw
+// (`first` is cleared on that call): all of them start at once, and one
+// atomic per workgroup on a single address at launch delayed the last
+// starts (long-context batch 105 -> 101 us, MHA 183 -> 180 us).  Later
+// draws take ticket t from the counter and run unit drawers + t.  Every
+// workgroup ends with exactly one failed counter draw, so a launch takes
+// max(total, drawers) tickets; the draw that sees the last one resets the
+// counter to zero for the next call on this workspace.  Decodes the unit
+// into (sequence, partition, KV head); false once the units are exhausted.
+// Starts with a barrier, so the previous unit's epilogue is done with LDS.
 template <bool PFX>
 __device__ __forceinline__ bool draw_unit(const DecodeArgs &a, const int *s_pf, const int *s_pp,
-                                          const int *s_ctx, int *s_unit, Unit &u, int drawers) {
+                                          const int *s_ctx, int *s_unit, Unit &u, int drawers,
+                                          int drawer, bool &first) {
     const int total_full = s_pf[a.num_seqs];
     const int total_units = (total_full + s_pp[a.num_seqs]) * a.num_kv_heads;
     __syncthreads();
+    if (first) {
+        first = false;
+        if (drawer < total_units) {
+            decode_unit<PFX>(a, s_pf, s_pp, s_ctx, drawer, u);
+            return true;
+        }
+    }
     if (threadIdx.x == 0) {
         const unsigned got = atomicAdd(a.work_counter, 1u);
-        if (got == (unsigned)total_units + (unsigned)drawers - 1u) atomicExch(a.work_counter, 0u);
-        *s_unit = (int)got;
+        const unsigned last = (unsigned)max(total_units, drawers) - 1u;
+        if (got == last) atomicExch(a.work_counter, 0u);
+        *s_unit = (int)got + drawers;
     }
     __syncthreads();
     const int unit = *s_unit;
@@ -291,7 +306,10 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, int *s_dyn,
     char *kt = s_region[wave];
 
     Unit u;
-    while (draw_unit<PFX>(a, s_pf, s_pp, s_ctx, &L.unit, u, drawers)) {
+    bool first = true;
+    // this workgroup's index among the drawers (the last `drawers` of the grid)
+    const int drawer = (int)blockIdx.x - ((int)gridDim.x - drawers);
+    while (draw_unit<PFX>(a, s_pf, s_pp, s_ctx, &L.unit, u, drawers, drawer, first)) {
         if (tid == 0) s_bad = 0;
 
         // query operand: head h0 + c % G, chunks 4j + q
