@@ -168,3 +168,19 @@ def test_prefix_largest_batch(cuda):
     ref = oracle_prefix_step(b)
     out = to_f64(gpu_prefix_step(b, upload(b, cuda), out_dtype="f32"))
     assert max_err(out, ref) <= TIGHT["bf16"], max_err(out, ref)
+
+
+def test_prefix_entry_point_without_a_prefix(cuda):
+    """prefix_len == 0 (no prefix table): the call is the plain decode.
+    Unsplit, each sequence's epilogue stores its output itself; split, the
+    partials go through the merge with no prefix slots before them."""
+    lens = [0, 1, 15, 16, 17, 300, 1025, 2048, 4000]
+    b = wl.make_prefix_batch(lens * 2, 0, num_heads=16, num_kv_heads=4, head_dim=128,
+                             block_size=16, dtype="bf16", seed=4242)
+    ref = oracle_prefix_step(b)
+    assert np.array_equal(ref[0], np.zeros_like(ref[0]))
+    for ps in (0, 256):
+        out = to_f64(gpu_prefix_step(b, upload(b, cuda), partition_size=ps, out_dtype="f32"))
+        assert max_err(out, ref) <= TIGHT["bf16"], (ps, max_err(out, ref))
+        out = to_f64(gpu_prefix_step(b, upload(b, cuda), partition_size=ps))
+        assert rounded_out_ok(out, ref, "bf16"), (ps, max_err(out, ref))
