@@ -62,7 +62,7 @@ void paged_prefill_mfma_kernel(PrefillArgs a) {
     __shared__ __attribute__((aligned(16))) char s_k[kMqaChunk * kMqaRowBytes];  // K rows of a chunk
     __shared__ __attribute__((aligned(16))) char s_v[kMqaChunk * kMqaVRow];        // V rows of a chunk
     __shared__ int s_pages[kPflSegPages];
-    __shared__ int s_scan[kThreads];
+    __shared__ int s_scan[kNumWaves];  // block_scan: one total per wave
     __shared__ int s_badtok;
 
     const int tid = threadIdx.x;

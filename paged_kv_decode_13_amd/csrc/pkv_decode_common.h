@@ -79,20 +79,25 @@ __device__ __forceinline__ Unit make_unit(const DecodeArgs &a) {
     return r;
 }
 
-// Inclusive prefix sum over the workgroup's threads (s_scan: kThreads ints).
+// Inclusive prefix sum over the workgroup's NT threads: a shuffle scan in
+// each wave, then each wave adds the totals of the waves before it
+// (s_scan: NT / 64 ints).  Ends with a barrier, so s_scan can be reused.
+template <int NT = kThreads>
 __device__ __forceinline__ int block_scan(int v, int *s_scan) {
-    const int tid = threadIdx.x;
-    s_scan[tid] = v;
-    __syncthreads();
-    for (int off = 1; off < kThreads; off <<= 1) {
-        const int x = tid >= off ? s_scan[tid - off] : 0;
-        __syncthreads();
-        s_scan[tid] += x;
-        __syncthreads();
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    int x = v;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int y = __shfl_up(x, off);
+        if (lane >= off) x += y;
     }
-    const int r = s_scan[tid];
+    if (lane == kWave - 1) s_scan[wave] = x;
     __syncthreads();
-    return r;
+    int base = 0;
+    for (int w = 0; w < wave; ++w) base += s_scan[w];
+    __syncthreads();
+    return x + base;
 }
 
 // Largest s in [0, n) with pre[s] <= x (pre non-decreasing, pre[0] = 0 <= x).
