@@ -88,10 +88,11 @@ pkv_status paged_kv_write(const void *key, const void *value, void *key_cache,
 
 /*
  * paged_decode_workspace_size -- bytes of device scratch paged_decode_attention
- * needs (0 only for an empty batch).  partition_size == 0 means one partition
- * per sequence.  Layout: a 256-byte work-counter area, then, when the context
- * is split (P = ceil(max_context_len / partition_size) > 1), fp32 partial
- * outputs [num_seqs, num_heads, P, head_dim] and per-partition (running max,
+ * takes (0 only for an empty batch); required when the context is split,
+ * optional otherwise.  partition_size == 0 means one partition per sequence.
+ * Layout: a 256-byte work-counter area, then, when the context is split
+ * (P = ceil(max_context_len / partition_size) > 1), fp32 partial outputs
+ * [num_seqs, num_heads, P, head_dim] and per-partition (running max,
  * normaliser) pairs [num_seqs, num_heads, P, 2].
  */
 size_t paged_decode_workspace_size(int32_t num_seqs, int32_t num_heads,
@@ -135,12 +136,17 @@ size_t paged_decode_workspace_size(int32_t num_seqs, int32_t num_heads,
  *                 second kernel merges by log-sum-exp
  *   dtype         PKV_F32, PKV_F16 or PKV_BF16; out_dtype is dtype or PKV_F32
  *   workspace     device scratch of at least paged_decode_workspace_size()
- *                 bytes, 16-byte aligned, owned by the caller.  Its counter
- *                 area must be zero before the first call that uses it (fill
- *                 the buffer with zeros once when allocating it); every call
- *                 leaves it zero again when its kernels finish.  Calls that
- *                 can run at the same time (different streams) must use
- *                 different workspaces.
+ *                 bytes, 16-byte aligned, owned by the caller; any initial
+ *                 contents (the decode kernel clears its work counter when
+ *                 it starts, in a way no earlier contents can defeat, so no
+ *                 call depends on what an earlier call left there).  May be
+ *                 NULL (workspace_bytes ignored) when the context is not
+ *                 split (partition_size == 0 or >= max_context_len): the
+ *                 decode then runs one workgroup per (sequence, KV head)
+ *                 instead of a persistent grid drawing work from a counter.
+ *                 A split call without one returns PKV_ERR_WORKSPACE.  Calls
+ *                 that can run at the same time (different streams) must
+ *                 use different workspaces: sharing one is a race.
  *
  * Accumulation is fp32 throughout.  Supported: head_dim in {64, 128};
  * block_size in {4, 8, 16, 32, 64}; G in {1, 2, 4, 8}; num_seqs <=
@@ -197,10 +203,9 @@ size_t paged_prefix_decode_workspace_size(int32_t num_seqs, int32_t num_heads,
  *   block_tables  [num_seqs, max_blocks_per_seq] int32; entries below
  *                 prefix_len / block_size and at or past
  *                 ceil(context_lens[s] / block_size) are never read
- *   workspace     at least paged_prefix_decode_workspace_size() bytes, same
- *                 rules as for paged_decode_attention (counter area zero
- *                 before first use; left zero by every call; one workspace
- *                 per concurrently running call)
+ *   workspace     at least paged_prefix_decode_workspace_size() bytes, any
+ *                 contents (as for paged_decode_attention); always required;
+ *                 one workspace per concurrently running call
  * Every other argument, the output and the error behaviour are those of
  * paged_decode_attention; an out-of-range prefix table entry makes the
  * outputs of the sequences that reach that page NaN.
@@ -298,7 +303,8 @@ pkv_status paged_kv_write_fp8(const void *key, const void *value, void *key_cach
  *   value_cache   [num_blocks, block_size, num_kv_heads, head_dim] E4M3 bytes
  *   k_scale,
  *   v_scale       [num_kv_heads] binary32 (device)
- *   workspace     paged_decode_workspace_size() bytes, same rules
+ *   workspace     paged_decode_workspace_size() bytes, same rules (NULL
+ *                 allowed when the context is not split)
  * Supported: head_dim 128, block_size in {4, 8, 16, 32, 64}, G in {1, 2, 4,
  * 8}, num_seqs <= PKV_MAX_SEQS.
  */

@@ -48,6 +48,7 @@ __all__ = [
     "paged_prefill_attention",
     "library_path",
     "PagedKVError",
+    "NO_WORKSPACE",
 ]
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -141,6 +142,33 @@ def _stream_handle(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
+class _NoWorkspace:
+    def __repr__(self) -> str:
+        return "NO_WORKSPACE"
+
+
+# Pass as ``workspace=`` to make an unsplit decode call without a workspace
+# (the C ABI's NULL workspace: one workgroup per (sequence, KV head), no
+# work counter).  A split call needs a workspace and raises.
+NO_WORKSPACE = _NoWorkspace()
+
+
+def _workspace(need: int, workspace, device):
+    """(pointer, bytes) of the call's workspace: the caller's buffer, NULL
+    for NO_WORKSPACE, or a fresh uninitialised one (no call depends on a
+    workspace's earlier contents)."""
+    torch = _torch()
+    if workspace is NO_WORKSPACE:
+        return None, 0
+    if workspace is None:
+        if not need:
+            return None, 0
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    else:
+        _gpu(workspace, "workspace")
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
 def paged_kv_write(key, value, key_cache, value_cache, slot_mapping) -> None:
     """Store token i's K/V rows ``key[i]``/``value[i]`` ([num_kv_heads,
     head_dim]) at ``slot_mapping[i]`` (int64, physical_block * block_size +
@@ -182,10 +210,10 @@ def paged_decode_attention(query, key_cache, value_cache, block_tables, context_
     (int32 [num_seqs]).  Returns ``out`` [num_seqs, num_heads, head_dim] in
     ``out_dtype`` (default: the cache dtype).  ``max_context_len`` is a host
     upper bound of ``context_lens``; ``partition_size`` > 0 splits contexts
-    into KV partitions merged by log-sum-exp.  ``workspace`` (a uint8 GPU
-    buffer of ``paged_decode_workspace_size`` bytes) may be passed to avoid an
-    allocation per call: zero it once when allocating it; calls leave it
-    zeroed."""
+    into KV partitions merged by log-sum-exp.  ``workspace`` (a GPU buffer of
+    at least ``paged_decode_workspace_size`` bytes, any contents) may be
+    passed to avoid an allocation per call; ``NO_WORKSPACE`` runs an unsplit
+    call without one."""
     torch = _torch()
     lib = _load()
     for t, n in ((query, "query"), (key_cache, "key_cache"), (value_cache, "value_cache"),
@@ -213,14 +241,7 @@ def paged_decode_attention(query, key_cache, value_cache, block_tables, context_
             raise ValueError("out must be [num_seqs, num_heads, head_dim]")
         odt = out.dtype
     need = paged_decode_workspace_size(b, h, d, int(max_context_len), int(partition_size))
-    ws_ptr, ws_bytes = None, 0
-    if need:
-        if workspace is None:
-            # the work counter at its start must be zero before first use
-            workspace = torch.zeros(need, dtype=torch.uint8, device=query.device)
-        else:
-            _gpu(workspace, "workspace")
-        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    ws_ptr, ws_bytes = _workspace(need, workspace, query.device)
     st = lib.paged_decode_attention(
         out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
         block_tables.data_ptr(), context_lens.data_ptr(), b, h, kvh, d, bs,
@@ -282,13 +303,7 @@ def paged_prefix_decode_attention(query, key_cache, value_cache, prefix_table, p
         odt = out.dtype
     need = paged_prefix_decode_workspace_size(b, h, kvh, d, int(max_context_len), int(prefix_len),
                                               int(partition_size))
-    ws_ptr, ws_bytes = None, 0
-    if need:
-        if workspace is None:
-            workspace = torch.zeros(need, dtype=torch.uint8, device=query.device)
-        else:
-            _gpu(workspace, "workspace")
-        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    ws_ptr, ws_bytes = _workspace(need, workspace, query.device)
     st = lib.paged_prefix_decode_attention(
         out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
         prefix_table.data_ptr(), int(prefix_len), block_tables.data_ptr(), context_lens.data_ptr(),
@@ -376,13 +391,7 @@ def paged_decode_attention_fp8(query, key_cache, value_cache, k_scale, v_scale, 
             raise ValueError("out must be [num_seqs, num_heads, head_dim]")
         odt = out.dtype
     need = paged_decode_workspace_size(b, h, d, int(max_context_len), int(partition_size))
-    ws_ptr, ws_bytes = None, 0
-    if need:
-        if workspace is None:
-            workspace = torch.zeros(need, dtype=torch.uint8, device=query.device)
-        else:
-            _gpu(workspace, "workspace")
-        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    ws_ptr, ws_bytes = _workspace(need, workspace, query.device)
     st = lib.paged_decode_attention_fp8(
         out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
         k_scale.data_ptr(), v_scale.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(),

@@ -41,6 +41,7 @@
 //    resident waves keep HBM requests in flight meanwhile.
 #include <math.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "pkv_decode_common.h"
@@ -169,12 +170,20 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs &a, const int *s_pf
 // (`first` is cleared on that call): all of them start at once, and one
 // atomic per workgroup on a single address at launch delayed the last
 // starts (long-context batch 105 -> 101 us, MHA 183 -> 180 us).  Later
-// draws take ticket t from the counter and run unit drawers + t.  Every
-// workgroup ends with exactly one failed counter draw, so a launch takes
-// max(total, drawers) tickets; the draw that sees the last one resets the
-// counter to zero for the next call on this workspace.  Decodes the unit
-// into (sequence, partition, KV head); false once the units are exhausted.
-// Starts with a barrier, so the previous unit's epilogue is done with LDS.
+// draws take ticket t from the counter and run unit drawers + t.
+//
+// No launch depends on what the counter held before it: drawer 0 clears it
+// (an atomic exchange) before anything else, and a ticket outside the valid
+// range ends the drawing workgroup's work.  A draw made before the clear
+// (only possible if drawer 0 starts a whole unit late) either returns a
+// valid ticket -- that unit then also goes to whoever draws the same ticket
+// after the clear, and both write identical results -- or ends that
+// workgroup early.  Drawer 0 draws only after its clear, and stops only on
+// a ticket past the last unit, which it can only receive once every valid
+// ticket has been handed out after the clear; so every unit runs.  Decodes
+// the unit into (sequence, partition, KV head); false once the units are
+// exhausted.  Starts with a barrier, so the previous unit's epilogue is done
+// with LDS.
 template <bool PFX>
 __device__ __forceinline__ bool draw_unit(const DecodeArgs &a, const int *s_pf, const int *s_pp,
                                           const int *s_ctx, int *s_unit, Unit &u, int drawers,
@@ -184,21 +193,39 @@ __device__ __forceinline__ bool draw_unit(const DecodeArgs &a, const int *s_pf, 
     __syncthreads();
     if (first) {
         first = false;
-        if (drawer < total_units) {
-            decode_unit<PFX>(a, s_pf, s_pp, s_ctx, drawer, u);
-            return true;
-        }
+        if (drawer == 0 && threadIdx.x == 0) atomicExch(a.work_counter, 0u);
+        if (drawer >= total_units) return false;  // so are all counter tickets
+        decode_unit<PFX>(a, s_pf, s_pp, s_ctx, drawer, u);
+        return true;
     }
     if (threadIdx.x == 0) {
         const unsigned got = atomicAdd(a.work_counter, 1u);
-        const unsigned last = (unsigned)max(total_units, drawers) - 1u;
-        if (got == last) atomicExch(a.work_counter, 0u);
-        *s_unit = (int)got + drawers;
+        const unsigned tickets = total_units > drawers ? (unsigned)(total_units - drawers) : 0u;
+        *s_unit = got < tickets ? (int)got + drawers : -1;
     }
     __syncthreads();
     const int unit = *s_unit;
-    if (unit >= total_units) return false;
+    if (unit < 0) return false;
     decode_unit<PFX>(a, s_pf, s_pp, s_ctx, unit, u);
+    return true;
+}
+
+// Without a workspace (one partition per sequence, no counter) the grid
+// holds one workgroup per (sequence, KV head) and the hardware dispatcher
+// balances them: unit = workgroup index, KV head fastest.
+__device__ __forceinline__ bool direct_unit(const DecodeArgs &a, Unit &u, bool &first) {
+    if (!first) return false;
+    first = false;
+    const int unit = blockIdx.x;
+    u.kvh = unit % a.num_kv_heads;
+    u.s = unit / a.num_kv_heads;
+    u.p = 0;
+    u.ctx = __builtin_amdgcn_readfirstlane(a.context_lens[u.s]);
+    u.bad_len = bad_context(a, u.ctx);
+    u.tok_begin = 0;
+    u.tok_end = u.bad_len ? 0 : u.ctx;
+    u.nparts = 1;
+    u.empty = false;
     return true;
 }
 
@@ -290,7 +317,10 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, int *s_dyn,
     int *s_pf = s_dyn;
     int *s_pp = s_dyn + a.num_seqs + 1;
     int *s_ctx = s_dyn + 2 * (a.num_seqs + 1);
-    build_unit_order<PFX>(a, s_pf, s_pp, s_ctx, s_pages);
+    // no counter: one unit per workgroup by index (unsplit calls without a
+    // workspace; the plain instantiations only)
+    const bool direct = !PFX && a.work_counter == nullptr;
+    if (!direct) build_unit_order<PFX>(a, s_pf, s_pp, s_ctx, s_pages);
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -309,7 +339,8 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, int *s_dyn,
     bool first = true;
     // this workgroup's index among the drawers (the last `drawers` of the grid)
     const int drawer = (int)blockIdx.x - ((int)gridDim.x - drawers);
-    while (draw_unit<PFX>(a, s_pf, s_pp, s_ctx, &L.unit, u, drawers, drawer, first)) {
+    while (direct ? direct_unit(a, u, first)
+                  : draw_unit<PFX>(a, s_pf, s_pp, s_ctx, &L.unit, u, drawers, drawer, first)) {
         if (tid == 0) s_bad = 0;
 
         // query operand: head h0 + c % G, chunks 4j + q
@@ -581,17 +612,53 @@ void paged_prefix_fused_kernel(DecodeArgs a, PrefixArgs p, int prefix_wgs) {
     decode_body<DT, G, true, false>(a, s_dyn, lds.d, (int)gridDim.x - prefix_wgs);
 }
 
+// Resident workgroups per CU of a kernel and the CU count, per (kernel,
+// device, dynamic LDS rounded up to 4 KiB): the HIP queries run once per
+// entry, not on every call.  Rounding the LDS up can only lower the count.
+namespace {
+struct OccEntry {
+    const void *fn;
+    int dev;
+    int dyn_kb4;
+    int cus;
+    int per_cu;
+};
+constexpr int kOccEntries = 256;
+std::mutex g_occ_mu;
+OccEntry g_occ[kOccEntries];
+int g_occ_n = 0;
+
+hipError_t occupancy(const void *fn, size_t dyn, int &cus, int &per_cu) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const int kb4 = (int)((dyn + 4095) / 4096);
+    {
+        std::lock_guard<std::mutex> lock(g_occ_mu);
+        for (int i = 0; i < g_occ_n; ++i)
+            if (g_occ[i].fn == fn && g_occ[i].dev == dev && g_occ[i].dyn_kb4 == kb4) {
+                cus = g_occ[i].cus;
+                per_cu = g_occ[i].per_cu;
+                return hipSuccess;
+            }
+    }
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, (size_t)kb4 * 4096);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(g_occ_mu);
+    if (g_occ_n < kOccEntries) g_occ[g_occ_n++] = OccEntry{fn, dev, kb4, cus, per_cu};
+    return hipSuccess;
+}
+}  // namespace
+
 // Workgroups of a persistent grid: as many as are resident at once
-// (occupancy query with `dyn` bytes of dynamic LDS), at most PKV_WG_PER_CU
-// per CU, capped by `units`.  0 on a HIP error (returned in `e`).
+// (occupancy with `dyn` bytes of dynamic LDS), at most PKV_WG_PER_CU per CU,
+// capped by `units`.  0 on a HIP error (returned in `e`).
 template <typename K>
 static int64_t resident_grid(K kernel, size_t dyn, int64_t units, hipError_t &e) {
-    int dev = 0, cus = 0, per_cu = 0;
-    e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e == hipSuccess)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(kernel),
-                                                         kThreads, dyn);
+    int cus = 0, per_cu = 0;
+    e = occupancy(reinterpret_cast<const void *>(kernel), dyn, cus, per_cu);
     if (e != hipSuccess) return 0;
     if (per_cu > PKV_WG_PER_CU) per_cu = PKV_WG_PER_CU;
     const int64_t grid = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
@@ -599,9 +666,16 @@ static int64_t resident_grid(K kernel, size_t dyn, int64_t units, hipError_t &e)
 }
 
 // Persistent grid: as many workgroups as are resident at once, capped by
-// the number of units.
+// the number of units, drawing from the workspace counter.
+// Without a workspace (one partition per sequence only) one workgroup per
+// (sequence, KV head), no counter.
 template <typename K>
 static hipError_t launch_persistent(K kernel, const DecodeArgs &a, hipStream_t stream) {
+    if (a.work_counter == nullptr) {
+        const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads;
+        hipLaunchKernelGGL(kernel, dim3((unsigned)units), dim3(kThreads), 0, stream, a);
+        return hipGetLastError();
+    }
     const size_t dyn = (size_t)(3 * a.num_seqs + 2) * sizeof(int);
     const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * a.num_partitions;  // upper bound
     hipError_t e;
@@ -670,6 +744,7 @@ hipError_t launch_paged_prefix_fused(const PrefixArgs &p, const DecodeArgs &a, i
 }
 
 hipError_t launch_paged_decode_mfma_suffix(const DecodeArgs &a, int dtype, hipStream_t stream) {
+    if (a.work_counter == nullptr) return hipErrorInvalidValue;  // the suffix grid always draws
     if (dtype == kBF16) return launch_group<kBF16, true>(a, stream);
     if (dtype == kF16) return launch_group<kF16, true>(a, stream);
     return hipErrorInvalidValue;

@@ -37,6 +37,15 @@ int32_t num_partitions(int32_t max_context_len, int32_t partition_size) {
     return (int32_t)(((int64_t)max_context_len + partition_size - 1) / partition_size);
 }
 
+// A decode call needs its workspace when the context is split (partials);
+// an unsplit call may pass NULL (then one workgroup per unit, no counter).
+// A workspace that is passed must be large enough and 16-byte aligned.
+pkv_status check_workspace(const void *workspace, size_t workspace_bytes, int32_t parts, size_t need) {
+    if (!workspace) return parts > 1 ? PKV_ERR_WORKSPACE : PKV_OK;
+    if (workspace_bytes < need) return PKV_ERR_WORKSPACE;
+    return aligned16(workspace) ? PKV_OK : PKV_ERR_ALIGN;
+}
+
 // Shared-prefix plan: blocks of kPrefixRowsPerBlock query rows per KV head, and
 // the prefix cut into splits of whole 64-token chunks (at most 2048 tokens
 // each) so that about kPrefixTargetUnits workgroups share the prefix work.
@@ -173,10 +182,10 @@ pkv_status paged_decode_attention(void *out, const void *query, const void *key_
     const int64_t units = (int64_t)num_seqs * num_kv_heads * parts;
     if (units > INT_MAX || (int64_t)num_seqs * num_heads > INT_MAX) return PKV_ERR_SHAPE;
     pkv::DecodeArgs a = {};
-    const size_t need = paged_decode_workspace_size(num_seqs, num_heads, head_dim, max_context_len,
-                                                    partition_size);
-    if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
-    if (!aligned16(workspace)) return PKV_ERR_ALIGN;
+    const pkv_status ws = check_workspace(workspace, workspace_bytes, parts,
+                                          paged_decode_workspace_size(num_seqs, num_heads, head_dim,
+                                                                      max_context_len, partition_size));
+    if (ws != PKV_OK) return ws;
     a.work_counter = reinterpret_cast<unsigned *>(workspace);
     if (parts > 1) {
         a.part_out = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + kCounterBytes);
@@ -397,10 +406,10 @@ pkv_status paged_decode_attention_fp8(void *out, const void *query, const void *
     const int32_t parts = num_partitions(max_context_len, partition_size);
     if ((int64_t)num_seqs * num_kv_heads * parts > INT_MAX || (int64_t)num_seqs * num_heads > INT_MAX)
         return PKV_ERR_SHAPE;
-    const size_t need = paged_decode_workspace_size(num_seqs, num_heads, head_dim, max_context_len,
-                                                    partition_size);
-    if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
-    if (!aligned16(workspace)) return PKV_ERR_ALIGN;
+    const pkv_status ws = check_workspace(workspace, workspace_bytes, parts,
+                                          paged_decode_workspace_size(num_seqs, num_heads, head_dim,
+                                                                      max_context_len, partition_size));
+    if (ws != PKV_OK) return ws;
     pkv::DecodeArgs a = {};
     a.work_counter = reinterpret_cast<unsigned *>(workspace);
     if (parts > 1) {

@@ -239,7 +239,9 @@ __device__ __forceinline__ void merge_partials(const DecodeArgs &a, int64_t base
 constexpr int kMergeWideFrom = 32;
 
 // MFMA decode kernel launcher (16-bit caches, head_dim 128); the merge
-// kernel is launched by the caller.
+// kernel is launched by the caller.  Without a workspace counter
+// (a.work_counter == nullptr; one partition per sequence only) the grid is
+// one workgroup per (sequence, KV head).
 hipError_t launch_paged_decode_mfma(const DecodeArgs &a, int dtype, hipStream_t stream);
 // The same over E4M3 caches with per-KV-head scales (DT: query and output).
 hipError_t launch_paged_decode_mfma_e4m3(const DecodeArgs &a, int dtype, hipStream_t stream);

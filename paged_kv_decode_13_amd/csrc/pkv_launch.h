@@ -38,7 +38,9 @@ struct WriteE4M3Args {
 
 struct DecodeArgs {
     void *out;                  // [B, H, D] (out dtype)
-    unsigned *work_counter;     // unit dispenser of the persistent kernel (zero between calls)
+    unsigned *work_counter;     // unit dispenser of the persistent kernel (any initial
+                                // contents: the launch clears it first); nullptr: one
+                                // workgroup per unit, no counter (unsplit calls only)
     float *part_out;            // [B, H, P, D] when split
     float *part_ml;             // [B, H, P, 2] when split
     const void *query;          // [B, H, D]

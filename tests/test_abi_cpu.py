@@ -101,7 +101,9 @@ def test_decode_validation(lib):
     need = lib.paged_decode_workspace_size(4, 32, 128, 1024, 512)
     assert _decode(lib, ps=512, ws=A, wsb=need - 1) == WORKSPACE
     assert _decode(lib, ps=512, ws=A + 8, wsb=need) == ALIGN
-    assert _decode(lib, ps=0, ws=None) == WORKSPACE  # the unit counter lives there too
+    # an unsplit call may pass no workspace (one workgroup per unit); a split
+    # one needs it for the partials, whatever the partition count
+    assert _decode(lib, ps=512, maxc=513, ws=None) == WORKSPACE
     assert _decode(lib, b=0, q=None) == OK  # empty batch: nothing launched
 
 
@@ -204,7 +206,7 @@ def test_fp8_decode_validation(lib):
     assert _decode8(lib, ks=None) == NULL
     assert _decode8(lib, vs=None) == NULL
     assert _decode8(lib, vc=A + 8) == ALIGN
-    assert _decode8(lib, ws=None) == WORKSPACE
+    assert _decode8(lib, ps=512, ws=None) == WORKSPACE  # split: the partials need it
     assert _decode8(lib, b=0, q=None) == OK
 
 

@@ -2,10 +2,11 @@
 log-sum-exp merge included), and the shared-prefix call, captured in a HIP
 graph and replayed (MI355X).
 
-The library allocates nothing and clears nothing with memset (the unit
-counter of the persistent kernel resets itself at the end of every launch),
-so a captured step can be replayed as is.  Each replay is checked against an
-eager call on the same inputs, bit for bit, with eager work and
+The library allocates nothing and clears nothing with memset (the
+persistent decode kernel clears its own work counter when it starts), so a
+captured step can be replayed as is.
+Each replay is checked against an eager call on the same inputs, bit for
+bit, with eager work (which also scribbles over the workspace) and
 synchronisations between the replays, and the first against the oracle."""
 import numpy as np
 import pytest
@@ -34,7 +35,7 @@ def test_decode_step_replays_in_graph(cuda, kv):
                       device=dev)
     need = pkv.paged_decode_workspace_size(batch.num_seqs, batch.num_heads, batch.head_dim,
                                            batch.max_context_len, batch.partition_size)
-    ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
+    ws = torch.full((max(need, 1),), 255, dtype=torch.uint8, device=dev)
 
     def step():
         if quant:
@@ -80,6 +81,7 @@ def test_decode_step_replays_in_graph(cuda, kv):
         torch.cuda.synchronize()
         eager = out.clone()
         out.fill_(float("nan"))
+        ws.fill_(250 + i)  # a stale work counter and partials before the replay
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
@@ -106,7 +108,7 @@ def test_shared_prefix_call_replays_in_graph(cuda):
     out = torch.empty((b.num_seqs, b.num_heads, b.head_dim), dtype=torch.float32, device=dev)
     need = pkv.paged_prefix_decode_workspace_size(b.num_seqs, b.num_heads, b.num_kv_heads,
                                                   b.head_dim, b.max_context_len, prefix, 512)
-    ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
+    ws = torch.full((max(need, 1),), 255, dtype=torch.uint8, device=dev)
 
     def step():
         pkv.paged_prefix_decode_attention(t["q"], t["kc"], t["vc"], pt, prefix, t["bt"], t["cl"],
@@ -133,6 +135,7 @@ def test_shared_prefix_call_replays_in_graph(cuda):
         torch.cuda.synchronize()
         eager = out.clone()
         out.fill_(float("nan"))
+        ws.fill_(250 + i)  # a stale work counter and partials before the replay
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()

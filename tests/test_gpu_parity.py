@@ -167,27 +167,76 @@ def test_parity_is_sensitive_to_mutations(cuda):
     assert max_err(to_f64(gpu_step(b, t, out_dtype="f32")), ref) > TIGHT["bf16"]
 
 
-def test_workspace_counter_is_left_zero(cuda):
-    """One zero-filled workspace serves consecutive calls of different shapes:
-    each call leaves its work counter at zero, and every result matches."""
+def test_workspace_any_initial_contents(cuda):
+    """One workspace serves consecutive calls of different shapes, and before
+    every call it is overwritten with arbitrary bytes (the counter area
+    included: all ones, random, a count just below the call's last ticket):
+    no call depends on what an earlier call left there."""
     import torch
 
     import paged_kv_decode_13_amd as pkv
 
-    ws = torch.zeros(1 << 22, dtype=torch.uint8, device=cuda)
+    ws = torch.empty(1 << 22, dtype=torch.uint8, device=cuda)
+    gen = torch.Generator(device="cpu").manual_seed(5)
     cases = [([300, 17, 4000], 8, 2, 512), ([5000], 32, 8, 1024), ([1, 2, 3, 64, 65], 16, 4, 0),
              ([2049, 99], 8, 8, 2048)]
-    for lens, h, kvh, ps in cases * 2:
+    fills = ["ones", "random", "near_last"]
+    for i, (lens, h, kvh, ps) in enumerate(cases * 2):
         b = wl.make_batch(lens, num_heads=h, num_kv_heads=kvh, head_dim=128, block_size=16,
                           dtype="f16", seed=len(lens) + h)
         t = upload(b, cuda)
         assert pkv.paged_decode_workspace_size(b.num_seqs, h, 128, b.max_context_len, ps) <= ws.numel()
+        fill = fills[i % len(fills)]
+        if fill == "ones":
+            ws.fill_(255)
+        elif fill == "random":
+            ws.copy_(torch.randint(0, 256, (ws.numel(),), dtype=torch.uint8, generator=gen))
+        else:
+            ws.fill_(0)
+            ws[:4].view(torch.int32).fill_(3)  # a small stale count
         out = pkv.paged_decode_attention(t["q"], t["kc"], t["vc"], t["bt"], t["cl"], 16, b.scale,
                                          max_context_len=b.max_context_len, partition_size=ps,
                                          out_dtype=torch.float32, workspace=ws)
         torch.cuda.synchronize()
-        assert int(ws[:4].view(torch.int32).item()) == 0
-        assert max_err(to_f64(out), oracle_step(b)) <= TIGHT["f16"]
+        assert max_err(to_f64(out), oracle_step(b)) <= TIGHT["f16"], (i, fill)
+
+
+@pytest.mark.parametrize("kv", [None, "e4m3"], ids=["f16", "e4m3"])
+def test_unsplit_without_workspace(cuda, kv):
+    """An unsplit call with no workspace (one workgroup per (sequence, KV
+    head), no counter) matches the oracle for every group size; a split call
+    without one is refused."""
+    import torch
+
+    import paged_kv_decode_13_amd as pkv
+
+    lens = [0, 1, 15, 16, 17, 300, 1025, 2500]
+    for g in (1, 2, 4, 8):
+        b = wl.make_batch(lens, num_heads=4 * g, num_kv_heads=4, head_dim=128, block_size=16,
+                          dtype="f16", seed=40 + g, write_new_token=True, kv_dtype=kv)
+        t = upload(b, cuda)
+        if kv:
+            pkv.paged_kv_write_fp8(t["nk"], t["nv"], t["kc"], t["vc"], t["slots"], t["ks"], t["vs"])
+            out = pkv.paged_decode_attention_fp8(
+                t["q"], t["kc"], t["vc"], t["ks"], t["vs"], t["bt"], t["cl"], 16, b.scale,
+                max_context_len=b.max_context_len, out_dtype=torch.float32,
+                workspace=pkv.NO_WORKSPACE)
+        else:
+            pkv.paged_kv_write(t["nk"], t["nv"], t["kc"], t["vc"], t["slots"])
+            out = pkv.paged_decode_attention(t["q"], t["kc"], t["vc"], t["bt"], t["cl"], 16, b.scale,
+                                             max_context_len=b.max_context_len,
+                                             out_dtype=torch.float32, workspace=pkv.NO_WORKSPACE)
+        torch.cuda.synchronize()
+        assert max_err(to_f64(out), oracle_step(b)) <= TIGHT["f16"], g
+    with pytest.raises(pkv.PagedKVError, match="WORKSPACE"):
+        if kv:
+            pkv.paged_decode_attention_fp8(t["q"], t["kc"], t["vc"], t["ks"], t["vs"], t["bt"],
+                                           t["cl"], 16, b.scale, max_context_len=b.max_context_len,
+                                           partition_size=512, workspace=pkv.NO_WORKSPACE)
+        else:
+            pkv.paged_decode_attention(t["q"], t["kc"], t["vc"], t["bt"], t["cl"], 16, b.scale,
+                                       max_context_len=b.max_context_len, partition_size=512,
+                                       workspace=pkv.NO_WORKSPACE)
 
 
 def test_unit_order_edges(cuda):

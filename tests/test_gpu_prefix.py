@@ -94,11 +94,11 @@ def test_prefix_out_of_range_contents(cuda):
     torch.cuda.synchronize()
 
 
-def test_prefix_deterministic_and_counter_left_zero(cuda):
+def test_prefix_deterministic_any_workspace_contents(cuda):
     """Three calls on one workspace with two suffix partitions per sequence,
     i.e. through the launch that runs the prefix units beside the persistent
-    suffix grid: identical outputs, and the work counter back at zero after
-    each call."""
+    suffix grid, the workspace overwritten with arbitrary bytes before each
+    (the counter area included): identical outputs."""
     import torch
 
     import paged_kv_decode_13_amd as pkv
@@ -108,15 +108,15 @@ def test_prefix_deterministic_and_counter_left_zero(cuda):
     t = upload(b, cuda)
     need = pkv.paged_prefix_decode_workspace_size(b.num_seqs, 32, 8, 128, b.max_context_len, 2048,
                                                   512)
-    ws = torch.zeros(need, dtype=torch.uint8, device=cuda)
+    ws = torch.empty(need, dtype=torch.uint8, device=cuda)
     pt = torch.from_numpy(b.meta["prefix_table"]).to(cuda)
     outs = []
-    for _ in range(3):
+    for fill in (255, 7, 0):
+        ws.fill_(fill)
         outs.append(pkv.paged_prefix_decode_attention(
             t["q"], t["kc"], t["vc"], pt, 2048, t["bt"], t["cl"], 32, b.scale,
             max_context_len=b.max_context_len, partition_size=512, workspace=ws).clone())
         torch.cuda.synchronize()
-        assert int(ws[:256].count_nonzero()) == 0
     assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
     assert torch.equal(outs[0].view(torch.int16), outs[2].view(torch.int16))
     ref = oracle_prefix_step(b)
