@@ -163,6 +163,36 @@ pkv_status paged_decode_attention(
     void *stream);
 
 /*
+ * paged_decode_attention_noalloc -- paged_decode_attention for callers that
+ * cannot allocate device memory or pass a workspace: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  It calls
+ * no allocating routine; the work counter and split partials live in a
+ * library-owned static device array of PKV_NOALLOC_SCRATCH_BYTES bytes per
+ * GPU (taken when the library's code is loaded on that GPU, held until the
+ * process ends; its address is looked up on the first call per GPU).
+ *
+ * Arguments, result and errors are those of paged_decode_attention without
+ * the workspace.  A call whose paged_decode_workspace_size() exceeds
+ * PKV_NOALLOC_SCRATCH_BYTES returns PKV_ERR_WORKSPACE before anything is
+ * enqueued (a smaller partition count fits: raise partition_size or split
+ * the batch).  Every call on one GPU shares that GPU's array: no call
+ * depends on what an earlier one left there, but calls whose kernels can
+ * overlap on one GPU (different streams, or threads without ordering) race
+ * on it and must be serialised by the caller.  `stream` must belong to the
+ * GPU whose array is used (the current device when `stream` is NULL).
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+pkv_status paged_decode_attention_noalloc(
+    void *out, const void *query, const void *key_cache,
+    const void *value_cache, const int32_t *block_tables,
+    const int32_t *context_lens, int32_t num_seqs, int32_t num_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t max_blocks_per_seq, int64_t num_blocks, int32_t max_context_len,
+    float scale, int32_t partition_size, pkv_dtype dtype,
+    pkv_dtype out_dtype, void *stream);
+
+/*
  * paged_prefix_decode_workspace_size -- bytes of device scratch
  * paged_prefix_decode_attention needs (0 for an empty batch or invalid
  * sizes).  Layout: the 256-byte work-counter area, then fp32 partial outputs

@@ -30,6 +30,10 @@ Entry points (same names as the C ABI):
   paged_prefill_attention(query, key_cache, value_cache, block_tables,
                           context_lens, query_start_loc, block_size, scale,
                           *, max_context_len, out=None, out_dtype=None)
+  paged_decode_attention_noalloc(query, key_cache, value_cache, block_tables,
+                                 context_lens, block_size, scale, *,
+                                 max_context_len, partition_size=0, out,
+                                 out_dtype=None)
 E4M3 caches are uint8 or torch.float8_e4m3fn tensors.
 """
 from __future__ import annotations
@@ -46,6 +50,8 @@ __all__ = [
     "paged_kv_write_fp8",
     "paged_decode_attention_fp8",
     "paged_prefill_attention",
+    "paged_decode_attention_noalloc",
+    "NOALLOC_SCRATCH_BYTES",
     "library_path",
     "PagedKVError",
     "NO_WORKSPACE",
@@ -55,6 +61,9 @@ _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG_DIR, "libpagedkv.so")
 
 PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
+# PKV_NOALLOC_SCRATCH_BYTES of include/pagedkv.h: the static scratch of
+# paged_decode_attention_noalloc on each GPU
+NOALLOC_SCRATCH_BYTES = 32 << 20
 _STATUS = {0: "PKV_OK", 1: "PKV_ERR_NULL", 2: "PKV_ERR_SHAPE", 3: "PKV_ERR_DTYPE",
            4: "PKV_ERR_UNSUPPORTED", 5: "PKV_ERR_ALIGN", 6: "PKV_ERR_WORKSPACE", 7: "PKV_ERR_HIP"}
 
@@ -106,6 +115,10 @@ def _load():
     lib.paged_prefill_attention.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i32,
                                             i64, i32, ctypes.c_float, ctypes.c_int, ctypes.c_int, p]
     lib.paged_prefill_attention.restype = ctypes.c_int
+    lib.paged_decode_attention_noalloc.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32, i32,
+                                                   i64, i32, ctypes.c_float, i32, ctypes.c_int,
+                                                   ctypes.c_int, p]
+    lib.paged_decode_attention_noalloc.restype = ctypes.c_int
     lib.pkv_status_string.argtypes = [ctypes.c_int]
     lib.pkv_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -249,6 +262,45 @@ def paged_decode_attention(query, key_cache, value_cache, block_tables, context_
         _dtype_code(odt), ws_ptr, ws_bytes, _stream_handle(query.device))
     if st != 0:
         raise PagedKVError(st, "paged_decode_attention")
+    return out
+
+
+def paged_decode_attention_noalloc(query, key_cache, value_cache, block_tables, context_lens,
+                                   block_size: int, scale: float, *, max_context_len: int,
+                                   partition_size: int = 0, out, out_dtype=None):
+    """``paged_decode_attention`` through the entry point that allocates
+    nothing: the split partials live in the library's static scratch of
+    ``NOALLOC_SCRATCH_BYTES`` per GPU (larger requests raise PKV_ERR_WORKSPACE).
+    ``out`` is required, so the call allocates nothing here either.  Calls
+    whose kernels can overlap on one GPU share that scratch and race."""
+    torch = _torch()
+    lib = _load()
+    for t, n in ((query, "query"), (key_cache, "key_cache"), (value_cache, "value_cache"),
+                 (block_tables, "block_tables"), (context_lens, "context_lens"), (out, "out")):
+        _gpu(t, n)
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    nb, bs, kvh, d = key_cache.shape
+    if bs != block_size:
+        raise ValueError("block_size does not match key_cache.shape[1]")
+    b, h, dq = query.shape
+    if dq != d or value_cache.shape != key_cache.shape:
+        raise ValueError("inconsistent shapes")
+    if block_tables.dim() != 2 or block_tables.shape[0] != b or tuple(context_lens.shape) != (b,):
+        raise ValueError("block_tables must be [num_seqs, max_blocks], context_lens [num_seqs]")
+    if not (query.dtype == key_cache.dtype == value_cache.dtype):
+        raise TypeError("query and caches must share one dtype")
+    if tuple(out.shape) != (b, h, d):
+        raise ValueError("out must be [num_seqs, num_heads, head_dim]")
+    if out_dtype is not None and out.dtype != out_dtype:
+        raise TypeError("out_dtype does not match out")
+    st = lib.paged_decode_attention_noalloc(
+        out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+        block_tables.data_ptr(), context_lens.data_ptr(), b, h, kvh, d, bs, block_tables.shape[1],
+        nb, int(max_context_len), float(scale), int(partition_size), _dtype_code(query.dtype),
+        _dtype_code(out.dtype), _stream_handle(query.device))
+    if st != 0:
+        raise PagedKVError(st, "paged_decode_attention_noalloc")
     return out
 
 

@@ -5,6 +5,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "pagedkv.h"
 #include "pkv_launch.h"
 
@@ -96,6 +98,122 @@ PrefixPlan prefix_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads
     return p;
 }
 
+
+// Checks shared by the decode entry points, and the launch arguments they
+// imply (all but the workspace).  kv8: E4M3 caches (16-bit queries,
+// head_dim 128, per-KV-head scales).  `empty` is set for a batch with
+// nothing to launch (the status is then PKV_OK).
+pkv_status decode_setup(pkv::DecodeArgs &a, bool &empty, bool kv8, void *out, const void *query,
+                        const void *key_cache, const void *value_cache, const float *k_scale,
+                        const float *v_scale, const int32_t *block_tables,
+                        const int32_t *context_lens, int32_t num_seqs, int32_t num_heads,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                        int32_t max_blocks_per_seq, int64_t num_blocks, int32_t max_context_len,
+                        float scale, int32_t partition_size, pkv_dtype dtype, pkv_dtype out_dtype) {
+    empty = false;
+    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq < 0 ||
+        num_blocks < 0 || max_context_len < 0 || partition_size < 0)
+        return PKV_ERR_SHAPE;
+    if (num_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
+    if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return PKV_ERR_DTYPE;
+    if (out_dtype != dtype && out_dtype != PKV_F32) return PKV_ERR_DTYPE;
+    if (kv8 ? (dtype == PKV_F32 || head_dim != 128) : (head_dim != 64 && head_dim != 128))
+        return PKV_ERR_UNSUPPORTED;
+    if (!pow2_block(block_size)) return PKV_ERR_UNSUPPORTED;
+    const int32_t group = num_heads / num_kv_heads;
+    if (group != 1 && group != 2 && group != 4 && group != 8) return PKV_ERR_UNSUPPORTED;
+    if (partition_size != 0 && partition_size % partition_granule(block_size) != 0)
+        return PKV_ERR_UNSUPPORTED;
+    if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size) return PKV_ERR_SHAPE;
+    if (num_blocks == 0 && max_context_len > 0) return PKV_ERR_SHAPE;  // no page to read
+    if (!isfinite(scale)) return PKV_ERR_SHAPE;
+    if (num_seqs > PKV_MAX_SEQS) return PKV_ERR_UNSUPPORTED;
+    if (num_seqs == 0) {
+        empty = true;
+        return PKV_OK;
+    }
+    if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens ||
+        (kv8 && (!k_scale || !v_scale)))
+        return PKV_ERR_NULL;
+    if (!aligned16(out) || !aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache))
+        return PKV_ERR_ALIGN;
+    const int32_t parts = num_partitions(max_context_len, partition_size);
+    if ((int64_t)num_seqs * num_kv_heads * parts > INT_MAX || (int64_t)num_seqs * num_heads > INT_MAX)
+        return PKV_ERR_SHAPE;
+    a = pkv::DecodeArgs{};
+    a.out = out;
+    a.query = query;
+    a.key_cache = key_cache;
+    a.value_cache = value_cache;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.num_blocks = num_blocks;
+    a.num_seqs = num_seqs;
+    a.num_heads = num_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.block_size = block_size;
+    a.log2_block_size = log2i(block_size);
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.max_context_len = max_context_len;
+    // Unsplit: one unit covers any admissible context.
+    a.partition_size = parts > 1 ? partition_size : (max_context_len > 0 ? max_context_len : 1);
+    a.num_partitions = parts;
+    a.scale_log2e = scale * 1.4426950408889634f;
+    a.out_f32 = out_dtype == PKV_F32 ? 1 : 0;
+    a.token_begin = 0;
+    a.part_stride = parts;
+    a.part_base = 0;
+    a.direct_out = 0;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    return PKV_OK;
+}
+
+// Point the launch arguments at a workspace laid out as
+// paged_decode_workspace_size describes (NULL: no counter, no partials).
+void bind_workspace(pkv::DecodeArgs &a, void *workspace, int32_t head_dim) {
+    a.work_counter = reinterpret_cast<unsigned *>(workspace);
+    a.part_out = nullptr;
+    a.part_ml = nullptr;
+    if (workspace && a.num_partitions > 1) {
+        a.part_out = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + kCounterBytes);
+        a.part_ml = a.part_out + (size_t)a.num_seqs * a.num_heads * a.num_partitions * head_dim;
+    }
+}
+
+// Scratch of the entry point that allocates nothing: one array per GPU the
+// library runs on, held until the process ends.  In host code `scratch`
+// only names the variable; its device address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+static __device__ __align__(256) unsigned char scratch[PKV_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// Device address of the scratch array on the device `stream` runs on.
+hipError_t scratch_address(hipStream_t stream, void **ptr) {
+    int dev = 0;
+    hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = 0;
+        e = hipGetDevice(&cur);
+        if (e != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        const hipError_t back = cur != dev ? hipSetDevice(cur) : hipSuccess;
+        if (e != hipSuccess) return e;
+        if (back != hipSuccess) return back;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 }  // namespace
 
 extern "C" {
@@ -156,66 +274,46 @@ pkv_status paged_decode_attention(void *out, const void *query, const void *key_
                                   int32_t max_context_len, float scale, int32_t partition_size,
                                   pkv_dtype dtype, pkv_dtype out_dtype, void *workspace,
                                   size_t workspace_bytes, void *stream) {
-    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq < 0 ||
-        num_blocks < 0 || max_context_len < 0 || partition_size < 0)
-        return PKV_ERR_SHAPE;
-    if (num_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
-    if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return PKV_ERR_DTYPE;
-    if (out_dtype != dtype && out_dtype != PKV_F32) return PKV_ERR_DTYPE;
-    if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
-    if (!pow2_block(block_size)) return PKV_ERR_UNSUPPORTED;
-    const int32_t group = num_heads / num_kv_heads;
-    if (group != 1 && group != 2 && group != 4 && group != 8) return PKV_ERR_UNSUPPORTED;
-    if (partition_size != 0 && partition_size % partition_granule(block_size) != 0)
-        return PKV_ERR_UNSUPPORTED;
-    if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size) return PKV_ERR_SHAPE;
-    if (num_blocks == 0 && max_context_len > 0) return PKV_ERR_SHAPE;  // no page to read
-    if (!isfinite(scale)) return PKV_ERR_SHAPE;
-    if (num_seqs > PKV_MAX_SEQS) return PKV_ERR_UNSUPPORTED;
-    if (num_seqs == 0) return PKV_OK;
-    if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens)
-        return PKV_ERR_NULL;
-    if (!aligned16(out) || !aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache))
-        return PKV_ERR_ALIGN;
-
-    const int32_t parts = num_partitions(max_context_len, partition_size);
-    const int64_t units = (int64_t)num_seqs * num_kv_heads * parts;
-    if (units > INT_MAX || (int64_t)num_seqs * num_heads > INT_MAX) return PKV_ERR_SHAPE;
-    pkv::DecodeArgs a = {};
-    const pkv_status ws = check_workspace(workspace, workspace_bytes, parts,
-                                          paged_decode_workspace_size(num_seqs, num_heads, head_dim,
-                                                                      max_context_len, partition_size));
-    if (ws != PKV_OK) return ws;
-    a.work_counter = reinterpret_cast<unsigned *>(workspace);
-    if (parts > 1) {
-        a.part_out = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + kCounterBytes);
-        a.part_ml = a.part_out + (size_t)num_seqs * num_heads * parts * head_dim;
-    }
-    a.out = out;
-    a.query = query;
-    a.key_cache = key_cache;
-    a.value_cache = value_cache;
-    a.block_tables = block_tables;
-    a.context_lens = context_lens;
-    a.num_blocks = num_blocks;
-    a.num_seqs = num_seqs;
-    a.num_heads = num_heads;
-    a.num_kv_heads = num_kv_heads;
-    a.block_size = block_size;
-    a.log2_block_size = log2i(block_size);
-    a.max_blocks_per_seq = max_blocks_per_seq;
-    a.max_context_len = max_context_len;
-    // Unsplit: one unit covers any admissible context.
-    a.partition_size = parts > 1 ? partition_size : (max_context_len > 0 ? max_context_len : 1);
-    a.num_partitions = parts;
-    a.scale_log2e = scale * 1.4426950408889634f;
-    a.out_f32 = out_dtype == PKV_F32 ? 1 : 0;
-    a.token_begin = 0;
-    a.part_stride = parts;
-    a.part_base = 0;
-    a.direct_out = 0;
+    pkv::DecodeArgs a;
+    bool empty = false;
+    pkv_status st = decode_setup(a, empty, false, out, query, key_cache, value_cache, nullptr, nullptr,
+                                 block_tables, context_lens, num_seqs, num_heads, num_kv_heads,
+                                 head_dim, block_size, max_blocks_per_seq, num_blocks,
+                                 max_context_len, scale, partition_size, dtype, out_dtype);
+    if (st != PKV_OK || empty) return st;
+    st = check_workspace(workspace, workspace_bytes, a.num_partitions,
+                         paged_decode_workspace_size(num_seqs, num_heads, head_dim, max_context_len,
+                                                     partition_size));
+    if (st != PKV_OK) return st;
+    bind_workspace(a, workspace, head_dim);
     hipError_t e = pkv::launch_paged_decode(a, (int)dtype, head_dim,
                                             reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+pkv_status paged_decode_attention_noalloc(void *out, const void *query, const void *key_cache,
+                                          const void *value_cache, const int32_t *block_tables,
+                                          const int32_t *context_lens, int32_t num_seqs,
+                                          int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                          int32_t block_size, int32_t max_blocks_per_seq,
+                                          int64_t num_blocks, int32_t max_context_len, float scale,
+                                          int32_t partition_size, pkv_dtype dtype,
+                                          pkv_dtype out_dtype, void *stream) {
+    pkv::DecodeArgs a;
+    bool empty = false;
+    pkv_status st = decode_setup(a, empty, false, out, query, key_cache, value_cache, nullptr, nullptr,
+                                 block_tables, context_lens, num_seqs, num_heads, num_kv_heads,
+                                 head_dim, block_size, max_blocks_per_seq, num_blocks,
+                                 max_context_len, scale, partition_size, dtype, out_dtype);
+    if (st != PKV_OK || empty) return st;
+    if (paged_decode_workspace_size(num_seqs, num_heads, head_dim, max_context_len, partition_size) >
+        PKV_NOALLOC_SCRATCH_BYTES)
+        return PKV_ERR_WORKSPACE;
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    void *ws = nullptr;
+    if (scratch_address(s, &ws) != hipSuccess) return PKV_ERR_HIP;
+    bind_workspace(a, ws, head_dim);
+    hipError_t e = pkv::launch_paged_decode(a, (int)dtype, head_dim, s);
     return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
@@ -381,62 +479,18 @@ pkv_status paged_decode_attention_fp8(void *out, const void *query, const void *
                                       int64_t num_blocks, int32_t max_context_len, float scale,
                                       int32_t partition_size, pkv_dtype dtype, pkv_dtype out_dtype,
                                       void *workspace, size_t workspace_bytes, void *stream) {
-    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq < 0 ||
-        num_blocks < 0 || max_context_len < 0 || partition_size < 0)
-        return PKV_ERR_SHAPE;
-    if (num_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
-    if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return PKV_ERR_DTYPE;
-    if (out_dtype != dtype && out_dtype != PKV_F32) return PKV_ERR_DTYPE;
-    if (dtype == PKV_F32 || head_dim != 128) return PKV_ERR_UNSUPPORTED;
-    if (!pow2_block(block_size)) return PKV_ERR_UNSUPPORTED;
-    const int32_t group = num_heads / num_kv_heads;
-    if (group != 1 && group != 2 && group != 4 && group != 8) return PKV_ERR_UNSUPPORTED;
-    if (partition_size != 0 && partition_size % partition_granule(block_size) != 0)
-        return PKV_ERR_UNSUPPORTED;
-    if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size) return PKV_ERR_SHAPE;
-    if (num_blocks == 0 && max_context_len > 0) return PKV_ERR_SHAPE;
-    if (!isfinite(scale)) return PKV_ERR_SHAPE;
-    if (num_seqs > PKV_MAX_SEQS) return PKV_ERR_UNSUPPORTED;
-    if (num_seqs == 0) return PKV_OK;
-    if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens ||
-        !k_scale || !v_scale)
-        return PKV_ERR_NULL;
-    if (!aligned16(out) || !aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache))
-        return PKV_ERR_ALIGN;
-    const int32_t parts = num_partitions(max_context_len, partition_size);
-    if ((int64_t)num_seqs * num_kv_heads * parts > INT_MAX || (int64_t)num_seqs * num_heads > INT_MAX)
-        return PKV_ERR_SHAPE;
-    const pkv_status ws = check_workspace(workspace, workspace_bytes, parts,
-                                          paged_decode_workspace_size(num_seqs, num_heads, head_dim,
-                                                                      max_context_len, partition_size));
-    if (ws != PKV_OK) return ws;
-    pkv::DecodeArgs a = {};
-    a.work_counter = reinterpret_cast<unsigned *>(workspace);
-    if (parts > 1) {
-        a.part_out = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + kCounterBytes);
-        a.part_ml = a.part_out + (size_t)num_seqs * num_heads * parts * head_dim;
-    }
-    a.out = out;
-    a.query = query;
-    a.key_cache = key_cache;
-    a.value_cache = value_cache;
-    a.block_tables = block_tables;
-    a.context_lens = context_lens;
-    a.num_blocks = num_blocks;
-    a.num_seqs = num_seqs;
-    a.num_heads = num_heads;
-    a.num_kv_heads = num_kv_heads;
-    a.block_size = block_size;
-    a.log2_block_size = log2i(block_size);
-    a.max_blocks_per_seq = max_blocks_per_seq;
-    a.max_context_len = max_context_len;
-    a.partition_size = parts > 1 ? partition_size : (max_context_len > 0 ? max_context_len : 1);
-    a.num_partitions = parts;
-    a.scale_log2e = scale * 1.4426950408889634f;
-    a.out_f32 = out_dtype == PKV_F32 ? 1 : 0;
-    a.part_stride = parts;
-    a.k_scale = k_scale;
-    a.v_scale = v_scale;
+    pkv::DecodeArgs a;
+    bool empty = false;
+    pkv_status st = decode_setup(a, empty, true, out, query, key_cache, value_cache, k_scale, v_scale,
+                                 block_tables, context_lens, num_seqs, num_heads, num_kv_heads,
+                                 head_dim, block_size, max_blocks_per_seq, num_blocks,
+                                 max_context_len, scale, partition_size, dtype, out_dtype);
+    if (st != PKV_OK || empty) return st;
+    st = check_workspace(workspace, workspace_bytes, a.num_partitions,
+                         paged_decode_workspace_size(num_seqs, num_heads, head_dim, max_context_len,
+                                                     partition_size));
+    if (st != PKV_OK) return st;
+    bind_workspace(a, workspace, head_dim);
     hipError_t e = pkv::launch_paged_decode_e4m3(a, (int)dtype, reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }

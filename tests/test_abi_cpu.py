@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
                           "paged_decode_attention", "paged_prefix_decode_workspace_size",
                           "paged_prefix_decode_attention", "paged_kv_write_fp8",
                           "paged_decode_attention_fp8", "paged_prefill_attention",
-                          "pkv_status_string"}
+                          "paged_decode_attention_noalloc", "pkv_status_string"}
     out = subprocess.run(["nm", "-D", "--defined-only", lib._name], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
@@ -105,6 +105,40 @@ def test_decode_validation(lib):
     # one needs it for the partials, whatever the partition count
     assert _decode(lib, ps=512, maxc=513, ws=None) == WORKSPACE
     assert _decode(lib, b=0, q=None) == OK  # empty batch: nothing launched
+
+
+def _noalloc(lib, **kw):
+    a = dict(out=A, q=A, kc=A, vc=A, bt=A, cl=A, b=4, h=32, kvh=8, d=128, bs=16, mb=64, nb=1000,
+             maxc=1024, scale=0.088, ps=0, dt=BF16, odt=BF16)
+    a.update(kw)
+    return lib.paged_decode_attention_noalloc(
+        a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["cl"], a["b"], a["h"], a["kvh"], a["d"],
+        a["bs"], a["mb"], a["nb"], a["maxc"], a["scale"], a["ps"], a["dt"], a["odt"], None)
+
+
+def test_noalloc_validation(lib):
+    """The entry point without a workspace: the same host checks as the
+    decode, and a request whose partials exceed the static scratch is
+    refused before anything is looked up or launched."""
+    p, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.paged_decode_attention_noalloc.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32, i32,
+                                                   i64, i32, ctypes.c_float, i32, ctypes.c_int,
+                                                   ctypes.c_int, p]
+    lib.paged_decode_attention_noalloc.restype = ctypes.c_int
+    assert _noalloc(lib, kvh=5) == SHAPE
+    assert _noalloc(lib, dt=7) == DTYPE
+    assert _noalloc(lib, d=96) == UNSUP
+    assert _noalloc(lib, ps=24) == UNSUP
+    assert _noalloc(lib, q=None) == NULL
+    assert _noalloc(lib, out=A + 4) == ALIGN
+    assert _noalloc(lib, b=0, q=None) == OK
+    # 32 MiB of scratch: 256 sequences x 32 heads x 8 partitions x 130 floats
+    # is 34 MB of partials, one partition fewer fits
+    scratch = 32 << 20
+    big = lib.paged_decode_workspace_size(256, 32, 128, 8 * 2048, 2048)
+    fits = lib.paged_decode_workspace_size(256, 32, 128, 7 * 2048, 2048)
+    assert fits <= scratch < big
+    assert _noalloc(lib, b=256, mb=1024, maxc=8 * 2048, ps=2048) == WORKSPACE
 
 
 def test_workspace_size(lib):
