@@ -28,3 +28,22 @@ def test_multi_gpu_request_is_refused():
                          capture_output=True, text=True, timeout=120)
     assert res.returncode == 2
     assert "one GPU" in res.stderr
+
+
+def test_parity_flags_errors_and_nan():
+    import numpy as np
+    import torch
+
+    ref = np.zeros((2, 3), dtype=np.float64)
+    ok = bench.parity(torch.full((2, 3), 4e-3), ref, "bf16", "six")
+    assert ok["ok"] and abs(ok["max_abs_err"] - 4e-3) < 1e-9
+    assert not bench.parity(torch.full((2, 3), 6e-3), ref, "bf16", "six")["ok"]
+    assert not bench.parity(torch.full((2, 3), 2e-5), ref, "f32", "six")["ok"]
+    nan = torch.zeros(2, 3)
+    nan[1, 2] = float("nan")
+    assert not bench.parity(nan, ref, "f16", "six")["ok"]
+
+
+def test_cpu_model_is_reported():
+    name = bench.cpu_model()
+    assert name is None or (isinstance(name, str) and name)
