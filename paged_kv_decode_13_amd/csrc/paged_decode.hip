@@ -203,7 +203,7 @@ __global__ __launch_bounds__(kThreads) void paged_decode_valu_kernel(DecodeArgs 
     }
     __syncthreads();
 
-    unit_epilogue<DT, D, G>(a, up, up.bad_len || s_bad != 0, s_m, s_l, &s_acc[0][0][0]);
+    unit_epilogue<DT, D, G>(a, up, up.p, up.bad_len || s_bad != 0, s_m, s_l, &s_acc[0][0][0]);
 }
 
 // Log-sum-exp merge of the partitions of one (sequence, query head), one

@@ -64,6 +64,11 @@
 #ifndef PKV_WG_PER_CU
 #define PKV_WG_PER_CU 2
 #endif
+// Register budget of the decode kernels: the allocator is held to this many
+// resident waves per SIMD (3: at most 168 VGPRs)
+#ifndef PKV_DECODE_MIN_WAVES
+#define PKV_DECODE_MIN_WAVES 3
+#endif
 
 namespace pkv {
 
@@ -100,11 +105,12 @@ __device__ __forceinline__ u32x4 widen_e4m3(const u32x2 w) {
                  e4m3_pair<DT, true>(w.y)};
 }
 
-// Unit order: all full partitions of the batch first, then the partial last
-// partitions.  Units of one size drain the grid evenly and the variable-size
+// Unit order: all whole runs of unit_parts partitions of the batch first,
+// then the single partitions after each sequence's runs (its last one may be
+// partial).  Units of one size drain the grid evenly and the variable-size
 // units come at the end, where they fill the gaps.  Builds the exclusive
-// prefix sums s_pf[0..B] (full partitions) and s_pp[0..B] (partial ones)
-// and caches the lengths in s_ctx.
+// prefix sums s_pf[0..B] (runs) and s_pp[0..B] (single partitions) and
+// caches the lengths in s_ctx.
 template <bool PFX>
 __device__ __forceinline__ void build_unit_order(const DecodeArgs &a, int *s_pf, int *s_pp,
                                                  int *s_ctx, int *s_scan) {
@@ -116,9 +122,9 @@ __device__ __forceinline__ void build_unit_order(const DecodeArgs &a, int *s_pf,
     for (int s = lo; s < hi; ++s) {
         const int ctx = a.context_lens[s];
         s_ctx[s] = ctx;
-        const int f = seq_full<PFX>(a, ctx);
+        const int f = seq_full_units<PFX>(a, ctx);
         nf += f;
-        np += seq_parts<PFX>(a, ctx) - f;
+        np += seq_units<PFX>(a, ctx) - f;
     }
     const int incf = block_scan(nf, s_scan);
     const int incp = block_scan(np, s_scan);
@@ -126,9 +132,9 @@ __device__ __forceinline__ void build_unit_order(const DecodeArgs &a, int *s_pf,
     for (int s = lo; s < hi; ++s) {
         s_pf[s] = rf;
         s_pp[s] = rp;
-        const int f = seq_full<PFX>(a, s_ctx[s]);
+        const int f = seq_full_units<PFX>(a, s_ctx[s]);
         rf += f;
-        rp += seq_parts<PFX>(a, s_ctx[s]) - f;
+        rp += seq_units<PFX>(a, s_ctx[s]) - f;
     }
     if (tid == kThreads - 1) {
         s_pf[B] = incf;
@@ -146,19 +152,27 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs &a, const int *s_pf
     const int total_full = s_pf[a.num_seqs];
     u.kvh = unit % a.num_kv_heads;
     const int sp = unit / a.num_kv_heads;
-    if (sp < total_full) {
+    int span;
+    if (sp < total_full) {  // a whole run of unit_parts partitions
         u.s = search_le(s_pf, a.num_seqs, sp);
         u.p = sp - s_pf[u.s];
-    } else {
-        u.s = search_le(s_pp, a.num_seqs, sp - total_full);
-        u.p = seq_full<PFX>(a, s_ctx[u.s]);
+        u.part0 = u.p * a.unit_parts;
+        span = run_tokens(a);
+    } else {                // one of the partitions after the sequence's runs
+        const int r = sp - total_full;
+        u.s = search_le(s_pp, a.num_seqs, r);
+        const int runs = seq_full_units<PFX>(a, s_ctx[u.s]);
+        u.p = runs + r - s_pp[u.s];
+        u.part0 = runs * a.unit_parts + r - s_pp[u.s];
+        span = a.partition_size;
     }
     u.s = __builtin_amdgcn_readfirstlane(u.s);
     u.p = __builtin_amdgcn_readfirstlane(u.p);
+    u.part0 = __builtin_amdgcn_readfirstlane(u.part0);
     u.ctx = __builtin_amdgcn_readfirstlane(s_ctx[u.s]);
     u.bad_len = bad_context(a, u.ctx);
-    u.tok_begin = first_token<PFX>(a) + u.p * a.partition_size;
-    u.tok_end = u.bad_len ? 0 : min(u.ctx, u.tok_begin + a.partition_size);
+    u.tok_begin = first_token<PFX>(a) + u.part0 * a.partition_size;
+    u.tok_end = u.bad_len ? 0 : min(u.ctx, u.tok_begin + span);
     u.nparts = seq_parts<PFX>(a, u.ctx);
     u.empty = false;
 }
@@ -224,6 +238,7 @@ __device__ __forceinline__ bool direct_unit(const DecodeArgs &a, Unit &u, bool &
     u.bad_len = bad_context(a, u.ctx);
     u.tok_begin = 0;
     u.tok_end = u.bad_len ? 0 : u.ctx;
+    u.part0 = 0;
     u.nparts = 1;
     u.empty = false;
     return true;
@@ -269,8 +284,11 @@ __device__ __forceinline__ bool direct_unit(const DecodeArgs &a, Unit &u, bool &
 // loads in flight.
 template <bool KV8>
 constexpr int tiles_per_step() { return KV8 ? PKV_TILES_PER_STEP_E4M3 : PKV_TILES_PER_STEP; }
+#ifndef PKV_QOP_LDS
+#define PKV_QOP_LDS (PKV_DECODE_MIN_WAVES >= 3)
+#endif
 template <bool KV8>
-constexpr bool qop_in_lds() { return tiles_per_step<KV8>() > 2; }
+constexpr bool qop_in_lds() { return PKV_QOP_LDS && tiles_per_step<KV8>() > 2; }
 
 // One wave's LDS region: the K rows of the 16-token tile being scored (the
 // score operand transpose), then the wave's accumulators for the epilogue.
@@ -291,7 +309,7 @@ struct DecodeLds {
 // The decode work loop of one workgroup, as a device function over LDS the
 // kernel provides (s_dyn: full-unit prefix [B + 1], partial-unit prefix
 // [B + 1], lengths [B]); drawers = the launch's workgroups that draw units.
-template <int DT, int G, bool PFX, bool KV8>
+template <int DT, int G, bool PFX, bool KV8, bool RUNS>
 __device__ __forceinline__ void decode_body(const DecodeArgs &a, int *s_dyn,
                                             DecodeLds<G, qop_in_lds<KV8>()> &L, int drawers) {
     constexpr int D = 128;
@@ -358,192 +376,203 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, int *s_dyn,
             }
         }
 
-        float m = -INFINITY;  // reference max of column c (equal in the four row groups)
-        float lsum = 0.f;     // this lane's share of column c's normaliser
-        f32x4_t acc[8];       // block dt: dims 8 (4q + r) + dt of column c
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
         const int64_t kvh_off = (int64_t)u.kvh * KV_ROW;
         float sl2 = a.scale_log2e;
         if constexpr (KV8) sl2 *= a.k_scale[u.kvh];
 
-        for (int seg = u.tok_begin; seg < u.tok_end; seg += kSegPages << lbs) {
-            const int seg_end = min(u.tok_end, seg + (kSegPages << lbs));
-            const int npages = (seg_end - seg + bs - 1) >> lbs;
-            __syncthreads();  // previous segment's readers are done with s_pages
-            stage_pages(a, u, seg >> lbs, npages, s_pages, &s_bad);
+        // page ids staged in LDS for tokens [stg_lo, stg_hi) (npages pages);
+        // the running state of the partition being streamed; tokens at or
+        // past seg_end are masked.  All wave-uniform.
+        int stg_lo = u.tok_begin, stg_hi = u.tok_begin, npages = 0, seg_end = 0;
+        float m = -INFINITY;  // reference max of column c (equal in the four row groups)
+        float lsum = 0.f;     // this lane's share of column c's normaliser
+        f32x4_t acc[8];       // block dt: dims 8 (4q + r) + dt of column c
+        auto reset = [&]() {
+            m = -INFINITY;
+            lsum = 0.f;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        };
+        auto stage = [&](int lo, int hi) {
+            stg_lo = lo;  // a page boundary: partitions and staged windows start on one
+            stg_hi = hi;
+            npages = (hi - lo + bs - 1) >> lbs;
+            __syncthreads();  // the previous window's readers are done with s_pages
+            stage_pages(a, u, lo >> lbs, npages, s_pages, &s_bad);
             __syncthreads();
+        };
 
-            // Byte offset of this lane's chunk of token t0 + 4q, the first of
-            // its four consecutive tokens (t0 is a multiple of 4 and pages
-            // hold >= 4 tokens, so the four share a page and lie one
-            // tok_stride apart).  A token past the segment or on a bad page id
-            // reads a row of page 0 (always in the pool) and is flagged
-            // invalid in `vmask` (its V zeroed; its score masked, or the
-            // output made NaN by the bad-page flag).
-            auto tile_base = [&](int t0, uint32_t &vmask) -> int64_t {
-                const int t = t0 + 4 * q;
-                const int pb = s_pages[min((t - seg) >> lbs, npages - 1)];
-                const int n_ok = pb >= 0 ? min(max(seg_end - t, 0), 4) : 0;
-                vmask = (1u << n_ok) - 1u;
-                const int64_t page = pb >= 0 ? pb : 0;
-                return (page * bs + (t & (bs - 1))) * tok_stride + kvh_off + c * KV_CHUNK;
-            };
-            auto load_k = [&](TileRegs &r, int t0) {
-                uint32_t unused;
-                const char *p = kbase + tile_base(t0, unused);
+        // Byte offset of this lane's chunk of token t0 + 4q, the first of
+        // its four consecutive tokens (t0 is a multiple of 4 and pages
+        // hold >= 4 tokens, so the four share a page and lie one
+        // tok_stride apart).  A token at or past seg_end (the end of the
+        // partition or of the staged window) or on a bad page id
+        // reads a row of page 0 (always in the pool) and is flagged
+        // invalid in `vmask` (its V zeroed; its score masked, or the
+        // output made NaN by the bad-page flag).
+        auto tile_base = [&](int t0, uint32_t &vmask) -> int64_t {
+            const int t = t0 + 4 * q;
+            const int pb = s_pages[min((t - stg_lo) >> lbs, npages - 1)];
+            const int n_ok = pb >= 0 ? min(max(seg_end - t, 0), 4) : 0;
+            vmask = (1u << n_ok) - 1u;
+            const int64_t page = pb >= 0 ? pb : 0;
+            return (page * bs + (t & (bs - 1))) * tok_stride + kvh_off + c * KV_CHUNK;
+        };
+        auto load_k = [&](TileRegs &r, int t0) {
+            uint32_t unused;
+            const char *p = kbase + tile_base(t0, unused);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if constexpr (KV8) r.k[i] = load8_stream(p + i * tok_stride);
+                else r.k[i] = load16_stream(p + i * tok_stride);
+            }
+        };
+        auto load_v = [&](TileRegs &r, int t0) {
+            const char *p = vbase + tile_base(t0, r.vmask);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if constexpr (KV8) r.v[i] = load8_stream(p + i * tok_stride);
+                else r.v[i] = load16_stream(p + i * tok_stride);
+            }
+        };
+        // S^T of one tile: K rows -> LDS (16-byte chunks XOR-swizzled by
+        // token), read back so that lane (q, c) holds token c, chunks
+        // 4j + q; four MFMAs against the query operand.  Rows are private
+        // to the wave and its LDS operations complete in order.
+        auto tile_scores = [&](const TileRegs &r) -> f32x4_t {
+            // E4M3 rows stay 8-bit in LDS (8-byte chunks, 128-byte rows)
+            // and are widened after the read, one operand at a time
+            constexpr int LROW = KV8 ? D : ROW_BYTES;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int tt = 4 * q + i;
+                char *dst = kt + tt * LROW + ((c ^ tt) & 15) * KV_CHUNK;
+                if constexpr (KV8) *reinterpret_cast<u32x2 *>(dst) = r.k[i];
+                else *reinterpret_cast<u32x4 *>(dst) = r.k[i];
+            }
+            asm volatile("" ::: "memory");
+            f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const char *src = kt + c * LROW + (((4 * j + q) ^ c) & 15) * KV_CHUNK;
+                u32x4 kop;
+                if constexpr (KV8) kop = widen_e4m3<DT>(*reinterpret_cast<const u32x2 *>(src));
+                else kop = *reinterpret_cast<const u32x4 *>(src);
+                sacc = mfma_16x16x32<DT>(kop, kQopLds ? s_qop[j][lane] : qop[j], sacc);
+            }
+            asm volatile("" ::: "memory");
+            return sacc;
+        };
+        // softmax and value product of the pair (tiles A, B at t0, t0 + 16)
+        // whose scores are sa, sb
+        auto pair_values = [&](const f32x4_t sa, const f32x4_t sb, const TileRegs &ra,
+                               const TileRegs &rb, int t0) {
+            float sc[8];  // tokens t0 + 4q + i (i < 4), t0 + 16 + 4q + i - 4 (i >= 4)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                sc[i] = sa[i] * sl2;
+                sc[4 + i] = sb[i] * sl2;
+            }
+            if (t0 + 2 * TILE > seg_end) {  // wave-uniform: only at the end of a segment
+                // tokens of this lane before the end; the count passes
+                // through an empty asm inside the branch, so the compares
+                // cannot be hoisted out of it
+                int nv = seg_end - (t0 + 4 * q);
+                asm volatile("" : "+v"(nv));
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    if constexpr (KV8) r.k[i] = load8_stream(p + i * tok_stride);
-                    else r.k[i] = load16_stream(p + i * tok_stride);
+                    sc[i] = (i < nv) ? sc[i] : -INFINITY;
+                    sc[4 + i] = (TILE + i < nv) ? sc[4 + i] : -INFINITY;
                 }
-            };
-            auto load_v = [&](TileRegs &r, int t0) {
-                const char *p = vbase + tile_base(t0, r.vmask);
+            }
+            float mx = sc[0];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    if constexpr (KV8) r.v[i] = load8_stream(p + i * tok_stride);
-                    else r.v[i] = load16_stream(p + i * tok_stride);
-                }
-            };
-            // S^T of one tile: K rows -> LDS (16-byte chunks XOR-swizzled by
-            // token), read back so that lane (q, c) holds token c, chunks
-            // 4j + q; four MFMAs against the query operand.  Rows are private
-            // to the wave and its LDS operations complete in order.
-            auto tile_scores = [&](const TileRegs &r) -> f32x4_t {
-                // E4M3 rows stay 8-bit in LDS (8-byte chunks, 128-byte rows)
-                // and are widened after the read, one operand at a time
-                constexpr int LROW = KV8 ? D : ROW_BYTES;
+            for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sc[i]);
+            mx = rowgroup_max(mx);
+            const bool bump = mx > m + kMaxSlack;  // m = -inf: any valid score
+            if (__builtin_amdgcn_ballot_w64(bump)) {
+                const float alpha = !bump ? 1.f : (m == -INFINITY ? 0.f : fast_exp2(m - mx));
+                m = bump ? mx : m;
+                lsum *= alpha;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int tt = 4 * q + i;
-                    char *dst = kt + tt * LROW + ((c ^ tt) & 15) * KV_CHUNK;
-                    if constexpr (KV8) *reinterpret_cast<u32x2 *>(dst) = r.k[i];
-                    else *reinterpret_cast<u32x4 *>(dst) = r.k[i];
-                }
-                asm volatile("" ::: "memory");
-                f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+                for (int dt = 0; dt < 8; ++dt) acc[dt] *= alpha;
+            }
+            // m = -inf only while the column has seen no valid score:
+            // every score here is then masked and 2^(-inf - 0) = 0
+            const float mref = m == -INFINITY ? 0.f : m;
+            float ps = 0.f;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const char *src = kt + c * LROW + (((4 * j + q) ^ c) & 15) * KV_CHUNK;
-                    u32x4 kop;
-                    if constexpr (KV8) kop = widen_e4m3<DT>(*reinterpret_cast<const u32x2 *>(src));
-                    else kop = *reinterpret_cast<const u32x4 *>(src);
-                    sacc = mfma_16x16x32<DT>(kop, kQopLds ? s_qop[j][lane] : qop[j], sacc);
-                }
-                asm volatile("" ::: "memory");
-                return sacc;
-            };
-            // softmax and value product of the pair (tiles A, B at t0, t0 + 16)
-            // whose scores are sa, sb
-            auto pair_values = [&](const f32x4_t sa, const f32x4_t sb, const TileRegs &ra,
-                                   const TileRegs &rb, int t0) {
-                float sc[8];  // tokens t0 + 4q + i (i < 4), t0 + 16 + 4q + i - 4 (i >= 4)
+            for (int i = 0; i < 8; ++i) {
+                sc[i] = fast_exp2(sc[i] - mref);
+                ps += sc[i];
+            }
+            lsum += ps;
+            u32x4 ph, pl;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    sc[i] = sa[i] * sl2;
-                    sc[4 + i] = sb[i] * sl2;
-                }
-                if (t0 + 2 * TILE > seg_end) {  // wave-uniform: only at the end of a segment
-                    // tokens of this lane before the end; the count passes
-                    // through an empty asm inside the branch, so the compares
-                    // cannot be hoisted out of it
-                    int nv = seg_end - (t0 + 4 * q);
-                    asm volatile("" : "+v"(nv));
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        sc[i] = (i < nv) ? sc[i] : -INFINITY;
-                        sc[4 + i] = (TILE + i < nv) ? sc[4 + i] : -INFINITY;
-                    }
-                }
-                float mx = sc[0];
-#pragma unroll
-                for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sc[i]);
-                mx = rowgroup_max(mx);
-                const bool bump = mx > m + kMaxSlack;  // m = -inf: any valid score
-                if (__builtin_amdgcn_ballot_w64(bump)) {
-                    const float alpha = !bump ? 1.f : (m == -INFINITY ? 0.f : fast_exp2(m - mx));
-                    m = bump ? mx : m;
-                    lsum *= alpha;
-#pragma unroll
-                    for (int dt = 0; dt < 8; ++dt) acc[dt] *= alpha;
-                }
-                // m = -inf only while the column has seen no valid score:
-                // every score here is then masked and 2^(-inf - 0) = 0
-                const float mref = m == -INFINITY ? 0.f : m;
-                float ps = 0.f;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    sc[i] = fast_exp2(sc[i] - mref);
-                    ps += sc[i];
-                }
-                lsum += ps;
-                u32x4 ph, pl;
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    uint32_t hi, lo;
-                    split_pack<DT>(sc[2 * w], sc[2 * w + 1], hi, lo);
-                    ph[w] = hi;
-                    pl[w] = lo;
-                }
+            for (int w = 0; w < 4; ++w) {
+                uint32_t hi, lo;
+                split_pack<DT>(sc[2 * w], sc[2 * w + 1], hi, lo);
+                ph[w] = hi;
+                pl[w] = lo;
+            }
 
-                // value operands: this lane's V rows (tokens 4q + i of tiles A
-                // and B, dims 8c..8c+7); invalid rows (past the segment, bad
-                // page) become zeros, since a zero probability times a NaN
-                // row would still be NaN
-                using VRow = std::conditional_t<KV8, u32x2, u32x4>;
-                VRow va[4], vb[4];
+            // value operands: this lane's V rows (tokens 4q + i of tiles A
+            // and B, dims 8c..8c+7); invalid rows (past the segment, bad
+            // page) become zeros, since a zero probability times a NaN
+            // row would still be NaN
+            using VRow = std::conditional_t<KV8, u32x2, u32x4>;
+            VRow va[4], vb[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                va[i] = ra.v[i];
+                vb[i] = rb.v[i];
+            }
+            if (__builtin_amdgcn_ballot_w64((ra.vmask & rb.vmask) != 0xFu)) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    va[i] = ra.v[i];
-                    vb[i] = rb.v[i];
+                    va[i] = (ra.vmask >> i) & 1u ? va[i] : VRow{};
+                    vb[i] = (rb.vmask >> i) & 1u ? vb[i] : VRow{};
                 }
-                if (__builtin_amdgcn_ballot_w64((ra.vmask & rb.vmask) != 0xFu)) {
+            }
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        va[i] = (ra.vmask >> i) & 1u ? va[i] : VRow{};
-                        vb[i] = (rb.vmask >> i) & 1u ? vb[i] : VRow{};
+            for (int w = 0; w < 4; ++w) {
+                // word w of each row (dims 8c + 2w, + 1) in 16-bit form
+                uint32_t xa[4], xb[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if constexpr (KV8) {
+                        xa[i] = (w & 1) ? e4m3_pair<DT, true>(w < 2 ? va[i].x : va[i].y)
+                                        : e4m3_pair<DT, false>(w < 2 ? va[i].x : va[i].y);
+                        xb[i] = (w & 1) ? e4m3_pair<DT, true>(w < 2 ? vb[i].x : vb[i].y)
+                                        : e4m3_pair<DT, false>(w < 2 ? vb[i].x : vb[i].y);
+                    } else {
+                        xa[i] = va[i][w];
+                        xb[i] = vb[i][w];
                     }
                 }
 #pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    // word w of each row (dims 8c + 2w, + 1) in 16-bit form
-                    uint32_t xa[4], xb[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        if constexpr (KV8) {
-                            xa[i] = (w & 1) ? e4m3_pair<DT, true>(w < 2 ? va[i].x : va[i].y)
-                                            : e4m3_pair<DT, false>(w < 2 ? va[i].x : va[i].y);
-                            xb[i] = (w & 1) ? e4m3_pair<DT, true>(w < 2 ? vb[i].x : vb[i].y)
-                                            : e4m3_pair<DT, false>(w < 2 ? vb[i].x : vb[i].y);
-                        } else {
-                            xa[i] = va[i][w];
-                            xb[i] = vb[i][w];
-                        }
-                    }
-#pragma unroll
-                    for (int odd = 0; odd < 2; ++odd) {
-                        // dim 8c + 2w + odd: v_perm pairs the 16-bit halves
-                        // of two tokens
-                        const int dt = 2 * w + odd;
-                        const uint32_t sel = odd ? 0x07060302u : 0x05040100u;
-                        u32x4 vop;
-                        vop[0] = __builtin_amdgcn_perm(xa[1], xa[0], sel);
-                        vop[1] = __builtin_amdgcn_perm(xa[3], xa[2], sel);
-                        vop[2] = __builtin_amdgcn_perm(xb[1], xb[0], sel);
-                        vop[3] = __builtin_amdgcn_perm(xb[3], xb[2], sel);
-                        acc[dt] = mfma_16x16x32<DT>(vop, ph, acc[dt]);
-                        acc[dt] = mfma_16x16x32<DT>(vop, pl, acc[dt]);
-                    }
+                for (int odd = 0; odd < 2; ++odd) {
+                    // dim 8c + 2w + odd: v_perm pairs the 16-bit halves
+                    // of two tokens
+                    const int dt = 2 * w + odd;
+                    const uint32_t sel = odd ? 0x07060302u : 0x05040100u;
+                    u32x4 vop;
+                    vop[0] = __builtin_amdgcn_perm(xa[1], xa[0], sel);
+                    vop[1] = __builtin_amdgcn_perm(xa[3], xa[2], sel);
+                    vop[2] = __builtin_amdgcn_perm(xb[1], xb[0], sel);
+                    vop[3] = __builtin_amdgcn_perm(xb[3], xb[2], sel);
+                    acc[dt] = mfma_16x16x32<DT>(vop, ph, acc[dt]);
+                    acc[dt] = mfma_16x16x32<DT>(vop, pl, acc[dt]);
                 }
-            };
+            }
+        };
 
-            constexpr int STEP = kNumWaves * TILE * TPS;
-            // Each wave step issues the loads of TPS consecutive tiles at
-            // once, then computes them pair by pair.  A tile past the
-            // segment is all invalid and computes to no change.
-            for (int t = seg + wave * TILE * TPS; t < seg_end; t += STEP) {
+        // Each wave step issues the loads of TPS consecutive tiles at once,
+        // then computes them pair by pair; steps start at t_first and move
+        // by t_stride while below seg_end.  A tile past seg_end is all
+        // invalid and computes to no change.
+        auto stream = [&](int t_first, int t_stride) {
+            for (int t = t_first; t < seg_end; t += t_stride) {
                 TileRegs r[TPS];
 #pragma unroll
                 for (int i = 0; i < TPS; ++i) {
@@ -559,37 +588,92 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, int *s_dyn,
                     pair_values(sa, sb, r[i], r[i + 1], t + i * TILE);
                 }
             }
+        };
+
+        if (RUNS && u.tok_end - u.tok_begin == kNumWaves * a.partition_size) {
+            // A whole run: wave w streams partition part0 + w alone and
+            // writes its partial from its registers -- the column's max is
+            // already shared by the wave's four row groups -- so the waves
+            // meet only at the next unit's draw.
+            stage(u.tok_begin, u.tok_end);
+            const int pt = u.tok_begin + wave * a.partition_size;
+            seg_end = pt + a.partition_size;
+            reset();
+            stream(pt, TILE * TPS);
+            const float Lc = rowgroup_sum(lsum);
+            if (c < G) {
+                const int h = h0 + c;
+                const int pi = u.part0 + wave;
+                const int64_t slot = PFX ? ((int64_t)u.s * a.num_heads + h) * a.part_stride + a.part_base + pi
+                                         : ((int64_t)u.s * a.num_heads + h) * a.num_partitions + pi;
+                const bool bad = u.bad_len || s_bad != 0;
+                const float vs = KV8 ? a.v_scale[u.kvh] : 1.f;
+                const float inv = Lc > 0.f ? 1.f / Lc : 0.f;
+                float *dst = a.part_out + slot * D + 32 * q;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    f32x4_t lo, hi;
+#pragma unroll
+                    for (int dt = 0; dt < 4; ++dt) {
+                        lo[dt] = bad ? __builtin_nanf("") : acc[dt][r] * inv * vs;
+                        hi[dt] = bad ? __builtin_nanf("") : acc[4 + dt][r] * inv * vs;
+                    }
+                    *reinterpret_cast<f32x4_t *>(dst + 8 * r) = lo;
+                    *reinterpret_cast<f32x4_t *>(dst + 8 * r + 4) = hi;
+                }
+                if (q == 0) {
+                    a.part_ml[slot * 2] = bad ? __builtin_nanf("") : m;
+                    a.part_ml[slot * 2 + 1] = Lc;
+                }
+            }
+            continue;  // the next draw starts with a barrier
         }
 
-        // the column's normaliser is the sum over the four row groups; lanes
-        // (q, c < G) hold head c's dims 32q + 8r + dt in acc[dt][r]
-        const float L = rowgroup_sum(lsum);
-        float *wacc = reinterpret_cast<float *>(kt);
-        if (c < G) {
+        // Otherwise the unit's partitions one after the other, the four
+        // waves interleaved (32-token pairs), each partition ending in a
+        // cross-wave epilogue (partial or output); page ids staged for up to
+        // kSegPages pages of the unit at a time.
+        for (int pt = u.tok_begin, pi = u.part0;; pt += a.partition_size, ++pi) {
+            const int pend = min(u.tok_end, pt + a.partition_size);
+            reset();
+            for (int seg = pt; seg < pend; seg = seg_end) {
+                if (seg >= stg_hi) stage(seg, min(u.tok_end, seg + (kSegPages << lbs)));
+                seg_end = min(pend, stg_hi);
+                stream(seg + wave * TILE * TPS, kNumWaves * TILE * TPS);
+            }
+
+            // the column's normaliser is the sum over the four row groups;
+            // lanes (q, c < G) hold head c's dims 32q + 8r + dt in acc[dt][r]
+            const float Lc = rowgroup_sum(lsum);
+            float *wacc = reinterpret_cast<float *>(kt);
+            if (c < G) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float *dst = wacc + c * D + 32 * q + 8 * r;
-                *reinterpret_cast<f32x4_t *>(dst) = f32x4_t{acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
-                *reinterpret_cast<f32x4_t *>(dst + 4) = f32x4_t{acc[4][r], acc[5][r], acc[6][r], acc[7][r]};
+                for (int r = 0; r < 4; ++r) {
+                    float *dst = wacc + c * D + 32 * q + 8 * r;
+                    *reinterpret_cast<f32x4_t *>(dst) = f32x4_t{acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
+                    *reinterpret_cast<f32x4_t *>(dst + 4) = f32x4_t{acc[4][r], acc[5][r], acc[6][r], acc[7][r]};
+                }
+                if (q == 0) {
+                    s_m[wave][c] = m;
+                    s_l[wave][c] = Lc;
+                }
             }
-            if (q == 0) {
-                s_m[wave][c] = m;
-                s_l[wave][c] = L;
-            }
+            __syncthreads();
+            unit_epilogue<DT, D, G, PFX, kRegion / 4>(a, u, pi, u.bad_len || s_bad != 0, s_m, s_l,
+                                                             reinterpret_cast<const float *>(&s_region[0][0]),
+                                                             KV8 ? a.v_scale[u.kvh] : 1.f);
+            if (pend >= u.tok_end) break;
+            __syncthreads();  // every wave's region has been read before the next K tiles land there
         }
-        __syncthreads();
-        unit_epilogue<DT, D, G, PFX, kRegion / 4>(a, u, u.bad_len || s_bad != 0, s_m, s_l,
-                                                         reinterpret_cast<const float *>(&s_region[0][0]),
-                                                         KV8 ? a.v_scale[u.kvh] : 1.f);
     }
 }
 
-template <int DT, int G, bool PFX, bool KV8>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8)))
+template <int DT, int G, bool PFX, bool KV8, bool RUNS>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PKV_DECODE_MIN_WAVES, 8)))
 void paged_decode_mfma_kernel(DecodeArgs a) {
     extern __shared__ int s_dyn[];
     __shared__ DecodeLds<G, qop_in_lds<KV8>()> lds;
-    decode_body<DT, G, PFX, KV8>(a, s_dyn, lds, gridDim.x);
+    decode_body<DT, G, PFX, KV8, RUNS>(a, s_dyn, lds, gridDim.x);
 }
 
 // Shared-prefix decode in one launch: workgroups [0, prefix_wgs) each run one
@@ -597,8 +681,8 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
 // persistent suffix grid.  The prefix units are latency-bound and the suffix
 // streams from HBM, so the two overlap; their LDS is one union.  Every suffix
 // partition writes a partial; a merge kernel joins them with the prefix's.
-template <int DT, int G>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8)))
+template <int DT, int G, bool RUNS>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PKV_DECODE_MIN_WAVES, 8)))
 void paged_prefix_fused_kernel(DecodeArgs a, PrefixArgs p, int prefix_wgs) {
     extern __shared__ int s_dyn[];
     __shared__ union {
@@ -609,7 +693,7 @@ void paged_prefix_fused_kernel(DecodeArgs a, PrefixArgs p, int prefix_wgs) {
         prefix_unit<DT>(p, xcd_unit(blockIdx.x, prefix_wgs), lds.x);
         return;
     }
-    decode_body<DT, G, true, false>(a, s_dyn, lds.d, (int)gridDim.x - prefix_wgs);
+    decode_body<DT, G, true, false, RUNS>(a, s_dyn, lds.d, (int)gridDim.x - prefix_wgs);
 }
 
 // Resident workgroups per CU of a kernel and the CU count, per (kernel,
@@ -685,13 +769,23 @@ static hipError_t launch_persistent(K kernel, const DecodeArgs &a, hipStream_t s
     return hipGetLastError();
 }
 
+// The kernels with the whole-run path (RUNS) are a second instantiation:
+// compiled into the ordinary one it cost the GQA E4M3 and shared-prefix
+// calls 0.7-2 us through register pressure.
+template <int DT, int G, bool PFX, bool KV8>
+static hipError_t launch_runs(const DecodeArgs &a, hipStream_t stream) {
+    if (a.unit_parts == kNumWaves)
+        return launch_persistent(paged_decode_mfma_kernel<DT, G, PFX, KV8, true>, a, stream);
+    return launch_persistent(paged_decode_mfma_kernel<DT, G, PFX, KV8, false>, a, stream);
+}
+
 template <int DT, bool PFX, bool KV8 = false>
 static hipError_t launch_group(const DecodeArgs &a, hipStream_t stream) {
     switch (a.num_heads / a.num_kv_heads) {
-        case 1: return launch_persistent(paged_decode_mfma_kernel<DT, 1, PFX, KV8>, a, stream);
-        case 2: return launch_persistent(paged_decode_mfma_kernel<DT, 2, PFX, KV8>, a, stream);
-        case 4: return launch_persistent(paged_decode_mfma_kernel<DT, 4, PFX, KV8>, a, stream);
-        case 8: return launch_persistent(paged_decode_mfma_kernel<DT, 8, PFX, KV8>, a, stream);
+        case 1: return launch_runs<DT, 1, PFX, KV8>(a, stream);
+        case 2: return launch_runs<DT, 2, PFX, KV8>(a, stream);
+        case 4: return launch_runs<DT, 4, PFX, KV8>(a, stream);
+        case 8: return launch_runs<DT, 8, PFX, KV8>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -710,10 +804,10 @@ hipError_t launch_paged_decode_mfma_e4m3(const DecodeArgs &a, int dtype, hipStre
 
 // The fused shared-prefix launch: prefix_units workgroups for the prefix,
 // then the persistent suffix grid (resident_grid over the suffix units).
-template <int DT, int G>
+template <int DT, int G, bool RUNS>
 static hipError_t launch_fused(const PrefixArgs &p, const DecodeArgs &a, int64_t prefix_units,
                                hipStream_t stream) {
-    auto kernel = paged_prefix_fused_kernel<DT, G>;
+    auto kernel = paged_prefix_fused_kernel<DT, G, RUNS>;
     const size_t dyn = (size_t)(3 * a.num_seqs + 2) * sizeof(int);
     const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * a.num_partitions;  // upper bound
     hipError_t e;
@@ -727,11 +821,16 @@ static hipError_t launch_fused(const PrefixArgs &p, const DecodeArgs &a, int64_t
 template <int DT>
 static hipError_t launch_fused_group(const PrefixArgs &p, const DecodeArgs &a, hipStream_t stream) {
     const int64_t prefix_units = (int64_t)p.row_blocks * p.num_splits * p.num_kv_heads;
+    const bool runs = a.unit_parts == kNumWaves;
     switch (a.num_heads / a.num_kv_heads) {
-        case 1: return launch_fused<DT, 1>(p, a, prefix_units, stream);
-        case 2: return launch_fused<DT, 2>(p, a, prefix_units, stream);
-        case 4: return launch_fused<DT, 4>(p, a, prefix_units, stream);
-        case 8: return launch_fused<DT, 8>(p, a, prefix_units, stream);
+        case 1: return runs ? launch_fused<DT, 1, true>(p, a, prefix_units, stream)
+                            : launch_fused<DT, 1, false>(p, a, prefix_units, stream);
+        case 2: return runs ? launch_fused<DT, 2, true>(p, a, prefix_units, stream)
+                            : launch_fused<DT, 2, false>(p, a, prefix_units, stream);
+        case 4: return runs ? launch_fused<DT, 4, true>(p, a, prefix_units, stream)
+                            : launch_fused<DT, 4, false>(p, a, prefix_units, stream);
+        case 8: return runs ? launch_fused<DT, 8, true>(p, a, prefix_units, stream)
+                            : launch_fused<DT, 8, false>(p, a, prefix_units, stream);
         default: return hipErrorInvalidValue;
     }
 }

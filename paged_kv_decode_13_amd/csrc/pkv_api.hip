@@ -39,6 +39,23 @@ int32_t num_partitions(int32_t max_context_len, int32_t partition_size) {
     return (int32_t)(((int64_t)max_context_len + partition_size - 1) / partition_size);
 }
 
+// Partitions per work unit of the persistent kernels: 4 when a span can hold
+// four partitions (parts >= 4), they are short (at most
+// PKV_WAVE_PARTITION_MAX tokens) and a run of four fits one page-id staging
+// window (256 pages), else 1.  A sequence's span then
+// starts with runs of four whole partitions, one unit each, in which each
+// wave streams one partition alone and writes its partial directly: no
+// cross-wave merge and no barrier at every partition end.  The rest of the
+// span is one unit per partition.
+#ifndef PKV_WAVE_PARTITION_MAX
+#define PKV_WAVE_PARTITION_MAX 1024
+#endif
+int32_t unit_parts(int32_t parts, int32_t partition_size, int32_t block_size) {
+    if (parts < pkv::kDecodeWaves || partition_size > PKV_WAVE_PARTITION_MAX) return 1;
+    if ((int64_t)pkv::kDecodeWaves * partition_size > (int64_t)pkv::kDecodeSegPages * block_size) return 1;
+    return pkv::kDecodeWaves;
+}
+
 // A decode call needs its workspace when the context is split (partials);
 // an unsplit call may pass NULL (then one workgroup per unit, no counter).
 // A workspace that is passed must be large enough and 16-byte aligned.
@@ -158,6 +175,7 @@ pkv_status decode_setup(pkv::DecodeArgs &a, bool &empty, bool kv8, void *out, co
     // Unsplit: one unit covers any admissible context.
     a.partition_size = parts > 1 ? partition_size : (max_context_len > 0 ? max_context_len : 1);
     a.num_partitions = parts;
+    a.unit_parts = unit_parts(parts, partition_size, block_size);
     a.scale_log2e = scale * 1.4426950408889634f;
     a.out_f32 = out_dtype == PKV_F32 ? 1 : 0;
     a.token_begin = 0;
@@ -422,6 +440,7 @@ pkv_status paged_prefix_decode_attention(
     a.max_context_len = max_context_len;
     a.partition_size = plan.suffix_partition;
     a.num_partitions = plan.suffix_parts;
+    a.unit_parts = unit_parts(plan.suffix_parts, plan.suffix_partition, block_size);
     a.scale_log2e = sl2;
     a.out_f32 = out_dtype == PKV_F32 ? 1 : 0;
     a.token_begin = prefix_len;

@@ -10,17 +10,18 @@
 
 namespace pkv {
 
-constexpr int kNumWaves = 4;
+constexpr int kNumWaves = kDecodeWaves;
 constexpr int kThreads = kNumWaves * kWave;
-constexpr int kSegPages = 256;  // page ids staged in LDS at a time
+constexpr int kSegPages = kDecodeSegPages;  // page ids staged in LDS at a time
 // Lazy running max: a reference max moves only when passed by more than this
 // (exp2 domain), so probabilities stay <= 256 and rescales are rare.
 constexpr float kMaxSlack = 8.f;
 
 struct Unit {
-    int s, kvh, p;
+    int s, kvh, p;           // p: the unit's index among its sequence's units
     int ctx;
     int tok_begin, tok_end;  // token range of this unit
+    int part0;               // partition index of the unit's first partition
     int nparts;              // partitions of this sequence (1: write out directly)
     bool bad_len;            // length outside what the table / grid can cover
     bool empty;              // unit past the end of its sequence: exit
@@ -62,6 +63,34 @@ __device__ __forceinline__ int seq_full(const DecodeArgs &a, int ctx) {
     return span / a.partition_size;
 }
 
+// Work units of the persistent kernels.  With unit_parts == 1 a unit is one
+// partition.  With unit_parts == kNumWaves a sequence's span starts with
+// runs of kNumWaves whole partitions, one unit each, in which every wave
+// streams one partition alone (no cross-wave merge: each wave writes its
+// partition's partial); the rest of the span is one unit per partition.
+// Either way the log-sum-exp merge joins partition_size-token partials.
+__device__ __forceinline__ int run_tokens(const DecodeArgs &a) { return a.partition_size * a.unit_parts; }
+
+// Units of a sequence that are whole runs of unit_parts partitions.
+template <bool PFX = false>
+__device__ __forceinline__ int seq_full_units(const DecodeArgs &a, int ctx) {
+    const int span = ctx - first_token<PFX>(a);
+    if (bad_context(a, ctx) || span <= 0) return 0;
+    return span / run_tokens(a);
+}
+
+// All units of a sequence: its whole runs, then one per remaining partition
+// (at least one unit, which writes the zeros, empty partial or NaNs of a
+// sequence with nothing to read).
+template <bool PFX = false>
+__device__ __forceinline__ int seq_units(const DecodeArgs &a, int ctx) {
+    const int span = ctx - first_token<PFX>(a);
+    if (bad_context(a, ctx) || span <= 0) return 1;
+    const int runs = span / run_tokens(a);
+    const int rest = span - runs * run_tokens(a);
+    return runs + (rest + a.partition_size - 1) / a.partition_size;
+}
+
 __device__ __forceinline__ Unit make_unit(const DecodeArgs &a) {
     // KV head fastest: the units that read the same pages run side by side.
     int u = blockIdx.x;
@@ -76,6 +105,7 @@ __device__ __forceinline__ Unit make_unit(const DecodeArgs &a) {
     r.empty = r.p > 0 && (r.bad_len || r.tok_begin >= r.ctx);
     r.tok_end = r.bad_len ? 0 : min(r.ctx, r.tok_begin + a.partition_size);
     r.nparts = (r.bad_len || r.ctx == 0) ? 1 : (r.ctx + a.partition_size - 1) / a.partition_size;
+    r.part0 = r.p;
     return r;
 }
 
@@ -138,11 +168,12 @@ __device__ __forceinline__ void store_out(const DecodeArgs &a, int64_t idx, floa
 }
 
 // Merge the per-wave states (running max m, normaliser l, unnormalised
-// accumulator) of one unit and store either the final output (one partition)
-// or the partition's normalised partial with its (m, l).  Wave w's
-// accumulator of head g is s_acc[w * WS + g * D + 0 .. D - 1].
+// accumulator) of partition pi of a unit's sequence and store either the
+// final output (one partition) or the partition's normalised partial with
+// its (m, l).  Wave w's accumulator of head g is s_acc[w * WS + g * D + 0 ..
+// D - 1].
 template <int DT, int D, int G, bool PFX = false, int WS = G * D>
-__device__ __forceinline__ void unit_epilogue(const DecodeArgs &a, const Unit &u, bool bad,
+__device__ __forceinline__ void unit_epilogue(const DecodeArgs &a, const Unit &u, int pi, bool bad,
                                               const float (*s_m)[G], const float (*s_l)[G],
                                               const float *s_acc, float vscale = 1.f) {
     const int h0 = u.kvh * G;
@@ -167,8 +198,8 @@ __device__ __forceinline__ void unit_epilogue(const DecodeArgs &a, const Unit &u
             store_out<DT>(a, ((int64_t)u.s * a.num_heads + h) * D + d, res);
         } else {
             // a suffix launch writes its partials after the prefix's slots
-            const int64_t slot = PFX ? ((int64_t)u.s * a.num_heads + h) * a.part_stride + a.part_base + u.p
-                                     : ((int64_t)u.s * a.num_heads + h) * a.num_partitions + u.p;
+            const int64_t slot = PFX ? ((int64_t)u.s * a.num_heads + h) * a.part_stride + a.part_base + pi
+                                     : ((int64_t)u.s * a.num_heads + h) * a.num_partitions + pi;
             a.part_out[slot * D + d] = res;
             if (d == 0) {
                 a.part_ml[slot * 2] = bad ? __builtin_nanf("") : M;

@@ -56,8 +56,9 @@ struct DecodeArgs {
     int32_t log2_block_size;
     int32_t max_blocks_per_seq;
     int32_t max_context_len;
-    int32_t partition_size;     // tokens per work unit (whole context when not split)
-    int32_t num_partitions;     // P: grid extent along the context
+    int32_t partition_size;     // tokens per partition (whole context when not split)
+    int32_t num_partitions;     // P: partial slots per (sequence, head)
+    int32_t unit_parts;         // partitions per work unit of the persistent kernels (>= 1)
     float scale_log2e;          // scale * log2(e): scores live in the exp2 domain
     int32_t out_f32;            // 1: out is binary32; 0: out has the cache dtype
     int32_t token_begin;        // first token read (a page boundary; 0 = whole history)
@@ -68,6 +69,11 @@ struct DecodeArgs {
     const float *k_scale;       // [KVH] E4M3 caches only: cached K = code * k_scale
     const float *v_scale;       // [KVH]
 };
+
+// Waves per workgroup of the decode kernels, and page ids staged in LDS at a
+// time (the host plans work units against both).
+constexpr int kDecodeWaves = 4;
+constexpr int kDecodeSegPages = 256;
 
 // MFMA column blocks of 16 query rows per wave in the multi-query kernels
 // (four waves per workgroup).  Two blocks let every K/V operand a wave reads

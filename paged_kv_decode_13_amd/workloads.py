@@ -13,7 +13,7 @@ type round-to-nearest-even):
                blocks, table = 10 ids of a seeded permutation, fp32, plus one
                new token written through slot_mapping;
   mha_fp16     32 seqs, 32/32 heads, head_dim 128, block 16, contexts uniform
-               in [1, 4096], fp16; 384-token KV partitions;
+               in [1, 4096], fp16; 512-token KV partitions;
   gqa_bf16     256 seqs, 32/8 heads, head_dim 128, block 16, contexts
                log-uniform in [128, 16000], bf16, one new token per sequence;
                2560-token KV partitions;
@@ -557,7 +557,7 @@ def make_config(name: str, *, block_size: int | None = None, seed: int | None = 
     if name == "mha_fp16":
         ctx = rng.integers(1, 4096, size=32, endpoint=True)
         return make_batch(ctx, num_heads=32, num_kv_heads=32, head_dim=128, block_size=16,
-                          dtype="f16", seed=seed, poison=poison, partition_size=384,
+                          dtype="f16", seed=seed, poison=poison, partition_size=512,
                           name=name, values=values)
     if name in ("gqa_bf16", "gqa_fp8"):
         ctx = np.floor(np.exp(rng.uniform(math.log(128), math.log(16000), size=256)))

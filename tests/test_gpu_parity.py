@@ -281,3 +281,36 @@ def test_bulk_prefill_write_then_decode(cuda):
         out = to_f64(gpu_step(b, t, write=False, partition_size=512 if bs <= 32 else 0,
                               out_dtype="f32"))
         assert max_err(out, oracle_step(b)) <= TIGHT[dtype], dtype
+
+
+@pytest.mark.parametrize("kv,bs,ps", [(None, 16, 256), (None, 4, 64), (None, 32, 512),
+                                      ("e4m3", 16, 128)],
+                         ids=["bf16-bs16-p256", "bf16-bs4-p64", "bf16-bs32-p512", "e4m3-bs16-p128"])
+def test_partition_runs(cuda, kv, bs, ps):
+    """Short partitions go in runs of four whole partitions per work unit,
+    one wave per partition, each wave writing its partial directly; the rest
+    of a span is one unit per partition.  Lengths at and around run
+    boundaries (exactly one run, a run and a partial partition, two runs, a
+    run and three singles, fewer than four partitions), every group size;
+    then a bad page inside a run makes exactly that sequence NaN."""
+    import torch
+
+    run = 4 * ps
+    lens = [run, run + 1, 2 * run, run + 3 * ps, 3 * ps, ps - 1, 0, 5 * run + 17, run - bs]
+    for g in (1, 2, 4, 8):
+        b = wl.make_batch(lens, num_heads=4 * g, num_kv_heads=4, head_dim=128, block_size=bs,
+                          dtype="bf16", seed=60 + g, write_new_token=True, partition_size=ps,
+                          kv_dtype=kv)
+        out = to_f64(gpu_step(b, upload(b, cuda), out_dtype="f32"))
+        assert max_err(out, oracle_step(b)) <= TIGHT["bf16"], (g, kv, bs, ps)
+    b = wl.make_batch(lens, num_heads=16, num_kv_heads=4, head_dim=128, block_size=bs,
+                      dtype="bf16", seed=71, write_new_token=True, partition_size=ps, kv_dtype=kv)
+    ref = oracle_step(b)
+    t = upload(b, cuda)
+    bt = b.block_tables.copy()
+    bt[2, (run + ps) // bs] = b.num_blocks + 5  # inside the second run of sequence 2
+    t["bt"] = torch.from_numpy(bt).to(cuda)
+    out = to_f64(gpu_step(b, t, out_dtype="f32"))
+    assert np.isnan(out[2]).all()
+    keep = [i for i in range(len(lens)) if i != 2]
+    assert max_err(out[keep], ref[keep]) <= TIGHT["bf16"]
