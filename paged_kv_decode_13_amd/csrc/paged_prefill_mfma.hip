@@ -51,7 +51,10 @@ __device__ __forceinline__ int prefill_tiles(const PrefillArgs &a, int s, int &q
 // latency better than two with double-buffered LDS (10.9 against 12.8 ms on
 // the 32-prompt workload); two blocks per wave at two workgroups per CU
 // took it to 9.5 ms, and a second LDS buffer there (one barrier per chunk)
-// measured 1.5% slower.
+// measured 1.5% slower.  A software pipeline (the next chunk's score MFMAs
+// issued before this chunk's softmax, K and V in two-slot LDS rings, one
+// barrier per chunk) reached 256 VGPRs, and without registers to prefetch
+// LDS operands every MFMA waited on its read: 10.1 against 9.0 ms.
 template <int DT>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(mqa_waves_per_simd(kPrefillBlocks), 8)))
@@ -133,6 +136,7 @@ void paged_prefill_mfma_kernel(PrefillArgs a) {
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) wlim = min(wlim, __shfl_xor(wlim, off));
     wlim = __builtin_amdgcn_readfirstlane(wlim);
+    const float sl2 = mqa_positive_scale<NB>(a.scale_log2e, qop);
 
     // staging roles as in the shared-prefix kernel
     const int lc = tid & 15;
@@ -188,7 +192,7 @@ void paged_prefill_mfma_kernel(PrefillArgs a) {
             __syncthreads();
             ok = load_chunk(t0 + kMqaChunk, kr, vr);
             __builtin_amdgcn_sched_barrier(0);
-            mqa_chunk<DT, NB>(s_k, s_v, qop, j, q, t0, lim, t0 + kMqaChunk > wlim, a.scale_log2e, st);
+            mqa_chunk<DT, NB>(s_k, s_v, qop, j, q, t0, lim, t0 + kMqaChunk > wlim, sl2, st);
             __syncthreads();
         }
     }

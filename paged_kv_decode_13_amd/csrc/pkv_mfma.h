@@ -51,6 +51,9 @@ __device__ __forceinline__ void split_pack(float p0, float p1, uint32_t &hi, uin
         typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
         const bf16x2_t h = {(__bf16)p0, (__bf16)p1};
         hi = __builtin_bit_cast(uint32_t, h);
+        // both halves come from the packed pair (one shift, one mask); the
+        // empty asm keeps the compiler from converting p0 a second time
+        asm("" : "+v"(hi));
         const float r0 = p0 - __uint_as_float(hi << 16);
         const float r1 = p1 - __uint_as_float(hi & 0xffff0000u);
         const bf16x2_t l = {(__bf16)r0, (__bf16)r1};

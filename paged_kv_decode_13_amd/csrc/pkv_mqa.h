@@ -75,6 +75,22 @@ __device__ __forceinline__ void mqa_store_chunk(char *kt, char *vt, int lc, int 
         *reinterpret_cast<u32x4 *>(vt + (4 * lg + i) * kMqaVRow + lc * 16) = vr[i];
 }
 
+// The score scale as the softmax wants it: positive.  A negative scale has
+// its sign moved into the query operand (the sign bit of every 16-bit
+// element flipped), and a zero scale becomes the smallest normal float, for
+// which 2^(x * scale) rounds to exactly 1 as 2^0 does (and -inf * scale
+// stays -inf for masked tokens).
+template <int NB>
+__device__ __forceinline__ float mqa_positive_scale(float sl2, u32x4 (&qop)[NB][4]) {
+    if (sl2 < 0.f) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) qop[b][kk] ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+    }
+    return fmaxf(fabsf(sl2), 1.17549435e-38f);
+}
+
 // Running state of one query row (lane j of each lane group q).
 struct MqaRowState {
     float m;          // reference max (equal in the row's four lane groups)
@@ -89,15 +105,14 @@ __device__ __forceinline__ void mqa_init(MqaRowState &st) {
     for (int dt = 0; dt < 8; ++dt) st.acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 }
 
-// One 64-token chunk (tokens t0 .. t0 + 63 staged in kt / vt) for this
-// wave's NB column blocks of 16 rows.  Row j of block b sees tokens
-// t < lim[b]; `masked` (wave-uniform) says some token of the chunk lies past
-// some row's limit.
+// Raw scores q.k of one 64-token chunk whose K rows are staged in kt, for
+// this wave's NB column blocks of 16 rows: sc[b][tile][r] is token
+// tile * 16 + 4q + r of row j of block b.  The score scale is applied in the
+// softmax (mqa_softmax_values), folded into the exponent's fused
+// multiply-add.
 template <int DT, int NB>
-__device__ __forceinline__ void mqa_chunk(const char *kt, const char *vt, const u32x4 (&qop)[NB][4],
-                                          int j, int q, int t0, const int (&lim)[NB], bool masked,
-                                          float sl2, MqaRowState (&st)[NB]) {
-    float sc[NB][4][4];  // [block][16-token tile][r]: token tile*16 + 4q + r, row j
+__device__ __forceinline__ void mqa_scores(const char *kt, const u32x4 (&qop)[NB][4], int j, int q,
+                                           float (&sc)[NB][4][4]) {
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
         f32x4_t sacc[NB];
@@ -113,8 +128,19 @@ __device__ __forceinline__ void mqa_chunk(const char *kt, const char *vt, const 
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) sc[b][tt][rr] = sacc[b][rr] * sl2;
+            for (int rr = 0; rr < 4; ++rr) sc[b][tt][rr] = sacc[b][rr];
     }
+}
+
+// The rest of one 64-token chunk (tokens t0 .. t0 + 63, V rows staged in
+// vt) given its raw scores: masking, the online softmax with the score
+// scale sl2 (> 0, exp2 domain; see mqa_positive_scale), the value product.
+// Row j of block b sees tokens t < lim[b]; `masked` (wave-uniform) says some
+// token of the chunk lies past some row's limit.
+template <int DT, int NB>
+__device__ __forceinline__ void mqa_softmax_values(const char *vt, int j, int q, int t0,
+                                                   const int (&lim)[NB], bool masked, float sl2,
+                                                   float (&sc)[NB][4][4], MqaRowState (&st)[NB]) {
     if (masked) {
         // tokens left of this lane's row limits: the counts pass through an
         // empty asm inside the branch, so the compares cannot be hoisted out
@@ -140,7 +166,8 @@ __device__ __forceinline__ void mqa_chunk(const char *kt, const char *vt, const 
         for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) mx = fmaxf(mx, sc[b][tt][rr]);
-        mx = rowgroup_max(mx);
+        // the scale is positive, so the scaled max is the raw max scaled
+        mx = rowgroup_max(mx) * sl2;
         // m = -inf until the row has seen a valid token
         const bool bump = mx > st[b].m + kMaxSlack;
         if (__builtin_amdgcn_ballot_w64(bump)) {
@@ -157,7 +184,7 @@ __device__ __forceinline__ void mqa_chunk(const char *kt, const char *vt, const 
         for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
-                sc[b][tt][rr] = fast_exp2(sc[b][tt][rr] - mref);
+                sc[b][tt][rr] = fast_exp2(fmaf(sc[b][tt][rr], sl2, -mref));
                 ps += sc[b][tt][rr];
             }
         st[b].lsum += ps;
@@ -199,6 +226,18 @@ __device__ __forceinline__ void mqa_chunk(const char *kt, const char *vt, const 
         }
     }
     __builtin_amdgcn_s_setprio(0);
+}
+
+// One 64-token chunk (tokens t0 .. t0 + 63 staged in kt / vt) for this
+// wave's NB column blocks of 16 rows: scores, then softmax and values; sl2
+// as for mqa_softmax_values.
+template <int DT, int NB>
+__device__ __forceinline__ void mqa_chunk(const char *kt, const char *vt, const u32x4 (&qop)[NB][4],
+                                          int j, int q, int t0, const int (&lim)[NB], bool masked,
+                                          float sl2, MqaRowState (&st)[NB]) {
+    float sc[NB][4][4];  // [block][16-token tile][r]: token tile*16 + 4q + r, row j
+    mqa_scores<DT, NB>(kt, qop, j, q, sc);
+    mqa_softmax_values<DT, NB>(vt, j, q, t0, lim, masked, sl2, sc, st);
 }
 
 // The row's normaliser: the sum of the four lane groups' shares.

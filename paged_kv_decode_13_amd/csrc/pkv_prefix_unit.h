@@ -101,6 +101,7 @@ __device__ __forceinline__ void prefix_unit(const PrefixArgs &a, const int unit,
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) wlim = min(wlim, __shfl_xor(wlim, off));
     wlim = __builtin_amdgcn_readfirstlane(wlim);
+    const float sl2 = mqa_positive_scale<NB>(a.scale_log2e, qop);
 
     // staging roles: thread (lg, lc) moves 16-byte chunk lc of tokens
     // 4 lg .. 4 lg + 3 of a chunk (one page: pages hold >= 4 tokens)
@@ -146,7 +147,7 @@ __device__ __forceinline__ void prefix_unit(const PrefixArgs &a, const int unit,
         ok = load_chunk(t0 + kMqaChunk, kr, vr);
         // keep the next chunk's loads ahead of this chunk's compute
         __builtin_amdgcn_sched_barrier(0);
-        mqa_chunk<DT, NB>(s_k, s_v, qop, j, q, t0, lim, t0 + kMqaChunk > wlim, a.scale_log2e, st);
+        mqa_chunk<DT, NB>(s_k, s_v, qop, j, q, t0, lim, t0 + kMqaChunk > wlim, sl2, st);
         __syncthreads();
     }
 
