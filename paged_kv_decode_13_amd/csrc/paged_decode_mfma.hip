@@ -105,26 +105,66 @@ __device__ __forceinline__ u32x4 widen_e4m3(const u32x2 w) {
                  e4m3_pair<DT, true>(w.y)};
 }
 
-// Unit order: all whole runs of unit_parts partitions of the batch first,
-// then the single partitions after each sequence's runs (its last one may be
-// partial).  Units of one size drain the grid evenly and the variable-size
-// units come at the end, where they fill the gaps.  Builds the exclusive
-// prefix sums s_pf[0..B] (runs) and s_pp[0..B] (single partitions) and
-// caches the lengths in s_ctx.
+// Unit order.  All whole runs of unit_parts partitions of the batch come
+// first: units of one size drain the grid evenly.  Then:
+//  - unit_parts == 1 (every whole partition is a run): the tail units, each
+//    sequence's partial last partition, longest first, so the last units
+//    drawn are the shortest and the grid ends together (longest-processing-
+//    time order; 256-sequence batch at 2560-token partitions 559 -> 541 us);
+//  - unit_parts > 1: each sequence's remaining partitions, its tail last,
+//    sequence by sequence.  (The 32-sequence MHA batch ran 176 us so and
+//    180 us with the whole partitions of every sequence before all tails.)
+//
+// Builds the exclusive prefix sums s_pf[0..B] (runs) and s_pp[0..B] (the
+// partitions after the runs that are not sorted tails), caches the lengths
+// in s_ctx, lists the sequences with a sorted tail unit in s_tail (by tail
+// length in kTailBuckets classes, longest class first, sequence order within
+// a class: a stable counting sort, so every workgroup builds the same list)
+// and stores their number in *s_ntail.  s_tmp: 192 ints of scratch.
+constexpr int kTailBuckets = 16;
+
+__device__ __forceinline__ bool sorted_tails(const DecodeArgs &a) { return a.unit_parts == 1; }
+
+// Partitions after a sequence's runs that sit in its s_pp range.
 template <bool PFX>
-__device__ __forceinline__ void build_unit_order(const DecodeArgs &a, int *s_pf, int *s_pp,
-                                                 int *s_ctx, int *s_scan) {
+__device__ __forceinline__ int seq_singles(const DecodeArgs &a, int ctx) {
+    return sorted_tails(a) ? seq_whole_singles<PFX>(a, ctx) : seq_units<PFX>(a, ctx) - seq_full_units<PFX>(a, ctx);
+}
+
+// Class of a sequence's sorted tail unit (0: longest), -1 if it has none.
+template <bool PFX>
+__device__ __forceinline__ int tail_bucket(const DecodeArgs &a, int ctx) {
+    const int t = seq_tail_tokens<PFX>(a, ctx);
+    if (t < 0) return -1;
+    return (int)((int64_t)(a.partition_size - 1 - t) * kTailBuckets / a.partition_size);
+}
+
+template <bool PFX>
+__device__ __forceinline__ void build_unit_order(const DecodeArgs &a, int *s_pf, int *s_pp, int *s_ctx,
+                                                 uint16_t *s_tail, int *s_ntail, int *s_tmp) {
     const int B = a.num_seqs;
     const int tid = threadIdx.x;
+    const bool sort = sorted_tails(a);
+    int *s_scan = s_tmp;                      // [kNumWaves]
+    int *s_hist = s_tmp + 8;                  // [kTailBuckets]
+    int *s_run = s_tmp + 8 + kTailBuckets;    // [kTailBuckets]: placed so far
+    int *s_cnt = s_tmp + 64;                  // [2][kNumWaves][kTailBuckets]
+    if (sort) {
+        if (tid < kTailBuckets) s_hist[tid] = 0;
+        __syncthreads();
+    }
     const int chunk = (B + kThreads - 1) / kThreads;
     const int lo = min(B, tid * chunk), hi = min(B, lo + chunk);
     int nf = 0, np = 0;
     for (int s = lo; s < hi; ++s) {
         const int ctx = a.context_lens[s];
         s_ctx[s] = ctx;
-        const int f = seq_full_units<PFX>(a, ctx);
-        nf += f;
-        np += seq_units<PFX>(a, ctx) - f;
+        nf += seq_full_units<PFX>(a, ctx);
+        np += seq_singles<PFX>(a, ctx);
+        if (sort) {
+            const int k = tail_bucket<PFX>(a, ctx);
+            if (k >= 0) atomicAdd(&s_hist[k], 1);
+        }
     }
     const int incf = block_scan(nf, s_scan);
     const int incp = block_scan(np, s_scan);
@@ -132,24 +172,65 @@ __device__ __forceinline__ void build_unit_order(const DecodeArgs &a, int *s_pf,
     for (int s = lo; s < hi; ++s) {
         s_pf[s] = rf;
         s_pp[s] = rp;
-        const int f = seq_full_units<PFX>(a, s_ctx[s]);
-        rf += f;
-        rp += seq_units<PFX>(a, s_ctx[s]) - f;
+        rf += seq_full_units<PFX>(a, s_ctx[s]);
+        rp += seq_singles<PFX>(a, s_ctx[s]);
     }
     if (tid == kThreads - 1) {
         s_pf[B] = incf;
         s_pp[B] = incp;
     }
+    if (tid < kWave) {  // exclusive scan of the class sizes in wave 0
+        const int n = sort && tid < kTailBuckets ? s_hist[tid] : 0;
+        int x = n;
+#pragma unroll
+        for (int off = 1; off < kTailBuckets; off <<= 1) {
+            const int y = __shfl_up(x, off);
+            if (tid >= off) x += y;
+        }
+        if (tid < kTailBuckets) s_run[tid] = x - n;  // first slot of class tid
+        if (tid == kTailBuckets - 1) *s_ntail = x;
+    }
+    __syncthreads();
+    if (*s_ntail == 0) return;
+    // 256 sequences per round: a sequence's slot is its class's start, plus
+    // the class members of earlier rounds, earlier waves and lower lanes
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    for (int r0 = 0, par = 0; r0 < B; r0 += kThreads, par ^= 1) {
+        const int s = r0 + tid;
+        const int key = s < B ? tail_bucket<PFX>(a, s_ctx[s]) : -1;
+        int *cnt = s_cnt + par * kNumWaves * kTailBuckets;
+        int rank = 0;
+#pragma unroll
+        for (int k = 0; k < kTailBuckets; ++k) {
+            const uint64_t m = __ballot(key == k);
+            if (lane == 0) cnt[wave * kTailBuckets + k] = __popcll(m);
+            if (key == k) rank = __popcll(m & ((1ull << lane) - 1ull));
+        }
+        __syncthreads();
+        if (key >= 0) {
+            int pos = s_run[key] + rank;
+            for (int w = 0; w < wave; ++w) pos += cnt[w * kTailBuckets + key];
+            s_tail[pos] = (uint16_t)s;
+        }
+        __syncthreads();
+        if (tid < kTailBuckets) {
+            int n = 0;
+            for (int w = 0; w < kNumWaves; ++w) n += cnt[w * kTailBuckets + tid];
+            s_run[tid] += n;
+        }
+    }
     __syncthreads();
 }
 
-// Unit index -> (sequence, partition, KV head) and its token range, from the
-// prefix sums of build_unit_order (KV head fastest, full partitions first).
-// The fields are wave-uniform; readfirstlane keeps them in scalar registers.
+// Unit index -> (sequence, partition, KV head) and its token range, in the
+// order of build_unit_order (KV head fastest).  The fields are
+// wave-uniform; readfirstlane keeps them in scalar registers.
 template <bool PFX>
 __device__ __forceinline__ void decode_unit(const DecodeArgs &a, const int *s_pf, const int *s_pp,
-                                            const int *s_ctx, int unit, Unit &u) {
+                                            const int *s_ctx, const uint16_t *s_tail, int unit, Unit &u) {
     const int total_full = s_pf[a.num_seqs];
+    const int total_single = s_pp[a.num_seqs];
     u.kvh = unit % a.num_kv_heads;
     const int sp = unit / a.num_kv_heads;
     int span;
@@ -158,12 +239,19 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs &a, const int *s_pf
         u.p = sp - s_pf[u.s];
         u.part0 = u.p * a.unit_parts;
         span = run_tokens(a);
-    } else {                // one of the partitions after the sequence's runs
+    } else if (sp < total_full + total_single) {  // a partition after the runs
         const int r = sp - total_full;
         u.s = search_le(s_pp, a.num_seqs, r);
         const int runs = seq_full_units<PFX>(a, s_ctx[u.s]);
         u.p = runs + r - s_pp[u.s];
         u.part0 = runs * a.unit_parts + r - s_pp[u.s];
+        span = a.partition_size;
+    } else {                // a tail unit
+        u.s = s_tail[sp - total_full - total_single];
+        const int runs = seq_full_units<PFX>(a, s_ctx[u.s]);
+        const int singles = seq_whole_singles<PFX>(a, s_ctx[u.s]);
+        u.p = runs + singles;
+        u.part0 = runs * a.unit_parts + singles;
         span = a.partition_size;
     }
     u.s = __builtin_amdgcn_readfirstlane(u.s);
@@ -200,16 +288,15 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs &a, const int *s_pf
 // with LDS.
 template <bool PFX>
 __device__ __forceinline__ bool draw_unit(const DecodeArgs &a, const int *s_pf, const int *s_pp,
-                                          const int *s_ctx, int *s_unit, Unit &u, int drawers,
-                                          int drawer, bool &first) {
-    const int total_full = s_pf[a.num_seqs];
-    const int total_units = (total_full + s_pp[a.num_seqs]) * a.num_kv_heads;
+                                          const int *s_ctx, const uint16_t *s_tail, int n_tail,
+                                          int *s_unit, Unit &u, int drawers, int drawer, bool &first) {
+    const int total_units = (s_pf[a.num_seqs] + s_pp[a.num_seqs] + n_tail) * a.num_kv_heads;
     __syncthreads();
     if (first) {
         first = false;
         if (drawer == 0 && threadIdx.x == 0) atomicExch(a.work_counter, 0u);
         if (drawer >= total_units) return false;  // so are all counter tickets
-        decode_unit<PFX>(a, s_pf, s_pp, s_ctx, drawer, u);
+        decode_unit<PFX>(a, s_pf, s_pp, s_ctx, s_tail, drawer, u);
         return true;
     }
     if (threadIdx.x == 0) {
@@ -220,7 +307,7 @@ __device__ __forceinline__ bool draw_unit(const DecodeArgs &a, const int *s_pf, 
     __syncthreads();
     const int unit = *s_unit;
     if (unit < 0) return false;
-    decode_unit<PFX>(a, s_pf, s_pp, s_ctx, unit, u);
+    decode_unit<PFX>(a, s_pf, s_pp, s_ctx, s_tail, unit, u);
     return true;
 }
 
@@ -300,6 +387,7 @@ struct DecodeLds {
     int pages[kSegPages];
     int bad;
     int unit;
+    int ntail;  // tail units of the batch (build_unit_order)
     float m[kNumWaves][G];
     float l[kNumWaves][G];
     __attribute__((aligned(16))) char region[kNumWaves][kDecodeRegion];
@@ -307,8 +395,9 @@ struct DecodeLds {
 };
 
 // The decode work loop of one workgroup, as a device function over LDS the
-// kernel provides (s_dyn: full-unit prefix [B + 1], partial-unit prefix
-// [B + 1], lengths [B]); drawers = the launch's workgroups that draw units.
+// kernel provides (s_dyn: ints run prefix [B + 1], whole-partition prefix
+// [B + 1], lengths [B], then the tail list, B 16-bit sequence indices);
+// drawers = the launch's workgroups that draw units.
 template <int DT, int G, bool PFX, bool KV8, bool RUNS>
 __device__ __forceinline__ void decode_body(const DecodeArgs &a, int *s_dyn,
                                             DecodeLds<G, qop_in_lds<KV8>()> &L, int drawers) {
@@ -335,10 +424,12 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, int *s_dyn,
     int *s_pf = s_dyn;
     int *s_pp = s_dyn + a.num_seqs + 1;
     int *s_ctx = s_dyn + 2 * (a.num_seqs + 1);
+    uint16_t *s_tail = reinterpret_cast<uint16_t *>(s_ctx + a.num_seqs);
     // no counter: one unit per workgroup by index (unsplit calls without a
     // workspace; the plain instantiations only)
     const bool direct = !PFX && a.work_counter == nullptr;
-    if (!direct) build_unit_order<PFX>(a, s_pf, s_pp, s_ctx, s_pages);
+    if (!direct) build_unit_order<PFX>(a, s_pf, s_pp, s_ctx, s_tail, &L.ntail, s_pages);
+    const int n_tail = direct ? 0 : L.ntail;
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -358,7 +449,8 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, int *s_dyn,
     // this workgroup's index among the drawers (the last `drawers` of the grid)
     const int drawer = (int)blockIdx.x - ((int)gridDim.x - drawers);
     while (direct ? direct_unit(a, u, first)
-                  : draw_unit<PFX>(a, s_pf, s_pp, s_ctx, &L.unit, u, drawers, drawer, first)) {
+                  : draw_unit<PFX>(a, s_pf, s_pp, s_ctx, s_tail, n_tail, &L.unit, u, drawers, drawer,
+                                   first)) {
         if (tid == 0) s_bad = 0;
 
         // query operand: head h0 + c % G, chunks 4j + q
@@ -739,6 +831,12 @@ hipError_t occupancy(const void *fn, size_t dyn, int &cus, int &per_cu) {
 // Workgroups of a persistent grid: as many as are resident at once
 // (occupancy with `dyn` bytes of dynamic LDS), at most PKV_WG_PER_CU per CU,
 // capped by `units`.  0 on a HIP error (returned in `e`).
+// Dynamic LDS of the unit-order tables: three int arrays of B (+ 1) and the
+// 16-bit tail list, rounded up to whole ints.
+static size_t unit_order_bytes(int num_seqs) {
+    return (size_t)(3 * num_seqs + 2) * sizeof(int) + ((size_t)num_seqs * 2 + 3) / 4 * 4;
+}
+
 template <typename K>
 static int64_t resident_grid(K kernel, size_t dyn, int64_t units, hipError_t &e) {
     int cus = 0, per_cu = 0;
@@ -760,7 +858,7 @@ static hipError_t launch_persistent(K kernel, const DecodeArgs &a, hipStream_t s
         hipLaunchKernelGGL(kernel, dim3((unsigned)units), dim3(kThreads), 0, stream, a);
         return hipGetLastError();
     }
-    const size_t dyn = (size_t)(3 * a.num_seqs + 2) * sizeof(int);
+    const size_t dyn = unit_order_bytes(a.num_seqs);
     const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * a.num_partitions;  // upper bound
     hipError_t e;
     const int64_t grid = resident_grid(kernel, dyn, units, e);
@@ -808,7 +906,7 @@ template <int DT, int G, bool RUNS>
 static hipError_t launch_fused(const PrefixArgs &p, const DecodeArgs &a, int64_t prefix_units,
                                hipStream_t stream) {
     auto kernel = paged_prefix_fused_kernel<DT, G, RUNS>;
-    const size_t dyn = (size_t)(3 * a.num_seqs + 2) * sizeof(int);
+    const size_t dyn = unit_order_bytes(a.num_seqs);
     const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * a.num_partitions;  // upper bound
     hipError_t e;
     const int64_t grid = resident_grid(kernel, dyn, units, e);

@@ -91,6 +91,27 @@ __device__ __forceinline__ int seq_units(const DecodeArgs &a, int ctx) {
     return runs + (rest + a.partition_size - 1) / a.partition_size;
 }
 
+// Whole single partitions after a sequence's runs (not its last partition
+// when that one is partial).
+template <bool PFX = false>
+__device__ __forceinline__ int seq_whole_singles(const DecodeArgs &a, int ctx) {
+    const int span = ctx - first_token<PFX>(a);
+    if (bad_context(a, ctx) || span <= 0) return 0;
+    return (span % run_tokens(a)) / a.partition_size;
+}
+
+// Tokens of a sequence's tail unit -- its last partition when that one is
+// partial -- or -1 when it has none.  A sequence with nothing to read or an
+// out-of-range length has a tail unit of 0 tokens (it writes the zeros,
+// empty partial or NaNs).
+template <bool PFX = false>
+__device__ __forceinline__ int seq_tail_tokens(const DecodeArgs &a, int ctx) {
+    const int span = ctx - first_token<PFX>(a);
+    if (bad_context(a, ctx) || span <= 0) return 0;
+    const int rest = span % a.partition_size;
+    return rest > 0 ? rest : -1;
+}
+
 __device__ __forceinline__ Unit make_unit(const DecodeArgs &a) {
     // KV head fastest: the units that read the same pages run side by side.
     int u = blockIdx.x;

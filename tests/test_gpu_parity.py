@@ -240,12 +240,16 @@ def test_unsplit_without_workspace(cuda, kv):
 
 
 def test_unit_order_edges(cuda):
-    """Full-partition-first unit order: lengths that are exact multiples of
-    the partition (no partial unit), all-partial batches, empty contexts,
-    and the largest batch one call accepts."""
+    """Unit order (whole partitions first, then the partial last partitions
+    longest first, by a counting sort every workgroup repeats): lengths that
+    are exact multiples of the partition (no partial unit), all-partial
+    batches, empty contexts, a 300-sequence batch (two sorting rounds, the
+    second partial) whose tails fall in every length class, and the largest
+    batch one call accepts."""
     import torch
 
     cases = [([512, 1024, 2048], 512), ([3, 5, 200, 0, 511], 512), ([0, 0, 700, 1536], 256),
+             ([(i * 53) % 1000 for i in range(300)], 512),
              ([1 + (i * 37) % 300 for i in range(4096)], 128)]
     for lens, ps in cases:
         b = wl.make_batch(lens, num_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
