@@ -52,7 +52,7 @@ if REPO not in sys.path:
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 matrix peak, AMD published
 METRIC = "effective KV-read HBM GB/s (% of MI355X peak) + decode tokens/s, paged attention"
-SHARED_PREFIX_PARTITION = 512
+SHARED_PREFIX_PARTITION = 1024
 COLD_FLUSH_BYTES = 1 << 30   # > L2 (4 MiB per XCD) + MALL (256 MiB)
 STREAM_READ_BYTES = 2 << 30  # contiguous buffer of the streaming-read yardstick
 # parity bars on outputs in the cache dtype (max |gpu - oracle|)

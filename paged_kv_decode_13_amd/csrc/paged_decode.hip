@@ -213,13 +213,21 @@ template <int DT, int D, int NW>
 __global__ __launch_bounds__(NW * kWave) void lse_merge_kernel(DecodeArgs a) {
     const int s = blockIdx.x / a.num_heads;
     const int h = blockIdx.x % a.num_heads;
-    const int ctx = a.context_lens[s];
-    if (bad_context(a, ctx) || ctx == 0) return;  // written by partition 0
-    int nparts = (ctx + a.partition_size - 1) / a.partition_size;
-    if (nparts <= 1) return;                       // written directly
-    nparts = min(nparts, a.num_partitions);
     const int64_t row = (int64_t)s * a.num_heads + h;
-    merge_partials<DT, D, NW>(a, row * a.num_partitions, nparts, row * D);
+    const int ctx = a.context_lens[s];
+    if constexpr (NW == 1) {
+        EarlyPartials<D> e;
+        load_early<D>(a, row * a.num_partitions, a.num_partitions, e);
+        if (bad_context(a, ctx) || ctx == 0) return;  // written by partition 0
+        const int nparts = min((ctx + a.partition_size - 1) / a.partition_size, a.num_partitions);
+        if (nparts <= 1) return;                       // written directly
+        merge_early<DT, D>(a, e, row * a.num_partitions, nparts, row * D);
+    } else {
+        if (bad_context(a, ctx) || ctx == 0) return;
+        const int nparts = min((ctx + a.partition_size - 1) / a.partition_size, a.num_partitions);
+        if (nparts <= 1) return;
+        merge_partials<DT, D, NW>(a, row * a.num_partitions, nparts, row * D);
+    }
 }
 
 template <int DT, int D, int G>

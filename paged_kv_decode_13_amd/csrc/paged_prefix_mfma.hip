@@ -35,14 +35,20 @@ __global__ __launch_bounds__(NW * kWave) void prefix_merge_kernel(DecodeArgs a) 
     constexpr int D = 128;
     const int s = blockIdx.x / a.num_heads;
     const int h = blockIdx.x % a.num_heads;
-    const int ctx = a.context_lens[s];
     const int64_t row = (int64_t)s * a.num_heads + h;
+    const int ctx = a.context_lens[s];
+    EarlyPartials<D> e;
+    if constexpr (NW == 1) load_early<D>(a, row * a.part_stride, a.part_stride, e);
     if (bad_context(a, ctx) || ctx == 0) {
         const float v = ctx == 0 ? 0.f : __builtin_nanf("");
         for (int d = threadIdx.x; d < D; d += NW * kWave) store_out<DT>(a, row * D + d, v);
         return;
     }
-    merge_partials<DT, D, NW>(a, row * a.part_stride, a.part_base + seq_parts<true>(a, ctx), row * D);
+    const int n = a.part_base + seq_parts<true>(a, ctx);
+    if constexpr (NW == 1)
+        merge_early<DT, D>(a, e, row * a.part_stride, n, row * D);
+    else
+        merge_partials<DT, D, NW>(a, row * a.part_stride, n, row * D);
 }
 
 // With a shared prefix, its units and the suffix decode share one launch

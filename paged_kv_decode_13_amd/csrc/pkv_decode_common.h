@@ -290,6 +290,69 @@ __device__ __forceinline__ void merge_partials(const DecodeArgs &a, int64_t base
 // it has many, so that each wave's loads fit in a couple of round trips.
 constexpr int kMergeWideFrom = 32;
 
+// One-wave merge of a row with few partials.  The loads of its first
+// kMergeEarly slots are issued together with the row's length lookup, before
+// the number of partials n is known (slots below `cap`, the row's slot
+// count, always lie in the workspace; values past n are never used), so a
+// row with n <= kMergeEarly costs one memory round trip instead of three
+// (length, maxima, partials).
+constexpr int kMergeEarly = 8;
+
+template <int D>
+struct EarlyPartials {
+    float m[kMergeEarly], l[kMergeEarly];
+    float o[kMergeEarly][D / kWave];
+};
+
+template <int D>
+__device__ __forceinline__ void load_early(const DecodeArgs &a, int64_t base, int cap, EarlyPartials<D> &e) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int k = 0; k < kMergeEarly; ++k) {
+        if (k < cap) {
+            const float2 ml = *reinterpret_cast<const float2 *>(a.part_ml + (base + k) * 2);
+            e.m[k] = ml.x;
+            e.l[k] = ml.y;
+#pragma unroll
+            for (int j = 0; j < D / kWave; ++j) e.o[k][j] = a.part_out[(base + k) * D + lane + j * kWave];
+        }
+    }
+}
+
+// out = sum_p w_p o_p / sum_p w_p, w_p = l_p 2^(m_p - max_q m_q), over the n
+// slots from base (the first ones from `e`); a NaN max makes the output NaN.
+template <int DT, int D>
+__device__ __forceinline__ void merge_early(const DecodeArgs &a, const EarlyPartials<D> &e, int64_t base,
+                                            int n, int64_t out_idx) {
+    constexpr int PL = D / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    float M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kMergeEarly; ++k)
+        if (k < n) M = fmaxf(M, e.m[k]);
+    for (int p = kMergeEarly; p < n; ++p) M = fmaxf(M, a.part_ml[(base + p) * 2]);
+    float L = 0.f, O[PL];
+#pragma unroll
+    for (int j = 0; j < PL; ++j) O[j] = 0.f;
+#pragma unroll
+    for (int k = 0; k < kMergeEarly; ++k) {
+        if (k < n) {
+            const float w = e.l[k] * fast_exp2(e.m[k] - M);
+            L += w;
+#pragma unroll
+            for (int j = 0; j < PL; ++j) O[j] = fmaf(w, e.o[k][j], O[j]);
+        }
+    }
+    for (int p = kMergeEarly; p < n; ++p) {
+        const float w = a.part_ml[(base + p) * 2 + 1] * fast_exp2(a.part_ml[(base + p) * 2] - M);
+        L += w;
+#pragma unroll
+        for (int j = 0; j < PL; ++j) O[j] = fmaf(w, a.part_out[(base + p) * D + lane + j * kWave], O[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < PL; ++j) store_out<DT>(a, out_idx + lane + j * kWave, O[j] / L);
+}
+
 // MFMA decode kernel launcher (16-bit caches, head_dim 128); the merge
 // kernel is launched by the caller.  Without a workspace counter
 // (a.work_counter == nullptr; one partition per sequence only) the grid is

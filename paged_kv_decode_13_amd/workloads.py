@@ -16,7 +16,7 @@ type round-to-nearest-even):
                in [1, 4096], fp16; 512-token KV partitions;
   gqa_bf16     256 seqs, 32/8 heads, head_dim 128, block 16, contexts
                log-uniform in [128, 16000], bf16, one new token per sequence;
-               2560-token KV partitions;
+               5120-token KV partitions (8192 for its E4M3-cache variant);
   long_bf16    4 seqs x 32768, 64/8 heads, head_dim 128, block 32, bf16,
                512-token KV partitions;
   prefix_fp16  128 seqs sharing one 2048-token prefix (same physical pages)
@@ -24,7 +24,8 @@ type round-to-nearest-even):
                head_dim 128, fp16, block 8/16/32/64 on identical logical data;
                1024-token KV partitions.
 (The partition sizes of the workloads without a prescribed one are the
-fastest of 256..4096 measured on MI355X.)
+fastest of 256..16384 measured on MI355X; the long-context workload's 512
+is part of its definition.)
 
 Pages of every table are disjoint runs of a shuffled pool sized to fit
 (except the shared prefix), so consecutive logical blocks are never
@@ -564,7 +565,7 @@ def make_config(name: str, *, block_size: int | None = None, seed: int | None = 
         ctx = np.clip(ctx, 128, 16000).astype(np.int64)
         return make_batch(ctx, num_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
                           dtype="bf16", seed=seed, write_new_token=True, poison=poison,
-                          partition_size=4096 if name == "gqa_fp8" else 2560, name=name,
+                          partition_size=8192 if name == "gqa_fp8" else 5120, name=name,
                           values=values, kv_dtype="e4m3" if name == "gqa_fp8" else None)
     if name == "long_bf16":
         return make_batch(np.full(4, 32768), num_heads=64, num_kv_heads=8, head_dim=128,
