@@ -21,6 +21,15 @@
 // in LDS 512 at a time.  The output is written directly (no partials): a
 // unit sees all of its rows' history.
 //
+// Precision of the value product: a binary32 output keeps the two-term
+// probability split (about 16 / 21 bits of each probability reach the fp32
+// accumulators); a 16-bit output, which keeps 8 (bf16) or 11 (fp16)
+// significant bits itself, takes each probability rounded once to the
+// 16-bit type (relative error u = 2^-8 or 2^-11) and the normaliser summed
+// from the same rounded values, so the error it adds to an output element
+// is at most u / (1 - u) times (the softmax-weighted mean of |v| over the
+// row's history plus |out|), and the value product needs half the MFMAs.
+//
 // Unit order: a sequence's tiles of one KV head are consecutive and share an
 // XCD (they read the same history through one L2), the tiles with the
 // longest history first.
@@ -55,7 +64,7 @@ __device__ __forceinline__ int prefill_tiles(const PrefillArgs &a, int s, int &q
 // issued before this chunk's softmax, K and V in two-slot LDS rings, one
 // barrier per chunk) reached 256 VGPRs, and without registers to prefetch
 // LDS operands every MFMA waited on its read: 10.1 against 9.0 ms.
-template <int DT>
+template <int DT, bool SPLIT>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(mqa_waves_per_simd(kPrefillBlocks), 8)))
 void paged_prefill_mfma_kernel(PrefillArgs a) {
@@ -192,14 +201,14 @@ void paged_prefill_mfma_kernel(PrefillArgs a) {
             __syncthreads();
             ok = load_chunk(t0 + kMqaChunk, kr, vr);
             __builtin_amdgcn_sched_barrier(0);
-            mqa_chunk<DT, NB>(s_k, s_v, qop, j, q, t0, lim, t0 + kMqaChunk > wlim, sl2, st);
+            mqa_chunk<DT, NB, SPLIT>(s_k, s_v, qop, j, q, t0, lim, t0 + kMqaChunk > wlim, sl2, st);
             __syncthreads();
         }
     }
 
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-        const float L = mqa_row_sum(st[b]);
+        const float L = mqa_row_sum<SPLIT>(st[b]);
         if (!row_ok[b]) continue;
         const bool nan = bad || s_badtok < lim[b];
         const float inv = L > 0.f ? 1.f / L : 0.f;
@@ -225,8 +234,12 @@ static hipError_t launch_dt(const PrefillArgs &a, hipStream_t stream) {
     const int64_t units = ((rows + kPflRows - 1) / kPflRows + a.num_seqs) * a.num_kv_heads;
     if (units == 0) return hipSuccess;
     const size_t dyn = (size_t)(a.num_seqs + 1) * sizeof(int);
-    hipLaunchKernelGGL(paged_prefill_mfma_kernel<DT>, dim3((unsigned)units), dim3(kThreads), dyn,
-                       stream, a);
+    if (a.out_f32)
+        hipLaunchKernelGGL((paged_prefill_mfma_kernel<DT, true>), dim3((unsigned)units), dim3(kThreads), dyn,
+                           stream, a);
+    else
+        hipLaunchKernelGGL((paged_prefill_mfma_kernel<DT, false>), dim3((unsigned)units), dim3(kThreads), dyn,
+                           stream, a);
     return hipGetLastError();
 }
 

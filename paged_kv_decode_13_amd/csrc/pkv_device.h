@@ -97,6 +97,7 @@ __device__ __forceinline__ u32x4 load16_stream(const void *p) {
 
 // 8 bytes: eight E4M3 elements of a quantised cache row.
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ u32x2 load8_stream(const void *p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
 }

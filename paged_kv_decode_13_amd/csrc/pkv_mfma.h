@@ -12,7 +12,6 @@ namespace pkv {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 template <int DT>
 __device__ __forceinline__ f32x4_t mfma_16x16x32(const u32x4 a, const u32x4 b, f32x4_t c) {
@@ -64,6 +63,51 @@ __device__ __forceinline__ void split_pack(float p0, float p1, uint32_t &hi, uin
         const float r0 = p0 - (float)h[0];
         const float r1 = p1 - (float)h[1];
         lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(r0, r1));
+    }
+}
+
+// max(a, b, c) in one instruction (the compiler emits two v_max_f32 for
+// nested fmaxf).  Masked scores are -inf, never NaN.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
+__device__ __forceinline__ float max2f(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
+// rowgroup_max for values that are never NaN (scores, masked ones -inf):
+// no quieting of the swapped-in values.
+__device__ __forceinline__ float rowgroup_max_nn(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = max2f(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return max2f(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// A register quad of 16-bit ones: the A operand that turns a value MFMA into
+// a sum of its B operand over k.
+template <int DT>
+__device__ __forceinline__ u32x4 ones16() {
+    constexpr uint32_t one = DT == kBF16 ? 0x3F803F80u : 0x3C003C00u;
+    return u32x4{one, one, one, one};
+}
+
+// Two probabilities -> one packed 16-bit pair, each rounded to nearest even.
+template <int DT>
+__device__ __forceinline__ uint32_t pack_rne(float p0, float p1) {
+    if constexpr (DT == kBF16) {
+        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+        const bf16x2_t h = {(__bf16)p0, (__bf16)p1};
+        return __builtin_bit_cast(uint32_t, h);
+    } else {
+        typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+        const f16x2_t h = {(_Float16)p0, (_Float16)p1};
+        return __builtin_bit_cast(uint32_t, h);
     }
 }
 

@@ -18,9 +18,12 @@
 //        O^T[16 d x 16 rows] += V^T[16 x 32 tokens] . P^T[32 x 16].
 //    The padding puts rows 32 bytes apart in the banks: both the 16-byte
 //    row stores and the transposed loads are free of bank conflicts.
-//    The probabilities enter the 16-bit MFMA as a two-term split p = hi + lo,
-//    so the product keeps about 16 (bf16) or 21 (fp16) bits of p and the
-//    accumulation is fp32.
+//    With SPLIT the probabilities enter the 16-bit MFMA as a two-term split
+//    p = hi + lo, so the product keeps about 16 (bf16) or 21 (fp16) bits of p;
+//    without it p is rounded once to the 16-bit type (nearest even: relative
+//    error at most 2^-8 for bf16, 2^-11 for fp16), which halves the value
+//    product's MFMAs, and the row's normaliser is summed by the matrix cores
+//    from the same rounded values.  The accumulation is fp32 either way.
 //  - One reference max per row, shared by the row's four lane groups (two
 //    lane swaps per chunk), so every probability of a chunk is relative to
 //    the same max and the value product can sum across lane groups.  It
@@ -91,16 +94,22 @@ __device__ __forceinline__ float mqa_positive_scale(float sl2, u32x4 (&qop)[NB][
     return fmaxf(fabsf(sl2), 1.17549435e-38f);
 }
 
-// Running state of one query row (lane j of each lane group q).
+// Running state of one query row (lane j of each lane group q).  The
+// normaliser is kept either on the VALU (lsum: this lane's share, with the
+// two-term split) or by the matrix cores (lacc: an MFMA of the rounded
+// probabilities against a block of ones, every element the row's sum of
+// exactly the probabilities the value product used).
 struct MqaRowState {
     float m;          // reference max (equal in the row's four lane groups)
-    float lsum;       // this lane's share of the normaliser
+    float lsum;       // this lane's share of the normaliser (SPLIT)
+    f32x4_t lacc;     // the row's normaliser in each element (not SPLIT)
     f32x4_t acc[8];   // O^T: head dims 16 dt + 4q + r of row j
 };
 
 __device__ __forceinline__ void mqa_init(MqaRowState &st) {
     st.m = -INFINITY;
     st.lsum = 0.f;
+    st.lacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) st.acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 }
@@ -137,7 +146,7 @@ __device__ __forceinline__ void mqa_scores(const char *kt, const u32x4 (&qop)[NB
 // scale sl2 (> 0, exp2 domain; see mqa_positive_scale), the value product.
 // Row j of block b sees tokens t < lim[b]; `masked` (wave-uniform) says some
 // token of the chunk lies past some row's limit.
-template <int DT, int NB>
+template <int DT, int NB, bool SPLIT>
 __device__ __forceinline__ void mqa_softmax_values(const char *vt, int j, int q, int t0,
                                                    const int (&lim)[NB], bool masked, float sl2,
                                                    float (&sc)[NB][4][4], MqaRowState (&st)[NB]) {
@@ -161,19 +170,19 @@ __device__ __forceinline__ void mqa_softmax_values(const char *vt, int j, int q,
     }
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-        float mx = -INFINITY;
+        float mx = max3f(sc[b][0][0], sc[b][0][1], sc[b][0][2]);
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) mx = fmaxf(mx, sc[b][tt][rr]);
+        for (int i = 3; i < 15; i += 2) mx = max3f(mx, sc[b][i >> 2][i & 3], sc[b][(i + 1) >> 2][(i + 1) & 3]);
+        mx = max2f(mx, sc[b][3][3]);
         // the scale is positive, so the scaled max is the raw max scaled
-        mx = rowgroup_max(mx) * sl2;
+        mx = rowgroup_max_nn(mx) * sl2;
         // m = -inf until the row has seen a valid token
         const bool bump = mx > st[b].m + kMaxSlack;
         if (__builtin_amdgcn_ballot_w64(bump)) {
             const float alpha = !bump ? 1.f : (st[b].m == -INFINITY ? 0.f : fast_exp2(st[b].m - mx));
             st[b].m = bump ? mx : st[b].m;
-            st[b].lsum *= alpha;
+            if constexpr (SPLIT) st[b].lsum *= alpha;
+            else st[b].lacc *= alpha;
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt) st[b].acc[dt] *= alpha;
         }
@@ -185,9 +194,9 @@ __device__ __forceinline__ void mqa_softmax_values(const char *vt, int j, int q,
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
                 sc[b][tt][rr] = fast_exp2(fmaf(sc[b][tt][rr], sl2, -mref));
-                ps += sc[b][tt][rr];
+                if constexpr (SPLIT) ps += sc[b][tt][rr];
             }
-        st[b].lsum += ps;
+        if constexpr (SPLIT) st[b].lsum += ps;
     }
     // The value MFMAs run at raised wave priority: the SIMD then issues them
     // as soon as they are ready and fills the matrix pipe's busy cycles with
@@ -200,13 +209,20 @@ __device__ __forceinline__ void mqa_softmax_values(const char *vt, int j, int q,
         u32x4 ph[NB], pl[NB];
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-            uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
-            split_pack<DT>(sc[b][2 * bb][0], sc[b][2 * bb][1], h0, l0);
-            split_pack<DT>(sc[b][2 * bb][2], sc[b][2 * bb][3], h1, l1);
-            split_pack<DT>(sc[b][2 * bb + 1][0], sc[b][2 * bb + 1][1], h2, l2);
-            split_pack<DT>(sc[b][2 * bb + 1][2], sc[b][2 * bb + 1][3], h3, l3);
-            ph[b] = u32x4{h0, h1, h2, h3};
-            pl[b] = u32x4{l0, l1, l2, l3};
+            if constexpr (SPLIT) {
+                uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
+                split_pack<DT>(sc[b][2 * bb][0], sc[b][2 * bb][1], h0, l0);
+                split_pack<DT>(sc[b][2 * bb][2], sc[b][2 * bb][3], h1, l1);
+                split_pack<DT>(sc[b][2 * bb + 1][0], sc[b][2 * bb + 1][1], h2, l2);
+                split_pack<DT>(sc[b][2 * bb + 1][2], sc[b][2 * bb + 1][3], h3, l3);
+                ph[b] = u32x4{h0, h1, h2, h3};
+                pl[b] = u32x4{l0, l1, l2, l3};
+            } else {
+                ph[b] = u32x4{pack_rne<DT>(sc[b][2 * bb][0], sc[b][2 * bb][1]),
+                              pack_rne<DT>(sc[b][2 * bb][2], sc[b][2 * bb][3]),
+                              pack_rne<DT>(sc[b][2 * bb + 1][0], sc[b][2 * bb + 1][1]),
+                              pack_rne<DT>(sc[b][2 * bb + 1][2], sc[b][2 * bb + 1][3])};
+            }
         }
         // A operand V^T[16 dt + j][token]: source lane j of row group q
         // points at head dims 16 dt + 4 (j & 3) .. + 3 of token
@@ -221,8 +237,12 @@ __device__ __forceinline__ void mqa_softmax_values(const char *vt, int j, int q,
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
                 st[b].acc[dt] = mfma_16x16x32<DT>(vop, ph[b], st[b].acc[dt]);
-                st[b].acc[dt] = mfma_16x16x32<DT>(vop, pl[b], st[b].acc[dt]);
+                if constexpr (SPLIT) st[b].acc[dt] = mfma_16x16x32<DT>(vop, pl[b], st[b].acc[dt]);
             }
+        }
+        if constexpr (!SPLIT) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) st[b].lacc = mfma_16x16x32<DT>(ones16<DT>(), ph[b], st[b].lacc);
         }
     }
     __builtin_amdgcn_s_setprio(0);
@@ -231,17 +251,21 @@ __device__ __forceinline__ void mqa_softmax_values(const char *vt, int j, int q,
 // One 64-token chunk (tokens t0 .. t0 + 63 staged in kt / vt) for this
 // wave's NB column blocks of 16 rows: scores, then softmax and values; sl2
 // as for mqa_softmax_values.
-template <int DT, int NB>
+template <int DT, int NB, bool SPLIT = true>
 __device__ __forceinline__ void mqa_chunk(const char *kt, const char *vt, const u32x4 (&qop)[NB][4],
                                           int j, int q, int t0, const int (&lim)[NB], bool masked,
                                           float sl2, MqaRowState (&st)[NB]) {
     float sc[NB][4][4];  // [block][16-token tile][r]: token tile*16 + 4q + r, row j
     mqa_scores<DT, NB>(kt, qop, j, q, sc);
-    mqa_softmax_values<DT, NB>(vt, j, q, t0, lim, masked, sl2, sc, st);
+    mqa_softmax_values<DT, NB, SPLIT>(vt, j, q, t0, lim, masked, sl2, sc, st);
 }
 
 // The row's normaliser: the sum of the four lane groups' shares.
-__device__ __forceinline__ float mqa_row_sum(const MqaRowState &st) { return rowgroup_sum(st.lsum); }
+template <bool SPLIT = true>
+__device__ __forceinline__ float mqa_row_sum(const MqaRowState &st) {
+    if constexpr (SPLIT) return rowgroup_sum(st.lsum);
+    else return st.lacc[0];
+}
 
 // Workgroup id -> unit so that consecutive units share an XCD (consecutive
 // workgroup ids are dealt to the 8 XCDs in turn); a bijection on [0, n).

@@ -133,6 +133,33 @@ def rounded_out_ok(gpu: np.ndarray, ref: np.ndarray, dtype: str) -> bool:
     return bool(np.all(np.abs(gpu - ref) <= TIGHT[dtype] + half_ulp))
 
 
+# Unit roundoff of the 16-bit types: the largest relative error of a value
+# rounded to nearest even (significands of 8 and 11 bits).
+PROB_UNIT = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11}
+
+
+def abs_pool(cache: np.ndarray, dtype: str) -> np.ndarray:
+    """|x| of every element of a 16-bit pool (the sign bit cleared: exact)."""
+    assert dtype in ("f16", "bf16") and cache.dtype == np.uint16
+    return cache & np.uint16(0x7FFF)
+
+
+def single_rounding_ok(gpu: np.ndarray, ref: np.ndarray, dtype: str, wabs: np.ndarray) -> bool:
+    """16-bit outputs of a value product whose probabilities are rounded once
+    to the 16-bit type, p~_i = p_i (1 + e_i) with |e_i| <= u, and normalised
+    by the sum of the same rounded values: o~ - o = sum_i p_i e_i (v_i - o) /
+    sum_i p~_i, so |o~ - o| <= u / (1 - u) * (E_p|v| + |o|), where ``wabs`` is
+    the softmax-weighted mean E_p|v| (the same attention over |V|); then the
+    bound of rounded_out_ok on top."""
+    if np.isnan(gpu).any():
+        return False
+    u = PROB_UNIT[dtype]
+    mag = np.maximum(np.abs(ref), 2.0 ** -14)
+    half_ulp = 0.5 * 2.0 ** (np.floor(np.log2(mag)) - MANT_BITS[dtype])
+    bound = TIGHT[dtype] + half_ulp + u / (1.0 - u) * (wabs + np.abs(ref))
+    return bool(np.all(np.abs(gpu - ref) <= bound))
+
+
 def max_err(gpu: np.ndarray, ref: np.ndarray) -> float:
     assert gpu.shape == ref.shape
     if np.isnan(gpu).any():

@@ -7,7 +7,7 @@ import pytest
 
 import oracle
 from paged_kv_decode_13_amd import workloads as wl
-from tests.gpu_helpers import TIGHT, TOL, max_err, rounded_out_ok, to_f64, upload
+from tests.gpu_helpers import TIGHT, TOL, abs_pool, max_err, single_rounding_ok, to_f64, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -37,6 +37,12 @@ def _oracle_prefill(b, kc=None, vc=None):
                                 b.dtype)
 
 
+def _weighted_abs_v(b):
+    """Per output element, the softmax-weighted mean of |v| over the row's
+    history: the oracle's prefill over the pool with |V|."""
+    return _oracle_prefill(b, vc=abs_pool(b.value_cache, b.dtype))
+
+
 EDGE = [(dt, bs, g) for dt, bs, g in itertools.product(("f16", "bf16"), (4, 8, 16, 32, 64),
                                                        (1, 2, 4, 8))]
 
@@ -45,7 +51,9 @@ EDGE = [(dt, bs, g) for dt, bs, g in itertools.product(("f16", "bf16"), (4, 8, 1
 def test_prefill_edges(cuda, dtype, bs, group):
     """Whole prompts of ragged lengths (one past 2048 tokens, so several
     staged page segments at block 4), chunked prefills continuing a cached
-    history, single-query rows, an empty sequence and q_len = ctx = 1."""
+    history, single-query rows, an empty sequence and q_len = ctx = 1.
+    binary32 outputs (two-term probabilities) within 1e-4; 16-bit outputs
+    (probabilities rounded once) within the single-rounding bound."""
     ctx = [1, 37, 64, 65, 200, 300, 2100, 70, 0, 5]
     ql = [1, 37, 64, 13, 200, 1, 40, 70, 0, 5]
     b = wl.make_prefill_attention(ctx, ql, num_heads=2 * group, num_kv_heads=2, head_dim=128,
@@ -55,7 +63,7 @@ def test_prefill_edges(cuda, dtype, bs, group):
     out = to_f64(_gpu_prefill(b, upload(b, cuda), out_dtype="f32"))
     assert max_err(out, ref) <= TIGHT[dtype], max_err(out, ref)
     out = to_f64(_gpu_prefill(b, upload(b, cuda)))
-    assert rounded_out_ok(out, ref, dtype), max_err(out, ref)
+    assert single_rounding_ok(out, ref, dtype, _weighted_abs_v(b)), max_err(out, ref)
 
 
 def test_prefill_single_queries_match_decode(cuda):
@@ -116,11 +124,16 @@ def test_prefill_out_of_range_contents(cuda):
     torch.cuda.synchronize()
 
 
-def test_prefill_full_workload_sampled(cuda):
+def test_prefill_full_workload_decimated(cuda):
     """The prompt workload at full size (32 prompts of 1024..8192 tokens):
     the bulk write of every prompt token through slot_mapping, then causal
-    attention of every prompt token; 96 sampled (token, head) rows against
-    the oracle's attention over the history that row sees."""
+    attention of every prompt token.  Compared element by element over a
+    deterministic decimation: every sequence, every query head (so every KV
+    head), the first and the last query row of every 64-token chunk -- which
+    touches every 32-token row tile of the kernel, each tile's diagonal
+    included -- each against the oracle's decode of that row over the
+    history it sees (a causal row at position p attends to tokens 0..p, the
+    decode of context p + 1), at the 5e-3 bar of 16-bit caches."""
     import torch
 
     import paged_kv_decode_13_amd as pkv
@@ -128,24 +141,26 @@ def test_prefill_full_workload_sampled(cuda):
     b = wl.add_prompt_queries(wl.make_prefill_config("prefill_bf16"), seed=11)
     t = upload(b, cuda)
     pkv.paged_kv_write(t["nk"], t["nv"], t["kc"], t["vc"], t["slots"])
-    out = _gpu_prefill(b, t).cpu()
+    out = _gpu_prefill(b, t)
     torch.cuda.synchronize()
     kc, vc = b.key_cache.copy(), b.value_cache.copy()
     oracle.paged_kv_write(b.new_key, b.new_value, kc, vc, b.slot_mapping)
     qsl = b.meta["query_start_loc"]
-    rng = np.random.default_rng(4)
-    g = b.num_heads // b.num_kv_heads
-    q = oracle.to_float64(b.meta["prompt_query"], "bf16")
-    worst = 0.0
-    for s_ in rng.choice(b.num_seqs, 8, replace=False):
-        ctx = int(b.context_lens[s_])
-        for kvh in rng.choice(b.num_kv_heads, 2, replace=False):
-            keys, vals = oracle.paged_gather(kc, vc, b.block_tables[s_], ctx, int(kvh), "bf16")
-            for pos in list(rng.choice(ctx, 5, replace=False)) + [ctx - 1]:
-                h = int(kvh) * g + int(rng.integers(g))
-                row = int(qsl[s_]) + int(pos)
-                ref = oracle.attention(q[row, h], keys[:pos + 1], vals[:pos + 1], b.scale)
-                got = out[row, h].float().numpy().astype(np.float64)
-                worst = max(worst, float(np.max(np.abs(got - ref))))
-    print(f"\n[prefill_bf16] sampled max|err| {worst:.3e}", flush=True)
-    assert worst <= TOL["bf16"]
+    rows, seqs, ctxs = [], [], []
+    for s_ in range(b.num_seqs):
+        n = int(b.context_lens[s_])
+        for c0 in range(0, n, 64):
+            for pos in sorted({c0, min(n - 1, c0 + 63)}):
+                rows.append(int(qsl[s_]) + pos)
+                seqs.append(s_)
+                ctxs.append(pos + 1)
+    rows = np.asarray(rows)
+    seqs = np.asarray(seqs)
+    print(f"\n[prefill_bf16] {rows.size} query rows x {b.num_heads} heads", flush=True)
+    ref = oracle.paged_decode(np.ascontiguousarray(b.meta["prompt_query"][rows]), kc, vc,
+                              np.ascontiguousarray(b.block_tables[seqs]),
+                              np.asarray(ctxs, dtype=np.int32), b.block_size, b.scale, "bf16")
+    got = to_f64(out[torch.from_numpy(rows).to(out.device)])
+    err = max_err(got, ref)
+    print(f"[prefill_bf16] max|err| {err:.3e}", flush=True)
+    assert err <= TOL["bf16"]
