@@ -44,6 +44,11 @@ constexpr int mqa_waves_per_simd(int nb) { return nb == 1 ? 3 : 2; }
 constexpr int kMqaChunk = 64;                       // tokens per LDS chunk
 constexpr int kMqaRowBytes = 256;                   // one 16-bit K or V row (D = 128)
 constexpr int kMqaVRow = kMqaRowBytes + 32;        // padded V row in LDS
+// VALU instructions placed after each value MFMA of the first half of a
+// chunk in the single-rounding value product (0: the compiler's schedule)
+#ifndef PKV_MQA_INTERLEAVE
+#define PKV_MQA_INTERLEAVE 3
+#endif
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
@@ -141,6 +146,75 @@ __device__ __forceinline__ void mqa_scores(const char *kt, const u32x4 (&qop)[NB
     }
 }
 
+// Value product of one 64-token chunk with single-rounded probabilities,
+// given each row's reference max mref: the probabilities of tokens 0..31
+// first, then the value MFMAs of those tokens (and their normaliser MFMA)
+// with the exponentials of tokens 32..63 scheduled between them, so that
+// the wave keeps the matrix pipe busy while it computes the second half's
+// probabilities; then the second half's MFMAs.  Runs at raised wave
+// priority (see mqa_softmax_values).
+template <int DT, int NB>
+__device__ __forceinline__ void mqa_values_single(const char *vt, int j, int q, float sl2,
+                                                  const float (&mref)[NB], float (&sc)[NB][4][4],
+                                                  MqaRowState (&st)[NB]) {
+    auto probs = [&](int bb) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int tt = 2 * bb; tt < 2 * bb + 2; ++tt)
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) sc[b][tt][rr] = fast_exp2(fmaf(sc[b][tt][rr], sl2, -mref[b]));
+    };
+    auto values = [&](int bb) {
+        u32x4 ph[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+            ph[b] = u32x4{pack_rne<DT>(sc[b][2 * bb][0], sc[b][2 * bb][1]),
+                          pack_rne<DT>(sc[b][2 * bb][2], sc[b][2 * bb][3]),
+                          pack_rne<DT>(sc[b][2 * bb + 1][0], sc[b][2 * bb + 1][1]),
+                          pack_rne<DT>(sc[b][2 * bb + 1][2], sc[b][2 * bb + 1][3])};
+        const char *vrow = vt + (32 * bb + 4 * q + (j >> 2)) * kMqaVRow + 8 * (j & 3);
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            const u32x2 v0 = lds_read_tr16(vrow + 32 * dt);
+            const u32x2 v1 = lds_read_tr16(vrow + 16 * kMqaVRow + 32 * dt);
+            const u32x4 vop = u32x4{v0[0], v0[1], v1[0], v1[1]};
+#pragma unroll
+            for (int b = 0; b < NB; ++b) st[b].acc[dt] = mfma_16x16x32<DT>(vop, ph[b], st[b].acc[dt]);
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) st[b].lacc = mfma_16x16x32<DT>(ones16<DT>(), ph[b], st[b].lacc);
+    };
+    probs(0);
+    __builtin_amdgcn_s_setprio(1);
+    __builtin_amdgcn_sched_barrier(0);
+    values(0);
+    probs(1);
+#if PKV_MQA_INTERLEAVE
+    // the transposed V reads one head-dim block ahead of the MFMAs that use
+    // them; a few VALU instructions of the second half's probabilities after
+    // every value MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // LDS reads
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, PKV_MQA_INTERLEAVE, 0);  // VALU
+        }
+        if (i < 7) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, PKV_MQA_INTERLEAVE, 0);
+    }
+#endif
+    __builtin_amdgcn_sched_barrier(0);
+    values(1);
+    __builtin_amdgcn_s_setprio(0);
+}
+
 // The rest of one 64-token chunk (tokens t0 .. t0 + 63, V rows staged in
 // vt) given its raw scores: masking, the online softmax with the score
 // scale sl2 (> 0, exp2 domain; see mqa_positive_scale), the value product.
@@ -168,6 +242,7 @@ __device__ __forceinline__ void mqa_softmax_values(const char *vt, int j, int q,
                 for (int rr = 0; rr < 4; ++rr)
                     sc[b][tt][rr] = (tt * 16 + rr < nv[b]) ? sc[b][tt][rr] : -INFINITY;
     }
+    float mref[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
         float mx = max3f(sc[b][0][0], sc[b][0][1], sc[b][0][2]);
@@ -187,16 +262,22 @@ __device__ __forceinline__ void mqa_softmax_values(const char *vt, int j, int q,
             for (int dt = 0; dt < 8; ++dt) st[b].acc[dt] *= alpha;
         }
         // a row with m = -inf has only masked scores here: 2^(-inf - 0) = 0
-        const float mref = st[b].m == -INFINITY ? 0.f : st[b].m;
-        float ps = 0.f;
+        mref[b] = st[b].m == -INFINITY ? 0.f : st[b].m;
+        if constexpr (SPLIT) {
+            float ps = 0.f;
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
+            for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                sc[b][tt][rr] = fast_exp2(fmaf(sc[b][tt][rr], sl2, -mref));
-                if constexpr (SPLIT) ps += sc[b][tt][rr];
-            }
-        if constexpr (SPLIT) st[b].lsum += ps;
+                for (int rr = 0; rr < 4; ++rr) {
+                    sc[b][tt][rr] = fast_exp2(fmaf(sc[b][tt][rr], sl2, -mref[b]));
+                    ps += sc[b][tt][rr];
+                }
+            st[b].lsum += ps;
+        }
+    }
+    if constexpr (!SPLIT) {
+        mqa_values_single<DT, NB>(vt, j, q, sl2, mref, sc, st);
+        return;
     }
     // The value MFMAs run at raised wave priority: the SIMD then issues them
     // as soon as they are ready and fills the matrix pipe's busy cycles with
