@@ -215,18 +215,18 @@ __global__ __launch_bounds__(NW * kWave) void lse_merge_kernel(DecodeArgs a) {
     const int h = blockIdx.x % a.num_heads;
     const int64_t row = (int64_t)s * a.num_heads + h;
     const int ctx = a.context_lens[s];
+    // one slot per work unit of the sequence (seq_units), one partition each
+    // unless runs of unit_parts partitions were joined in the decode kernel
     if constexpr (NW == 1) {
         EarlyPartials<D> e;
         load_early<D>(a, row * a.num_partitions, a.num_partitions, e);
         if (bad_context(a, ctx) || ctx == 0) return;  // written by partition 0
-        const int nparts = min((ctx + a.partition_size - 1) / a.partition_size, a.num_partitions);
-        if (nparts <= 1) return;                       // written directly
-        merge_early<DT, D>(a, e, row * a.num_partitions, nparts, row * D);
+        if (seq_parts(a, ctx) <= 1) return;            // written directly
+        merge_early<DT, D>(a, e, row * a.num_partitions, seq_units(a, ctx), row * D);
     } else {
         if (bad_context(a, ctx) || ctx == 0) return;
-        const int nparts = min((ctx + a.partition_size - 1) / a.partition_size, a.num_partitions);
-        if (nparts <= 1) return;
-        merge_partials<DT, D, NW>(a, row * a.num_partitions, nparts, row * D);
+        if (seq_parts(a, ctx) <= 1) return;
+        merge_partials<DT, D, NW>(a, row * a.num_partitions, seq_units(a, ctx), row * D);
     }
 }
 
@@ -263,14 +263,20 @@ static hipError_t launch_merge(const DecodeArgs &a, hipStream_t stream) {
 template <int DT>
 static hipError_t launch_dtype(const DecodeArgs &a, int head_dim, hipStream_t stream) {
     hipError_t e;
-    if (head_dim == 128) {
-        // 16-bit caches take the matrix-core kernel; binary32 the VALU kernel
-        e = (DT == kF32) ? launch_valu_group<DT, 128>(a, stream) : launch_paged_decode_mfma(a, DT, stream);
+    if (head_dim == 128 && DT != kF32) {  // 16-bit caches: the matrix-core kernel
+        e = launch_paged_decode_mfma(a, DT, stream);
         return e != hipSuccess ? e : launch_merge<DT, 128>(a, stream);
     }
+    // binary32 caches or head_dim 64: the VALU kernel, one slot per partition
+    DecodeArgs v = a;
+    v.unit_parts = 1;
+    if (head_dim == 128) {
+        e = launch_valu_group<DT, 128>(v, stream);
+        return e != hipSuccess ? e : launch_merge<DT, 128>(v, stream);
+    }
     if (head_dim == 64) {
-        e = launch_valu_group<DT, 64>(a, stream);
-        return e != hipSuccess ? e : launch_merge<DT, 64>(a, stream);
+        e = launch_valu_group<DT, 64>(v, stream);
+        return e != hipSuccess ? e : launch_merge<DT, 64>(v, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -682,81 +682,51 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, int *s_dyn,
             }
         };
 
+        reset();
         if (RUNS && u.tok_end - u.tok_begin == kNumWaves * a.partition_size) {
-            // A whole run: wave w streams partition part0 + w alone and
-            // writes its partial from its registers -- the column's max is
-            // already shared by the wave's four row groups -- so the waves
-            // meet only at the next unit's draw.
+            // A whole run: wave w streams partition part0 + w alone, so the
+            // waves meet only at the epilogue, which joins their four states
+            // into the run's one partial (a quarter of the partials for the
+            // merge to read).
             stage(u.tok_begin, u.tok_end);
             const int pt = u.tok_begin + wave * a.partition_size;
             seg_end = pt + a.partition_size;
-            reset();
             stream(pt, TILE * TPS);
-            const float Lc = rowgroup_sum(lsum);
-            if (c < G) {
-                const int h = h0 + c;
-                const int pi = u.part0 + wave;
-                const int64_t slot = PFX ? ((int64_t)u.s * a.num_heads + h) * a.part_stride + a.part_base + pi
-                                         : ((int64_t)u.s * a.num_heads + h) * a.num_partitions + pi;
-                const bool bad = u.bad_len || s_bad != 0;
-                const float vs = KV8 ? a.v_scale[u.kvh] : 1.f;
-                const float inv = Lc > 0.f ? 1.f / Lc : 0.f;
-                float *dst = a.part_out + slot * D + 32 * q;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    f32x4_t lo, hi;
-#pragma unroll
-                    for (int dt = 0; dt < 4; ++dt) {
-                        lo[dt] = bad ? __builtin_nanf("") : acc[dt][r] * inv * vs;
-                        hi[dt] = bad ? __builtin_nanf("") : acc[4 + dt][r] * inv * vs;
-                    }
-                    *reinterpret_cast<f32x4_t *>(dst + 8 * r) = lo;
-                    *reinterpret_cast<f32x4_t *>(dst + 8 * r + 4) = hi;
-                }
-                if (q == 0) {
-                    a.part_ml[slot * 2] = bad ? __builtin_nanf("") : m;
-                    a.part_ml[slot * 2 + 1] = Lc;
-                }
-            }
-            continue;  // the next draw starts with a barrier
-        }
-
-        // Otherwise the unit's partitions one after the other, the four
-        // waves interleaved (32-token pairs), each partition ending in a
-        // cross-wave epilogue (partial or output); page ids staged for up to
-        // kSegPages pages of the unit at a time.
-        for (int pt = u.tok_begin, pi = u.part0;; pt += a.partition_size, ++pi) {
-            const int pend = min(u.tok_end, pt + a.partition_size);
-            reset();
-            for (int seg = pt; seg < pend; seg = seg_end) {
+        } else {
+            // One partition, the four waves interleaved (32-token pairs);
+            // page ids staged for up to kSegPages pages of it at a time.
+            for (int seg = u.tok_begin; seg < u.tok_end; seg = seg_end) {
                 if (seg >= stg_hi) stage(seg, min(u.tok_end, seg + (kSegPages << lbs)));
-                seg_end = min(pend, stg_hi);
+                seg_end = min(u.tok_end, stg_hi);
                 stream(seg + wave * TILE * TPS, kNumWaves * TILE * TPS);
             }
-
-            // the column's normaliser is the sum over the four row groups;
-            // lanes (q, c < G) hold head c's dims 32q + 8r + dt in acc[dt][r]
-            const float Lc = rowgroup_sum(lsum);
-            float *wacc = reinterpret_cast<float *>(kt);
-            if (c < G) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float *dst = wacc + c * D + 32 * q + 8 * r;
-                    *reinterpret_cast<f32x4_t *>(dst) = f32x4_t{acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
-                    *reinterpret_cast<f32x4_t *>(dst + 4) = f32x4_t{acc[4][r], acc[5][r], acc[6][r], acc[7][r]};
-                }
-                if (q == 0) {
-                    s_m[wave][c] = m;
-                    s_l[wave][c] = Lc;
-                }
-            }
-            __syncthreads();
-            unit_epilogue<DT, D, G, PFX, kRegion / 4>(a, u, pi, u.bad_len || s_bad != 0, s_m, s_l,
-                                                             reinterpret_cast<const float *>(&s_region[0][0]),
-                                                             KV8 ? a.v_scale[u.kvh] : 1.f);
-            if (pend >= u.tok_end) break;
-            __syncthreads();  // every wave's region has been read before the next K tiles land there
         }
+
+        // Epilogue: the column's normaliser is the sum over the four row
+        // groups; lanes (q, c < G) hold head c's dims 32q + 8r + dt in
+        // acc[dt][r].  The waves' states meet in LDS, and the unit stores
+        // the output (an unsplit sequence) or its partial, in slot u.p of
+        // the row (one slot per unit).
+        const float Lc = rowgroup_sum(lsum);
+        float *wacc = reinterpret_cast<float *>(kt);
+        if (c < G) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float *dst = wacc + c * D + 32 * q + 8 * r;
+                *reinterpret_cast<f32x4_t *>(dst) = f32x4_t{acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
+                *reinterpret_cast<f32x4_t *>(dst + 4) = f32x4_t{acc[4][r], acc[5][r], acc[6][r], acc[7][r]};
+            }
+            if (q == 0) {
+                s_m[wave][c] = m;
+                s_l[wave][c] = Lc;
+            }
+        }
+        __syncthreads();
+        unit_epilogue<DT, D, G, PFX, kRegion / 4>(a, u, u.p, u.bad_len || s_bad != 0, s_m, s_l,
+                                                         reinterpret_cast<const float *>(&s_region[0][0]),
+                                                         KV8 ? a.v_scale[u.kvh] : 1.f);
+        // the next draw starts with a barrier: every wave's region has been
+        // read before the next unit's K tiles land there
     }
 }
 

@@ -44,7 +44,7 @@ __global__ __launch_bounds__(NW * kWave) void prefix_merge_kernel(DecodeArgs a) 
         for (int d = threadIdx.x; d < D; d += NW * kWave) store_out<DT>(a, row * D + d, v);
         return;
     }
-    const int n = a.part_base + seq_parts<true>(a, ctx);
+    const int n = a.part_base + seq_units<true>(a, ctx);  // one slot per suffix unit
     if constexpr (NW == 1)
         merge_early<DT, D>(a, e, row * a.part_stride, n, row * D);
     else

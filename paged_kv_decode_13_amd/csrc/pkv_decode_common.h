@@ -66,9 +66,10 @@ __device__ __forceinline__ int seq_full(const DecodeArgs &a, int ctx) {
 // Work units of the persistent kernels.  With unit_parts == 1 a unit is one
 // partition.  With unit_parts == kNumWaves a sequence's span starts with
 // runs of kNumWaves whole partitions, one unit each, in which every wave
-// streams one partition alone (no cross-wave merge: each wave writes its
-// partition's partial); the rest of the span is one unit per partition.
-// Either way the log-sum-exp merge joins partition_size-token partials.
+// streams one partition alone (the waves meet only at the unit's epilogue,
+// which joins their four partition states); the rest of the span is one
+// unit per partition.  Either way every unit of a split sequence writes one
+// partial slot, so a row has seq_units slots for the merge to join.
 __device__ __forceinline__ int run_tokens(const DecodeArgs &a) { return a.partition_size * a.unit_parts; }
 
 // Units of a sequence that are whole runs of unit_parts partitions.
