@@ -11,14 +11,14 @@
 // query i at position p = ctx - q_len + i attends to tokens 0..p through the
 // sequence's block table.
 //
-// Work unit = (sequence, KV head, tile of kPflRows = 128 query rows, 32 per
+// Work unit = (sequence, KV head, tile of kPflRows = 192 query rows, 48 per
 // wave); a query row is one (query token, head of the group) pair, so a tile
-// holds 128 / G consecutive query tokens.  Each unit streams the visible
+// holds 192 / G consecutive query tokens.  Each unit streams the visible
 // history [0, last position of the tile] through the chunk machinery of
-// pkv_mqa.h (64 tokens at a time, K and V rows in LDS, scores and values as
-// MFMA products); each row masks the tokens past its own position, so only
-// the chunks on the tile's diagonal carry masking work.  Page ids are staged
-// in LDS 512 at a time.  The output is written directly (no partials): a
+// pkv_mqa.h (64 tokens at a time, K and V rows loaded straight into LDS,
+// scores and values as MFMA products); each row masks the tokens past its
+// own position, so only the chunks on the tile's diagonal carry masking
+// work.  Page ids are staged in LDS 512 at a time.  The output is written directly (no partials): a
 // unit sees all of its rows' history.
 //
 // Precision of the value product: a binary32 output keeps the two-term
@@ -43,8 +43,6 @@ namespace pkv {
 constexpr int kPflSegPages = 512;  // page ids staged in LDS at a time
 constexpr int kPflRows = kNumWaves * 16 * kPrefillBlocks;  // query rows per tile
 
-
-
 // Row tiles of a sequence; 0 when its query range lies outside
 // [0, total_queries] (such rows are never read or written).
 __device__ __forceinline__ int prefill_tiles(const PrefillArgs &a, int s, int &q0, int &q_len) {
@@ -55,15 +53,15 @@ __device__ __forceinline__ int prefill_tiles(const PrefillArgs &a, int s, int &q
     return ((q_len << a.log2_group) + kPflRows - 1) / kPflRows;
 }
 
-// One 37 KiB LDS chunk buffer per workgroup.  With one 16-row block per
-// wave three workgroups fit per CU (<= 168 VGPRs) and hid the chunk loads'
-// latency better than two with double-buffered LDS (10.9 against 12.8 ms on
-// the 32-prompt workload); two blocks per wave at two workgroups per CU
-// took it to 9.5 ms, and a second LDS buffer there (one barrier per chunk)
-// measured 1.5% slower.  A software pipeline (the next chunk's score MFMAs
-// issued before this chunk's softmax, K and V in two-slot LDS rings, one
-// barrier per chunk) reached 256 VGPRs, and without registers to prefetch
-// LDS operands every MFMA waited on its read: 10.1 against 9.0 ms.
+// Chunks arrive through direct-to-LDS loads into two buffers (70 KiB of
+// LDS per workgroup, two workgroups per CU): the loads of chunk n + 1 need
+// no registers, so each wave holds three 16-row column blocks (one operand
+// read from LDS feeds three MFMAs) within the budget of two waves per SIMD.
+// Measured on the 32-prompt workload against the earlier design (one LDS
+// buffer, the next chunk in registers, two blocks per wave): 6.93-7.00 ->
+// 6.26-6.28 ms.  Earlier steps: one block per wave at three workgroups per
+// CU 10.9 ms, two blocks 9.5 ms; a software pipeline (the next chunk's score
+// MFMAs before this chunk's softmax) reached 256 VGPRs and was slower.
 template <int DT, bool SPLIT>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(mqa_waves_per_simd(kPrefillBlocks), 8)))
@@ -71,8 +69,11 @@ void paged_prefill_mfma_kernel(PrefillArgs a) {
     constexpr int D = 128;
     constexpr int ROW = kMqaRowBytes;
     extern __shared__ int s_tpre[];  // [B + 1]: exclusive prefix sum of tiles
-    __shared__ __attribute__((aligned(16))) char s_k[kMqaChunk * kMqaRowBytes];  // K rows of a chunk
-    __shared__ __attribute__((aligned(16))) char s_v[kMqaChunk * kMqaVRow];        // V rows of a chunk
+    // two chunk buffers, each K rows then V rows in the kMqaDirect layout;
+    // separate arrays, so the compiler can tell the reads of one from the
+    // loads in flight into the other
+    __shared__ __attribute__((aligned(16))) char s_kv0[2 * kMqaDirectBytes];
+    __shared__ __attribute__((aligned(16))) char s_kv1[2 * kMqaDirectBytes];
     __shared__ int s_pages[kPflSegPages];
     __shared__ int s_scan[kNumWaves];  // block_scan: one total per wave
     __shared__ int s_badtok;
@@ -147,13 +148,13 @@ void paged_prefill_mfma_kernel(PrefillArgs a) {
     wlim = __builtin_amdgcn_readfirstlane(wlim);
     const float sl2 = mqa_positive_scale<NB>(a.scale_log2e, qop);
 
-    // staging roles as in the shared-prefix kernel
+    // staging roles: thread lg = tid / 16 loads tokens 4 lg .. 4 lg + 3 of
+    // a chunk (one page), 16 bytes of each
     const int lc = tid & 15;
     const int lg = tid >> 4;
     const char *kbase = reinterpret_cast<const char *>(a.key_cache);
     const char *vbase = reinterpret_cast<const char *>(a.value_cache);
     const int64_t tok_stride = (int64_t)a.num_kv_heads * ROW;
-    const int64_t lane_off = (int64_t)kvh * ROW + lc * 16;
     const int32_t *table = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
 
     MqaRowState st[NB];
@@ -174,35 +175,63 @@ void paged_prefill_mfma_kernel(PrefillArgs a) {
         }
         __syncthreads();
 
-        // tokens past the segment or on a bad page read page-0 rows (always
-        // in the pool): V staged as zeros, scores masked.  The range ends at
-        // any token, so validity is per token (bit k: token 4 lg + k).
-        auto load_chunk = [&](int t0, u32x4 (&kr)[4], u32x4 (&vr)[4]) -> uint32_t {
+        const int nch = (seg_end - seg + kMqaChunk - 1) / kMqaChunk;
+        // Thread (wave w, lane group qq, lane lc of the group) loads tokens
+        // 4 lg + i (lg = 4 w + qq, i = 0..3) straight into LDS in the
+        // kMqaDirect layout: load i of wave w fills group i of block w, and
+        // the thread's 16 bytes are K chunk lc ^ qq and V chunk lc ^ 2 qq.
+        const int qq = lg & 3;
+        const int koff = (lc ^ qq) * 16;
+        const int voff = (lc ^ (2 * qq)) * 16;
+        // Tokens past the segment or on a bad page read page-0 rows (always
+        // in the pool): V zeroed after the loads land, scores masked.  The
+        // range ends at any token, so validity is per token (bit i: token
+        // 4 lg + i).
+        auto issue = [&](int t0, char *buf) -> uint32_t {
             const int t = t0 + 4 * lg;
             const int pb = s_pages[min((t - seg) >> lbs, npages - 1)];
             const bool page_ok = (t < seg_end) & (pb >= 0);
-            const int64_t base = ((int64_t)(page_ok ? pb : 0) * bs + (t & (bs - 1))) * tok_stride + lane_off;
+            const int64_t base = ((int64_t)(page_ok ? pb : 0) * bs + (t & (bs - 1))) * tok_stride +
+                                 (int64_t)kvh * ROW;
+            const char *ks = kbase + base + koff;
+            const char *vs = vbase + base + voff;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                kr[k] = load16(kbase + base + k * tok_stride);
-                vr[k] = load16(vbase + base + k * tok_stride);
+            for (int i = 0; i < 4; ++i) {
+                char *kd = buf + wave * kMqaBlockBytes + i * kMqaGroupBytes;
+                __builtin_amdgcn_global_load_lds(ks + i * tok_stride, (__attribute__((address_space(3))) void *)kd,
+                                                 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(vs + i * tok_stride,
+                                                 (__attribute__((address_space(3))) void *)(kd + kMqaDirectBytes),
+                                                 16, 0, 0);
             }
             const int n_ok = page_ok ? min(4, seg_end - t) : 0;
             return (1u << n_ok) - 1u;
         };
-        const int nch = (seg_end - seg + kMqaChunk - 1) / kMqaChunk;
-        // chunk n is computed from the LDS buffer while chunk n + 1 is in
-        // flight in registers (one buffer, two barriers per chunk)
-        u32x4 kr[4], vr[4];
-        uint32_t ok = load_chunk(seg, kr, vr);
-        for (int n = 0; n < nch; ++n) {
+        // chunk n is computed from one buffer while chunk n + 1 loads into
+        // the other (one barrier per chunk); unrolled by two so that every
+        // step names its two buffers
+        uint32_t ok = issue(seg, s_kv0);
+        auto step = [&](int n, char *cur, char *nxt) {
             const int t0 = seg + n * kMqaChunk;
-            mqa_store_chunk(s_k, s_v, lc, lg, kr, vr, ok);
-            __syncthreads();
-            ok = load_chunk(t0 + kMqaChunk, kr, vr);
-            __builtin_amdgcn_sched_barrier(0);
-            mqa_chunk<DT, NB, SPLIT>(s_k, s_v, qop, j, q, t0, lim, t0 + kMqaChunk > wlim, sl2, st);
-            __syncthreads();
+            // this thread's loads of chunk n have landed; V rows of tokens
+            // that are not valid become zeros (a zero probability times a
+            // NaN row would still be NaN), their scores are masked
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            if (ok != 0xFu) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (!((ok >> i) & 1u))
+                        *reinterpret_cast<u32x4 *>(cur + kMqaDirectBytes + wave * kMqaBlockBytes +
+                                                   i * kMqaGroupBytes + lane * 16) = u32x4{0, 0, 0, 0};
+            }
+            __syncthreads();  // chunk n is staged; every wave is done with chunk n - 1
+            if (n + 1 < nch) ok = issue(t0 + kMqaChunk, nxt);
+            mqa_chunk<DT, NB, SPLIT, kMqaDirect>(cur, cur + kMqaDirectBytes, qop, j, q, t0, lim,
+                                                  t0 + kMqaChunk > wlim, sl2, st);
+        };
+        for (int n = 0; n < nch; n += 2) {
+            step(n, s_kv0, s_kv1);
+            if (n + 1 < nch) step(n + 1, s_kv1, s_kv0);
         }
     }
 

@@ -76,13 +76,14 @@ constexpr int kDecodeWaves = 4;
 constexpr int kDecodeSegPages = 256;
 
 // MFMA column blocks of 16 query rows per wave in the multi-query kernels
-// (four waves per workgroup).  Two blocks let every K/V operand a wave reads
-// from LDS feed twice the rows (the prefill: 11.2 -> 9.5 ms on the 32-prompt
-// workload); the shared-prefix kernel has few rows per KV head and keeps
-// one, for more workgroups.  The host plans the prefix row blocks with
-// kPrefixRowsPerBlock.
+// (four waves per workgroup).  More blocks let every K/V operand a wave reads
+// from LDS feed more rows (the prefill: one block 11.2 ms, two 9.5 ms on the
+// 32-prompt workload; three, once its chunks load straight into LDS and need
+// no staging registers, 6.27 against 6.75 ms for two); the shared-prefix
+// kernel has few rows per KV head and keeps one, for more workgroups.  The
+// host plans the prefix row blocks with kPrefixRowsPerBlock.
 #ifndef PKV_PREFILL_BLOCKS
-#define PKV_PREFILL_BLOCKS 2
+#define PKV_PREFILL_BLOCKS 3
 #endif
 #ifndef PKV_PREFIX_BLOCKS
 #define PKV_PREFIX_BLOCKS 1

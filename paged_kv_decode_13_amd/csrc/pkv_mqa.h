@@ -3,21 +3,25 @@
 // 4 x 16 x NB query rows (NB MFMA column blocks of 16 rows per wave) and
 // streams the K/V rows of one KV head through LDS 64 tokens at
 // a time, 16-bit caches, head_dim 128.  Every K or V operand a wave reads
-// from LDS feeds the MFMAs of all its column blocks.
+// from LDS feeds the MFMAs of all its column blocks.  A chunk is staged from
+// registers (the shared-prefix kernel) or placed by direct-to-LDS loads (the
+// prefill kernel); the two LDS layouts are described below, the arithmetic
+// is the same.
 //
 //  - K keeps its row layout in LDS (16-byte chunks XOR-swizzled by token);
 //    the score MFMA reads lane (i, q) = token i, head-dim chunk 4kk + q, and
 //    the query operand uses the same chunk order:
 //        S^T[16 tokens x 16 rows] = K[16 x 128] . Q^T[128 x 16].
-//  - V also keeps its row layout in LDS, rows padded to 288 bytes, and the
-//    value MFMA reads it transposed with the gfx950 LDS transpose load
+//  - V also keeps its row layout in LDS (rows padded to 288 bytes when
+//    staged from registers), and the value MFMA reads it transposed with the gfx950 LDS transpose load
 //    (ds_read_b64_tr_b16: within each 16-lane group, output lane 4a + b
 //    receives element b of the 8-byte pieces that lanes a, a + 4, a + 8,
 //    a + 12 point at), so a lane gathers the eight tokens whose
 //    probabilities it already holds from two such loads:
 //        O^T[16 d x 16 rows] += V^T[16 x 32 tokens] . P^T[32 x 16].
 //    The padding puts rows 32 bytes apart in the banks: both the 16-byte
-//    row stores and the transposed loads are free of bank conflicts.
+//    row stores and the transposed loads are free of bank conflicts (the
+//    direct layout gets the same from padding per load and a per-row XOR).
 //    With SPLIT the probabilities enter the 16-bit MFMA as a two-term split
 //    p = hi + lo, so the product keeps about 16 (bf16) or 21 (fp16) bits of p;
 //    without it p is rounded once to the 16-bit type (nearest even: relative
@@ -39,7 +43,7 @@
 namespace pkv {
 
 // Register budget of a kernel with NB column blocks per wave: three waves
-// per SIMD with one block, two with two.
+// per SIMD with one block, two with more.
 constexpr int mqa_waves_per_simd(int nb) { return nb == 1 ? 3 : 2; }
 constexpr int kMqaChunk = 64;                       // tokens per LDS chunk
 constexpr int kMqaRowBytes = 256;                   // one 16-bit K or V row (D = 128)
@@ -51,6 +55,50 @@ constexpr int kMqaVRow = kMqaRowBytes + 32;        // padded V row in LDS
 #endif
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+// LDS layouts of a staged 64-token chunk.
+//  kMqaRegStaged: written from registers (mqa_store_chunk): K row t at
+//    t * 256 with 16-byte chunk c at (c ^ t) & 15; V row t at t * 288
+//    (padded rows, natural chunk order).
+//  kMqaDirect: written by direct-to-LDS loads, each of which puts lane l's
+//    16 bytes at byte 16 l of one contiguous KiB: four 256-byte rows.  The
+//    thread with lane group g (lanes 16 g .. 16 g + 15) of wave w loads the
+//    four tokens 16 w + 4 g + i (i = 0..3, one page), token i by load i, so
+//    token t sits in block t >> 4, group t & 3 (one load), row g = (t >> 2) & 3
+//    of the group.  Groups are kMqaGroupBytes apart (64 bytes of padding
+//    after each KiB): rows of different groups start in different banks.
+//    Within a row, K chunk c sits at c ^ g and V's 32-byte piece d at d ^ g,
+//    which spreads the four rows of a group over the banks too.  A score
+//    read (16 tokens, one chunk each) then covers 16 distinct chunk
+//    positions of the banks, and a transposed V read 8 distinct 32-byte
+//    bank groups per 32 lanes.  Every lane reads the same K and V chunk of
+//    its four tokens, so one source offset per lane serves all four loads.
+enum { kMqaRegStaged = 0, kMqaDirect = 1 };
+constexpr int kMqaGroupBytes = 4 * kMqaRowBytes + 64;  // four rows of one load, then padding
+constexpr int kMqaBlockBytes = 4 * kMqaGroupBytes;     // 16 tokens
+constexpr int kMqaDirectBytes = 4 * kMqaBlockBytes;    // K (or V) rows of a chunk
+
+// Byte offset of 16-byte chunk c of K row t (0 <= t < 64) in the K rows.
+template <int L>
+__device__ __forceinline__ int mqa_k_off(int t, int c) {
+    if constexpr (L == kMqaRegStaged) {
+        return t * kMqaRowBytes + ((c ^ t) & 15) * 16;
+    } else {
+        const int g = (t >> 2) & 3;
+        return (t >> 4) * kMqaBlockBytes + (t & 3) * kMqaGroupBytes + g * kMqaRowBytes + ((c ^ g) & 15) * 16;
+    }
+}
+
+// Byte offset of byte `byte` (a multiple of 8) of V row t in the V rows.
+template <int L>
+__device__ __forceinline__ int mqa_v_off(int t, int byte) {
+    if constexpr (L == kMqaRegStaged) {
+        return t * kMqaVRow + byte;
+    } else {
+        const int g = (t >> 2) & 3;
+        return (t >> 4) * kMqaBlockBytes + (t & 3) * kMqaGroupBytes + g * kMqaRowBytes + (byte ^ (g << 5));
+    }
+}
 
 // Transposed 8-byte LDS load (see the header comment) of the piece at `p`.
 __device__ __forceinline__ u32x2 lds_read_tr16(const char *p) {
@@ -124,7 +172,7 @@ __device__ __forceinline__ void mqa_init(MqaRowState &st) {
 // tile * 16 + 4q + r of row j of block b.  The score scale is applied in the
 // softmax (mqa_softmax_values), folded into the exponent's fused
 // multiply-add.
-template <int DT, int NB>
+template <int DT, int NB, int L = kMqaRegStaged>
 __device__ __forceinline__ void mqa_scores(const char *kt, const u32x4 (&qop)[NB][4], int j, int q,
                                            float (&sc)[NB][4][4]) {
 #pragma unroll
@@ -134,8 +182,7 @@ __device__ __forceinline__ void mqa_scores(const char *kt, const u32x4 (&qop)[NB
         for (int b = 0; b < NB; ++b) sacc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-            const u32x4 kop = *reinterpret_cast<const u32x4 *>(
-                kt + (tt * 16 + j) * kMqaRowBytes + (((4 * kk + q) ^ j) & 15) * 16);
+            const u32x4 kop = *reinterpret_cast<const u32x4 *>(kt + mqa_k_off<L>(tt * 16 + j, 4 * kk + q));
 #pragma unroll
             for (int b = 0; b < NB; ++b) sacc[b] = mfma_16x16x32<DT>(kop, qop[b][kk], sacc[b]);
         }
@@ -153,7 +200,7 @@ __device__ __forceinline__ void mqa_scores(const char *kt, const u32x4 (&qop)[NB
 // the wave keeps the matrix pipe busy while it computes the second half's
 // probabilities; then the second half's MFMAs.  Runs at raised wave
 // priority (see mqa_softmax_values).
-template <int DT, int NB>
+template <int DT, int NB, int L>
 __device__ __forceinline__ void mqa_values_single(const char *vt, int j, int q, float sl2,
                                                   const float (&mref)[NB], float (&sc)[NB][4][4],
                                                   MqaRowState (&st)[NB]) {
@@ -173,11 +220,11 @@ __device__ __forceinline__ void mqa_values_single(const char *vt, int j, int q, 
                           pack_rne<DT>(sc[b][2 * bb][2], sc[b][2 * bb][3]),
                           pack_rne<DT>(sc[b][2 * bb + 1][0], sc[b][2 * bb + 1][1]),
                           pack_rne<DT>(sc[b][2 * bb + 1][2], sc[b][2 * bb + 1][3])};
-        const char *vrow = vt + (32 * bb + 4 * q + (j >> 2)) * kMqaVRow + 8 * (j & 3);
+        const int vt0 = 32 * bb + 4 * q + (j >> 2);
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
-            const u32x2 v0 = lds_read_tr16(vrow + 32 * dt);
-            const u32x2 v1 = lds_read_tr16(vrow + 16 * kMqaVRow + 32 * dt);
+            const u32x2 v0 = lds_read_tr16(vt + mqa_v_off<L>(vt0, 32 * dt + 8 * (j & 3)));
+            const u32x2 v1 = lds_read_tr16(vt + mqa_v_off<L>(vt0 + 16, 32 * dt + 8 * (j & 3)));
             const u32x4 vop = u32x4{v0[0], v0[1], v1[0], v1[1]};
 #pragma unroll
             for (int b = 0; b < NB; ++b) st[b].acc[dt] = mfma_16x16x32<DT>(vop, ph[b], st[b].acc[dt]);
@@ -220,7 +267,7 @@ __device__ __forceinline__ void mqa_values_single(const char *vt, int j, int q, 
 // scale sl2 (> 0, exp2 domain; see mqa_positive_scale), the value product.
 // Row j of block b sees tokens t < lim[b]; `masked` (wave-uniform) says some
 // token of the chunk lies past some row's limit.
-template <int DT, int NB, bool SPLIT>
+template <int DT, int NB, bool SPLIT, int L = kMqaRegStaged>
 __device__ __forceinline__ void mqa_softmax_values(const char *vt, int j, int q, int t0,
                                                    const int (&lim)[NB], bool masked, float sl2,
                                                    float (&sc)[NB][4][4], MqaRowState (&st)[NB]) {
@@ -276,7 +323,7 @@ __device__ __forceinline__ void mqa_softmax_values(const char *vt, int j, int q,
         }
     }
     if constexpr (!SPLIT) {
-        mqa_values_single<DT, NB>(vt, j, q, sl2, mref, sc, st);
+        mqa_values_single<DT, NB, L>(vt, j, q, sl2, mref, sc, st);
         return;
     }
     // The value MFMAs run at raised wave priority: the SIMD then issues them
@@ -309,11 +356,11 @@ __device__ __forceinline__ void mqa_softmax_values(const char *vt, int j, int q,
         // points at head dims 16 dt + 4 (j & 3) .. + 3 of token
         // 32 bb + 16 h + 4 q + (j >> 2); the load for h = 0 gives the
         // lane's tokens of tile 2 bb, h = 1 those of tile 2 bb + 1
-        const char *vrow = vt + (32 * bb + 4 * q + (j >> 2)) * kMqaVRow + 8 * (j & 3);
+        const int vt0 = 32 * bb + 4 * q + (j >> 2);
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
-            const u32x2 v0 = lds_read_tr16(vrow + 32 * dt);
-            const u32x2 v1 = lds_read_tr16(vrow + 16 * kMqaVRow + 32 * dt);
+            const u32x2 v0 = lds_read_tr16(vt + mqa_v_off<L>(vt0, 32 * dt + 8 * (j & 3)));
+            const u32x2 v1 = lds_read_tr16(vt + mqa_v_off<L>(vt0 + 16, 32 * dt + 8 * (j & 3)));
             const u32x4 vop = u32x4{v0[0], v0[1], v1[0], v1[1]};
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
@@ -332,13 +379,13 @@ __device__ __forceinline__ void mqa_softmax_values(const char *vt, int j, int q,
 // One 64-token chunk (tokens t0 .. t0 + 63 staged in kt / vt) for this
 // wave's NB column blocks of 16 rows: scores, then softmax and values; sl2
 // as for mqa_softmax_values.
-template <int DT, int NB, bool SPLIT = true>
+template <int DT, int NB, bool SPLIT = true, int L = kMqaRegStaged>
 __device__ __forceinline__ void mqa_chunk(const char *kt, const char *vt, const u32x4 (&qop)[NB][4],
                                           int j, int q, int t0, const int (&lim)[NB], bool masked,
                                           float sl2, MqaRowState (&st)[NB]) {
     float sc[NB][4][4];  // [block][16-token tile][r]: token tile*16 + 4q + r, row j
-    mqa_scores<DT, NB>(kt, qop, j, q, sc);
-    mqa_softmax_values<DT, NB, SPLIT>(vt, j, q, t0, lim, masked, sl2, sc, st);
+    mqa_scores<DT, NB, L>(kt, qop, j, q, sc);
+    mqa_softmax_values<DT, NB, SPLIT, L>(vt, j, q, t0, lim, masked, sl2, sc, st);
 }
 
 // The row's normaliser: the sum of the four lane groups' shares.
