@@ -209,7 +209,7 @@ __global__ __launch_bounds__(kThreads) void paged_decode_valu_kernel(DecodeArgs 
 // Log-sum-exp merge of the partitions of one (sequence, query head), one
 // workgroup of NW waves each (sequences with one partition were written
 // directly).
-template <int DT, int D, int NW>
+template <int DT, int D, int NW, bool EARLY>
 __global__ __launch_bounds__(NW * kWave) void lse_merge_kernel(DecodeArgs a) {
     const int s = blockIdx.x / a.num_heads;
     const int h = blockIdx.x % a.num_heads;
@@ -217,12 +217,13 @@ __global__ __launch_bounds__(NW * kWave) void lse_merge_kernel(DecodeArgs a) {
     const int ctx = a.context_lens[s];
     // one slot per work unit of the sequence (seq_units), one partition each
     // unless runs of unit_parts partitions were joined in the decode kernel
-    if constexpr (NW == 1) {
+    if constexpr (EARLY) {
         EarlyPartials<D> e;
-        load_early<D>(a, row * a.num_partitions, a.num_partitions, e);
+        const int k0 = (threadIdx.x / kWave) * kMergeEarly;
+        load_early<D>(a, row * a.num_partitions + k0, a.num_partitions - k0, e);
         if (bad_context(a, ctx) || ctx == 0) return;  // written by partition 0
         if (seq_parts(a, ctx) <= 1) return;            // written directly
-        merge_early<DT, D>(a, e, row * a.num_partitions, seq_units(a, ctx), row * D);
+        merge_early<DT, D, NW>(a, e, row * a.num_partitions, seq_units(a, ctx), row * D);
     } else {
         if (bad_context(a, ctx) || ctx == 0) return;
         if (seq_parts(a, ctx) <= 1) return;
@@ -249,14 +250,29 @@ static hipError_t launch_valu_group(const DecodeArgs &a, hipStream_t stream) {
     }
 }
 
+// Slots of a row whose context is the call's longest (the merge's
+// typical row size: every unit of a split sequence writes one slot).
+static int64_t slots_at_longest(const DecodeArgs &a) {
+    const int64_t span = a.max_context_len;
+    if (span <= 0) return 1;
+    const int64_t run = (int64_t)a.partition_size * a.unit_parts;
+    const int64_t runs = span / run, rest = span - runs * run;
+    return runs + (rest + a.partition_size - 1) / a.partition_size;
+}
+
 template <int DT, int D>
 static hipError_t launch_merge(const DecodeArgs &a, hipStream_t stream) {
     if (a.num_partitions <= 1) return hipSuccess;
-    const int64_t rows = (int64_t)a.num_seqs * a.num_heads;
-    if (a.num_partitions >= kMergeWideFrom)
-        hipLaunchKernelGGL((lse_merge_kernel<DT, D, kNumWaves>), dim3((unsigned)rows), dim3(kThreads), 0, stream, a);
-    else
-        hipLaunchKernelGGL((lse_merge_kernel<DT, D, 1>), dim3((unsigned)rows), dim3(kWave), 0, stream, a);
+    const unsigned rows = (unsigned)((int64_t)a.num_seqs * a.num_heads);
+    switch (merge_waves(slots_at_longest(a))) {
+        case 1: hipLaunchKernelGGL((lse_merge_kernel<DT, D, 1, true>), dim3(rows), dim3(kWave), 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((lse_merge_kernel<DT, D, 2, true>), dim3(rows), dim3(2 * kWave), 0, stream, a); break;
+        case kNumWaves:
+            hipLaunchKernelGGL((lse_merge_kernel<DT, D, kNumWaves, true>), dim3(rows), dim3(kThreads), 0, stream, a);
+            break;
+        default:
+            hipLaunchKernelGGL((lse_merge_kernel<DT, D, kNumWaves, false>), dim3(rows), dim3(kThreads), 0, stream, a);
+    }
     return hipGetLastError();
 }
 

@@ -30,7 +30,7 @@ namespace pkv {
 
 // Log-sum-exp merge of every partial slot of one (sequence, query head):
 // the prefix splits, then the suffix partitions.  Writes every output.
-template <int DT, int NW>
+template <int DT, int NW, bool EARLY>
 __global__ __launch_bounds__(NW * kWave) void prefix_merge_kernel(DecodeArgs a) {
     constexpr int D = 128;
     const int s = blockIdx.x / a.num_heads;
@@ -38,15 +38,18 @@ __global__ __launch_bounds__(NW * kWave) void prefix_merge_kernel(DecodeArgs a) 
     const int64_t row = (int64_t)s * a.num_heads + h;
     const int ctx = a.context_lens[s];
     EarlyPartials<D> e;
-    if constexpr (NW == 1) load_early<D>(a, row * a.part_stride, a.part_stride, e);
+    if constexpr (EARLY) {
+        const int k0 = (threadIdx.x / kWave) * kMergeEarly;
+        load_early<D>(a, row * a.part_stride + k0, a.part_stride - k0, e);
+    }
     if (bad_context(a, ctx) || ctx == 0) {
         const float v = ctx == 0 ? 0.f : __builtin_nanf("");
         for (int d = threadIdx.x; d < D; d += NW * kWave) store_out<DT>(a, row * D + d, v);
         return;
     }
     const int n = a.part_base + seq_units<true>(a, ctx);  // one slot per suffix unit
-    if constexpr (NW == 1)
-        merge_early<DT, D>(a, e, row * a.part_stride, n, row * D);
+    if constexpr (EARLY)
+        merge_early<DT, D, NW>(a, e, row * a.part_stride, n, row * D);
     else
         merge_partials<DT, D, NW>(a, row * a.part_stride, n, row * D);
 }
@@ -61,11 +64,16 @@ static hipError_t launch_all(const PrefixArgs &p, const DecodeArgs &a, hipStream
     hipError_t e = units > 0 ? launch_paged_prefix_fused(p, a, DT, stream)
                              : launch_paged_decode_mfma_suffix(a, DT, stream);
     if (e != hipSuccess || a.direct_out) return e;
-    const int64_t rows = (int64_t)a.num_seqs * a.num_heads;
-    if (a.part_stride >= kMergeWideFrom)
-        hipLaunchKernelGGL((prefix_merge_kernel<DT, kNumWaves>), dim3((unsigned)rows), dim3(kThreads), 0, stream, a);
-    else
-        hipLaunchKernelGGL((prefix_merge_kernel<DT, 1>), dim3((unsigned)rows), dim3(kWave), 0, stream, a);
+    const unsigned rows = (unsigned)((int64_t)a.num_seqs * a.num_heads);
+    switch (merge_waves(a.part_stride)) {  // the row's slot capacity
+        case 1: hipLaunchKernelGGL((prefix_merge_kernel<DT, 1, true>), dim3(rows), dim3(kWave), 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((prefix_merge_kernel<DT, 2, true>), dim3(rows), dim3(2 * kWave), 0, stream, a); break;
+        case kNumWaves:
+            hipLaunchKernelGGL((prefix_merge_kernel<DT, kNumWaves, true>), dim3(rows), dim3(kThreads), 0, stream, a);
+            break;
+        default:
+            hipLaunchKernelGGL((prefix_merge_kernel<DT, kNumWaves, false>), dim3(rows), dim3(kThreads), 0, stream, a);
+    }
     return hipGetLastError();
 }
 

@@ -287,17 +287,24 @@ __device__ __forceinline__ void merge_partials(const DecodeArgs &a, int64_t base
         }
     }
 }
-// Waves per merge workgroup: one while a row has few partials; four once
-// it has many, so that each wave's loads fit in a couple of round trips.
-constexpr int kMergeWideFrom = 32;
-
-// One-wave merge of a row with few partials.  The loads of its first
-// kMergeEarly slots are issued together with the row's length lookup, before
-// the number of partials n is known (slots below `cap`, the row's slot
-// count, always lie in the workspace; values past n are never used), so a
-// row with n <= kMergeEarly costs one memory round trip instead of three
-// (length, maxima, partials).
+// Merges of rows with up to kNumWaves * kMergeEarly partials: each of NW
+// waves issues the loads of its kMergeEarly slots (wave w: slots
+// w * kMergeEarly ..) together with the row's length lookup, before the
+// number of partials n is known (slots below `cap`, the row's slot count,
+// always lie in the workspace; values past n are never used), so such a row
+// costs one memory round trip instead of three (length, maxima, partials).
+// Rows with more slots use merge_partials.
 constexpr int kMergeEarly = 8;
+
+// Waves of an early-load merge for rows of up to `slots` partials (slots
+// past kMergeEarly per wave are loaded after the length lookup), or 0: the
+// loop merge (merge_partials, four waves) for longer rows.
+inline int merge_waves(int64_t slots) {
+    if (slots <= kMergeEarly) return 1;
+    if (slots <= 2 * kMergeEarly) return 2;
+    if (slots <= kNumWaves * kMergeEarly) return kNumWaves;
+    return 0;
+}
 
 template <int D>
 struct EarlyPartials {
@@ -321,37 +328,69 @@ __device__ __forceinline__ void load_early(const DecodeArgs &a, int64_t base, in
 }
 
 // out = sum_p w_p o_p / sum_p w_p, w_p = l_p 2^(m_p - max_q m_q), over the n
-// slots from base (the first ones from `e`); a NaN max makes the output NaN.
-template <int DT, int D>
+// slots from base.  Wave w holds slots w * kMergeEarly .. + kMergeEarly - 1
+// in `e` (see load_early) and loads slots NW * kMergeEarly + w, + NW, ...
+// itself; with NW > 1 the waves' maxima and sums meet in LDS.  A NaN max
+// makes the output NaN.
+template <int DT, int D, int NW>
 __device__ __forceinline__ void merge_early(const DecodeArgs &a, const EarlyPartials<D> &e, int64_t base,
                                             int n, int64_t out_idx) {
     constexpr int PL = D / kWave;
-    const int lane = threadIdx.x & (kWave - 1);
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int k0 = wave * kMergeEarly;  // this wave's first early slot
     float M = -INFINITY;
 #pragma unroll
     for (int k = 0; k < kMergeEarly; ++k)
-        if (k < n) M = fmaxf(M, e.m[k]);
-    for (int p = kMergeEarly; p < n; ++p) M = fmaxf(M, a.part_ml[(base + p) * 2]);
+        if (k0 + k < n) M = fmaxf(M, e.m[k]);
+    for (int p = NW * kMergeEarly + wave; p < n; p += NW) M = fmaxf(M, a.part_ml[(base + p) * 2]);
+    if constexpr (NW > 1) {
+        __shared__ float s_m[NW];
+        if (lane == 0) s_m[wave] = M;
+        __syncthreads();
+        M = s_m[0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) M = fmaxf(M, s_m[w]);
+    }
     float L = 0.f, O[PL];
 #pragma unroll
     for (int j = 0; j < PL; ++j) O[j] = 0.f;
 #pragma unroll
     for (int k = 0; k < kMergeEarly; ++k) {
-        if (k < n) {
+        if (k0 + k < n) {
             const float w = e.l[k] * fast_exp2(e.m[k] - M);
             L += w;
 #pragma unroll
             for (int j = 0; j < PL; ++j) O[j] = fmaf(w, e.o[k][j], O[j]);
         }
     }
-    for (int p = kMergeEarly; p < n; ++p) {
+    for (int p = NW * kMergeEarly + wave; p < n; p += NW) {
         const float w = a.part_ml[(base + p) * 2 + 1] * fast_exp2(a.part_ml[(base + p) * 2] - M);
         L += w;
 #pragma unroll
         for (int j = 0; j < PL; ++j) O[j] = fmaf(w, a.part_out[(base + p) * D + lane + j * kWave], O[j]);
     }
+    if constexpr (NW == 1) {
 #pragma unroll
-    for (int j = 0; j < PL; ++j) store_out<DT>(a, out_idx + lane + j * kWave, O[j] / L);
+        for (int j = 0; j < PL; ++j) store_out<DT>(a, out_idx + lane + j * kWave, O[j] / L);
+    } else {
+        __shared__ float s_lw[NW];
+        __shared__ float s_ow[NW][D];
+#pragma unroll
+        for (int j = 0; j < PL; ++j) s_ow[wave][lane + j * kWave] = O[j];
+        if (lane == 0) s_lw[wave] = L;
+        __syncthreads();
+        for (int d = tid; d < D; d += NW * kWave) {
+            float o = 0.f, l = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                o += s_ow[w][d];
+                l += s_lw[w];
+            }
+            store_out<DT>(a, out_idx + d, o / l);
+        }
+    }
 }
 
 // MFMA decode kernel launcher (16-bit caches, head_dim 128); the merge
