@@ -124,23 +124,36 @@ def load_traffic(workload: str):
 
 
 def cpu_model() -> str | None:
-    """The host CPU's model name as lscpu reports it (else /proc/cpuinfo)."""
+    """The host CPU's model name as lscpu reports it (else /proc/cpuinfo),
+    with its family, model and stepping numbers, which identify the part
+    where the name alone is generic."""
+    fields = {}
     if shutil.which("lscpu"):
         try:
             out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=20).stdout
             for ln in out.splitlines():
-                if ln.strip().startswith("Model name:"):
-                    return ln.split(":", 1)[1].strip()
+                if ":" in ln:
+                    k, v = ln.split(":", 1)
+                    fields.setdefault(k.strip(), v.strip())
         except (OSError, subprocess.SubprocessError):
             pass
-    try:
-        with open("/proc/cpuinfo") as f:
-            for ln in f:
-                if ln.startswith("model name"):
-                    return ln.split(":", 1)[1].strip()
-    except OSError:
-        pass
-    return None
+    if "Model name" not in fields:
+        try:
+            with open("/proc/cpuinfo") as f:
+                for ln in f:
+                    if ":" in ln:
+                        k, v = ln.split(":", 1)
+                        key = {"model name": "Model name", "cpu family": "CPU family",
+                               "model": "Model", "stepping": "Stepping"}.get(k.strip())
+                        if key:
+                            fields.setdefault(key, v.strip())
+        except OSError:
+            pass
+    name = fields.get("Model name")
+    if name is None:
+        return None
+    ids = [f"{k.lower()} {fields[k]}" for k in ("CPU family", "Model", "Stepping") if k in fields]
+    return f"{name} ({', '.join(ids)})" if ids else name
 
 
 def upload(batch, dev):
@@ -745,7 +758,7 @@ def run_write(batch, t, steps: int, warmup: int) -> dict:
                    "block_size": batch.block_size, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "kv_write_kernel", "achieved": round(gbs, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None},
+                     "traffic": load_traffic("write_" + batch.name)},
         "cpu_baseline": None,
     }
 
@@ -824,7 +837,7 @@ def run_prefill(batch, t, steps: int, warmup: int, keep_out: bool = False) -> di
         "algorithmic_flops": flops,
         "roofline": {"bound": "mfma", "kernel": "paged_prefill_mfma_kernel",
                      "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
+                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": load_traffic(batch.name)},
         "cpu_baseline": None,
     }
     if keep_out:
