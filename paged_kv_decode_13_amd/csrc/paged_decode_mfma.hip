@@ -136,7 +136,10 @@ template <bool PFX>
 __device__ __forceinline__ int tail_bucket(const DecodeArgs &a, int ctx) {
     const int t = seq_tail_tokens<PFX>(a, ctx);
     if (t < 0) return -1;
-    return (int)((int64_t)(a.partition_size - 1 - t) * kTailBuckets / a.partition_size);
+    // floor((ps - 1 - t) * kTailBuckets / ps) in binary32 (an ordering key
+    // only; every workgroup computes the same one), clamped to the classes
+    const float f = (float)(a.partition_size - 1 - t) * (float)kTailBuckets / (float)a.partition_size;
+    return min(kTailBuckets - 1, (int)f);
 }
 
 template <bool PFX>
@@ -144,49 +147,69 @@ __device__ __forceinline__ void build_unit_order(const DecodeArgs &a, int *s_pf,
                                                  uint16_t *s_tail, int *s_ntail, int *s_tmp) {
     const int B = a.num_seqs;
     const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
     const bool sort = sorted_tails(a);
-    int *s_scan = s_tmp;                      // [kNumWaves]
-    int *s_hist = s_tmp + 8;                  // [kTailBuckets]
-    int *s_run = s_tmp + 8 + kTailBuckets;    // [kTailBuckets]: placed so far
+    int *s_scan = s_tmp;                      // [2][kNumWaves]: wave totals of runs, singles
+    int *s_run = s_tmp + 8;                   // [kTailBuckets]: first free slot of each class
+    int *s_whist = s_tmp + 8 + kTailBuckets;  // [kNumWaves][kTailBuckets]: class sizes per wave
     int *s_cnt = s_tmp + 64;                  // [2][kNumWaves][kTailBuckets]
-    if (sort) {
-        if (tid < kTailBuckets) s_hist[tid] = 0;
-        __syncthreads();
-    }
+    // Each thread takes `chunk` consecutive sequences: their lengths, their
+    // unit counts (kept in s_pf / s_pp until they become prefix sums) and,
+    // by wave ballots, the sizes of their tail classes (lane k of a wave
+    // counts class k).
     const int chunk = (B + kThreads - 1) / kThreads;
     const int lo = min(B, tid * chunk), hi = min(B, lo + chunk);
-    int nf = 0, np = 0;
-    for (int s = lo; s < hi; ++s) {
-        const int ctx = a.context_lens[s];
-        s_ctx[s] = ctx;
-        nf += seq_full_units<PFX>(a, ctx);
-        np += seq_singles<PFX>(a, ctx);
+    int nf = 0, np = 0, hist = 0;
+    for (int i = 0; i < chunk; ++i) {
+        const int s = lo + i;
+        int key = -1;
+        if (s < hi) {
+            const int ctx = a.context_lens[s];
+            s_ctx[s] = ctx;
+            const int f = seq_full_units<PFX>(a, ctx), p = seq_singles<PFX>(a, ctx);
+            s_pf[s] = f;
+            s_pp[s] = p;
+            nf += f;
+            np += p;
+            if (sort) key = tail_bucket<PFX>(a, ctx);
+        }
         if (sort) {
-            const int k = tail_bucket<PFX>(a, ctx);
-            if (k >= 0) atomicAdd(&s_hist[k], 1);
+#pragma unroll
+            for (int k = 0; k < kTailBuckets; ++k) {
+                const uint64_t m = __ballot(key == k);
+                if (lane == k) hist += __popcll(m);
+            }
         }
     }
-    const int incf = block_scan(nf, s_scan);
-    const int incp = block_scan(np, s_scan);
-    int rf = incf - nf, rp = incp - np;
+    const int xf = wave_scan(nf), xp = wave_scan(np);
+    if (lane == kWave - 1) {
+        s_scan[wave] = xf;
+        s_scan[kNumWaves + wave] = xp;
+    }
+    if (sort && lane < kTailBuckets) s_whist[wave * kTailBuckets + lane] = hist;
+    __syncthreads();
+    int rf = xf - nf, rp = xp - np;  // exclusive prefix within the wave
+    for (int w = 0; w < wave; ++w) {
+        rf += s_scan[w];
+        rp += s_scan[kNumWaves + w];
+    }
     for (int s = lo; s < hi; ++s) {
+        const int f = s_pf[s], p = s_pp[s];
         s_pf[s] = rf;
         s_pp[s] = rp;
-        rf += seq_full_units<PFX>(a, s_ctx[s]);
-        rp += seq_singles<PFX>(a, s_ctx[s]);
+        rf += f;
+        rp += p;
     }
     if (tid == kThreads - 1) {
-        s_pf[B] = incf;
-        s_pp[B] = incp;
+        s_pf[B] = rf;
+        s_pp[B] = rp;
     }
     if (tid < kWave) {  // exclusive scan of the class sizes in wave 0
-        const int n = sort && tid < kTailBuckets ? s_hist[tid] : 0;
-        int x = n;
-#pragma unroll
-        for (int off = 1; off < kTailBuckets; off <<= 1) {
-            const int y = __shfl_up(x, off);
-            if (tid >= off) x += y;
-        }
+        int n = 0;
+        if (sort && tid < kTailBuckets)
+            for (int w = 0; w < kNumWaves; ++w) n += s_whist[w * kTailBuckets + tid];
+        const int x = wave_scan(n);
         if (tid < kTailBuckets) s_run[tid] = x - n;  // first slot of class tid
         if (tid == kTailBuckets - 1) *s_ntail = x;
     }
@@ -194,8 +217,6 @@ __device__ __forceinline__ void build_unit_order(const DecodeArgs &a, int *s_pf,
     if (*s_ntail == 0) return;
     // 256 sequences per round: a sequence's slot is its class's start, plus
     // the class members of earlier rounds, earlier waves and lower lanes
-    const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
     for (int r0 = 0, par = 0; r0 < B; r0 += kThreads, par ^= 1) {
         const int s = r0 + tid;
         const int key = s < B ? tail_bucket<PFX>(a, s_ctx[s]) : -1;

@@ -131,19 +131,29 @@ __device__ __forceinline__ Unit make_unit(const DecodeArgs &a) {
     return r;
 }
 
-// Inclusive prefix sum over the workgroup's NT threads: a shuffle scan in
-// each wave, then each wave adds the totals of the waves before it
-// (s_scan: NT / 64 ints).  Ends with a barrier, so s_scan can be reused.
+// Inclusive prefix sum across the 64 lanes of a wave by DPP lane moves (no
+// LDS round trips): shifts by 1, 2, 4 and 8 lanes within each row of 16,
+// then the last lane of rows 0 and 2 added to rows 1 and 3, then lane 31 to
+// rows 2 and 3.  Lanes a shift reads from outside the row add 0; rows
+// outside a row mask keep their value.
+__device__ __forceinline__ int wave_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return x;
+}
+
+// Inclusive prefix sum over the workgroup's NT threads: a scan in each wave,
+// then each wave adds the totals of the waves before it (s_scan: NT / 64
+// ints).  Ends with a barrier, so s_scan can be reused.
 template <int NT = kThreads>
 __device__ __forceinline__ int block_scan(int v, int *s_scan) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    int x = v;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const int y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
+    const int x = wave_scan(v);
     if (lane == kWave - 1) s_scan[wave] = x;
     __syncthreads();
     int base = 0;
