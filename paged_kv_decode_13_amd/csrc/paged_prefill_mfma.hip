@@ -243,15 +243,18 @@ void paged_prefill_mfma_kernel(PrefillArgs a) {
         const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
+            // four consecutive head dims: one 16- or 8-byte store (rows are
+            // 256-byte aligned); 16-bit outputs rounded to nearest even by
+            // the pair conversion
             const int64_t o = qrow[b] + 16 * dt + 4 * q;
+            f32x4_t v;
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const float v = nan ? __builtin_nanf("") : st[b].acc[dt][rr] * inv;
-                if (a.out_f32)
-                    reinterpret_cast<float *>(a.out)[o + rr] = v;
-                else
-                    reinterpret_cast<uint16_t *>(a.out)[o + rr] = f32_to_bits16<DT>(v);
-            }
+            for (int rr = 0; rr < 4; ++rr) v[rr] = nan ? __builtin_nanf("") : st[b].acc[dt][rr] * inv;
+            if (a.out_f32)
+                *reinterpret_cast<f32x4_t *>(reinterpret_cast<float *>(a.out) + o) = v;
+            else
+                *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(a.out) + o) =
+                    u32x2{pack_rne<DT>(v[0], v[1]), pack_rne<DT>(v[2], v[3])};
         }
     }
 }
