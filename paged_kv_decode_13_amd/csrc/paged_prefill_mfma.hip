@@ -235,26 +235,60 @@ void paged_prefill_mfma_kernel(PrefillArgs a) {
         }
     }
 
+    if (a.out_f32) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const float L = mqa_row_sum<SPLIT>(st[b]);
+            if (!row_ok[b]) continue;
+            const bool nan = bad || s_badtok < lim[b];
+            const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                // four consecutive head dims in one 16-byte store
+                f32x4_t v;
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) v[rr] = nan ? __builtin_nanf("") : st[b].acc[dt][rr] * inv;
+                *reinterpret_cast<f32x4_t *>(reinterpret_cast<float *>(a.out) + qrow[b] + 16 * dt + 4 * q) = v;
+            }
+        }
+        return;
+    }
+    // 16-bit outputs: each wave's 16 NB rows go through LDS (the chunk
+    // buffers, free once every wave has left the chunk loop), rounded to
+    // nearest even by the pair conversion, so that the stores cover whole
+    // 256-byte rows.  Rows sit kOutRow bytes apart in LDS (padding spreads
+    // the eight-byte writes of one dim group over the banks).
+    constexpr int kOutRow = 2 * D + 16;
+    static_assert(2 * 16 * NB * kOutRow <= kMqaDirectBytes * 2, "two waves' rows fit one chunk buffer");
+    __syncthreads();
+    char *ob = (wave < 2 ? s_kv0 : s_kv1) + (wave & 1) * (16 * NB * kOutRow);
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
         const float L = mqa_row_sum<SPLIT>(st[b]);
-        if (!row_ok[b]) continue;
         const bool nan = bad || s_badtok < lim[b];
         const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
-            // four consecutive head dims: one 16- or 8-byte store (rows are
-            // 256-byte aligned); 16-bit outputs rounded to nearest even by
-            // the pair conversion
-            const int64_t o = qrow[b] + 16 * dt + 4 * q;
             f32x4_t v;
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) v[rr] = nan ? __builtin_nanf("") : st[b].acc[dt][rr] * inv;
-            if (a.out_f32)
-                *reinterpret_cast<f32x4_t *>(reinterpret_cast<float *>(a.out) + o) = v;
-            else
-                *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(a.out) + o) =
-                    u32x2{pack_rne<DT>(v[0], v[1]), pack_rne<DT>(v[2], v[3])};
+            *reinterpret_cast<u32x2 *>(ob + (b * 16 + j) * kOutRow + (16 * dt + 4 * q) * 2) =
+                u32x2{pack_rne<DT>(v[0], v[1]), pack_rne<DT>(v[2], v[3])};
+        }
+    }
+    // each wave reads back only its own rows (LDS accesses of a wave are
+    // in order): lane (row group rg, chunk c) takes 16 bytes of row 4 it + rg
+    const int rg = lane >> 4, c = lane & 15;
+#pragma unroll
+    for (int it = 0; it < 4 * NB; ++it) {
+        const int rw = 4 * it + rg;  // row of this wave: block rw / 16, row rw % 16 of it
+        const int r = tile * kPflRows + wave * 16 * NB + rw;
+        if (r < nrows) {
+            const int i = r >> a.log2_group;
+            const int h = kvh * G + (r & (G - 1));
+            const int64_t orow = ((int64_t)(q0 + i) * a.num_heads + h) * D;
+            *reinterpret_cast<u32x4 *>(reinterpret_cast<uint16_t *>(a.out) + orow + 8 * c) =
+                *reinterpret_cast<const u32x4 *>(ob + rw * kOutRow + 16 * c);
         }
     }
 }
