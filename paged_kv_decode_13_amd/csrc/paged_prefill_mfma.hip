@@ -62,7 +62,7 @@ __device__ __forceinline__ int prefill_tiles(const PrefillArgs &a, int s, int &q
 // 6.26-6.28 ms.  Earlier steps: one block per wave at three workgroups per
 // CU 10.9 ms, two blocks 9.5 ms; a software pipeline (the next chunk's score
 // MFMAs before this chunk's softmax) reached 256 VGPRs and was slower.
-template <int DT, bool SPLIT>
+template <int DT, bool SPLIT, bool NARROW>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(mqa_waves_per_simd(kPrefillBlocks), 8)))
 void paged_prefill_mfma_kernel(PrefillArgs a) {
@@ -191,18 +191,34 @@ void paged_prefill_mfma_kernel(PrefillArgs a) {
             const int t = t0 + 4 * lg;
             const int pb = s_pages[min((t - seg) >> lbs, npages - 1)];
             const bool page_ok = (t < seg_end) & (pb >= 0);
-            const int64_t base = ((int64_t)(page_ok ? pb : 0) * bs + (t & (bs - 1))) * tok_stride +
-                                 (int64_t)kvh * ROW;
-            const char *ks = kbase + base + koff;
-            const char *vs = vbase + base + voff;
+            const int page = page_ok ? pb : 0;
+            if constexpr (NARROW) {
+                // pools under 4 GiB: 32-bit offsets from the pools' bases
+                const uint32_t base = ((uint32_t)page * (uint32_t)bs + (uint32_t)(t & (bs - 1))) *
+                                          (uint32_t)tok_stride + (uint32_t)(kvh * ROW);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                char *kd = buf + wave * kMqaBlockBytes + i * kMqaGroupBytes;
-                __builtin_amdgcn_global_load_lds(ks + i * tok_stride, (__attribute__((address_space(3))) void *)kd,
-                                                 16, 0, 0);
-                __builtin_amdgcn_global_load_lds(vs + i * tok_stride,
-                                                 (__attribute__((address_space(3))) void *)(kd + kMqaDirectBytes),
-                                                 16, 0, 0);
+                for (int i = 0; i < 4; ++i) {
+                    char *kd = buf + wave * kMqaBlockBytes + i * kMqaGroupBytes;
+                    const uint32_t o = base + (uint32_t)i * (uint32_t)tok_stride;
+                    __builtin_amdgcn_global_load_lds(kbase + (o + (uint32_t)koff),
+                                                     (__attribute__((address_space(3))) void *)kd, 16, 0, 0);
+                    __builtin_amdgcn_global_load_lds(vbase + (o + (uint32_t)voff),
+                                                     (__attribute__((address_space(3))) void *)(kd + kMqaDirectBytes),
+                                                     16, 0, 0);
+                }
+            } else {
+                const int64_t base = ((int64_t)page * bs + (t & (bs - 1))) * tok_stride + (int64_t)kvh * ROW;
+                const char *ks = kbase + base + koff;
+                const char *vs = vbase + base + voff;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    char *kd = buf + wave * kMqaBlockBytes + i * kMqaGroupBytes;
+                    __builtin_amdgcn_global_load_lds(ks + i * tok_stride, (__attribute__((address_space(3))) void *)kd,
+                                                     16, 0, 0);
+                    __builtin_amdgcn_global_load_lds(vs + i * tok_stride,
+                                                     (__attribute__((address_space(3))) void *)(kd + kMqaDirectBytes),
+                                                     16, 0, 0);
+                }
             }
             const int n_ok = page_ok ? min(4, seg_end - t) : 0;
             return (1u << n_ok) - 1u;
@@ -300,12 +316,17 @@ static hipError_t launch_dt(const PrefillArgs &a, hipStream_t stream) {
     const int64_t units = ((rows + kPflRows - 1) / kPflRows + a.num_seqs) * a.num_kv_heads;
     if (units == 0) return hipSuccess;
     const size_t dyn = (size_t)(a.num_seqs + 1) * sizeof(int);
-    if (a.out_f32)
-        hipLaunchKernelGGL((paged_prefill_mfma_kernel<DT, true>), dim3((unsigned)units), dim3(kThreads), dyn,
-                           stream, a);
-    else
-        hipLaunchKernelGGL((paged_prefill_mfma_kernel<DT, false>), dim3((unsigned)units), dim3(kThreads), dyn,
-                           stream, a);
+    // every K or V byte of a pool under 4 GiB is a 32-bit offset from its base
+    const bool narrow = (uint64_t)a.num_blocks * (uint64_t)a.block_size * (uint64_t)a.num_kv_heads *
+                            (uint64_t)kMqaRowBytes <= 0xFFFFFFFFull;
+    const dim3 grid((unsigned)units), block(kThreads);
+    if (a.out_f32) {
+        if (narrow) hipLaunchKernelGGL((paged_prefill_mfma_kernel<DT, true, true>), grid, block, dyn, stream, a);
+        else hipLaunchKernelGGL((paged_prefill_mfma_kernel<DT, true, false>), grid, block, dyn, stream, a);
+    } else {
+        if (narrow) hipLaunchKernelGGL((paged_prefill_mfma_kernel<DT, false, true>), grid, block, dyn, stream, a);
+        else hipLaunchKernelGGL((paged_prefill_mfma_kernel<DT, false, false>), grid, block, dyn, stream, a);
+    }
     return hipGetLastError();
 }
 

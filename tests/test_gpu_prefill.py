@@ -164,3 +164,43 @@ def test_prefill_full_workload_decimated(cuda):
     err = max_err(got, ref)
     print(f"[prefill_bf16] max|err| {err:.3e}", flush=True)
     assert err <= TOL["bf16"]
+
+
+def test_pool_past_4gib(cuda):
+    """A pool larger than 4 GiB with the batch's pages at its top (every K/V
+    byte read lies past the 4 GiB mark): the prefill's 64-bit addressing
+    (pools under 4 GiB use 32-bit offsets from the pool's base) and the
+    decode's, against the oracle on the same rows in the batch's own compact
+    pool."""
+    import torch
+
+    from tests.gpu_helpers import gpu_step, oracle_step
+
+    b = wl.make_prefill_attention([300, 1000, 64, 0, 777], [300, 17, 64, 0, 5], num_heads=8,
+                                  num_kv_heads=2, head_dim=128, block_size=16, dtype="bf16",
+                                  seed=4242)
+    nb = b.key_cache.shape[0]
+    page_bytes = b.block_size * b.num_kv_heads * b.head_dim * 2
+    big = (9 << 29) // page_bytes + nb  # 4.5 GiB of pages below the batch's
+    base = big - nb
+    assert base * page_bytes > (4 << 30)
+    print(f"\n[pool-past-4gib] {big} pages of {page_bytes} B", flush=True)
+    t = upload(b, cuda)
+    kc = torch.zeros((big,) + tuple(t["kc"].shape[1:]), dtype=t["kc"].dtype, device=cuda)
+    vc = torch.zeros_like(kc)
+    kc[base:] = t["kc"]
+    vc[base:] = t["vc"]
+    table = b.block_tables.astype(np.int64)
+    table = np.where((table >= 0) & (table < nb), table + base, table).astype(np.int32)
+    t.update(kc=kc, vc=vc, bt=torch.from_numpy(table).to(cuda))
+    ref = _oracle_prefill(b)
+    out = to_f64(_gpu_prefill(b, t, out_dtype="f32"))
+    assert max_err(out, ref) <= TIGHT["bf16"], max_err(out, ref)
+    out = to_f64(_gpu_prefill(b, t))
+    assert single_rounding_ok(out, ref, "bf16", _weighted_abs_v(b)), max_err(out, ref)
+    dref = oracle_step(b, write=False)
+    for ps in (0, 64):
+        dout = to_f64(gpu_step(b, t, partition_size=ps, out_dtype="f32", write=False))
+        assert max_err(dout, dref) <= TIGHT["bf16"], (ps, max_err(dout, dref))
+    del kc, vc
+    torch.cuda.empty_cache()
