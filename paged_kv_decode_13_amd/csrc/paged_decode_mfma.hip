@@ -161,6 +161,9 @@ __device__ __forceinline__ void build_unit_order(const DecodeArgs &a, int *s_pf,
     const int chunk = (B + kThreads - 1) / kThreads;
     const int lo = min(B, tid * chunk), hi = min(B, lo + chunk);
     int nf = 0, np = 0, hist = 0;
+    // one sequence per thread (B <= kThreads): its class and its rank among
+    // the members of that class in its wave, from the same ballots
+    int key1 = -1, rank1 = 0;
     for (int i = 0; i < chunk; ++i) {
         const int s = lo + i;
         int key = -1;
@@ -179,8 +182,10 @@ __device__ __forceinline__ void build_unit_order(const DecodeArgs &a, int *s_pf,
             for (int k = 0; k < kTailBuckets; ++k) {
                 const uint64_t m = __ballot(key == k);
                 if (lane == k) hist += __popcll(m);
+                if (key == k) rank1 = __popcll(m & ((1ull << lane) - 1ull));
             }
         }
+        key1 = key;
     }
     const int xf = wave_scan(nf), xp = wave_scan(np);
     if (lane == kWave - 1) {
@@ -215,6 +220,17 @@ __device__ __forceinline__ void build_unit_order(const DecodeArgs &a, int *s_pf,
     }
     __syncthreads();
     if (*s_ntail == 0) return;
+    if (chunk == 1) {
+        // a sequence's slot is its class's start, plus the class members of
+        // earlier waves and lower lanes (s_whist is intact: no round ran)
+        if (key1 >= 0) {
+            int pos = s_run[key1] + rank1;
+            for (int w = 0; w < wave; ++w) pos += s_whist[w * kTailBuckets + key1];
+            s_tail[pos] = (uint16_t)lo;
+        }
+        __syncthreads();
+        return;
+    }
     // 256 sequences per round: a sequence's slot is its class's start, plus
     // the class members of earlier rounds, earlier waves and lower lanes
     for (int r0 = 0, par = 0; r0 < B; r0 += kThreads, par ^= 1) {
