@@ -272,13 +272,13 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs &a, const int *s_pf
     const int sp = unit / a.num_kv_heads;
     int span;
     if (sp < total_full) {  // a whole run of unit_parts partitions
-        u.s = search_le(s_pf, a.num_seqs, sp);
+        u.s = wave_search_le(s_pf, a.num_seqs, sp);
         u.p = sp - s_pf[u.s];
         u.part0 = u.p * a.unit_parts;
         span = run_tokens(a);
     } else if (sp < total_full + total_single) {  // a partition after the runs
         const int r = sp - total_full;
-        u.s = search_le(s_pp, a.num_seqs, r);
+        u.s = wave_search_le(s_pp, a.num_seqs, r);
         const int runs = seq_full_units<PFX>(a, s_ctx[u.s]);
         u.p = runs + r - s_pp[u.s];
         u.part0 = runs * a.unit_parts + r - s_pp[u.s];

@@ -172,6 +172,25 @@ __device__ __forceinline__ int search_le(const int *pre, int n, int x) {
     return lo;
 }
 
+// The same by a whole wave (every lane active; pre in LDS, x wave-uniform):
+// a 64-way search, each round one LDS read per lane and a ballot.  Lane l
+// probes entry lo + l * stride; the probes <= x form a prefix of the lanes,
+// whose length narrows the range 64-fold.  Up to 4096 entries take two
+// rounds where a binary search takes up to 12 dependent reads.
+__device__ __forceinline__ int wave_search_le(const int *pre, int n, int x) {
+    const int lane = threadIdx.x & (kWave - 1);
+    int lo = 0, len = n;  // the answer lies in [lo, lo + len)
+    while (len > 1) {
+        const int stride = (len + kWave - 1) / kWave;
+        const int i = lo + lane * stride;
+        const bool le = lane * stride < len && pre[i] <= x;
+        const int c = __popcll(__ballot(le));  // >= 1: pre[lo] <= x
+        lo += (c - 1) * stride;
+        len = min(stride, len - (c - 1) * stride);
+    }
+    return lo;
+}
+
 // Stage the physical block ids of logical blocks [lb0, lb0 + npages) of the
 // sequence in LDS (-1 and a flag for ids outside the pool).  Caller brackets
 // with __syncthreads().
