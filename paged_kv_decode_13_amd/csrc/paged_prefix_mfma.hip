@@ -54,6 +54,28 @@ __global__ __launch_bounds__(NW * kWave) void prefix_merge_kernel(DecodeArgs a) 
         merge_partials<DT, D, NW>(a, row * a.part_stride, n, row * D);
 }
 
+// The same for rows of at most kMergeEarly slots, one wave per row and
+// RW rows (consecutive heads of a sequence) per workgroup: the 128-sequence
+// batch has 4096 rows, and one workgroup per row spent the merge launching
+// them.
+template <int DT, int RW>
+__global__ __launch_bounds__(RW * kWave) void prefix_merge_rows_kernel(DecodeArgs a) {
+    constexpr int D = 128;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t row = (int64_t)blockIdx.x * RW + threadIdx.x / kWave;
+    if (row >= (int64_t)a.num_seqs * a.num_heads) return;  // a whole wave
+    const int s = (int)(row / a.num_heads);
+    const int ctx = a.context_lens[s];
+    EarlyPartials<D> e;
+    load_early<D>(a, row * a.part_stride, a.part_stride, e);
+    if (bad_context(a, ctx) || ctx == 0) {
+        const float v = ctx == 0 ? 0.f : __builtin_nanf("");
+        for (int d = lane; d < D; d += kWave) store_out<DT>(a, row * D + d, v);
+        return;
+    }
+    merge_early<DT, D, 1>(a, e, row * a.part_stride, a.part_base + seq_units<true>(a, ctx), row * D);
+}
+
 // With a shared prefix, its units and the suffix decode share one launch
 // (they overlap: the prefix work is latency-bound, the suffix streams) and
 // the merge joins every partial; without one, the suffix decode alone,
@@ -65,8 +87,12 @@ static hipError_t launch_all(const PrefixArgs &p, const DecodeArgs &a, hipStream
                              : launch_paged_decode_mfma_suffix(a, DT, stream);
     if (e != hipSuccess || a.direct_out) return e;
     const unsigned rows = (unsigned)((int64_t)a.num_seqs * a.num_heads);
+    constexpr int kRows = 4;
     switch (merge_waves(a.part_stride)) {  // the row's slot capacity
-        case 1: hipLaunchKernelGGL((prefix_merge_kernel<DT, 1, true>), dim3(rows), dim3(kWave), 0, stream, a); break;
+        case 1:
+            hipLaunchKernelGGL((prefix_merge_rows_kernel<DT, kRows>), dim3((rows + kRows - 1) / kRows),
+                               dim3(kRows * kWave), 0, stream, a);
+            break;
         case 2: hipLaunchKernelGGL((prefix_merge_kernel<DT, 2, true>), dim3(rows), dim3(2 * kWave), 0, stream, a); break;
         case kNumWaves:
             hipLaunchKernelGGL((prefix_merge_kernel<DT, kNumWaves, true>), dim3(rows), dim3(kThreads), 0, stream, a);

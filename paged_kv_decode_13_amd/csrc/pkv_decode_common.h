@@ -367,8 +367,8 @@ __device__ __forceinline__ void merge_early(const DecodeArgs &a, const EarlyPart
     constexpr int PL = D / kWave;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
-    const int k0 = wave * kMergeEarly;  // this wave's first early slot
+    const int wave = NW == 1 ? 0 : tid / kWave;  // a one-wave merge may share its workgroup
+    const int k0 = wave * kMergeEarly;           // this wave's first early slot
     float M = -INFINITY;
 #pragma unroll
     for (int k = 0; k < kMergeEarly; ++k)
