@@ -244,8 +244,9 @@ def test_unit_order_edges(cuda):
     longest first, by a counting sort every workgroup repeats): lengths that
     are exact multiples of the partition (no partial unit), all-partial
     batches, empty contexts, a 300-sequence batch (two sorting rounds, the
-    second partial) whose tails fall in every length class, and the largest
-    batch one call accepts."""
+    second partial) whose tails fall in every length class, the largest
+    batch one call accepts, and a merge over a row count that is not a
+    multiple of four."""
     import torch
 
     cases = [([512, 1024, 2048], 512), ([3, 5, 200, 0, 511], 512), ([0, 0, 700, 1536], 256),
@@ -257,6 +258,13 @@ def test_unit_order_edges(cuda):
         ref = oracle_step(b)
         out = to_f64(gpu_step(b, upload(b, cuda), partition_size=ps, out_dtype="f32"))
         assert max_err(out, ref) <= TIGHT["bf16"], (len(lens), ps)
+    # 1367 sequences x 3 heads = 4101 rows: the merge takes four rows per
+    # workgroup from 4096 rows on, and the last workgroup holds one
+    b = wl.make_batch([1 + (i * 29) % 90 for i in range(1367)], num_heads=3, num_kv_heads=3,
+                      head_dim=128, block_size=16, dtype="bf16", seed=1367)
+    ref = oracle_step(b)
+    out = to_f64(gpu_step(b, upload(b, cuda), partition_size=16, out_dtype="f32"))
+    assert max_err(out, ref) <= TIGHT["bf16"]
     import paged_kv_decode_13_amd as pkv
 
     with pytest.raises(pkv.PagedKVError):
