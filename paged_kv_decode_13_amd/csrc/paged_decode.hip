@@ -233,7 +233,8 @@ __global__ __launch_bounds__(NW * kWave) void lse_merge_kernel(DecodeArgs a) {
 
 // The same for rows of at most kMergeEarly slots, one wave per row and RW
 // rows (consecutive heads of a sequence) per workgroup, for calls with many
-// rows (the 256-sequence, 32-head batches: 8192 rows, 5.9 -> 5.2 us).
+// rows (the 256-sequence, 32-head batches: 8192 rows; the E4M3 call 279.8
+// -> 279.0 us, the 16-bit one unchanged).
 template <int DT, int D, int RW>
 __global__ __launch_bounds__(RW * kWave) void lse_merge_rows_kernel(DecodeArgs a) {
     const int64_t row = (int64_t)blockIdx.x * RW + threadIdx.x / kWave;

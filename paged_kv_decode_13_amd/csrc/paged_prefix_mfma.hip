@@ -55,9 +55,8 @@ __global__ __launch_bounds__(NW * kWave) void prefix_merge_kernel(DecodeArgs a) 
 }
 
 // The same for rows of at most kMergeEarly slots, one wave per row and
-// RW rows (consecutive heads of a sequence) per workgroup: the 128-sequence
-// batch has 4096 rows, and one workgroup per row spent the merge launching
-// them.
+// RW rows (consecutive heads of a sequence) per workgroup (the 128-sequence
+// batch: 4096 rows of three slots; call 58.3 -> 57.9 us at block 16).
 template <int DT, int RW>
 __global__ __launch_bounds__(RW * kWave) void prefix_merge_rows_kernel(DecodeArgs a) {
     constexpr int D = 128;
