@@ -53,6 +53,9 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 matrix peak, AMD published
 METRIC = "effective KV-read HBM GB/s (% of MI355X peak) + decode tokens/s, paged attention"
 SHARED_PREFIX_PARTITION = 1024
+# time a step's slot write and decode as two launches (paged_kv_write, then
+# paged_decode_attention) instead of paged_decode_step (--unfused-step)
+UNFUSED_STEP = False
 COLD_FLUSH_BYTES = 1 << 30   # > L2 (4 MiB per XCD) + MALL (256 MiB)
 STREAM_READ_BYTES = 2 << 30  # contiguous buffer of the streaming-read yardstick
 # parity bars on outputs in the cache dtype (max |gpu - oracle|)
@@ -276,13 +279,23 @@ def cpu_record(batch, *, runs: int = 3, one_thread: bool = False, shared_prefix:
 # GPU timing
 
 
+def fused_step(batch, t, shared_prefix: bool = False) -> bool:
+    """Whether a step's slot write rides in the decode launch
+    (paged_decode_step): a batch with new tokens, 16-bit caches, head_dim 128."""
+    return ("slots" in t and batch.cache_dtype in ("f16", "bf16") and batch.head_dim == 128
+            and not shared_prefix and not UNFUSED_STEP)
+
+
 def make_calls(batch, t, partition_size: int, out, ws, shared_prefix: bool = False):
-    """(write, decode) closures of one step on the current stream."""
+    """(write, decode) closures of one step on the current stream; with the
+    fused step the write is part of the decode call and ``write`` does
+    nothing."""
     import torch
 
     import paged_kv_decode_13_amd as pkv
 
-    has_write = "slots" in t
+    fused = fused_step(batch, t, shared_prefix)
+    has_write = "slots" in t and not fused
     quant = batch.cache_dtype == "e4m3"
     ptab = None
     if shared_prefix:
@@ -296,7 +309,12 @@ def make_calls(batch, t, partition_size: int, out, ws, shared_prefix: bool = Fal
             pkv.paged_kv_write(t["nk"], t["nv"], t["kc"], t["vc"], t["slots"])
 
     def decode():
-        if quant:
+        if fused:
+            pkv.paged_decode_step(t["q"], t["kc"], t["vc"], t["nk"], t["nv"], t["slots"], t["bt"],
+                                  t["cl"], batch.block_size, batch.scale,
+                                  max_context_len=batch.max_context_len,
+                                  partition_size=partition_size, out=out, workspace=ws)
+        elif quant:
             pkv.paged_decode_attention_fp8(
                 t["q"], t["kc"], t["vc"], t["ks"], t["vs"], t["bt"], t["cl"], batch.block_size,
                 batch.scale, max_context_len=batch.max_context_len,
@@ -887,7 +905,12 @@ def main() -> int:
                     help="skip timing the step replayed from a captured HIP graph")
     ap.add_argument("--no-parity", action="store_true",
                     help="skip the headline's oracle comparison (profiling runs)")
+    ap.add_argument("--unfused-step", action="store_true",
+                    help="time a step's slot write and decode as two launches instead of "
+                         "paged_decode_step")
     args = ap.parse_args()
+    global UNFUSED_STEP
+    UNFUSED_STEP = bool(args.unfused_step)
 
     if args.gpus != 1:
         print(f"bench.py measures the decode path on one GPU; --gpus {args.gpus} is not "
@@ -981,6 +1004,9 @@ def main() -> int:
     if shared:
         kernel = ("paged_prefix_decode_attention call (prefix units and suffix decode in one "
                   "kernel + log-sum-exp merge)")
+    elif fused_step(batch, t):
+        kernel = "paged_decode_step call (decode kernel with the slot write" + (
+            " + log-sum-exp merge)" if ps and batch.max_context_len > ps else ")")
     else:
         kernel = "paged_decode_attention call (decode kernel" + (
             " + log-sum-exp merge)" if ps and batch.max_context_len > ps else ")")
@@ -1015,6 +1041,11 @@ def main() -> int:
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s": round(batch.num_seqs / step_s, 1),
         "kv_bytes_logical": kv_bytes,
+        "step_entry_point": ("paged_decode_step" if fused_step(batch, t, shared) else
+                             ("paged_kv_write + " if "slots" in t else "") +
+                             ("paged_prefix_decode_attention" if shared else
+                              "paged_decode_attention_fp8" if batch.cache_dtype == "e4m3" else
+                              "paged_decode_attention")),
         "write_ms": round(r["write_ms"], 5),
         "decode_ms": round(r["decode_ms"], 5),
         "decode_ms_median": round(r["decode_ms_median"], 5),

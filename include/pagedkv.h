@@ -163,6 +163,46 @@ pkv_status paged_decode_attention(
     void *stream);
 
 /*
+ * paged_decode_step -- one decode step in one launch: the slot write of
+ * each sequence's new token and the decode attention over the history that
+ * ends with it.
+ *
+ * [P2] section "PagedAttention 如何接入 mini vLLM": a decode step writes the
+ * current token's K/V through its slot, then attends over the sequence's
+ * history through the block table; section "写入 slot 和读取 block table 必须
+ * 一致": the slot written is the place the attention reads that token from.
+ * The result is paged_kv_write(new_key, new_value, ..., slot_mapping,
+ * num_seqs) followed by paged_decode_attention, under one condition: a
+ * non-negative slot_mapping[s] must be the slot of position
+ * context_lens[s] - 1 of sequence s (block_tables[s][(ctx - 1) /
+ * block_size] * block_size + (ctx - 1) % block_size), the position the
+ * step appends.  The kernel then reads that token from new_key/new_value
+ * while it stores them, so the launch needs no ordering between the store
+ * and the reads.  A sequence whose slot is another (or out of range, or
+ * whose context is empty) gets NaN outputs and its rows are not stored; a
+ * negative slot stores nothing and attends over the history as it is.
+ *
+ *   new_key,
+ *   new_value     [num_seqs, num_kv_heads, head_dim]  dtype  (read)
+ *   slot_mapping  [num_seqs] int64 (device)
+ *   key_cache,
+ *   value_cache   written at the valid slots
+ *   other arguments as paged_decode_attention.
+ * Supported: dtype PKV_F16 or PKV_BF16 (out_dtype dtype or PKV_F32),
+ * head_dim 128, block_size in {4, 8, 16, 32, 64}, G in {1, 2, 4, 8},
+ * num_seqs <= PKV_MAX_SEQS; else PKV_ERR_UNSUPPORTED (use paged_kv_write
+ * and paged_decode_attention).  Slots of different sequences must differ.
+ */
+pkv_status paged_decode_step(
+    void *out, const void *query, void *key_cache, void *value_cache,
+    const void *new_key, const void *new_value, const int64_t *slot_mapping,
+    const int32_t *block_tables, const int32_t *context_lens, int32_t num_seqs,
+    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t max_blocks_per_seq, int64_t num_blocks, int32_t max_context_len,
+    float scale, int32_t partition_size, pkv_dtype dtype, pkv_dtype out_dtype,
+    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * paged_decode_attention_noalloc -- paged_decode_attention for callers that
  * cannot allocate device memory or pass a workspace: code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation.  It calls

@@ -44,6 +44,7 @@ import os
 __all__ = [
     "paged_kv_write",
     "paged_decode_attention",
+    "paged_decode_step",
     "paged_decode_workspace_size",
     "paged_prefix_decode_attention",
     "paged_prefix_decode_workspace_size",
@@ -100,6 +101,9 @@ def _load():
                                            i32, ctypes.c_float, i32, ctypes.c_int, ctypes.c_int,
                                            p, sz, p]
     lib.paged_decode_attention.restype = ctypes.c_int
+    lib.paged_decode_step.argtypes = [p, p, p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i64,
+                                      i32, ctypes.c_float, i32, ctypes.c_int, ctypes.c_int, p, sz, p]
+    lib.paged_decode_step.restype = ctypes.c_int
     lib.paged_prefix_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     lib.paged_prefix_decode_workspace_size.restype = sz
     lib.paged_prefix_decode_attention.argtypes = [p, p, p, p, p, i32, p, p, i32, i32, i32, i32, i32,
@@ -262,6 +266,62 @@ def paged_decode_attention(query, key_cache, value_cache, block_tables, context_
         _dtype_code(odt), ws_ptr, ws_bytes, _stream_handle(query.device))
     if st != 0:
         raise PagedKVError(st, "paged_decode_attention")
+    return out
+
+
+def paged_decode_step(query, key_cache, value_cache, new_key, new_value, slot_mapping, block_tables,
+                      context_lens, block_size: int, scale: float, *, max_context_len: int,
+                      partition_size: int = 0, out=None, out_dtype=None, workspace=None):
+    """One decode step in one launch: sequence s's new K/V rows
+    ``new_key[s]``/``new_value[s]`` ([num_kv_heads, head_dim]) are stored at
+    ``slot_mapping[s]`` (int64; negative: none), which must be the slot of
+    its position ``context_lens[s] - 1``, and ``query`` attends over the
+    history including them: the result of ``paged_kv_write`` then
+    ``paged_decode_attention``.  A sequence whose slot is not that position's
+    gets NaN and its rows are not stored.  16-bit caches, head_dim 128."""
+    torch = _torch()
+    lib = _load()
+    for t, n in ((query, "query"), (key_cache, "key_cache"), (value_cache, "value_cache"),
+                 (new_key, "new_key"), (new_value, "new_value"), (slot_mapping, "slot_mapping"),
+                 (block_tables, "block_tables"), (context_lens, "context_lens")):
+        _gpu(t, n)
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    if slot_mapping.dtype != torch.int64:
+        raise TypeError("slot_mapping must be int64")
+    nb, bs, kvh, d = key_cache.shape
+    if bs != block_size:
+        raise ValueError("block_size does not match key_cache.shape[1]")
+    b, h, dq = query.shape
+    if dq != d or value_cache.shape != key_cache.shape:
+        raise ValueError("inconsistent shapes")
+    if block_tables.dim() != 2 or block_tables.shape[0] != b or tuple(context_lens.shape) != (b,):
+        raise ValueError("block_tables must be [num_seqs, max_blocks], context_lens [num_seqs]")
+    if tuple(new_key.shape) != (b, kvh, d) or new_value.shape != new_key.shape:
+        raise ValueError("new_key/new_value must be [num_seqs, num_kv_heads, head_dim]")
+    if tuple(slot_mapping.shape) != (b,):
+        raise ValueError("slot_mapping must be [num_seqs]")
+    if not (query.dtype == key_cache.dtype == value_cache.dtype == new_key.dtype == new_value.dtype):
+        raise TypeError("query, new rows and caches must share one dtype")
+    dt = _dtype_code(query.dtype)
+    odt = query.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((b, h, d), dtype=odt, device=query.device)
+    else:
+        _gpu(out, "out")
+        if tuple(out.shape) != (b, h, d):
+            raise ValueError("out must be [num_seqs, num_heads, head_dim]")
+        odt = out.dtype
+    need = paged_decode_workspace_size(b, h, d, int(max_context_len), int(partition_size))
+    ws_ptr, ws_bytes = _workspace(need, workspace, query.device)
+    st = lib.paged_decode_step(
+        out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+        new_key.data_ptr(), new_value.data_ptr(), slot_mapping.data_ptr(), block_tables.data_ptr(),
+        context_lens.data_ptr(), b, h, kvh, d, bs, block_tables.shape[1], nb, int(max_context_len),
+        float(scale), int(partition_size), dt, _dtype_code(odt), ws_ptr, ws_bytes,
+        _stream_handle(query.device))
+    if st != 0:
+        raise PagedKVError(st, "paged_decode_step")
     return out
 
 

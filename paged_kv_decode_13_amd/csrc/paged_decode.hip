@@ -330,6 +330,15 @@ hipError_t launch_paged_decode_e4m3(const DecodeArgs &a, int dtype, hipStream_t 
     return hipErrorInvalidValue;
 }
 
+hipError_t launch_paged_decode_step(const DecodeArgs &a, int dtype, hipStream_t stream) {
+    if ((int64_t)a.num_seqs * a.num_kv_heads * a.num_partitions == 0) return hipSuccess;
+    hipError_t e = launch_paged_decode_mfma_write(a, dtype, stream);
+    if (e != hipSuccess) return e;
+    if (dtype == kBF16) return launch_merge<kBF16, 128>(a, stream);
+    if (dtype == kF16) return launch_merge<kF16, 128>(a, stream);
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_paged_decode(const DecodeArgs &a, int dtype, int head_dim, hipStream_t stream) {
     if ((int64_t)a.num_seqs * a.num_kv_heads * a.num_partitions == 0) return hipSuccess;
     switch (dtype) {

@@ -435,9 +435,12 @@ struct DecodeLds {
 // kernel provides (s_dyn: ints run prefix [B + 1], whole-partition prefix
 // [B + 1], lengths [B], then the tail list, B 16-bit sequence indices);
 // drawers = the launch's workgroups that draw units.
-template <int DT, int G, bool PFX, bool KV8, bool RUNS>
+// W: the decode step's slot write is part of the launch (see the new-token
+// block in the unit loop).
+template <int DT, int G, bool PFX, bool KV8, bool RUNS, bool W = false>
 __device__ __forceinline__ void decode_body(const DecodeArgs &a, int *s_dyn,
                                             DecodeLds<G, qop_in_lds<KV8>()> &L, int drawers) {
+    static_assert(!W || (!PFX && !KV8), "the fused slot write serves the plain 16-bit decode");
     constexpr int D = 128;
     constexpr int ROW_BYTES = D * 2;
     constexpr int TILE = 16;
@@ -502,6 +505,40 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, int *s_dyn,
                 // every wave of the unit holds the same operand: wave 0 parks
                 // it before the segment loop's first barrier
                 if (kQopLds && wave == 0) s_qop[j][lane] = qop[j];
+            }
+        }
+
+        // The decode step's new token (W): the unit whose range holds its
+        // sequence's position ctx - 1 stores the new K and V rows of its KV
+        // head at the slot, and reads that token from the new rows instead
+        // of the pool (no other unit reads those bytes, so the launch needs
+        // no ordering between the store and the reads).  A slot that is not
+        // the table's slot of ctx - 1 makes the sequence NaN and is not
+        // written.
+        int nt = -1;  // position of the new token this unit holds, or -1
+        const char *nk_row = nullptr, *nv_row = nullptr;
+        if constexpr (W) {
+            const int pos = u.ctx - 1;
+            if (!u.bad_len && pos >= u.tok_begin && pos < u.tok_end) {
+                const int64_t slot = a.slot_mapping[u.s];
+                if (slot >= 0) {
+                    const int32_t pb = a.block_tables[(int64_t)u.s * a.max_blocks_per_seq + (pos >> lbs)];
+                    const bool ok = pb >= 0 && (int64_t)pb < a.num_blocks &&
+                                    slot == (int64_t)pb * bs + (pos & (bs - 1));
+                    if (ok) {
+                        nt = pos;
+                        const int64_t row = ((int64_t)u.s * a.num_kv_heads + u.kvh) * KV_ROW;
+                        nk_row = reinterpret_cast<const char *>(a.new_key) + row;
+                        nv_row = reinterpret_cast<const char *>(a.new_value) + row;
+                        if (wave == 0 && q == 0) {  // 16 lanes: 16-byte chunk c of each row
+                            const int64_t dst = slot * tok_stride + (int64_t)u.kvh * KV_ROW + c * KV_CHUNK;
+                            store16(const_cast<char *>(kbase) + dst, load16(nk_row + c * KV_CHUNK));
+                            store16(const_cast<char *>(vbase) + dst, load16(nv_row + c * KV_CHUNK));
+                        }
+                    } else if (tid == 0) {
+                        s_bad = 1;
+                    }
+                }
             }
         }
 
@@ -708,6 +745,24 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, int *s_dyn,
                     load_k(r[i], t + i * TILE);
                     load_v(r[i], t + i * TILE);
                 }
+                if constexpr (W) {
+                    if (nt >= t && nt < t + TPS * TILE) {  // the step holding the new token
+                        const int d = nt - t;
+                        const int ti = d >> 4, qn = (d >> 2) & 3, rn = d & 3;
+                        if (q == qn) {  // the lanes holding it: rows from the new K/V
+                            const u32x4 kk = load16(nk_row + c * KV_CHUNK);
+                            const u32x4 vv = load16(nv_row + c * KV_CHUNK);
+#pragma unroll
+                            for (int i = 0; i < TPS; ++i)
+#pragma unroll
+                                for (int rr = 0; rr < 4; ++rr)
+                                    if (i == ti && rr == rn) {
+                                        r[i].k[rr] = kk;
+                                        r[i].v[rr] = vv;
+                                    }
+                        }
+                    }
+                }
                 // keep every load of the step ahead of the compute
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -767,12 +822,12 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, int *s_dyn,
     }
 }
 
-template <int DT, int G, bool PFX, bool KV8, bool RUNS>
+template <int DT, int G, bool PFX, bool KV8, bool RUNS, bool W = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PKV_DECODE_MIN_WAVES, 8)))
 void paged_decode_mfma_kernel(DecodeArgs a) {
     extern __shared__ int s_dyn[];
     __shared__ DecodeLds<G, qop_in_lds<KV8>()> lds;
-    decode_body<DT, G, PFX, KV8, RUNS>(a, s_dyn, lds, gridDim.x);
+    decode_body<DT, G, PFX, KV8, RUNS, W>(a, s_dyn, lds, gridDim.x);
 }
 
 // Shared-prefix decode in one launch: workgroups [0, prefix_wgs) each run one
@@ -877,20 +932,20 @@ static hipError_t launch_persistent(K kernel, const DecodeArgs &a, hipStream_t s
 // The kernels with the whole-run path (RUNS) are a second instantiation:
 // compiled into the ordinary one it cost the GQA E4M3 and shared-prefix
 // calls 0.7-2 us through register pressure.
-template <int DT, int G, bool PFX, bool KV8>
+template <int DT, int G, bool PFX, bool KV8, bool W = false>
 static hipError_t launch_runs(const DecodeArgs &a, hipStream_t stream) {
     if (a.unit_parts == kNumWaves)
-        return launch_persistent(paged_decode_mfma_kernel<DT, G, PFX, KV8, true>, a, stream);
-    return launch_persistent(paged_decode_mfma_kernel<DT, G, PFX, KV8, false>, a, stream);
+        return launch_persistent(paged_decode_mfma_kernel<DT, G, PFX, KV8, true, W>, a, stream);
+    return launch_persistent(paged_decode_mfma_kernel<DT, G, PFX, KV8, false, W>, a, stream);
 }
 
-template <int DT, bool PFX, bool KV8 = false>
+template <int DT, bool PFX, bool KV8 = false, bool W = false>
 static hipError_t launch_group(const DecodeArgs &a, hipStream_t stream) {
     switch (a.num_heads / a.num_kv_heads) {
-        case 1: return launch_runs<DT, 1, PFX, KV8>(a, stream);
-        case 2: return launch_runs<DT, 2, PFX, KV8>(a, stream);
-        case 4: return launch_runs<DT, 4, PFX, KV8>(a, stream);
-        case 8: return launch_runs<DT, 8, PFX, KV8>(a, stream);
+        case 1: return launch_runs<DT, 1, PFX, KV8, W>(a, stream);
+        case 2: return launch_runs<DT, 2, PFX, KV8, W>(a, stream);
+        case 4: return launch_runs<DT, 4, PFX, KV8, W>(a, stream);
+        case 8: return launch_runs<DT, 8, PFX, KV8, W>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -898,6 +953,12 @@ static hipError_t launch_group(const DecodeArgs &a, hipStream_t stream) {
 hipError_t launch_paged_decode_mfma(const DecodeArgs &a, int dtype, hipStream_t stream) {
     if (dtype == kBF16) return launch_group<kBF16, false>(a, stream);
     if (dtype == kF16) return launch_group<kF16, false>(a, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_paged_decode_mfma_write(const DecodeArgs &a, int dtype, hipStream_t stream) {
+    if (dtype == kBF16) return launch_group<kBF16, false, false, true>(a, stream);
+    if (dtype == kF16) return launch_group<kF16, false, false, true>(a, stream);
     return hipErrorInvalidValue;
 }
 

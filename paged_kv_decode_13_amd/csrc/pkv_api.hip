@@ -309,6 +309,37 @@ pkv_status paged_decode_attention(void *out, const void *query, const void *key_
     return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
+pkv_status paged_decode_step(void *out, const void *query, void *key_cache, void *value_cache,
+                             const void *new_key, const void *new_value, const int64_t *slot_mapping,
+                             const int32_t *block_tables, const int32_t *context_lens, int32_t num_seqs,
+                             int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+                             int32_t max_context_len, float scale, int32_t partition_size,
+                             pkv_dtype dtype, pkv_dtype out_dtype, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+    pkv::DecodeArgs a;
+    bool empty = false;
+    pkv_status st = decode_setup(a, empty, false, out, query, key_cache, value_cache, nullptr, nullptr,
+                                 block_tables, context_lens, num_seqs, num_heads, num_kv_heads,
+                                 head_dim, block_size, max_blocks_per_seq, num_blocks,
+                                 max_context_len, scale, partition_size, dtype, out_dtype);
+    if (st != PKV_OK) return st;
+    if (dtype == PKV_F32 || head_dim != 128) return PKV_ERR_UNSUPPORTED;
+    if (empty) return PKV_OK;
+    if (!new_key || !new_value || !slot_mapping) return PKV_ERR_NULL;
+    if (!aligned16(new_key) || !aligned16(new_value)) return PKV_ERR_ALIGN;
+    st = check_workspace(workspace, workspace_bytes, a.num_partitions,
+                         paged_decode_workspace_size(num_seqs, num_heads, head_dim, max_context_len,
+                                                     partition_size));
+    if (st != PKV_OK) return st;
+    bind_workspace(a, workspace, head_dim);
+    a.new_key = new_key;
+    a.new_value = new_value;
+    a.slot_mapping = slot_mapping;
+    hipError_t e = pkv::launch_paged_decode_step(a, (int)dtype, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
 pkv_status paged_decode_attention_noalloc(void *out, const void *query, const void *key_cache,
                                           const void *value_cache, const int32_t *block_tables,
                                           const int32_t *context_lens, int32_t num_seqs,

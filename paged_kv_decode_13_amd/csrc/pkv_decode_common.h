@@ -427,6 +427,9 @@ __device__ __forceinline__ void merge_early(const DecodeArgs &a, const EarlyPart
 // (a.work_counter == nullptr; one partition per sequence only) the grid is
 // one workgroup per (sequence, KV head).
 hipError_t launch_paged_decode_mfma(const DecodeArgs &a, int dtype, hipStream_t stream);
+// The same with the decode step's slot write in the launch (a.new_key,
+// a.new_value, a.slot_mapping set; see DecodeArgs).
+hipError_t launch_paged_decode_mfma_write(const DecodeArgs &a, int dtype, hipStream_t stream);
 // The same over E4M3 caches with per-KV-head scales (DT: query and output).
 hipError_t launch_paged_decode_mfma_e4m3(const DecodeArgs &a, int dtype, hipStream_t stream);
 // The same over tokens [token_begin, ctx), partials only (shared-prefix path).

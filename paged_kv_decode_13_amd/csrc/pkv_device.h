@@ -89,6 +89,8 @@ __device__ __forceinline__ u32x4 load16(const void *p) {
     return *reinterpret_cast<const u32x4 *>(p);
 }
 
+__device__ __forceinline__ void store16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
+
 // Streaming 16-byte load: the KV history is read once per step, so it is
 // marked non-temporal to keep it from displacing reused lines.
 __device__ __forceinline__ u32x4 load16_stream(const void *p) {

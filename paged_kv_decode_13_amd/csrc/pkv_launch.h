@@ -68,6 +68,13 @@ struct DecodeArgs {
                                 // the suffix epilogue stores out (no merge)
     const float *k_scale;       // [KVH] E4M3 caches only: cached K = code * k_scale
     const float *v_scale;       // [KVH]
+    // The decode step's slot write fused into the decode (16-bit caches):
+    // sequence s's new row new_key/new_value[s] ([KVH, D]) goes to slot
+    // slot_mapping[s] (negative: none), which must be the slot of position
+    // ctx - 1; key_cache / value_cache are then written.  nullptr: no write.
+    const void *new_key;
+    const void *new_value;
+    const int64_t *slot_mapping;
 };
 
 // Waves per workgroup of the decode kernels, and page ids staged in LDS at a
@@ -150,6 +157,9 @@ hipError_t launch_kv_write_e4m3(const WriteE4M3Args &a, int src_dtype, hipStream
 // dtype: 0 f32, 1 f16, 2 bf16.  Launches the decode kernel and, when
 // num_partitions > 1, the log-sum-exp merge.
 hipError_t launch_paged_decode(const DecodeArgs &a, int dtype, int head_dim, hipStream_t stream);
+// The decode step with its slot write in the decode launch (16-bit caches,
+// head_dim 128; a.new_key, a.new_value, a.slot_mapping set), then the merge.
+hipError_t launch_paged_decode_step(const DecodeArgs &a, int dtype, hipStream_t stream);
 
 // Decode over E4M3 caches (head_dim 128; dtype of query and output: f16 or
 // bf16), then the merge when the context is split.

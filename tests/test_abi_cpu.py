@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
                           "paged_decode_attention", "paged_prefix_decode_workspace_size",
                           "paged_prefix_decode_attention", "paged_kv_write_fp8",
                           "paged_decode_attention_fp8", "paged_prefill_attention",
-                          "paged_decode_attention_noalloc", "pkv_status_string"}
+                          "paged_decode_attention_noalloc", "paged_decode_step", "pkv_status_string"}
     out = subprocess.run(["nm", "-D", "--defined-only", lib._name], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
@@ -105,6 +105,32 @@ def test_decode_validation(lib):
     # one needs it for the partials, whatever the partition count
     assert _decode(lib, ps=512, maxc=513, ws=None) == WORKSPACE
     assert _decode(lib, b=0, q=None) == OK  # empty batch: nothing launched
+
+
+def _step(lib, **kw):
+    a = dict(out=A, q=A, kc=A, vc=A, nk=A, nv=A, sm=A, bt=A, cl=A, b=4, h=32, kvh=8, d=128, bs=16,
+             mb=64, nb=1000, maxc=1024, scale=0.088, ps=0, dt=BF16, odt=BF16, ws=None, wsb=0)
+    a.update(kw)
+    return lib.paged_decode_step(a["out"], a["q"], a["kc"], a["vc"], a["nk"], a["nv"], a["sm"], a["bt"],
+                                 a["cl"], a["b"], a["h"], a["kvh"], a["d"], a["bs"], a["mb"], a["nb"],
+                                 a["maxc"], a["scale"], a["ps"], a["dt"], a["odt"], a["ws"], a["wsb"],
+                                 None)
+
+
+def test_decode_step_validation(lib):
+    # the decode's own checks come first, then the fused write's
+    assert _step(lib, b=-1) == SHAPE
+    assert _step(lib, h=30) == SHAPE
+    assert _step(lib, dt=5) == DTYPE
+    assert _step(lib, bs=12) == UNSUP
+    assert _step(lib, dt=F32, odt=F32) == UNSUP  # the fused write serves 16-bit caches
+    assert _step(lib, d=64) == UNSUP
+    assert _step(lib, q=None) == NULL
+    assert _step(lib, nk=None) == NULL
+    assert _step(lib, sm=None) == NULL
+    assert _step(lib, nv=A + 4) == ALIGN
+    assert _step(lib, ps=512, ws=None) == WORKSPACE
+    assert _step(lib, b=0, q=None, nk=None) == OK  # empty batch: nothing launched
 
 
 def _noalloc(lib, **kw):
