@@ -350,11 +350,13 @@ def workspace_for(batch, partition_size: int, shared_prefix: bool, dev):
 
 def time_steps(batch, t, partition_size: int, steps: int, warmup: int, shared_prefix: bool = False,
                cold_steps: int = 0, graph: bool = False, warm_s: float = 0.0):
-    """Eager steps (write + decode) with HIP events around each part, after
-    ``warmup`` untimed steps (and, with warm_s > 0, untimed steps until that
-    many seconds have passed); then, optionally, the step captured in a HIP
-    graph and replayed (events around each replay, and the back-to-back
-    rate), and cold steps (a 1 GiB read-modify-write before each)."""
+    """``steps`` eager steps (write + decode) timed back to back between two
+    events, after ``warmup`` untimed steps (and, with warm_s > 0, untimed
+    steps until that many seconds have passed); the same steps again with
+    HIP events around each part (per-call medians and p99); then,
+    optionally, the step captured in a HIP graph and replayed (events around
+    each replay, and the back-to-back rate), and cold steps (a 1 GiB
+    read-modify-write before each)."""
     import torch
 
     dev = t["q"].device
@@ -376,20 +378,29 @@ def time_steps(batch, t, partition_size: int, steps: int, warmup: int, shared_pr
                 write()
                 decode()
             torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    # The K timed steps run back to back between two events: an event
+    # recorded between kernels costs the stream a few microseconds (two
+    # events with nothing between them read about 5 us apart), so the
+    # per-call events of the medians below ride on a second pass of the same
+    # K steps.
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     start.record()
+    for _ in range(steps):
+        write()
+        decode()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     for e in evs:
         e[0].record()
         write()
         e[1].record()
         decode()
         e[2].record()
-    end.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
     step_ms = [e[0].elapsed_time(e[2]) for e in evs]
     write_ms = [e[0].elapsed_time(e[1]) for e in evs]
     decode_ms = [e[1].elapsed_time(e[2]) for e in evs]
