@@ -110,3 +110,48 @@ def test_step_full_gqa_workload(cuda):
     kc, vc = _oracle_pools(b)
     assert np.array_equal(_bits(t["kc"]), kc.reshape(-1).view(np.uint16))
     assert np.array_equal(_bits(t["vc"]), vc.reshape(-1).view(np.uint16))
+
+
+def test_step_replays_in_graph(cuda):
+    """paged_decode_step captured in a HIP graph and replayed after new
+    queries and new rows were copied in: every replay bit for bit equal to
+    an eager call on the same inputs, pools included."""
+    import torch
+
+    import paged_kv_decode_13_amd as pkv
+
+    b = wl.make_batch([1, 15, 16, 17, 300, 1025, 4000, 2048], num_heads=32, num_kv_heads=8,
+                      head_dim=128, block_size=16, dtype="bf16", seed=78, write_new_token=True)
+    t = upload(b, cuda)
+    out = torch.empty((b.num_seqs, b.num_heads, b.head_dim), dtype=torch.float32, device=cuda)
+    need = pkv.paged_decode_workspace_size(b.num_seqs, b.num_heads, b.head_dim, b.max_context_len, 512)
+    ws = torch.full((max(need, 1),), 255, dtype=torch.uint8, device=cuda)
+
+    def step():
+        pkv.paged_decode_step(t["q"], t["kc"], t["vc"], t["nk"], t["nv"], t["slots"], t["bt"], t["cl"],
+                              b.block_size, b.scale, max_context_len=b.max_context_len,
+                              partition_size=512, out=out, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    for i in range(3):
+        for key, shape in (("q", b.query.shape), ("nk", b.new_key.shape), ("nv", b.new_value.shape)):
+            t[key].copy_(torch.from_numpy(
+                wl.encode(rng.standard_normal(int(np.prod(shape))).astype(np.float32), "bf16")
+                .reshape(shape)).view(torch.bfloat16).to(cuda))
+        step()
+        torch.cuda.synchronize()
+        eager, kc_e, vc_e = out.clone(), t["kc"].clone(), t["vc"].clone()
+        out.fill_(float("nan"))
+        ws.fill_(250 + i)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), i
+        assert torch.equal(t["kc"].view(torch.int16), kc_e.view(torch.int16)), i
+        assert torch.equal(t["vc"].view(torch.int16), vc_e.view(torch.int16)), i
