@@ -281,8 +281,8 @@ def cpu_record(batch, *, runs: int = 3, one_thread: bool = False, shared_prefix:
 
 def fused_step(batch, t, shared_prefix: bool = False) -> bool:
     """Whether a step's slot write rides in the decode launch
-    (paged_decode_step): a batch with new tokens, 16-bit caches, head_dim 128."""
-    return ("slots" in t and batch.cache_dtype in ("f16", "bf16") and batch.head_dim == 128
+    (paged_decode_step): a batch with new tokens and a cache that is not E4M3."""
+    return ("slots" in t and batch.cache_dtype in ("f32", "f16", "bf16")
             and not shared_prefix and not UNFUSED_STEP)
 
 

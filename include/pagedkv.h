@@ -178,9 +178,10 @@ pkv_status paged_decode_attention(
  * block_size] * block_size + (ctx - 1) % block_size), the position the
  * step appends.  The kernel then reads that token from new_key/new_value
  * while it stores them, so the launch needs no ordering between the store
- * and the reads.  A sequence whose slot is another (or out of range, or
- * whose context is empty) gets NaN outputs and its rows are not stored; a
- * negative slot stores nothing and attends over the history as it is.
+ * and the reads.  A sequence whose slot is another one (or out of range)
+ * stores nothing and gets NaN outputs; one whose context is empty stores
+ * nothing and gets zeros, as in paged_decode_attention; a negative slot
+ * stores nothing and attends over the history as it is.
  *
  *   new_key,
  *   new_value     [num_seqs, num_kv_heads, head_dim]  dtype  (read)
@@ -188,10 +189,9 @@ pkv_status paged_decode_attention(
  *   key_cache,
  *   value_cache   written at the valid slots
  *   other arguments as paged_decode_attention.
- * Supported: dtype PKV_F16 or PKV_BF16 (out_dtype dtype or PKV_F32),
- * head_dim 128, block_size in {4, 8, 16, 32, 64}, G in {1, 2, 4, 8},
- * num_seqs <= PKV_MAX_SEQS; else PKV_ERR_UNSUPPORTED (use paged_kv_write
- * and paged_decode_attention).  Slots of different sequences must differ.
+ * Supported: what paged_decode_attention supports (every dtype, head_dim
+ * 64 or 128); errors as there, and PKV_ERR_NULL / PKV_ERR_ALIGN for the
+ * new rows and slots.  Slots of different sequences must differ.
  */
 pkv_status paged_decode_step(
     void *out, const void *query, void *key_cache, void *value_cache,

@@ -278,7 +278,8 @@ def paged_decode_step(query, key_cache, value_cache, new_key, new_value, slot_ma
     its position ``context_lens[s] - 1``, and ``query`` attends over the
     history including them: the result of ``paged_kv_write`` then
     ``paged_decode_attention``.  A sequence whose slot is not that position's
-    gets NaN and its rows are not stored.  16-bit caches, head_dim 128."""
+    gets NaN and its rows are not stored.  The caches, head sizes and
+    groups of ``paged_decode_attention``."""
     torch = _torch()
     lib = _load()
     for t, n in ((query, "query"), (key_cache, "key_cache"), (value_cache, "value_cache"),

@@ -38,7 +38,11 @@
 
 namespace pkv {
 
-template <int DT, int D, int G>
+// W: the decode step's slot write is part of the launch, as in the matrix-core
+// kernel: the unit holding position ctx - 1 stores the new rows of its KV
+// head at a slot that must be that position's, and reads that token from
+// the new rows instead of the pool.
+template <int DT, int D, int G, bool W = false>
 __global__ __launch_bounds__(kThreads) void paged_decode_valu_kernel(DecodeArgs a) {
     using TR = ElemTraits<DT>;
     constexpr int EPL = TR::per16;  // elements per lane per row
@@ -66,6 +70,36 @@ __global__ __launch_bounds__(kThreads) void paged_decode_valu_kernel(DecodeArgs 
     const int tok_begin = up.tok_begin;
     const int tok_end = up.tok_end;
     if (tid == 0) s_bad = 0;
+
+    int nt = -1;  // W: position of the new token this unit holds, or -1
+    const char *nk_row = nullptr, *nv_row = nullptr;
+    if constexpr (W) {
+        const int pos = up.ctx - 1;
+        if (!up.bad_len && pos >= tok_begin && pos < tok_end) {
+            const int64_t slot = a.slot_mapping[up.s];
+            if (slot >= 0) {
+                const int32_t pb =
+                    a.block_tables[(int64_t)up.s * a.max_blocks_per_seq + (pos >> a.log2_block_size)];
+                const bool ok = pb >= 0 && (int64_t)pb < a.num_blocks &&
+                                slot == (int64_t)pb * a.block_size + (pos & (a.block_size - 1));
+                if (ok) {
+                    nt = pos;
+                    const int64_t row = ((int64_t)up.s * a.num_kv_heads + up.kvh) * ROW_BYTES;
+                    nk_row = reinterpret_cast<const char *>(a.new_key) + row;
+                    nv_row = reinterpret_cast<const char *>(a.new_value) + row;
+                    if (wave == 0 && rg == 0) {  // LPR lanes: 16-byte column li of each row
+                        const int64_t dst = (slot * a.num_kv_heads + up.kvh) * ROW_BYTES + li * 16;
+                        store16(reinterpret_cast<char *>(const_cast<void *>(a.key_cache)) + dst,
+                                load16(nk_row + li * 16));
+                        store16(reinterpret_cast<char *>(const_cast<void *>(a.value_cache)) + dst,
+                                load16(nv_row + li * 16));
+                    }
+                } else if (tid == 0) {
+                    s_bad = 1;
+                }
+            }
+        }
+    }
 
     // query rows of the head group, pre-scaled into the exp2 domain
     const int h0 = up.kvh * G;
@@ -119,8 +153,13 @@ __global__ __launch_bounds__(kThreads) void paged_decode_valu_kernel(DecodeArgs 
                     if (ok[i]) {
                         const int64_t row = ((int64_t)pb * bs + (t & (bs - 1))) * a.num_kv_heads + up.kvh;
                         const int64_t byte = row * ROW_BYTES + li * 16;
-                        kr[i] = load16_stream(kbase + byte);
-                        vr[i] = load16_stream(vbase + byte);
+                        if (W && t == nt) {  // the new token: from the new rows
+                            kr[i] = load16(nk_row + li * 16);
+                            vr[i] = load16(nv_row + li * 16);
+                        } else {
+                            kr[i] = load16_stream(kbase + byte);
+                            vr[i] = load16_stream(vbase + byte);
+                        }
                     }
                 }
             }
@@ -248,21 +287,21 @@ __global__ __launch_bounds__(RW * kWave) void lse_merge_rows_kernel(DecodeArgs a
     merge_early<DT, D, 1>(a, e, row * a.num_partitions, seq_units(a, ctx), row * D);
 }
 
-template <int DT, int D, int G>
+template <int DT, int D, int G, bool W>
 static hipError_t launch_valu(const DecodeArgs &a, hipStream_t stream) {
     const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * a.num_partitions;
-    hipLaunchKernelGGL((paged_decode_valu_kernel<DT, D, G>), dim3((unsigned)units), dim3(kThreads), 0,
+    hipLaunchKernelGGL((paged_decode_valu_kernel<DT, D, G, W>), dim3((unsigned)units), dim3(kThreads), 0,
                        stream, a);
     return hipGetLastError();
 }
 
-template <int DT, int D>
+template <int DT, int D, bool W = false>
 static hipError_t launch_valu_group(const DecodeArgs &a, hipStream_t stream) {
     switch (a.num_heads / a.num_kv_heads) {
-        case 1: return launch_valu<DT, D, 1>(a, stream);
-        case 2: return launch_valu<DT, D, 2>(a, stream);
-        case 4: return launch_valu<DT, D, 4>(a, stream);
-        case 8: return launch_valu<DT, D, 8>(a, stream);
+        case 1: return launch_valu<DT, D, 1, W>(a, stream);
+        case 2: return launch_valu<DT, D, 2, W>(a, stream);
+        case 4: return launch_valu<DT, D, 4, W>(a, stream);
+        case 8: return launch_valu<DT, D, 8, W>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -300,22 +339,24 @@ static hipError_t launch_merge(const DecodeArgs &a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int DT>
+// W: the decode step with its slot write (a.new_key, a.new_value,
+// a.slot_mapping set).
+template <int DT, bool W = false>
 static hipError_t launch_dtype(const DecodeArgs &a, int head_dim, hipStream_t stream) {
     hipError_t e;
     if (head_dim == 128 && DT != kF32) {  // 16-bit caches: the matrix-core kernel
-        e = launch_paged_decode_mfma(a, DT, stream);
+        e = W ? launch_paged_decode_mfma_write(a, DT, stream) : launch_paged_decode_mfma(a, DT, stream);
         return e != hipSuccess ? e : launch_merge<DT, 128>(a, stream);
     }
     // binary32 caches or head_dim 64: the VALU kernel, one slot per partition
     DecodeArgs v = a;
     v.unit_parts = 1;
     if (head_dim == 128) {
-        e = launch_valu_group<DT, 128>(v, stream);
+        e = launch_valu_group<DT, 128, W>(v, stream);
         return e != hipSuccess ? e : launch_merge<DT, 128>(v, stream);
     }
     if (head_dim == 64) {
-        e = launch_valu_group<DT, 64>(v, stream);
+        e = launch_valu_group<DT, 64, W>(v, stream);
         return e != hipSuccess ? e : launch_merge<DT, 64>(v, stream);
     }
     return hipErrorInvalidValue;
@@ -330,13 +371,14 @@ hipError_t launch_paged_decode_e4m3(const DecodeArgs &a, int dtype, hipStream_t 
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_paged_decode_step(const DecodeArgs &a, int dtype, hipStream_t stream) {
+hipError_t launch_paged_decode_step(const DecodeArgs &a, int dtype, int head_dim, hipStream_t stream) {
     if ((int64_t)a.num_seqs * a.num_kv_heads * a.num_partitions == 0) return hipSuccess;
-    hipError_t e = launch_paged_decode_mfma_write(a, dtype, stream);
-    if (e != hipSuccess) return e;
-    if (dtype == kBF16) return launch_merge<kBF16, 128>(a, stream);
-    if (dtype == kF16) return launch_merge<kF16, 128>(a, stream);
-    return hipErrorInvalidValue;
+    switch (dtype) {
+        case kF32: return launch_dtype<kF32, true>(a, head_dim, stream);
+        case kF16: return launch_dtype<kF16, true>(a, head_dim, stream);
+        case kBF16: return launch_dtype<kBF16, true>(a, head_dim, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_paged_decode(const DecodeArgs &a, int dtype, int head_dim, hipStream_t stream) {

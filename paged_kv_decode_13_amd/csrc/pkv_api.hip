@@ -323,9 +323,7 @@ pkv_status paged_decode_step(void *out, const void *query, void *key_cache, void
                                  block_tables, context_lens, num_seqs, num_heads, num_kv_heads,
                                  head_dim, block_size, max_blocks_per_seq, num_blocks,
                                  max_context_len, scale, partition_size, dtype, out_dtype);
-    if (st != PKV_OK) return st;
-    if (dtype == PKV_F32 || head_dim != 128) return PKV_ERR_UNSUPPORTED;
-    if (empty) return PKV_OK;
+    if (st != PKV_OK || empty) return st;
     if (!new_key || !new_value || !slot_mapping) return PKV_ERR_NULL;
     if (!aligned16(new_key) || !aligned16(new_value)) return PKV_ERR_ALIGN;
     st = check_workspace(workspace, workspace_bytes, a.num_partitions,
@@ -336,7 +334,8 @@ pkv_status paged_decode_step(void *out, const void *query, void *key_cache, void
     a.new_key = new_key;
     a.new_value = new_value;
     a.slot_mapping = slot_mapping;
-    hipError_t e = pkv::launch_paged_decode_step(a, (int)dtype, reinterpret_cast<hipStream_t>(stream));
+    hipError_t e =
+        pkv::launch_paged_decode_step(a, (int)dtype, head_dim, reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 

@@ -157,9 +157,10 @@ hipError_t launch_kv_write_e4m3(const WriteE4M3Args &a, int src_dtype, hipStream
 // dtype: 0 f32, 1 f16, 2 bf16.  Launches the decode kernel and, when
 // num_partitions > 1, the log-sum-exp merge.
 hipError_t launch_paged_decode(const DecodeArgs &a, int dtype, int head_dim, hipStream_t stream);
-// The decode step with its slot write in the decode launch (16-bit caches,
-// head_dim 128; a.new_key, a.new_value, a.slot_mapping set), then the merge.
-hipError_t launch_paged_decode_step(const DecodeArgs &a, int dtype, hipStream_t stream);
+// The decode step with its slot write in the decode launch (a.new_key,
+// a.new_value, a.slot_mapping set), then the merge; the kernels of
+// launch_paged_decode.
+hipError_t launch_paged_decode_step(const DecodeArgs &a, int dtype, int head_dim, hipStream_t stream);
 
 // Decode over E4M3 caches (head_dim 128; dtype of query and output: f16 or
 // bf16), then the merge when the context is split.

@@ -123,8 +123,10 @@ def test_decode_step_validation(lib):
     assert _step(lib, h=30) == SHAPE
     assert _step(lib, dt=5) == DTYPE
     assert _step(lib, bs=12) == UNSUP
-    assert _step(lib, dt=F32, odt=F32) == UNSUP  # the fused write serves 16-bit caches
-    assert _step(lib, d=64) == UNSUP
+    assert _step(lib, d=96) == UNSUP
+    # binary32 caches and head_dim 64 reach the fused write's own checks
+    assert _step(lib, dt=F32, odt=F32, nk=None) == NULL
+    assert _step(lib, d=64, nv=A + 4) == ALIGN
     assert _step(lib, q=None) == NULL
     assert _step(lib, nk=None) == NULL
     assert _step(lib, sm=None) == NULL

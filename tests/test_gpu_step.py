@@ -65,13 +65,41 @@ def test_step_matches_write_then_decode(cuda, dtype, bs, group):
         assert np.array_equal(_bits(t["vc"]), vc_ref.reshape(-1).view(np.uint16)), ps
 
 
+VALU_CASES = [("f32", 128, 16, 1), ("f32", 128, 4, 8), ("f32", 64, 64, 4), ("f16", 64, 16, 8),
+              ("bf16", 64, 8, 2)]
+
+
+@pytest.mark.parametrize("dtype,dim,bs,group", VALU_CASES,
+                         ids=[f"{a}-d{b}-bs{c}-g{d}" for a, b, c, d in VALU_CASES])
+def test_step_vector_kernel(cuda, dtype, dim, bs, group):
+    """The step on the caches the vector-ALU kernel serves (binary32, or
+    head_dim 64): the same boundary lengths, the unsplit grid without a
+    workspace and split partitions, outputs against the oracle's
+    write-then-decode and the pools byte for byte."""
+    import paged_kv_decode_13_amd as pkv
+
+    lens = [1, bs - 1, bs, bs + 1, 3 * bs + 1, 0, 137, 700, 2100]
+    b = wl.make_batch(lens, num_heads=2 * group, num_kv_heads=2, head_dim=dim, block_size=bs,
+                      dtype=dtype, seed=4100 + dim + bs * 3 + group, write_new_token=True)
+    print(f"\n[step] {dtype} d={dim} bs={bs} G={group}", flush=True)
+    ref = oracle_step(b)
+    kc_ref, vc_ref = _oracle_pools(b)
+    for ps, ws in ((0, pkv.NO_WORKSPACE), (128 if bs <= 64 else bs, None), (512, None)):
+        t = upload(b, cuda)
+        out = to_f64(_step(b, t, partition_size=ps, workspace=ws))
+        assert max_err(out, ref) <= TIGHT[dtype], (ps, ws)
+        assert np.array_equal(_bits(t["kc"]), kc_ref.reshape(-1).view(np.uint16)), ps
+        assert np.array_equal(_bits(t["vc"]), vc_ref.reshape(-1).view(np.uint16)), ps
+
+
 def test_step_slot_rules(cuda):
     """A negative slot stores nothing and attends over the history as it
     is; a slot that is not the sequence's position ctx - 1 makes exactly
-    that sequence NaN and is not written; 16-bit outputs."""
+    that sequence NaN and is not written; an empty context with a slot
+    stores nothing and gives zeros; 16-bit outputs."""
     import torch
 
-    lens = [40, 300, 17, 1025]
+    lens = [40, 300, 17, 1025, 0]
     b = wl.make_batch(lens, num_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
                       dtype="bf16", seed=77, write_new_token=True)
     slots = b.slot_mapping.copy()
@@ -82,17 +110,19 @@ def test_step_slot_rules(cuda):
     b.value_cache[s0 // 16, s0 % 16] = b.new_key[0]
     slots[0] = -1
     slots[2] = int(slots[2]) - 1      # sequence 2 points one row early
+    slots[4] = int(slots[1]) + 1      # an empty context given a slot
     t = upload(b, cuda)
     t["slots"] = torch.from_numpy(slots).to(cuda)
     out = to_f64(_step(b, t, partition_size=256))
     # reference: write the valid slots only (sequence 2's is refused), then decode
     ok = slots.copy()
-    ok[2] = -1
+    ok[2] = ok[4] = -1
     kc, vc = _oracle_pools(b, ok)
     ref = oracle.paged_decode(b.query, kc, vc, b.block_tables, b.context_lens, b.block_size,
                               b.scale, b.dtype)
     assert np.isnan(out[2]).all()
-    keep = [0, 1, 3]
+    assert (out[4] == 0).all()
+    keep = [0, 1, 3, 4]
     assert max_err(out[keep], ref[keep]) <= TIGHT["bf16"]
     assert np.array_equal(_bits(t["kc"]), kc.reshape(-1).view(np.uint16))
     assert np.array_equal(_bits(t["vc"]), vc.reshape(-1).view(np.uint16))
