@@ -286,6 +286,16 @@ def fused_step(batch, t, shared_prefix: bool = False) -> bool:
             and not shared_prefix and not UNFUSED_STEP)
 
 
+def step_entry(batch, t, shared_prefix: bool = False) -> str:
+    """The entry point(s) one step calls."""
+    if fused_step(batch, t, shared_prefix):
+        return "paged_decode_step"
+    return (("paged_kv_write + " if "slots" in t else "") +
+            ("paged_prefix_decode_attention" if shared_prefix else
+             "paged_decode_attention_fp8" if batch.cache_dtype == "e4m3" else
+             "paged_decode_attention"))
+
+
 def make_calls(batch, t, partition_size: int, out, ws, shared_prefix: bool = False):
     """(write, decode) closures of one step on the current stream; with the
     fused step the write is part of the decode call and ``write`` does
@@ -603,9 +613,7 @@ def decode_record(batch, dev, *, steps: int, warmup: int, partition_size: int | 
     traffic = load_traffic(traffic_key) if traffic_key else None
     rec = {
         "workload": batch.name,
-        "entry_point": ("paged_prefix_decode_attention" if shared_prefix else
-                        "paged_decode_attention_fp8" if batch.cache_dtype == "e4m3" else
-                        "paged_decode_attention"),
+        "entry_point": step_entry(batch, t, shared_prefix).split(" + ")[-1],
         "num_seqs": batch.num_seqs, "num_heads": batch.num_heads,
         "num_kv_heads": batch.num_kv_heads, "head_dim": batch.head_dim,
         "block_size": batch.block_size, "partition_size": ps,
@@ -1052,11 +1060,7 @@ def main() -> int:
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s": round(batch.num_seqs / step_s, 1),
         "kv_bytes_logical": kv_bytes,
-        "step_entry_point": ("paged_decode_step" if fused_step(batch, t, shared) else
-                             ("paged_kv_write + " if "slots" in t else "") +
-                             ("paged_prefix_decode_attention" if shared else
-                              "paged_decode_attention_fp8" if batch.cache_dtype == "e4m3" else
-                              "paged_decode_attention")),
+        "step_entry_point": step_entry(batch, t, shared),
         "write_ms": round(r["write_ms"], 5),
         "decode_ms": round(r["decode_ms"], 5),
         "decode_ms_median": round(r["decode_ms_median"], 5),

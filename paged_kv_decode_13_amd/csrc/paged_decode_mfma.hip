@@ -516,7 +516,6 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, int *s_dyn,
         // the table's slot of ctx - 1 makes the sequence NaN and is not
         // written.
         int nt = -1;  // position of the new token this unit holds, or -1
-        const char *nk_row = nullptr, *nv_row = nullptr;
         if constexpr (W) {
             const int pos = u.ctx - 1;
             if (!u.bad_len && pos >= u.tok_begin && pos < u.tok_end) {
@@ -527,13 +526,13 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, int *s_dyn,
                                     slot == (int64_t)pb * bs + (pos & (bs - 1));
                     if (ok) {
                         nt = pos;
-                        const int64_t row = ((int64_t)u.s * a.num_kv_heads + u.kvh) * KV_ROW;
-                        nk_row = reinterpret_cast<const char *>(a.new_key) + row;
-                        nv_row = reinterpret_cast<const char *>(a.new_value) + row;
                         if (wave == 0 && q == 0) {  // 16 lanes: 16-byte chunk c of each row
+                            const int64_t src = ((int64_t)u.s * a.num_kv_heads + u.kvh) * KV_ROW + c * KV_CHUNK;
                             const int64_t dst = slot * tok_stride + (int64_t)u.kvh * KV_ROW + c * KV_CHUNK;
-                            store16(const_cast<char *>(kbase) + dst, load16(nk_row + c * KV_CHUNK));
-                            store16(const_cast<char *>(vbase) + dst, load16(nv_row + c * KV_CHUNK));
+                            store16(const_cast<char *>(kbase) + dst,
+                                    load16(reinterpret_cast<const char *>(a.new_key) + src));
+                            store16(const_cast<char *>(vbase) + dst,
+                                    load16(reinterpret_cast<const char *>(a.new_value) + src));
                         }
                     } else if (tid == 0) {
                         s_bad = 1;
@@ -584,21 +583,27 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, int *s_dyn,
             const int64_t page = pb >= 0 ? pb : 0;
             return (page * bs + (t & (bs - 1))) * tok_stride + kvh_off + c * KV_CHUNK;
         };
-        auto load_k = [&](TileRegs &r, int t0) {
+        // Row `alt_row` of the lane's four (if 0..3) is read from `alt`
+        // instead of the pool: the decode step's new token.
+        auto load_k = [&](TileRegs &r, int t0, int alt_row = -1, const char *alt = nullptr) {
             uint32_t unused;
             const char *p = kbase + tile_base(t0, unused);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                if constexpr (KV8) r.k[i] = load8_stream(p + i * tok_stride);
-                else r.k[i] = load16_stream(p + i * tok_stride);
+                const char *pi = p + i * tok_stride;
+                if constexpr (W) pi = i == alt_row ? alt : pi;
+                if constexpr (KV8) r.k[i] = load8_stream(pi);
+                else r.k[i] = load16_stream(pi);
             }
         };
-        auto load_v = [&](TileRegs &r, int t0) {
+        auto load_v = [&](TileRegs &r, int t0, int alt_row = -1, const char *alt = nullptr) {
             const char *p = vbase + tile_base(t0, r.vmask);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                if constexpr (KV8) r.v[i] = load8_stream(p + i * tok_stride);
-                else r.v[i] = load16_stream(p + i * tok_stride);
+                const char *pi = p + i * tok_stride;
+                if constexpr (W) pi = i == alt_row ? alt : pi;
+                if constexpr (KV8) r.v[i] = load8_stream(pi);
+                else r.v[i] = load16_stream(pi);
             }
         };
         // S^T of one tile: K rows -> LDS (16-byte chunks XOR-swizzled by
@@ -740,27 +745,26 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, int *s_dyn,
         auto stream = [&](int t_first, int t_stride) {
             for (int t = t_first; t < seg_end; t += t_stride) {
                 TileRegs r[TPS];
+                if (W && nt >= t && nt < t + TPS * TILE) {
+                    // the step holding the new token: the lanes that hold
+                    // its row read it from new_key/new_value (offsets
+                    // recomputed here, so no pointer stays live across the
+                    // stream)
+                    const int d = nt - t;
+                    const int ti = d >> 4, rn = q == ((d >> 2) & 3) ? d & 3 : -1;
+                    const int64_t src = ((int64_t)u.s * a.num_kv_heads + u.kvh) * KV_ROW + c * KV_CHUNK;
+                    const char *nk = reinterpret_cast<const char *>(a.new_key) + src;
+                    const char *nv = reinterpret_cast<const char *>(a.new_value) + src;
 #pragma unroll
-                for (int i = 0; i < TPS; ++i) {
-                    load_k(r[i], t + i * TILE);
-                    load_v(r[i], t + i * TILE);
-                }
-                if constexpr (W) {
-                    if (nt >= t && nt < t + TPS * TILE) {  // the step holding the new token
-                        const int d = nt - t;
-                        const int ti = d >> 4, qn = (d >> 2) & 3, rn = d & 3;
-                        if (q == qn) {  // the lanes holding it: rows from the new K/V
-                            const u32x4 kk = load16(nk_row + c * KV_CHUNK);
-                            const u32x4 vv = load16(nv_row + c * KV_CHUNK);
+                    for (int i = 0; i < TPS; ++i) {
+                        load_k(r[i], t + i * TILE, i == ti ? rn : -1, nk);
+                        load_v(r[i], t + i * TILE, i == ti ? rn : -1, nv);
+                    }
+                } else {
 #pragma unroll
-                            for (int i = 0; i < TPS; ++i)
-#pragma unroll
-                                for (int rr = 0; rr < 4; ++rr)
-                                    if (i == ti && rr == rn) {
-                                        r[i].k[rr] = kk;
-                                        r[i].v[rr] = vv;
-                                    }
-                        }
+                    for (int i = 0; i < TPS; ++i) {
+                        load_k(r[i], t + i * TILE);
+                        load_v(r[i], t + i * TILE);
                     }
                 }
                 // keep every load of the step ahead of the compute
